@@ -1,0 +1,187 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-head Latent Attention decode
+ * library (libmla.so).
+ *
+ * What it computes.  DeepSeek-V3's MLA, as the DeepSeek-V3 reading lesson
+ * "Читаем техотчёт DeepSeek-V3 вместе" (ai.flicky.cc), section 2.1.1 "MLA: что
+ * попадает в кэш", and the paper summary "Báo cáo Kỹ thuật DeepSeek-V3"
+ * (xyznot.com), "Phương pháp" item 1, state it:
+ *
+ *     c_t^KV = W^DKV h_t,  k_t^R = RoPE(W^KR h_t),  k^C = W^UK c^KV,
+ *     v^C = W^UV c^KV,  key of head i = [k^C_{t,i}; k^R_t],
+ *     c^Q = W^DQ h,  W^UQ c^Q = per head [q^C_i ; q^R_i],  q^R rotated.
+ *
+ * Only c^KV and k^R are cached (§2.1.1 and the summary's closing sentence of
+ * item 1).  At decode W^UK is folded into the query (§2.1.1 Question 2) and
+ * W^UV is applied after the attention-weighted sum of latents (linearity of
+ * v^C = W^UV c^KV).  The attention itself is a scaled softmax over the
+ * visible cached tokens.
+ *
+ * Conventions (the pages leave these open):
+ *   - Weights are row-major [out, in], so y = W x as the formulas write it:
+ *     W_DKV [d_c, d_model], W_KR [d_rope, d_model], W_DQ [d_cq, d_model],
+ *     W_UQ [n_heads*(d_head+d_rope), d_cq] with rows head-major and, within a
+ *     head, d_head content rows then d_rope RoPE rows; W_UK and W_UV
+ *     [n_heads*d_head, d_c] (rows of head i are i*d_head .. i*d_head+d_head-1).
+ *   - RoPE rotates channel pairs (2m, 2m+1) by pos * theta^(-2m/d_rope).
+ *   - Positions are 0-based; token t of a sequence sits at position t.  At
+ *     decode, seqlens[b] already counts the s_q new tokens, query j sits at
+ *     p_j = seqlens[b] - s_q + j and sees tokens 0..p_j (causal).
+ *   - Every pointer argument except `dims`, `cache` (the descriptor itself)
+ *     and the returned strings is DEVICE memory, contiguous, row-major, owned
+ *     by the caller.  The library never allocates or frees and keeps no
+ *     mutable global state; calls on different streams do not interfere.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; nothing synchronises.  Arguments are validated on the host
+ *     before anything is enqueued: on error a negative mla_status is returned
+ *     and nothing is launched.  Device-side metadata (block tables, seqlens,
+ *     positions) is trusted: out-of-range page ids or positions are undefined
+ *     behaviour.
+ *
+ * Cache layout.  Token t of sequence b lives in page block_table[b*max_pages
+ * + t/page_size], slot t%page_size.  A page of an F32 or BF16 cache is
+ * [page_size][d_c + d_rope] elements, each row c^KV (d_c) then k^R (d_rope,
+ * already rotated at the token's position).  A page of an FP8_E4M3 cache is
+ *     codes  u8   [page_size][d_c]          (OCP E4M3FN, max 448)
+ *     scales f32  [page_size][d_c/128]      (one per 1x128 channel tile)
+ *     rope   bf16 [page_size][d_rope]
+ * following the lesson's §3.3 "Обучение в FP8": E4M3 for all tensors, one
+ * scale per 1x128 activation tile.  Scale s = amax/448 (1 for an all-zero
+ * tile), code = round-to-nearest-even(x/s) saturated to +-448, value = code*s.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MLA_API __attribute__((visibility("default")))
+#else
+#define MLA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  MLA_ERR_DIMS = -2,        /* a size is out of range or inconsistent             */
+  MLA_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination     */
+  MLA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                   */
+  MLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
+  MLA_ERR_UNSUPPORTED = -6, /* valid but not implemented for these dims           */
+  MLA_ERR_HIP = -7          /* a HIP runtime call failed while enqueueing         */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2 /* cache only */
+} mla_dtype;
+
+/* Model dimensions (lesson's V3 shape dictionary: d_model 7168, 128 heads of
+ * d_head 128, d_rope 64, d_c 512, d_cq 1536).  page_size is the number of
+ * tokens per cache page.  Limits: all > 0; d_head, d_rope, d_c even;
+ * d_rope <= 128; d_c <= 1024; d_cq <= 4096; d_model <= 16384; n_heads <= 256;
+ * page_size <= 256 and a multiple of 16; for an FP8 cache d_c % 128 == 0.   */
+typedef struct {
+  int32_t d_model, n_heads, d_head, d_rope, d_c, d_cq, page_size;
+  float rope_theta;
+} mla_dims;
+
+/* A caller-owned paged latent cache: `pages` (device) holds `num_pages`
+ * pages of mla_page_bytes(dims, dtype) bytes each.                          */
+typedef struct {
+  void* pages;
+  int32_t dtype;     /* mla_dtype: MLA_F32, MLA_BF16 or MLA_FP8_E4M3 */
+  int32_t num_pages;
+} mla_cache;
+
+/* Bytes of one cache page of `cache_dtype` (0 for invalid arguments).       */
+MLA_API size_t mla_page_bytes(const mla_dims* dims, int32_t cache_dtype);
+
+/* Latent-cache append (lesson §2.1.1 KV equations; summary item 1):
+ * for each of the n_tok rows of h [n_tok, d_model] (dtype act_dtype, F32 or
+ * BF16), computes c^KV = W_DKV h and k^R = RoPE(W_KR h, pos[r]) with fp32
+ * accumulation and stores the row into sequence seq_id[r] at position pos[r]
+ * of the paged cache (converted, or quantised per 1x128 tile for FP8).
+ * seq_id, pos: int32 [n_tok] device.  block_table: int32 [*, max_pages]
+ * device.  W_DKV/W_KR have dtype act_dtype.  n_tok == 0 is a no-op.
+ * BF16 caches require BF16 activations or F32 activations; F32 caches
+ * require F32 activations.                                                  */
+MLA_API int mla_cache_append(const mla_dims* dims, int32_t act_dtype, const void* h,
+                     int32_t n_tok, const int32_t* seq_id, const int32_t* pos,
+                     const void* W_DKV, const void* W_KR, const mla_cache* cache,
+                     const int32_t* block_table, int32_t max_pages,
+                     void* stream);
+
+/* Direct cache write: stores given latent rows c_kv [n_tok, d_c] and already
+ * rotated k_rope [n_tok, d_rope] (dtype act_dtype, F32 or BF16) at
+ * (seq_id[r], pos[r]), converting or quantising exactly as mla_cache_append
+ * does with its fp32 results.  For tests that plant cache contents and for
+ * callers that produce latents elsewhere.                                   */
+MLA_API int mla_cache_write(const mla_dims* dims, int32_t act_dtype, const void* c_kv,
+                    const void* k_rope, int32_t n_tok, const int32_t* seq_id,
+                    const int32_t* pos, const mla_cache* cache,
+                    const int32_t* block_table, int32_t max_pages, void* stream);
+
+/* Number of KV splits mla_decode uses when num_splits == 0: enough
+ * (sequence, split) work items to fill the GPU, never more than max_pages.  */
+MLA_API int32_t mla_default_splits(const mla_dims* dims, int32_t batch, int32_t s_q,
+                           int32_t max_pages);
+
+/* Workspace bytes needed by mla_decode/mla_combine for these sizes
+ * (num_splits >= 1; 0 for invalid arguments).                               */
+MLA_API size_t mla_workspace_bytes(const mla_dims* dims, int32_t act_dtype,
+                           int32_t batch, int32_t s_q, int32_t num_splits);
+
+/* Decode, first half: query projection, absorption and split-KV attention.
+ *   hq [batch*s_q, d_model] (act_dtype): hidden states of the s_q newest
+ *     tokens of each sequence, row b*s_q + j; or, when W_DQ is NULL, their
+ *     compressed queries c^Q [batch*s_q, d_cq] (summary item 1: c^Q).
+ *   W_DQ [d_cq, d_model] or NULL; W_UQ [n_heads*(d_head+d_rope), d_cq];
+ *   W_UK [n_heads*d_head, d_c]  (act_dtype).
+ *   cache, block_table [batch, max_pages], seqlens int32 [batch] (device;
+ *     seqlens[b] >= s_q, or 0 for an empty sequence whose output is 0).
+ *   softmax_scale: tau in softmax(tau * q.k).
+ *   num_splits: KV splits per sequence (1..max_pages, 0 = default).
+ * For each query row, head i and split s it computes, over the split's
+ * visible tokens, the softmax-normalised sum of latents c_t (the absorbed
+ * form: scores tau*(q^C_i^T W^UK_i c_t + q^R_i . k^R_t)) and its
+ * log-sum-exp, and leaves them, with the split plan, in the workspace
+ * ws [ws_bytes >= mla_workspace_bytes(...)] for mla_combine.
+ * Supported: act F32 with an F32 or FP8 cache; act BF16 with a BF16 or FP8
+ * cache.  s_q in 1..8.                                                      */
+MLA_API int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq,
+               int32_t batch, int32_t s_q, const void* W_DQ, const void* W_UQ,
+               const void* W_UK, const mla_cache* cache,
+               const int32_t* block_table, int32_t max_pages,
+               const int32_t* seqlens, float softmax_scale, int32_t num_splits,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Decode, second half: merges the splits that the preceding mla_decode on
+ * this workspace left (log-sum-exp weighted; empty splits skipped), then
+ * applies W^UV per head:
+ *   out [batch, s_q, n_heads, d_head] (act_dtype) = W^UV_i * O_lat_i;
+ *   lse_out [batch, s_q, n_heads] fp32 natural-log log-sum-exp of the scaled
+ *   scores, or NULL.  An empty sequence gives out = 0 and lse = -inf.
+ * batch, s_q, act_dtype and ws must be those of the preceding mla_decode on
+ * the same stream.                                                          */
+MLA_API int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch,
+                int32_t s_q, const void* ws, size_t ws_bytes, const void* W_UV,
+                void* out, float* lse_out, void* stream);
+
+/* Static description of a status code.                                      */
+MLA_API const char* mla_status_str(int status);
+
+/* Library build identifier (kernel set and target), static string.         */
+MLA_API const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,160 @@
+"""ctypes binding of libmla.so (the C ABI declared in include/mla.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of the library.  Torch tensors are accepted for device memory and
+streams; their data pointers are passed straight through.  If the library is
+missing the import fails loudly -- there is no fallback implementation.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+
+MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE = 0, -1, -2, -3
+MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = -4, -5, -6, -7
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+
+EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
+           "mla_workspace_bytes", "mla_decode", "mla_combine", "mla_status_str", "mla_version")
+
+
+class mla_dims(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
+
+
+class mla_cache(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({status_str(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          f"python -m mla_latent_kv_29_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    D = ctypes.POINTER(mla_dims)
+    C = ctypes.POINTER(mla_cache)
+    sig = {
+        "mla_page_bytes": (SZ, [D, I32]),
+        "mla_cache_append": (ctypes.c_int, [D, I32, P, I32, P, P, P, P, C, P, I32, P]),
+        "mla_cache_write": (ctypes.c_int, [D, I32, P, P, I32, P, P, C, P, I32, P]),
+        "mla_default_splits": (I32, [D, I32, I32, I32]),
+        "mla_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
+        "mla_decode": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
+        "mla_combine": (ctypes.c_int, [D, I32, I32, I32, P, SZ, P, P, P, P]),
+        "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "mla_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def status_str(status):
+    return _lib.mla_status_str(int(status)).decode()
+
+
+def version():
+    return _lib.mla_version().decode()
+
+
+def make_dims(d):
+    """mla_dims from a dict with d_model, n_heads, d_head, d_rope, d_c, d_cq,
+    page_size, rope_theta."""
+    return mla_dims(int(d["d_model"]), int(d["n_heads"]), int(d["d_head"]), int(d["d_rope"]),
+                    int(d["d_c"]), int(d["d_cq"]), int(d["page_size"]), float(d["rope_theta"]))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, st):
+    if st != MLA_OK:
+        raise MLAError(fn, st)
+
+
+def mla_page_bytes(dims, cache_dtype):
+    return int(_lib.mla_page_bytes(ctypes.byref(dims), int(cache_dtype)))
+
+
+def mla_default_splits(dims, batch, s_q, max_pages):
+    return int(_lib.mla_default_splits(ctypes.byref(dims), int(batch), int(s_q), int(max_pages)))
+
+
+def mla_workspace_bytes(dims, act_dtype, batch, s_q, num_splits):
+    return int(_lib.mla_workspace_bytes(ctypes.byref(dims), int(act_dtype), int(batch), int(s_q), int(num_splits)))
+
+
+def cache_struct(pages, cache_dtype, num_pages):
+    return mla_cache(ctypes.c_void_p(_ptr(pages)), int(cache_dtype), int(num_pages))
+
+
+def mla_cache_append(dims, act_dtype, h, n_tok, seq_id, pos, W_DKV, W_KR, cache, block_table, max_pages,
+                     stream=None, check=True):
+    st = _lib.mla_cache_append(ctypes.byref(dims), int(act_dtype), _ptr(h), int(n_tok), _ptr(seq_id), _ptr(pos),
+                               _ptr(W_DKV), _ptr(W_KR), ctypes.byref(cache), _ptr(block_table), int(max_pages),
+                               _stream(stream))
+    if check:
+        _check("mla_cache_append", st)
+    return st
+
+
+def mla_cache_write(dims, act_dtype, c_kv, k_rope, n_tok, seq_id, pos, cache, block_table, max_pages,
+                    stream=None, check=True):
+    st = _lib.mla_cache_write(ctypes.byref(dims), int(act_dtype), _ptr(c_kv), _ptr(k_rope), int(n_tok),
+                              _ptr(seq_id), _ptr(pos), ctypes.byref(cache), _ptr(block_table), int(max_pages),
+                              _stream(stream))
+    if check:
+        _check("mla_cache_write", st)
+    return st
+
+
+def mla_decode(dims, act_dtype, hq, batch, s_q, W_DQ, W_UQ, W_UK, cache, block_table, max_pages, seqlens,
+               softmax_scale, num_splits, ws, ws_bytes, stream=None, check=True):
+    st = _lib.mla_decode(ctypes.byref(dims), int(act_dtype), _ptr(hq), int(batch), int(s_q), _ptr(W_DQ),
+                         _ptr(W_UQ), _ptr(W_UK), ctypes.byref(cache), _ptr(block_table), int(max_pages),
+                         _ptr(seqlens), float(softmax_scale), int(num_splits), _ptr(ws), int(ws_bytes),
+                         _stream(stream))
+    if check:
+        _check("mla_decode", st)
+    return st
+
+
+def mla_combine(dims, act_dtype, batch, s_q, ws, ws_bytes, W_UV, out, lse_out=None, stream=None, check=True):
+    st = _lib.mla_combine(ctypes.byref(dims), int(act_dtype), int(batch), int(s_q), _ptr(ws), int(ws_bytes),
+                          _ptr(W_UV), _ptr(out), _ptr(lse_out), _stream(stream))
+    if check:
+        _check("mla_combine", st)
+    return st

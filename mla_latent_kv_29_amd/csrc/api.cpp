@@ -1,0 +1,196 @@
+// C-ABI entry points of libmla.so: argument validation, split planning,
+// workspace layout and dispatch to the kernel launchers.  Nothing here
+// allocates device memory or synchronises.
+#include <stdlib.h>
+#include <string.h>
+#include "internal.hpp"
+
+using namespace mla;
+
+namespace {
+
+constexpr int MAX_S_Q = 8;
+constexpr int TARGET_ITEMS = 512;  // (sequence, row block, split) work items aimed for per decode
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->d_head <= 0 || d->d_rope <= 0 || d->d_c <= 0 || d->d_cq <= 0 ||
+      d->page_size <= 0)
+    return MLA_ERR_DIMS;
+  if ((d->d_head | d->d_rope | d->d_c) & 1) return MLA_ERR_DIMS;
+  if (d->d_rope > 128 || d->d_c > 1024 || d->d_cq > 4096 || d->d_model > 16384 || d->n_heads > 256 ||
+      d->d_head > 512)
+    return MLA_ERR_DIMS;
+  if (d->page_size > 256 || d->page_size % 16) return MLA_ERR_DIMS;
+  if (!(d->rope_theta > 0.0f)) return MLA_ERR_DIMS;
+  return MLA_OK;
+}
+
+bool valid_act(int t) { return t == MLA_F32 || t == MLA_BF16; }
+bool valid_cache(int t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
+
+int check_cache(const mla_dims* d, const mla_cache* c, const int32_t* bt, int32_t max_pages) {
+  if (!c || !c->pages || !bt) return MLA_ERR_NULL;
+  if (!valid_cache(c->dtype)) return MLA_ERR_DTYPE;
+  if (c->dtype == MLA_FP8_E4M3 && d->d_c % 128) return MLA_ERR_UNSUPPORTED;
+  if (c->num_pages <= 0 || max_pages <= 0) return MLA_ERR_DIMS;
+  if (!aligned16(c->pages) || !aligned16(bt)) return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+bool force_generic() {
+  const char* e = getenv("MLA_FORCE_GENERIC");
+  return e && e[0] == '1';
+}
+
+int resolve_splits(const mla_dims* d, int32_t batch, int32_t s_q, int32_t max_pages, int32_t num_splits,
+                   int* S, int* pps) {
+  int s = num_splits > 0 ? num_splits : mla_default_splits(d, batch, s_q, max_pages);
+  if (s > max_pages) s = max_pages;
+  if (s < 1) s = 1;
+  int p = (max_pages + s - 1) / s;
+  *pps = p;
+  *S = (max_pages + p - 1) / p;
+  return MLA_OK;
+}
+
+int append_common(const mla_dims* dims, int32_t act, const void* a0, const void* a1, int32_t n_tok,
+                  const int32_t* seq_id, const int32_t* pos, const void* W_DKV, const void* W_KR,
+                  const mla_cache* cache, const int32_t* bt, int32_t max_pages, void* stream, bool write) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_act(act)) return MLA_ERR_DTYPE;
+  if (n_tok < 0) return MLA_ERR_DIMS;
+  if ((st = check_cache(dims, cache, bt, max_pages))) return st;
+  if (n_tok == 0) return MLA_OK;
+  if (!a0 || !seq_id || !pos) return MLA_ERR_NULL;
+  if (write ? !a1 : (!W_DKV || !W_KR)) return MLA_ERR_NULL;
+  if (!aligned16(a0) || !aligned16(seq_id) || !aligned16(pos)) return MLA_ERR_ALIGN;
+  if (write ? !aligned16(a1) : (!aligned16(W_DKV) || !aligned16(W_KR))) return MLA_ERR_ALIGN;
+  AppendArgs a;
+  a.d = *dims; a.act = act; a.h = a0; a.k_rope = a1; a.n_tok = n_tok; a.seq_id = seq_id; a.pos = pos;
+  a.W_DKV = W_DKV; a.W_KR = W_KR; a.pages = (uint8_t*)cache->pages; a.g = make_geom(*dims, cache->dtype);
+  a.block_table = bt; a.max_pages = max_pages; a.stream = (hipStream_t)stream;
+  hipError_t e;
+  if (write) e = generic_write(a);
+  else if (!force_generic() && fast_append_supported(*dims, act)) e = fast_append(a);
+  else e = generic_append(a);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_page_bytes(const mla_dims* dims, int32_t cache_dtype) {
+  if (check_dims(dims) || !valid_cache(cache_dtype)) return 0;
+  if (cache_dtype == MLA_FP8_E4M3 && dims->d_c % 128) return 0;
+  return page_bytes_of(dims->d_c, dims->d_rope, dims->page_size, cache_dtype);
+}
+
+int mla_cache_append(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok, const int32_t* seq_id,
+                     const int32_t* pos, const void* W_DKV, const void* W_KR, const mla_cache* cache,
+                     const int32_t* block_table, int32_t max_pages, void* stream) {
+  return append_common(dims, act_dtype, h, nullptr, n_tok, seq_id, pos, W_DKV, W_KR, cache, block_table, max_pages,
+                       stream, false);
+}
+
+int mla_cache_write(const mla_dims* dims, int32_t act_dtype, const void* c_kv, const void* k_rope, int32_t n_tok,
+                    const int32_t* seq_id, const int32_t* pos, const mla_cache* cache, const int32_t* block_table,
+                    int32_t max_pages, void* stream) {
+  return append_common(dims, act_dtype, c_kv, k_rope, n_tok, seq_id, pos, nullptr, nullptr, cache, block_table,
+                       max_pages, stream, true);
+}
+
+int32_t mla_default_splits(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_pages) {
+  if (check_dims(dims) || batch <= 0 || s_q <= 0 || max_pages <= 0) return 0;
+  const int rows = dims->n_heads * s_q;
+  const int row_blocks = (rows + 127) / 128;
+  long items = (long)batch * row_blocks;
+  int s = (int)((TARGET_ITEMS + items - 1) / items);
+  if (s > max_pages) s = max_pages;
+  if (s > MAX_SPLITS) s = MAX_SPLITS;
+  return s < 1 ? 1 : s;
+}
+
+size_t mla_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t s_q, int32_t num_splits) {
+  if (check_dims(dims) || !valid_act(act_dtype) || batch <= 0 || s_q <= 0 || s_q > MAX_S_Q || num_splits <= 0 ||
+      num_splits > MAX_SPLITS)
+    return 0;
+  return ws_layout(*dims, act_dtype, batch, s_q, num_splits).total;
+}
+
+int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q, const void* W_DQ,
+               const void* W_UQ, const void* W_UK, const mla_cache* cache, const int32_t* block_table,
+               int32_t max_pages, const int32_t* seqlens, float softmax_scale, int32_t num_splits, void* ws,
+               size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
+  if (batch < 0 || s_q < 1 || s_q > MAX_S_Q || num_splits < 0 || num_splits > MAX_SPLITS) return MLA_ERR_DIMS;
+  if ((st = check_cache(dims, cache, block_table, max_pages))) return st;
+  if (act_dtype == MLA_BF16 && cache->dtype == MLA_F32) return MLA_ERR_DTYPE;
+  if (!(softmax_scale == softmax_scale)) return MLA_ERR_DIMS;
+  if (batch == 0) return MLA_OK;
+  if (!hq || !W_UQ || !W_UK || !seqlens || !ws) return MLA_ERR_NULL;
+  if (!aligned16(hq) || !aligned16(W_UQ) || !aligned16(W_UK) || !aligned16(seqlens) || !aligned16(ws) ||
+      (W_DQ && !aligned16(W_DQ)))
+    return MLA_ERR_ALIGN;
+  DecodeArgs a;
+  a.d = *dims; a.act = act_dtype; a.cache_dtype = cache->dtype; a.hq = hq; a.batch = batch; a.s_q = s_q;
+  a.W_DQ = W_DQ; a.W_UQ = W_UQ; a.W_UK = W_UK; a.pages = (const uint8_t*)cache->pages;
+  a.g = make_geom(*dims, cache->dtype); a.block_table = block_table; a.max_pages = max_pages; a.seqlens = seqlens;
+  a.scale = softmax_scale;
+  resolve_splits(dims, batch, s_q, max_pages, num_splits, &a.S, &a.pages_per_split);
+  a.L = ws_layout(*dims, act_dtype, batch, s_q, a.S);
+  if (ws_bytes < a.L.total) return MLA_ERR_WORKSPACE;
+  a.ws = (uint8_t*)ws; a.stream = (hipStream_t)stream;
+  hipError_t e;
+  if (!force_generic() && fast_decode_supported(*dims, act_dtype, cache->dtype, s_q)) e = fast_decode(a);
+  else e = generic_decode(a);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t s_q, const void* ws, size_t ws_bytes,
+                const void* W_UV, void* out, float* lse_out, void* stream) {
+  (void)ws_bytes;
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
+  if (batch < 0 || s_q < 1 || s_q > MAX_S_Q) return MLA_ERR_DIMS;
+  if (batch == 0) return MLA_OK;
+  if (!ws || !W_UV || !out) return MLA_ERR_NULL;
+  if (!aligned16(ws) || !aligned16(W_UV) || !aligned16(out) || (lse_out && !aligned16(lse_out))) return MLA_ERR_ALIGN;
+  // The split count is known only to the preceding mla_decode; the kernels read
+  // it from the workspace header.  Host-side, the smallest layout must fit.
+  const size_t need = ws_layout(*dims, act_dtype, batch, s_q, 1).total;
+  if (ws_bytes < need) return MLA_ERR_WORKSPACE;
+  CombineArgs a;
+  a.d = *dims; a.act = act_dtype; a.batch = batch; a.s_q = s_q; a.ws = (const uint8_t*)ws;
+  a.W_UV = W_UV; a.out = out; a.lse_out = lse_out; a.stream = (hipStream_t)stream;
+  a.L = ws_layout(*dims, act_dtype, batch, s_q, 1);
+  hipError_t e;
+  if (!force_generic() && fast_decode_supported(*dims, act_dtype, MLA_BF16, s_q)) e = fast_combine(a);
+  else e = generic_combine(a);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+const char* mla_status_str(int s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "required pointer is NULL";
+    case MLA_ERR_DIMS: return "size out of range or inconsistent";
+    case MLA_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MLA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_UNSUPPORTED: return "not implemented for these dims";
+    case MLA_ERR_HIP: return "HIP runtime error while enqueueing";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_version(void) { return "libmla gfx950 (generic VALU + MFMA decode kernels)"; }
+
+}  // extern "C"

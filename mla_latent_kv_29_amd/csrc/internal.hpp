@@ -1,0 +1,113 @@
+// Host-side plumbing shared by the API layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include "common.hpp"
+
+namespace mla {
+
+// Workspace layout of one decode step (every region 256-byte aligned).
+//   header   : int32[64] plan written by mla_decode, read by mla_combine
+//   cq_part  : f32 [KSPLIT_MAX][R][d_cq]   split-K partials of c^Q = W^DQ h
+//   cq       : act [R][d_cq]               c^Q
+//   u        : f32 [R][H][d_head+d_rope]   W^UQ c^Q (bf16 q^C for the MFMA path)
+//   qt       : act [R][H][d_c+d_rope]      absorbed, scaled query [q_abs | q^R]
+//   lpart    : f32 [B][S][s_q][H]          per-split log2-sum-exp2 of scores
+//   opart    : f32 [B][S][s_q][H][d_c]     per-split normalised latent outputs
+// R = batch * s_q.  Everything up to lpart is independent of the split count
+// S; opart follows lpart, so a kernel that reads S from the header finds it
+// with opart_offset().
+constexpr int KSPLIT_MAX = 16;
+constexpr int MAX_SPLITS = 4096;
+constexpr int WS_HEADER_INTS = 64;
+constexpr int32_t WS_MAGIC = 0x4d4c4144;  // "MLAD"
+
+struct WsLayout {
+  size_t header, cq_part, cq, u, qt, opart, lpart, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline size_t opart_offset(size_t lpart_off, int batch, int S, int s_q, int H) {
+  return lpart_off + align256((size_t)batch * S * s_q * H * 4);
+}
+
+inline WsLayout ws_layout(const mla_dims& d, int act, int batch, int s_q, int S) {
+  const size_t R = (size_t)batch * s_q, H = d.n_heads;
+  const size_t es = act == MLA_F32 ? 4 : 2;
+  WsLayout w;
+  size_t o = 0;
+  w.header = o;  o = align256(o + WS_HEADER_INTS * 4);
+  w.cq_part = o; o = align256(o + (size_t)KSPLIT_MAX * R * d.d_cq * 4);
+  w.cq = o;      o = align256(o + R * d.d_cq * es);
+  w.u = o;       o = align256(o + R * H * (d.d_head + d.d_rope) * 4);
+  w.qt = o;      o = align256(o + R * H * (d.d_c + d.d_rope) * es);
+  w.lpart = o;   o = align256(o + (size_t)batch * S * s_q * H * 4);
+  w.opart = o;   o = align256(o + (size_t)batch * S * s_q * H * d.d_c * 4);
+  w.total = o;
+  return w;
+}
+
+// Header fields (int32 indices).
+enum { HDR_MAGIC = 0, HDR_S = 1, HDR_PPS = 2, HDR_BATCH = 3, HDR_SQ = 4, HDR_H = 5, HDR_DC = 6 };
+
+struct DecodeArgs {
+  mla_dims d;
+  int act, cache_dtype;
+  const void* hq;
+  int batch, s_q;
+  const void *W_DQ, *W_UQ, *W_UK;
+  const uint8_t* pages;
+  CacheGeom g;
+  const int32_t* block_table;
+  int max_pages;
+  const int32_t* seqlens;
+  float scale;           // softmax scale tau
+  int S, pages_per_split;
+  uint8_t* ws;
+  WsLayout L;
+  hipStream_t stream;
+};
+
+struct CombineArgs {
+  mla_dims d;
+  int act;
+  int batch, s_q;
+  const uint8_t* ws;
+  WsLayout L;
+  const void* W_UV;
+  void* out;
+  float* lse_out;
+  hipStream_t stream;
+};
+
+struct AppendArgs {
+  mla_dims d;
+  int act;
+  const void* h;        // append: hidden states; write: c_kv
+  const void* k_rope;   // write only
+  int n_tok;
+  const int32_t *seq_id, *pos;
+  const void *W_DKV, *W_KR;
+  uint8_t* pages;
+  CacheGeom g;
+  const int32_t* block_table;
+  int max_pages;
+  hipStream_t stream;
+};
+
+// Launchers (return the first HIP error of the enqueue, hipSuccess otherwise).
+hipError_t generic_append(const AppendArgs& a);
+hipError_t generic_write(const AppendArgs& a);
+hipError_t generic_decode(const DecodeArgs& a);
+hipError_t generic_combine(const CombineArgs& a);
+hipError_t write_header(const DecodeArgs& a);
+
+bool fast_append_supported(const mla_dims& d, int act);
+bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q);
+hipError_t fast_append(const AppendArgs& a);
+hipError_t fast_decode(const DecodeArgs& a);
+hipError_t fast_combine(const CombineArgs& a);
+
+}  // namespace mla

@@ -1,0 +1,94 @@
+"""Device-buffer bookkeeping around the C ABI for one decode workload.
+
+`DecodeSession` owns (as torch tensors) the paged cache, block table,
+seqlens, workspace and output buffers of a batch, builds the cache through
+mla_cache_append and runs mla_decode + mla_combine.  It does no arithmetic of
+its own: every number is produced by libmla.so.
+"""
+import numpy as np
+import torch
+
+from . import _lib as L
+
+ACT = {"f32": L.MLA_F32, "bf16": L.MLA_BF16}
+CACHE = {"f32": L.MLA_F32, "bf16": L.MLA_BF16, "fp8": L.MLA_FP8_E4M3}
+
+
+class DecodeSession:
+    def __init__(self, dims, act, cache_dtype, lengths, table, num_pages, s_q, num_splits=0, device="cuda"):
+        """dims: dict of model dims; act: 'f32'|'bf16'; cache_dtype: 'f32'|'bf16'|'fp8';
+        lengths: int array [batch] (seqlens, including the s_q query tokens);
+        table: int32 numpy [batch, max_pages]; num_pages: size of the page pool."""
+        self.dims = dict(dims)
+        self.cdims = L.make_dims(dims)
+        self.act_name, self.cache_name = act, cache_dtype
+        self.act, self.cache_dtype = ACT[act], CACHE[cache_dtype]
+        self.tdtype = torch.float32 if act == "f32" else torch.bfloat16
+        self.device = device
+        self.batch = len(lengths)
+        self.s_q = s_q
+        self.lengths = np.asarray(lengths, dtype=np.int64)
+        self.max_pages = int(table.shape[1])
+        self.num_pages = int(num_pages)
+        self.page_bytes = L.mla_page_bytes(self.cdims, self.cache_dtype)
+        if self.page_bytes == 0:
+            raise ValueError("invalid dims / cache dtype")
+        self.pages = torch.zeros((self.num_pages, self.page_bytes), dtype=torch.uint8, device=device)
+        self.cache = L.cache_struct(self.pages, self.cache_dtype, self.num_pages)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(device)
+        self.seqlens = torch.from_numpy(self.lengths.astype(np.int32)).to(device)
+        self.set_splits(num_splits)
+        H, dh = dims["n_heads"], dims["d_head"]
+        self.out = torch.empty((self.batch, s_q, H, dh), dtype=self.tdtype, device=device)
+        self.lse = torch.empty((self.batch, s_q, H), dtype=torch.float32, device=device)
+
+    def set_splits(self, num_splits):
+        s = num_splits if num_splits > 0 else L.mla_default_splits(self.cdims, self.batch, self.s_q, self.max_pages)
+        self.num_splits = s
+        self.ws_bytes = L.mla_workspace_bytes(self.cdims, self.act, self.batch, self.s_q, s)
+        if self.ws_bytes == 0:
+            raise ValueError("invalid workspace request")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+
+    # ---------------------------------------------------------------- cache
+    def append(self, h, b, t0, W, stream=None):
+        """Append rows h [n, d_model] as tokens t0..t0+n-1 of sequence b."""
+        n = h.shape[0]
+        seq_id = torch.full((n,), b, dtype=torch.int32, device=self.device)
+        pos = torch.arange(t0, t0 + n, dtype=torch.int32, device=self.device)
+        L.mla_cache_append(self.cdims, self.act, h, n, seq_id, pos, W["W_DKV"], W["W_KR"], self.cache,
+                           self.block_table, self.max_pages, stream)
+
+    def append_rows(self, h, seq_id, pos, W, stream=None):
+        L.mla_cache_append(self.cdims, self.act, h, h.shape[0], seq_id, pos, W["W_DKV"], W["W_KR"], self.cache,
+                           self.block_table, self.max_pages, stream)
+
+    def write(self, c_kv, k_rope, b, t0, stream=None):
+        n = c_kv.shape[0]
+        seq_id = torch.full((n,), b, dtype=torch.int32, device=self.device)
+        pos = torch.arange(t0, t0 + n, dtype=torch.int32, device=self.device)
+        L.mla_cache_write(self.cdims, self.act, c_kv, k_rope, n, seq_id, pos, self.cache, self.block_table,
+                          self.max_pages, stream)
+
+    def build_from_h(self, gen_h, W, chunk=16384, stream=None):
+        """Append every token of every sequence; gen_h(b, t0, t1) -> h rows."""
+        for b in range(self.batch):
+            Lb = int(self.lengths[b])
+            for t0 in range(0, Lb, chunk):
+                t1 = min(Lb, t0 + chunk)
+                self.append(gen_h(b, t0, t1), b, t0, W, stream)
+
+    # ---------------------------------------------------------------- decode
+    def decode(self, hq, W, softmax_scale, use_dq=True, stream=None):
+        """hq: [batch*s_q, d_model] hidden states (or c^Q [batch*s_q, d_cq] with use_dq=False)."""
+        L.mla_decode(self.cdims, self.act, hq, self.batch, self.s_q, W["W_DQ"] if use_dq else None, W["W_UQ"],
+                     W["W_UK"], self.cache, self.block_table, self.max_pages, self.seqlens, softmax_scale,
+                     self.num_splits, self.ws, self.ws_bytes, stream)
+        L.mla_combine(self.cdims, self.act, self.batch, self.s_q, self.ws, self.ws_bytes, W["W_UV"], self.out,
+                      self.lse, stream)
+        return self.out, self.lse
+
+    # ---------------------------------------------------------------- inspection
+    def page_view(self):
+        """Raw pages as uint8 [num_pages, page_bytes] (for layout tests)."""
+        return self.pages

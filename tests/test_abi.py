@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/mla.h declares, computes sizes as documented and rejects
+invalid arguments before enqueueing anything (stream argument 0, no device
+pointer is ever dereferenced on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+import mla_latent_kv_29_amd as m
+from mla_latent_kv_29_amd import _lib as L
+from mla_latent_kv_29_amd import inputs
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return set(re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", src))
+
+
+def test_header_declarations_are_all_exported():
+    decl = declared_symbols()
+    assert decl == set(L.EXPORTS), decl ^ set(L.EXPORTS)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    assert m.status_str(0) == "ok"
+    for s in range(-7, 0):
+        assert m.status_str(s) and m.status_str(s) != "unknown status"
+    assert "gfx950" in m.version()
+
+
+def test_page_bytes_layouts():
+    d = m.make_dims(inputs.V3_DIMS)
+    assert m.mla_page_bytes(d, m.MLA_BF16) == 64 * 576 * 2
+    assert m.mla_page_bytes(d, m.MLA_F32) == 64 * 576 * 4
+    assert m.mla_page_bytes(d, m.MLA_FP8_E4M3) == 64 * (512 + 4 * 4 + 2 * 64)  # 41 984
+    t = m.make_dims(inputs.TINY_DIMS)
+    assert m.mla_page_bytes(t, m.MLA_FP8_E4M3) == 0       # d_c % 128 != 0
+    assert m.mla_page_bytes(t, 7) == 0
+
+
+def test_default_splits_and_workspace():
+    d = m.make_dims(inputs.V3_DIMS)
+    for batch, s_q, mp in [(64, 1, 64), (4, 1, 2048), (128, 2, 128), (1, 1, 1)]:
+        s = m.mla_default_splits(d, batch, s_q, mp)
+        assert 1 <= s <= mp
+        assert m.mla_workspace_bytes(d, m.MLA_BF16, batch, s_q, s) > 0
+    assert m.mla_workspace_bytes(d, m.MLA_BF16, 64, 9, 1) == 0
+    assert m.mla_workspace_bytes(d, m.MLA_BF16, 64, 1, 0) == 0
+    w1 = m.mla_workspace_bytes(d, m.MLA_BF16, 64, 1, 1)
+    w4 = m.mla_workspace_bytes(d, m.MLA_BF16, 64, 1, 4)
+    assert w4 - w1 >= 3 * 64 * 128 * 512 * 4
+
+
+FAKE = 1 << 40  # aligned non-null value; never dereferenced on the paths below
+
+
+def _dims(**kw):
+    d = dict(inputs.V3_DIMS)
+    d.update(kw)
+    return m.make_dims(d)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d_c=0), L.MLA_ERR_DIMS), (dict(d_rope=7), L.MLA_ERR_DIMS), (dict(page_size=63), L.MLA_ERR_DIMS),
+    (dict(d_rope=256), L.MLA_ERR_DIMS), (dict(rope_theta=0.0), L.MLA_ERR_DIMS),
+])
+def test_decode_rejects_bad_dims(kw, expect):
+    d = _dims(**kw)
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 10)
+    st = m.mla_decode(d, m.MLA_BF16, FAKE, 1, 1, FAKE, FAKE, FAKE, cache, FAKE, 4, FAKE, 0.1, 1, FAKE,
+                      1 << 30, stream=0, check=False)
+    assert st == expect
+
+
+def test_decode_argument_errors():
+    d = _dims()
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 10)
+    args = lambda **o: dict(dict(act=m.MLA_BF16, hq=FAKE, batch=2, s_q=1, wdq=FAKE, cache=cache, bt=FAKE,
+                                 mp=4, sl=FAKE, ns=1, ws=FAKE, wsb=1 << 34), **o)
+
+    def call(a):
+        return m.mla_decode(d, a["act"], a["hq"], a["batch"], a["s_q"], a["wdq"], FAKE, FAKE, a["cache"], a["bt"],
+                            a["mp"], a["sl"], 0.1, a["ns"], a["ws"], a["wsb"], stream=0, check=False)
+
+    assert call(args(act=5)) == L.MLA_ERR_DTYPE
+    assert call(args(s_q=0)) == L.MLA_ERR_DIMS
+    assert call(args(s_q=9)) == L.MLA_ERR_DIMS
+    assert call(args(hq=None)) == L.MLA_ERR_NULL
+    assert call(args(ws=None)) == L.MLA_ERR_NULL
+    assert call(args(bt=None)) == L.MLA_ERR_NULL
+    assert call(args(hq=FAKE + 2)) == L.MLA_ERR_ALIGN
+    assert call(args(wsb=1000)) == L.MLA_ERR_WORKSPACE
+    assert call(args(mp=0)) == L.MLA_ERR_DIMS
+    assert call(args(cache=L.cache_struct(FAKE, m.MLA_F32, 10))) == L.MLA_ERR_DTYPE   # bf16 act, f32 cache
+    assert call(args(cache=L.cache_struct(FAKE, 9, 10))) == L.MLA_ERR_DTYPE
+    assert call(args(batch=0)) == L.MLA_OK                                            # no-op
+    t = m.make_dims(inputs.TINY_DIMS)
+    st = m.mla_decode(t, m.MLA_F32, FAKE, 1, 1, FAKE, FAKE, FAKE, L.cache_struct(FAKE, m.MLA_FP8_E4M3, 4), FAKE, 4,
+                      FAKE, 0.1, 1, FAKE, 1 << 30, stream=0, check=False)
+    assert st == L.MLA_ERR_UNSUPPORTED                                               # fp8 needs d_c % 128 == 0
+
+
+def test_append_and_combine_argument_errors():
+    d = _dims()
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 10)
+    assert m.mla_cache_append(d, m.MLA_BF16, FAKE, 0, FAKE, FAKE, FAKE, FAKE, cache, FAKE, 4, stream=0,
+                              check=False) == L.MLA_OK
+    assert m.mla_cache_append(d, m.MLA_BF16, None, 3, FAKE, FAKE, FAKE, FAKE, cache, FAKE, 4, stream=0,
+                              check=False) == L.MLA_ERR_NULL
+    assert m.mla_cache_append(d, m.MLA_BF16, FAKE, -1, FAKE, FAKE, FAKE, FAKE, cache, FAKE, 4, stream=0,
+                              check=False) == L.MLA_ERR_DIMS
+    assert m.mla_cache_append(d, m.MLA_BF16, FAKE, 3, FAKE, FAKE + 4, FAKE, FAKE, cache, FAKE, 4, stream=0,
+                              check=False) == L.MLA_ERR_ALIGN
+    assert m.mla_cache_write(d, m.MLA_BF16, FAKE, None, 3, FAKE, FAKE, cache, FAKE, 4, stream=0,
+                             check=False) == L.MLA_ERR_NULL
+    assert m.mla_combine(d, m.MLA_BF16, 2, 1, FAKE, 10, FAKE, FAKE, None, stream=0, check=False) == \
+        L.MLA_ERR_WORKSPACE
+    assert m.mla_combine(d, m.MLA_BF16, 2, 1, FAKE, 1 << 34, None, FAKE, None, stream=0, check=False) == \
+        L.MLA_ERR_NULL
+    assert m.mla_combine(d, m.MLA_BF16, 0, 1, None, 0, None, None, None, stream=0, check=False) == L.MLA_OK
