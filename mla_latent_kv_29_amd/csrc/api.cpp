@@ -34,7 +34,8 @@ bool valid_cache(int t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E
 int check_cache(const mla_dims* d, const mla_cache* c, const int32_t* bt, int32_t max_pages) {
   if (!c || !c->pages || !bt) return MLA_ERR_NULL;
   if (!valid_cache(c->dtype)) return MLA_ERR_DTYPE;
-  if (c->dtype == MLA_FP8_E4M3 && d->d_c % 128) return MLA_ERR_UNSUPPORTED;
+  if (c->dtype == MLA_FP8_E4M3 && (d->d_c % 128 || d->d_rope % 8)) return MLA_ERR_UNSUPPORTED;
+  if (c->dtype == MLA_BF16 && (d->d_c + d->d_rope) % 8) return MLA_ERR_UNSUPPORTED;
   if (c->num_pages <= 0 || max_pages <= 0) return MLA_ERR_DIMS;
   if (!aligned16(c->pages) || !aligned16(bt)) return MLA_ERR_ALIGN;
   return MLA_OK;
@@ -86,7 +87,8 @@ extern "C" {
 
 size_t mla_page_bytes(const mla_dims* dims, int32_t cache_dtype) {
   if (check_dims(dims) || !valid_cache(cache_dtype)) return 0;
-  if (cache_dtype == MLA_FP8_E4M3 && dims->d_c % 128) return 0;
+  if (cache_dtype == MLA_FP8_E4M3 && (dims->d_c % 128 || dims->d_rope % 8)) return 0;
+  if (cache_dtype == MLA_BF16 && (dims->d_c + dims->d_rope) % 8) return 0;
   return page_bytes_of(dims->d_c, dims->d_rope, dims->page_size, cache_dtype);
 }
 

@@ -1,0 +1,320 @@
+// Split-KV MLA decode attention on MFMA for the DeepSeek-V3 shape
+// (d_c 512, d_rope 64, 128 heads, 64-token bf16 pages), gfx950.
+//
+// What it computes (absorbed form; DeepSeek-V3 reading lesson, §2.1.1 and
+// Question 2): for every query row (head i, query j) of sequence b and every
+// cached token t visible to it inside this split,
+//     s_t = qt_i . [c_t ; k^R_t]      (qt = tau*log2(e)*[W^UK_i^T q^C_i ; q^R_i])
+// an online softmax in the exp2 domain, and O_i = sum_t p_t c_t / sum_t p_t
+// (the attention-weighted latent; W^UV is applied later by the combine).
+//
+// Work item = (sequence b, split s, row block of 128 rows = one query j and
+// all 128 heads).  Four waves, one per SIMD, each owns 32 heads:
+//   * its 32 rows of qt stay in VGPRs for the whole split (36 MFMA B operands)
+//   * S^T[32 tokens x 32 heads] = K . Q^T with v_mfma_f32_32x32x16_bf16,
+//     K read from LDS row-wise (one 16-byte chunk per lane)
+//   * softmax per lane (one head, 16 tokens; the other 16 sit in lane ^ 32)
+//   * O^T[512 x 32 heads] += V^T . P^T, V^T read from LDS with the gfx950
+//     transposing ds_read_b64_tr_b16; P^T comes straight from the S^T
+//     accumulator registers (no lane exchange); O^T lives in 256 AGPRs.
+// Cache tokens stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+// staging) through a 3-deep ring of 32-token stages (110 592 B of LDS); the
+// 64-wide RoPE part of the queries sits in LDS beside it (16 KiB) so that the
+// 512-wide absorbed part (128 VGPRs) and O (256 AGPRs) fit one wave per SIMD.
+// The chunk-major swizzled page layout (layout.hpp) makes that copy verbatim
+// and both LDS access patterns bank-conflict free.
+#include "internal.hpp"
+#include "layout.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int H = 128, DC = 512, DKV = 576, PAGE = 64;
+constexpr int NCH = DKV / 8;               // 72 sixteen-byte chunks per token
+constexpr int ST_T = 32;                   // tokens per pipeline stage
+constexpr int NST = 3;                     // stages in the LDS ring
+constexpr int ST_BYTES = NCH * ST_T * 16;  // 36 864
+constexpr int QR_OFF = NST * ST_BYTES;     // q^R rows of the 128 heads: 128 x 64 bf16
+constexpr int LDS_BYTES = QR_OFF + H * 64 * 2;  // 126 976
+constexpr float RESCALE_SLACK = 8.0f;      // log2 headroom before O is rescaled
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 32-token half of a page into one LDS stage: 36 wave-instructions of
+// 1 KiB (chunks 2q and 2q+1), nine per wave.
+__device__ __forceinline__ void issue_stage(const uint8_t* page, int half, uint8_t* dst, int wave, int lane) {
+  const uint8_t* src = page + (size_t)(lane >> 5) * (PAGE * 16) + half * (ST_T * 16) + (lane & 31) * 16;
+#pragma unroll
+  for (int n = 0; n < 9; ++n) {
+    const int q = wave + 4 * n;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)(2 * q) * (PAGE * 16)), (lds_void*)(dst + q * 1024),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ const uint8_t* stage_page(const uint8_t* pages, size_t page_bytes, const int32_t* bt_row,
+                                                     int t0) {
+  return pages + (size_t)bt_row[t0 / PAGE] * page_bytes;
+}
+
+// Everything a pass over the split needs.
+struct SplitCtx {
+  const uint8_t* pages;
+  size_t page_bytes;
+  const int32_t* bt_row;
+  int t_begin, ntok, nst;
+  uint8_t* lds;
+  int wave, lane, cg;
+  int kofs_even, kofs_odd, vofs1, vofs2, qr_x;
+  const uint8_t* qr_lds;
+};
+
+// S^T[32 tokens][32 heads] of one stage: 36 MFMAs, K fragments prefetched two
+// k-steps ahead, the absorbed query part from VGPRs, the RoPE part from LDS.
+__device__ __forceinline__ f32x16 stage_scores(const SplitCtx& c, const uint8_t* st, const bf16x8 (&qf)[32]) {
+  f32x16 sc = {};
+  bf16x8 ka = *(const bf16x8*)(st + c.kofs_even);
+  bf16x8 kb = *(const bf16x8*)(st + 1024 + c.kofs_odd);
+#pragma unroll
+  for (int kk = 0; kk < 36; ++kk) {
+    bf16x8 kn = ka;
+    if (kk + 2 < 36) kn = *(const bf16x8*)(st + 1024 * (kk + 2) + ((kk & 1) ? c.kofs_odd : c.kofs_even));
+    bf16x8 qb;
+    if (kk < 32) qb = qf[kk];
+    else qb = *(const bf16x8*)(c.qr_lds + (((2 * (kk - 32) + c.cg) ^ c.qr_x) * 16));
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, sc, 0, 0, 0);
+    ka = kb;
+    kb = kn;
+  }
+  return sc;
+}
+
+// Issues the first two stages of a pass into the ring.
+__device__ __forceinline__ void prologue(const SplitCtx& c) {
+  for (int k = 0; k < 2 && k < c.nst; ++k) {
+    const int t0 = c.t_begin + k * ST_T;
+    issue_stage(stage_page(c.pages, c.page_bytes, c.bt_row, t0), (t0 / ST_T) & 1, c.lds + k * ST_BYTES, c.wave,
+                c.lane);
+  }
+}
+
+// Waits for stage k, then refills the ring slot that stage k-1 used.
+__device__ __forceinline__ const uint8_t* advance(const SplitCtx& c, int k) {
+  if (k + 1 < c.nst) wait_vmcnt<9>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  if (k + 2 < c.nst) {
+    const int t0 = c.t_begin + (k + 2) * ST_T;
+    issue_stage(stage_page(c.pages, c.page_bytes, c.bt_row, t0), (t0 / ST_T) & 1, c.lds + ((k + 2) % NST) * ST_BYTES,
+                c.wave, c.lane);
+  }
+  return c.lds + (k % NST) * ST_BYTES;
+}
+
+// Masks the scores of tokens past the end of the split, returns the row max
+// over this lane's 16 tokens.
+__device__ __forceinline__ float mask_max(const SplitCtx& c, f32x16& sc, int k) {
+  const int nvalid = min(ST_T, c.ntok - k * ST_T);
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = 8 * (r >> 2) + 4 * c.cg + (r & 3);
+    if (t >= nvalid) sc[r] = -INFINITY;
+    mloc = fmaxf(mloc, sc[r]);
+  }
+  return mloc;
+}
+
+constexpr float HEADROOM = 96.0f;
+
+// The pass over the split.  O and l accumulate exp2(s - m_ref) weights and O
+// is never rescaled, so its 256 accumulators stay in AGPRs.  With fixed ==
+// false, m_ref is set to the first stage's maximum and the return value says
+// whether a later score rose more than HEADROOM above it in some row of the
+// wave; with fixed == true m_ref is the exact maximum of the split.
+__device__ __forceinline__ bool attend_pass(const SplitCtx& c, const bf16x8 (&qf)[32], bool fixed, float& m_ref,
+                                            f32x16 (&o)[16], float& l_run) {
+  prologue(c);
+  bool ovf = false;
+  for (int k = 0; k < c.nst; ++k) {
+    const uint8_t* st = advance(c, k);
+    f32x16 sc = stage_scores(c, st, qf);
+    float mloc = mask_max(c, sc, k);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    if (!fixed && k == 0) m_ref = mloc;
+    ovf |= mloc > m_ref + HEADROOM;
+    bf16x8 pb[2];
+    float ls = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bf16_t pv = (bf16_t)exp2f(fminf(sc[r] - m_ref, HEADROOM));
+      ls += (float)pv;
+      pb[r >> 3][r & 7] = pv;
+    }
+    l_run += ls;
+
+    // O^T[c][h] += V^T[c][t] P^T[t][h] for the stage's tokens 16hf..16hf+15
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint8_t* a1 = st + cb * (4 * ST_T * 16) + hf * 256 + c.vofs1;
+        const uint8_t* a2 = st + cb * (4 * ST_T * 16) + hf * 256 + c.vofs2;
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
+        const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s8), pb[hf], o[cb], 0, 0, 0);
+      }
+    }
+  }
+  return ovf;
+}
+
+// Scores only: the exact row maximum over the split.
+__device__ __forceinline__ float max_pass(const SplitCtx& c, const bf16x8 (&qf)[32]) {
+  prologue(c);
+  float mx = -INFINITY;
+  for (int k = 0; k < c.nst; ++k) {
+    const uint8_t* st = advance(c, k);
+    f32x16 sc = stage_scores(c, st, qf);
+    mx = fmaxf(mx, mask_max(c, sc, k));
+  }
+  return fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
+
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
+                    const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt,
+                    int max_pages, const int32_t* __restrict__ seqlens, float* __restrict__ opart,
+                    float* __restrict__ lpart) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int RB = s_q;
+  // The RB row blocks of one (b, s) share blockIdx % 8, i.e. one XCD and its
+  // L2, and are dispatched next to each other.
+  const int bid = blockIdx.x;
+  const int p = (bid / (8 * RB)) * 8 + bid % 8;
+  const int j = (bid / 8) % RB;
+  if (p >= P_items) return;
+  const int b = p / S, s = p % S;
+
+  const int L = seqlens[b];
+  int vis = L > 0 ? L - s_q + j + 1 : 0;
+  vis = vis < 0 ? 0 : vis;
+  SplitCtx c;
+  c.t_begin = s * pps * PAGE;
+  const int t_end = min(vis, c.t_begin + pps * PAGE);
+  c.ntok = t_end > c.t_begin ? t_end - c.t_begin : 0;
+  c.nst = (c.ntok + ST_T - 1) / ST_T;
+
+  const int cg = lane >> 5;  // lane half: k-group / token quad in the MFMA layouts
+  const int hrow = wave * 32 + (lane & 31);
+  const size_t prow = (((size_t)b * S + s) * s_q + j) * H + hrow;
+  float* orow = opart + prow * DC;
+
+  if (c.nst == 0) {
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) *(float4*)(orow + 32 * cb + 8 * r4 + 4 * cg) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (cg == 0) lpart[prow] = -INFINITY;
+    return;
+  }
+
+  // This wave's 32 query rows as MFMA B operands: lane holds qt[hrow][16kk + 8cg .. +8]
+  // for the 32 absorbed k-steps; the RoPE part of all 128 rows goes to LDS,
+  // row h at QR_OFF + 128h with its eight 16-byte chunks permuted by (h/2)%8.
+  const bf16_t* qblk = qt + (size_t)(b * s_q + j) * H * DKV;
+  const bf16_t* qrow = qblk + (size_t)hrow * DKV + 8 * cg;
+  bf16x8 qf[32];
+#pragma unroll
+  for (int kk = 0; kk < 32; ++kk) qf[kk] = *(const bf16x8*)(qrow + 16 * kk);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i = wave + 4 * n;
+    const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
+    __builtin_amdgcn_global_load_lds((gbl_void*)(qblk + (size_t)h * DKV + DC + 8 * lc),
+                                     (lds_void*)(lds + QR_OFF + i * 1024), 16, 0, 0);
+  }
+
+  c.pages = pages;
+  c.page_bytes = page_bytes;
+  c.bt_row = bt + (size_t)b * max_pages;
+  c.lds = lds;
+  c.wave = wave;
+  c.lane = lane;
+  c.cg = cg;
+  const int tr = lane & 31;
+  c.kofs_even = cg * (ST_T * 16) + (tr ^ (4 * cg)) * 16;       // chunk 2kk+cg, kk even
+  c.kofs_odd = cg * (ST_T * 16) + (tr ^ (4 * (2 + cg))) * 16;  // chunk 2kk+cg, kk odd
+  c.qr_lds = lds + QR_OFF + hrow * 128;
+  c.qr_x = (hrow >> 1) & 7;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tq = i16 >> 2, qq = i16 & 3;
+  // V^T reads: chunk C = 4cb + 2(g16&1) + (qq>>1), so C&3 is lane-constant
+  const int cl = 2 * (g16 & 1) + (qq >> 1);
+  const int cx = 4 * (cl & 3);
+  c.vofs1 = cl * (ST_T * 16) + ((4 * (g16 >> 1) + tq) ^ cx) * 16 + (qq & 1) * 8;
+  c.vofs2 = cl * (ST_T * 16) + ((8 + 4 * (g16 >> 1) + tq) ^ cx) * 16 + (qq & 1) * 8;
+
+  f32x16 o[16];
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.0f;
+  // Normally one pass.  If some score rose more than 2^96 above the first
+  // stage's maximum, the item is redone: a scores-only pass finds the exact
+  // maximum, then a full pass accumulates against it.
+  bool fixed = false;
+#pragma clang loop unroll(disable)
+  for (;;) {
+    const bool ovf = attend_pass(c, qf, fixed, m_ref, o, l_run);
+    __syncthreads();  // every wave is done with the ring
+    if (fixed || !__syncthreads_or(ovf)) break;
+    m_ref = max_pass(c, qf);
+    __syncthreads();
+    fixed = true;
+    l_run = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *(float4*)(orow + 32 * cb + 8 * r4 + 4 * cg) =
+          make_float4(o[cb][4 * r4] * inv, o[cb][4 * r4 + 1] * inv, o[cb][4 * r4 + 2] * inv, o[cb][4 * r4 + 3] * inv);
+    __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time through VGPRs
+  }
+  if (cg == 0) lpart[prow] = m_ref + log2f(l_tot);
+}
+
+}  // namespace
+
+hipError_t fast_attention(const DecodeArgs& a) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_v3_bf16, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int P_items = a.batch * a.S;
+  const int RB = a.s_q;
+  const int grid = ((P_items + 7) / 8) * 8 * RB;
+  hipLaunchKernelGGL(k_attn_v3_bf16, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split,
+                     P_items, (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages,
+                     a.seqlens, (float*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart));
+  return hipGetLastError();
+}
+
+}  // namespace mla

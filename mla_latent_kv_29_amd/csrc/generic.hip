@@ -7,6 +7,7 @@
 // §2.1.1 (latents, concatenated per-head key, absorption in Question 2) and
 // the summary "Báo cáo Kỹ thuật DeepSeek-V3", Phương pháp item 1 (c^Q).
 #include "internal.hpp"
+#include "layout.hpp"
 #include <math.h>
 
 namespace mla {
@@ -23,15 +24,15 @@ __device__ __forceinline__ const uint8_t* page_ptr(const CacheGeom& g, const uin
 
 __device__ __forceinline__ float cache_lat(const CacheGeom& g, const uint8_t* pg, int slot, int c) {
   if (g.dtype == MLA_F32) return ((const float*)pg)[(size_t)slot * (g.d_c + g.d_rope) + c];
-  if (g.dtype == MLA_BF16) return (float)((const bf16_t*)pg)[(size_t)slot * (g.d_c + g.d_rope) + c];
+  if (g.dtype == MLA_BF16) return (float)*(const bf16_t*)(pg + bf16_page_off(slot, c, g.page_size));
   float s = ((const float*)(pg + g.fp8_scale_off))[slot * (g.d_c / 128) + c / 128];
-  return e4m3_to_f32(pg[(size_t)slot * g.d_c + c]) * s;
+  return e4m3_to_f32(pg[fp8_code_off(slot, c, g.page_size)]) * s;
 }
 
 __device__ __forceinline__ float cache_rope(const CacheGeom& g, const uint8_t* pg, int slot, int m) {
   if (g.dtype == MLA_F32) return ((const float*)pg)[(size_t)slot * (g.d_c + g.d_rope) + g.d_c + m];
-  if (g.dtype == MLA_BF16) return (float)((const bf16_t*)pg)[(size_t)slot * (g.d_c + g.d_rope) + g.d_c + m];
-  return (float)((const bf16_t*)(pg + g.fp8_rope_off))[slot * g.d_rope + m];
+  if (g.dtype == MLA_BF16) return (float)*(const bf16_t*)(pg + bf16_page_off(slot, g.d_c + m, g.page_size));
+  return (float)*(const bf16_t*)(pg + g.fp8_rope_off + fp8_rope_elem_off(slot, m, g.page_size));
 }
 
 // Block of 256 threads stores one fp32 latent row (c^KV then rotated k^R,
@@ -41,19 +42,19 @@ __device__ void store_row(const CacheGeom& g, uint8_t* pg, int slot, const float
   if (g.dtype == MLA_F32) {
     for (int k = tid; k < D; k += blockDim.x) ((float*)pg)[(size_t)slot * D + k] = row[k];
   } else if (g.dtype == MLA_BF16) {
-    for (int k = tid; k < D; k += blockDim.x) ((bf16_t*)pg)[(size_t)slot * D + k] = (bf16_t)row[k];
+    for (int k = tid; k < D; k += blockDim.x) *(bf16_t*)(pg + bf16_page_off(slot, k, g.page_size)) = (bf16_t)row[k];
   } else {
     const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6, nt = g.d_c / 128;
     for (int tile = wave; tile < nt; tile += nw) {
       float v0 = row[tile * 128 + lane], v1 = row[tile * 128 + 64 + lane];
       float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
       float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-      pg[(size_t)slot * g.d_c + tile * 128 + lane] = f32_to_e4m3(v0 / s);
-      pg[(size_t)slot * g.d_c + tile * 128 + 64 + lane] = f32_to_e4m3(v1 / s);
+      pg[fp8_code_off(slot, tile * 128 + lane, g.page_size)] = f32_to_e4m3(v0 / s);
+      pg[fp8_code_off(slot, tile * 128 + 64 + lane, g.page_size)] = f32_to_e4m3(v1 / s);
       if (lane == 0) ((float*)(pg + g.fp8_scale_off))[slot * nt + tile] = s;
     }
     for (int m = tid; m < g.d_rope; m += blockDim.x)
-      ((bf16_t*)(pg + g.fp8_rope_off))[slot * g.d_rope + m] = (bf16_t)row[g.d_c + m];
+      *(bf16_t*)(pg + g.fp8_rope_off + fp8_rope_elem_off(slot, m, g.page_size)) = (bf16_t)row[g.d_c + m];
   }
 }
 
@@ -303,13 +304,12 @@ hipError_t write_header(const DecodeArgs& a) {
 }
 
 template <typename T>
-static hipError_t generic_decode_t(const DecodeArgs& a) {
+static hipError_t generic_query_t(const DecodeArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
   const float scale2 = a.scale * LOG2E;
   float* u = (float*)(a.ws + a.L.u);
   T* qt = (T*)(a.ws + a.L.qt);
-  const T* cq_in = (const T*)a.hq;
   const size_t nu = (size_t)R * H * (d.d_head + d.d_rope);
   if (a.W_DQ) {
     float* cq = (float*)(a.ws + a.L.cq_part);
@@ -320,23 +320,40 @@ static hipError_t generic_decode_t(const DecodeArgs& a) {
                        H * (d.d_head + d.d_rope), d.d_cq, (const float*)cq, (const T*)a.W_UQ, u);
   } else {
     hipLaunchKernelGGL((k_gemm_xwT<T, T>), dim3((unsigned)((nu + 3) / 4)), dim3(256), 0, a.stream, R,
-                       H * (d.d_head + d.d_rope), d.d_cq, cq_in, (const T*)a.W_UQ, u);
+                       H * (d.d_head + d.d_rope), d.d_cq, (const T*)a.hq, (const T*)a.W_UQ, u);
   }
   hipLaunchKernelGGL((k_qrope_generic<T>), dim3(R * H), dim3(64), 0, a.stream, H, a.s_q, d.d_head, d.d_rope, d.d_c,
                      d.rope_theta, scale2, a.seqlens, (const float*)u, qt);
   hipLaunchKernelGGL((k_absorb_generic<T, T>), dim3(R * H), dim3(256), 0, a.stream, H, d.d_head, d.d_rope, d.d_c,
                      scale2, (const float*)u, (const T*)a.W_UK, qt);
-  const size_t lds = (size_t)(d.d_c + d.d_rope + 256 + 8) * 4;
-  hipLaunchKernelGGL((k_attn_generic<T>), dim3(R * H, a.S), dim3(256), lds, a.stream, H, a.s_q, a.g,
-                     (const T*)qt, a.pages, a.block_table, a.max_pages, a.seqlens, a.S, a.pages_per_split,
-                     (float*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart));
   return hipGetLastError();
 }
 
-hipError_t generic_decode(const DecodeArgs& a) {
+template <typename T>
+static hipError_t generic_attention_t(const DecodeArgs& a) {
+  const mla_dims& d = a.d;
+  const int R = a.batch * a.s_q, H = d.n_heads;
+  const size_t lds = (size_t)(d.d_c + d.d_rope + 256 + 8) * 4;
+  hipLaunchKernelGGL((k_attn_generic<T>), dim3(R * H, a.S), dim3(256), lds, a.stream, H, a.s_q, a.g,
+                     (const T*)(a.ws + a.L.qt), a.pages, a.block_table, a.max_pages, a.seqlens, a.S,
+                     a.pages_per_split, (float*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart));
+  return hipGetLastError();
+}
+
+hipError_t generic_query(const DecodeArgs& a) {
   hipError_t e = write_header(a);
   if (e != hipSuccess) return e;
-  return a.act == MLA_F32 ? generic_decode_t<float>(a) : generic_decode_t<bf16_t>(a);
+  return a.act == MLA_F32 ? generic_query_t<float>(a) : generic_query_t<bf16_t>(a);
+}
+
+hipError_t generic_attention(const DecodeArgs& a) {
+  return a.act == MLA_F32 ? generic_attention_t<float>(a) : generic_attention_t<bf16_t>(a);
+}
+
+hipError_t generic_decode(const DecodeArgs& a) {
+  hipError_t e = generic_query(a);
+  if (e != hipSuccess) return e;
+  return generic_attention(a);
 }
 
 hipError_t generic_combine(const CombineArgs& a) {

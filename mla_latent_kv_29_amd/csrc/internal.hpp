@@ -101,6 +101,8 @@ struct AppendArgs {
 hipError_t generic_append(const AppendArgs& a);
 hipError_t generic_write(const AppendArgs& a);
 hipError_t generic_decode(const DecodeArgs& a);
+hipError_t generic_query(const DecodeArgs& a);       // header, c^Q, W^UQ, RoPE, absorption -> qt
+hipError_t generic_attention(const DecodeArgs& a);   // qt + cache -> per-split partials
 hipError_t generic_combine(const CombineArgs& a);
 hipError_t write_header(const DecodeArgs& a);
 
@@ -109,5 +111,6 @@ bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q)
 hipError_t fast_append(const AppendArgs& a);
 hipError_t fast_decode(const DecodeArgs& a);
 hipError_t fast_combine(const CombineArgs& a);
+hipError_t fast_attention(const DecodeArgs& a);
 
 }  // namespace mla
