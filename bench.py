@@ -1,0 +1,211 @@
+"""MLA decode throughput on one MI355X: cached tokens attended per second.
+
+One step = mla_decode (query projection from h with W^DQ, W^UQ, absorption
+with W^UK, split-KV attention over the latent cache) + mla_combine (split
+merge and W^UV) for every sequence of the batch, on a cache that
+mla_cache_append built beforehand.  Inputs are seeded synthetic data at the
+DeepSeek-V3 MLA shape; several copies of cache and weights are rotated from
+step to step so that no step finds its data in the 256 MB last-level cache.
+
+Prints ONE JSON line (see --help).  The dominant kernel is the split-KV
+attention (mla_decode_attend): its duration is taken with HIP events around
+that call on the stream it runs on, inside the timed region.
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode cached-tokens/s + % HBM/MFMA roofline, B=64 L=4096 bf16, 1 GPU"
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 flop/s, MI355X
+
+
+def algorithmic(spec, dims, lengths):
+    """Algorithmic bytes and flops of one step and of one attention launch."""
+    H, dh, dr, dc, dq, d = (dims[k] for k in ("n_heads", "d_head", "d_rope", "d_c", "d_cq", "d_model"))
+    s_q = spec["s_q"]
+    tok_bytes = {"bf16": (dc + dr) * 2, "fp8": dc + 4 * (dc // 128) + 2 * dr, "f32": (dc + dr) * 4}[spec["cache"]]
+    es = 2 if spec["act"] == "bf16" else 4
+    L = [int(x) for x in lengths]
+    vis = sum(max(0, Lb - s_q + j + 1) for Lb in L for j in range(s_q))
+    cache = sum(L) * tok_bytes
+    attn_flops = vis * H * 2 * ((dc + dr) + dc)
+    R = len(L) * s_q
+    w_bytes = es * (dq * d + H * (dh + dr) * dq + 2 * H * dh * dc)
+    io_bytes = es * (R * d + R * H * dh)
+    q_flops = 2 * R * (dq * d + H * (dh + dr) * dq + H * dh * dc)
+    o_flops = 2 * R * H * dh * dc
+    return dict(step_bytes=cache + w_bytes + io_bytes, step_flops=attn_flops + q_flops + o_flops,
+                attn_bytes=cache, attn_flops=attn_flops)
+
+
+def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=16):
+    """The float64 oracle (decode from cached latents, explicit per-head k^C and
+    v^C) on a bounded sample of sequences of the same workload; cached
+    tokens/s = sum of sample lengths / oracle time."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = None
+    Wn = {k: v.to("cpu", torch.float64).numpy() for k, v in W.items()}
+    s_q = spec["s_q"]
+    order = np.argsort(lengths)[::-1] if spec["lengths"][0] != "fixed" else range(len(lengths))
+    t_used, toks, n = 0.0, 0, 0
+    for b in list(order)[:max_seqs]:
+        Lb = int(lengths[b])
+        h = gen_h(int(b), 0, Lb).to("cpu", torch.float64).numpy()
+        c, kr = oracle.kv_latents(h, Wn["W_DKV"], Wn["W_KR"], np.arange(Lb), dims["rope_theta"])
+        hq = h[Lb - s_q:Lb]
+        tau = 1.0 / math.sqrt(dims["d_head"] + dims["d_rope"])
+        t0 = time.perf_counter()
+        oracle.decode_from_latents(c, kr, hq, Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], dims, Lb, s_q, tau)
+        t_used += time.perf_counter() - t0
+        toks += Lb
+        n += 1
+        if t_used >= budget_s:
+            break
+    return {"value": toks / t_used, "unit": "cached-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} sequence(s), {toks} cached tokens, float64 numpy, decode from cached latents "
+                      f"(explicit k^C/v^C per head), {t_used:.1f} s",
+            "host_cpus": os.cpu_count(), "cpu_model": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v3_bf16_b64_l4096")
+    ap.add_argument("--splits", type=int, default=0, help="KV splits per sequence (0 = library default)")
+    ap.add_argument("--rotate", type=int, default=3, help="copies of cache+weights rotated across steps")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures one GPU's "
+              f"share at its real shape and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mla_latent_kv_29_amd import inputs
+    from mla_latent_kv_29_amd import _lib as L
+    from mla_latent_kv_29_amd.session import DecodeSession
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    spec = inputs.WORKLOADS[args.workload]
+    dims = spec["dims"]
+    wl = spec["index"]
+    tdt = inputs.torch_dtype(spec["act"])
+    lengths = inputs.seqlens(spec["lengths"], spec["batch"], 0, wl)
+    table, pool = inputs.block_table(lengths, dims["page_size"], spec["table"], 0, wl)
+    W = inputs.weights(dims, spec["sigma"], tdt, dev, 0, wl)
+    sess = DecodeSession(dims, spec["act"], spec["cache"], lengths, table, pool, spec["s_q"], args.splits, dev)
+    gen_h = lambda b, t0, t1: inputs.hidden(dims, b, t0, t1, tdt, dev, 0, wl)
+
+    # ---- cache build (not part of the step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sess.build_from_h(gen_h, W, chunk=32768)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    s_q = spec["s_q"]
+    hq = torch.cat([gen_h(b, int(Lb) - s_q, int(Lb)) for b, Lb in enumerate(lengths)], 0).contiguous()
+    tau = 1.0 / math.sqrt(dims["d_head"] + dims["d_rope"])
+
+    # ---- rotation sets: same values in distinct buffers
+    sets = [(sess.pages, W)]
+    for _ in range(1, max(1, args.rotate)):
+        sets.append((sess.pages.clone(), {k: v.clone() for k, v in W.items()}))
+    caches = [L.cache_struct(p, sess.cache_dtype, sess.num_pages) for p, _ in sets]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    c = sess.cdims
+    dargs = lambda i: (c, sess.act, hq, sess.batch, s_q, sets[i][1]["W_DQ"], sets[i][1]["W_UQ"], sets[i][1]["W_UK"],
+                       caches[i], sess.block_table, sess.max_pages, sess.seqlens, tau, sess.num_splits, sess.ws,
+                       sess.ws_bytes, sp)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i, e=None):
+        k = i % len(sets)
+        if e is not None:
+            e[0].record(stream)
+        L.mla_decode_query(*dargs(k))
+        if e is not None:
+            e[1].record(stream)
+        L.mla_decode_attend(*dargs(k))
+        if e is not None:
+            e[2].record(stream)
+        L.mla_combine(c, sess.act, sess.batch, s_q, sess.ws, sess.ws_bytes, sets[k][1]["W_UV"], sess.out, sess.lse,
+                      sp)
+        if e is not None:
+            e[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    a_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    c_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in range(args.steps)]
+    ms_per_step = wall / args.steps * 1e3
+    tokens = float(np.sum(lengths))
+    alg = algorithmic(spec, dims, lengths)
+
+    attn_s = float(np.mean(a_ms)) * 1e-3
+    if spec["cache"] == "fp8":
+        bound, achieved, peak, unit = "mfma", alg["attn_flops"] / attn_s / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", alg["attn_bytes"] / attn_s / 1e9, HBM_PEAK / 1e9, "GB/s"
+    t_bound = max(alg["step_bytes"] / HBM_PEAK, alg["step_flops"] / MFMA_BF16_PEAK)
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "cached-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec["act"] if spec["cache"] != "fp8" else "bf16+fp8cache",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,sigma^2) weights at DeepSeek-V3 MLA shapes)",
+        "config": {"workload": args.workload, "batch": int(spec["batch"]), "seq_len": spec["lengths"][1]
+                   if spec["lengths"][0] == "fixed" else f"U[{spec['lengths'][1]},{spec['lengths'][2]}]",
+                   "s_q": s_q, "cache": spec["cache"], "splits": sess.num_splits,
+                   "cached_tokens": int(tokens), "rotation_sets": len(sets)},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": None, "kernel": "k_attn_v3_bf16 (mla_decode_attend)",
+                     "attn_ms_mean": float(np.mean(a_ms))},
+        "step_roofline": {"t_bound_us": t_bound * 1e6, "frac": t_bound / (ms_per_step * 1e-3),
+                          "step_bytes": alg["step_bytes"], "step_flops": alg["step_flops"]},
+        "phases_ms": {"query": float(np.median(q_ms)), "attend": float(np.median(a_ms)),
+                      "combine": float(np.median(c_ms))},
+        "cache_build_s": build_s,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, dims, W, gen_h, lengths, args.cpu_budget)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -162,6 +162,24 @@ MLA_API int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq,
                const int32_t* seqlens, float softmax_scale, int32_t num_splits,
                void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of mla_decode, for callers that want to schedule or time
+ * them separately (same arguments and validation as mla_decode):
+ * mla_decode_query runs the query projection and absorption and records the
+ * split plan in ws; mla_decode_attend then runs the split-KV attention over
+ * the cache using the queries in ws.  mla_decode == query then attend.      */
+MLA_API int mla_decode_query(const mla_dims* dims, int32_t act_dtype, const void* hq,
+               int32_t batch, int32_t s_q, const void* W_DQ, const void* W_UQ,
+               const void* W_UK, const mla_cache* cache,
+               const int32_t* block_table, int32_t max_pages,
+               const int32_t* seqlens, float softmax_scale, int32_t num_splits,
+               void* ws, size_t ws_bytes, void* stream);
+MLA_API int mla_decode_attend(const mla_dims* dims, int32_t act_dtype, const void* hq,
+               int32_t batch, int32_t s_q, const void* W_DQ, const void* W_UQ,
+               const void* W_UK, const mla_cache* cache,
+               const int32_t* block_table, int32_t max_pages,
+               const int32_t* seqlens, float softmax_scale, int32_t num_splits,
+               void* ws, size_t ws_bytes, void* stream);
+
 /* Decode, second half: merges the splits that the preceding mla_decode on
  * this workspace left (log-sum-exp weighted; empty splits skipped), then
  * applies W^UV per head:
@@ -176,6 +194,10 @@ MLA_API int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch,
 
 /* Static description of a status code.                                      */
 MLA_API const char* mla_status_str(int status);
+
+/* Description of the HIP error behind the last MLA_ERR_HIP returned on the
+ * calling thread ("none" if there was none); static string.                 */
+MLA_API const char* mla_last_hip_error(void);
 
 /* Library build identifier (kernel set and target), static string.         */
 MLA_API const char* mla_version(void);

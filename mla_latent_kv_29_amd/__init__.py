@@ -8,9 +8,9 @@ seeded synthetic inputs.
 """
 from . import _lib
 from ._lib import (mla_page_bytes, mla_cache_append, mla_cache_write, mla_default_splits,
-                   mla_workspace_bytes, mla_decode, mla_combine, status_str, version, make_dims,
+                   mla_workspace_bytes, mla_decode, mla_decode_query, mla_decode_attend, mla_combine, status_str, version, make_dims,
                    MLAError, MLA_F32, MLA_BF16, MLA_FP8_E4M3)
 
 __all__ = ["mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
-           "mla_workspace_bytes", "mla_decode", "mla_combine", "status_str", "version", "make_dims",
+           "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine", "status_str", "version", "make_dims",
            "MLAError", "MLA_F32", "MLA_BF16", "MLA_FP8_E4M3"]

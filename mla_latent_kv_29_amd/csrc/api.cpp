@@ -14,6 +14,14 @@ constexpr int TARGET_ITEMS = 512;  // (sequence, row block, split) work items ai
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+thread_local hipError_t t_last_hip = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  t_last_hip = e;
+  return MLA_ERR_HIP;
+}
+
 int check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_NULL;
   if (d->d_model <= 0 || d->n_heads <= 0 || d->d_head <= 0 || d->d_rope <= 0 || d->d_c <= 0 || d->d_cq <= 0 ||
@@ -76,9 +84,9 @@ int append_common(const mla_dims* dims, int32_t act, const void* a0, const void*
   a.block_table = bt; a.max_pages = max_pages; a.stream = (hipStream_t)stream;
   hipError_t e;
   if (write) e = generic_write(a);
-  else if (!force_generic() && fast_append_supported(*dims, act)) e = fast_append(a);
+  else if (!force_generic() && fast_append_supported(*dims, act, cache->dtype)) e = fast_append(a);
   else e = generic_append(a);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return hip_status(e);
 }
 
 }  // namespace
@@ -124,10 +132,10 @@ size_t mla_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t batc
   return ws_layout(*dims, act_dtype, batch, s_q, num_splits).total;
 }
 
-int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q, const void* W_DQ,
-               const void* W_UQ, const void* W_UK, const mla_cache* cache, const int32_t* block_table,
-               int32_t max_pages, const int32_t* seqlens, float softmax_scale, int32_t num_splits, void* ws,
-               size_t ws_bytes, void* stream) {
+static int decode_impl(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q,
+                       const void* W_DQ, const void* W_UQ, const void* W_UK, const mla_cache* cache,
+                       const int32_t* block_table, int32_t max_pages, const int32_t* seqlens, float softmax_scale,
+                       int32_t num_splits, void* ws, size_t ws_bytes, void* stream, int parts) {
   int st = check_dims(dims);
   if (st) return st;
   if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
@@ -149,10 +157,35 @@ int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t 
   a.L = ws_layout(*dims, act_dtype, batch, s_q, a.S);
   if (ws_bytes < a.L.total) return MLA_ERR_WORKSPACE;
   a.ws = (uint8_t*)ws; a.stream = (hipStream_t)stream;
-  hipError_t e;
-  if (!force_generic() && fast_decode_supported(*dims, act_dtype, cache->dtype, s_q)) e = fast_decode(a);
-  else e = generic_decode(a);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  const bool fast = !force_generic() && fast_decode_supported(*dims, act_dtype, cache->dtype, s_q);
+  hipError_t e = hipSuccess;
+  if (parts & 1) e = fast ? fast_query(a) : generic_query(a);
+  if (e == hipSuccess && (parts & 2)) e = fast ? fast_attention(a) : generic_attention(a);
+  return hip_status(e);
+}
+
+int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q, const void* W_DQ,
+               const void* W_UQ, const void* W_UK, const mla_cache* cache, const int32_t* block_table,
+               int32_t max_pages, const int32_t* seqlens, float softmax_scale, int32_t num_splits, void* ws,
+               size_t ws_bytes, void* stream) {
+  return decode_impl(dims, act_dtype, hq, batch, s_q, W_DQ, W_UQ, W_UK, cache, block_table, max_pages, seqlens,
+                     softmax_scale, num_splits, ws, ws_bytes, stream, 3);
+}
+
+int mla_decode_query(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q,
+                     const void* W_DQ, const void* W_UQ, const void* W_UK, const mla_cache* cache,
+                     const int32_t* block_table, int32_t max_pages, const int32_t* seqlens, float softmax_scale,
+                     int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(dims, act_dtype, hq, batch, s_q, W_DQ, W_UQ, W_UK, cache, block_table, max_pages, seqlens,
+                     softmax_scale, num_splits, ws, ws_bytes, stream, 1);
+}
+
+int mla_decode_attend(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q,
+                      const void* W_DQ, const void* W_UQ, const void* W_UK, const mla_cache* cache,
+                      const int32_t* block_table, int32_t max_pages, const int32_t* seqlens, float softmax_scale,
+                      int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(dims, act_dtype, hq, batch, s_q, W_DQ, W_UQ, W_UK, cache, block_table, max_pages, seqlens,
+                     softmax_scale, num_splits, ws, ws_bytes, stream, 2);
 }
 
 int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t s_q, const void* ws, size_t ws_bytes,
@@ -176,7 +209,7 @@ int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t 
   hipError_t e;
   if (!force_generic() && fast_decode_supported(*dims, act_dtype, MLA_BF16, s_q)) e = fast_combine(a);
   else e = generic_combine(a);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return hip_status(e);
 }
 
 const char* mla_status_str(int s) {
@@ -191,6 +224,10 @@ const char* mla_status_str(int s) {
     case MLA_ERR_HIP: return "HIP runtime error while enqueueing";
     default: return "unknown status";
   }
+}
+
+const char* mla_last_hip_error(void) {
+  return t_last_hip == hipSuccess ? "none" : hipGetErrorString(t_last_hip);
 }
 
 const char* mla_version(void) { return "libmla gfx950 (generic VALU + MFMA decode kernels)"; }

@@ -2,6 +2,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <tuple>
+#include <utility>
 #include "../../include/mla.h"
 
 typedef __bf16 bf16_t;
@@ -12,6 +14,28 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 namespace mla {
+
+// Kernel launch that returns this launch's own status (no dependence on the
+// thread's sticky last-error state).
+template <typename K, typename Tup, size_t... I>
+inline hipError_t launch_impl(K kern, dim3 grid, dim3 block, size_t shmem, hipStream_t st, Tup& a,
+                              std::index_sequence<I...>) {
+  void* p[] = {(void*)&std::get<I>(a)..., nullptr};
+  return hipLaunchKernel((const void*)kern, grid, block, p, shmem, st);
+}
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                         Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> a(std::forward<Args>(args)...);
+  return launch_impl(kern, grid, block, shmem, st, a, std::index_sequence_for<KArgs...>{});
+}
+
+#define MLA_TRY(x)                            \
+  do {                                        \
+    hipError_t e_ = (x);                      \
+    if (e_ != hipSuccess) return e_;          \
+  } while (0)
 
 // ---------------------------------------------------------------- scalars
 __device__ __forceinline__ float to_f32(float x) { return x; }

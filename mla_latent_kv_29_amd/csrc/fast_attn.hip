@@ -40,6 +40,11 @@ constexpr float RESCALE_SLACK = 8.0f;      // log2 headroom before O is rescaled
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
+// LDS-typed pointers keep address arithmetic in 32 bits with constant offsets
+// folded into the ds_read immediate field.
+typedef __attribute__((address_space(3))) uint8_t lu8;
+typedef __attribute__((address_space(3))) const bf16x8 lbf16x8;
+typedef __attribute__((address_space(3))) i16x4 li16x4;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -49,7 +54,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One 32-token half of a page into one LDS stage: 36 wave-instructions of
 // 1 KiB (chunks 2q and 2q+1), nine per wave.
-__device__ __forceinline__ void issue_stage(const uint8_t* page, int half, uint8_t* dst, int wave, int lane) {
+__device__ __forceinline__ void issue_stage(const uint8_t* page, int half, lu8* dst, int wave, int lane) {
   const uint8_t* src = page + (size_t)(lane >> 5) * (PAGE * 16) + half * (ST_T * 16) + (lane & 31) * 16;
 #pragma unroll
   for (int n = 0; n < 9; ++n) {
@@ -59,76 +64,100 @@ __device__ __forceinline__ void issue_stage(const uint8_t* page, int half, uint8
   }
 }
 
-__device__ __forceinline__ const uint8_t* stage_page(const uint8_t* pages, size_t page_bytes, const int32_t* bt_row,
-                                                     int t0) {
-  return pages + (size_t)bt_row[t0 / PAGE] * page_bytes;
-}
 
 // Everything a pass over the split needs.
 struct SplitCtx {
   const uint8_t* pages;
   size_t page_bytes;
   const int32_t* bt_row;
+  int p0;       // first page index (in the block-table row) of the split
+  int bt_lane;  // lane l holds bt_row[p0 + l] (first 64 pages of the split)
   int t_begin, ntok, nst;
-  uint8_t* lds;
+  lu8* lds;
   int wave, lane, cg;
   int kofs_even, kofs_odd, vofs1, vofs2, qr_x;
-  const uint8_t* qr_lds;
+  const lu8* qr_lds;
 };
 
 // S^T[32 tokens][32 heads] of one stage: 36 MFMAs, K fragments prefetched two
 // k-steps ahead, the absorbed query part from VGPRs, the RoPE part from LDS.
-__device__ __forceinline__ f32x16 stage_scores(const SplitCtx& c, const uint8_t* st, const bf16x8 (&qf)[32]) {
-  f32x16 sc = {};
-  bf16x8 ka = *(const bf16x8*)(st + c.kofs_even);
-  bf16x8 kb = *(const bf16x8*)(st + 1024 + c.kofs_odd);
+__device__ __forceinline__ f32x16 stage_scores(const SplitCtx& c, const lu8* st, const bf16x8 (&qf)[32]) {
+  // two independent accumulation chains (even / odd k-steps)
+  f32x16 s0 = {}, s1 = {};
+  const lu8* ke = st + c.kofs_even;
+  const lu8* ko = st + c.kofs_odd;
+  bf16x8 k0 = *(lbf16x8*)(ke);
+  bf16x8 k1 = *(lbf16x8*)(ko + 1024);
+  bf16x8 k2 = *(lbf16x8*)(ke + 2048);
+  bf16x8 k3 = *(lbf16x8*)(ko + 3072);
 #pragma unroll
-  for (int kk = 0; kk < 36; ++kk) {
-    bf16x8 kn = ka;
-    if (kk + 2 < 36) kn = *(const bf16x8*)(st + 1024 * (kk + 2) + ((kk & 1) ? c.kofs_odd : c.kofs_even));
-    bf16x8 qb;
-    if (kk < 32) qb = qf[kk];
-    else qb = *(const bf16x8*)(c.qr_lds + (((2 * (kk - 32) + c.cg) ^ c.qr_x) * 16));
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, sc, 0, 0, 0);
-    ka = kb;
-    kb = kn;
+  for (int kk = 0; kk < 36; kk += 2) {
+    bf16x8 n0 = k0, n1 = k1;
+    if (kk + 4 < 36) {
+      n0 = *(lbf16x8*)(ke + 1024 * (kk + 4));
+      n1 = *(lbf16x8*)(ko + 1024 * (kk + 5));
+    }
+    bf16x8 q0, q1;
+    if (kk < 32) {
+      q0 = qf[kk];
+      q1 = qf[kk + 1];
+    } else {
+      q0 = *(lbf16x8*)(c.qr_lds + (((2 * (kk - 32) + c.cg) ^ c.qr_x) * 16));
+      q1 = *(lbf16x8*)(c.qr_lds + (((2 * (kk + 1 - 32) + c.cg) ^ c.qr_x) * 16));
+    }
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q0, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q1, s1, 0, 0, 0);
+    k0 = k2;
+    k1 = k3;
+    k2 = n0;
+    k3 = n1;
   }
-  return sc;
+  return s0 + s1;
+}
+
+// Page holding token t0 (block-table entries of the split are held in lanes).
+__device__ __forceinline__ const uint8_t* stage_page(const SplitCtx& c, int t0) {
+  const int idx = t0 / PAGE - c.p0;
+  const int page = idx < 64 ? __builtin_amdgcn_readlane(c.bt_lane, idx) : c.bt_row[t0 / PAGE];
+  return c.pages + (size_t)page * c.page_bytes;
 }
 
 // Issues the first two stages of a pass into the ring.
 __device__ __forceinline__ void prologue(const SplitCtx& c) {
   for (int k = 0; k < 2 && k < c.nst; ++k) {
     const int t0 = c.t_begin + k * ST_T;
-    issue_stage(stage_page(c.pages, c.page_bytes, c.bt_row, t0), (t0 / ST_T) & 1, c.lds + k * ST_BYTES, c.wave,
+    issue_stage(stage_page(c, t0), (t0 / ST_T) & 1, c.lds + k * ST_BYTES, c.wave,
                 c.lane);
   }
 }
 
 // Waits for stage k, then refills the ring slot that stage k-1 used.
-__device__ __forceinline__ const uint8_t* advance(const SplitCtx& c, int k) {
+__device__ __forceinline__ const lu8* advance(const SplitCtx& c, int k) {
   if (k + 1 < c.nst) wait_vmcnt<9>();
   else wait_vmcnt<0>();
   __syncthreads();
   if (k + 2 < c.nst) {
     const int t0 = c.t_begin + (k + 2) * ST_T;
-    issue_stage(stage_page(c.pages, c.page_bytes, c.bt_row, t0), (t0 / ST_T) & 1, c.lds + ((k + 2) % NST) * ST_BYTES,
+    issue_stage(stage_page(c, t0), (t0 / ST_T) & 1, c.lds + ((k + 2) % NST) * ST_BYTES,
                 c.wave, c.lane);
   }
   return c.lds + (k % NST) * ST_BYTES;
 }
 
-// Masks the scores of tokens past the end of the split, returns the row max
-// over this lane's 16 tokens.
+// Masks the scores of tokens past the end of the split (only the last stage
+// can be partial), returns the row max over this lane's 16 tokens.
 __device__ __forceinline__ float mask_max(const SplitCtx& c, f32x16& sc, int k) {
-  const int nvalid = min(ST_T, c.ntok - k * ST_T);
-  float mloc = -INFINITY;
+  const int nvalid = c.ntok - k * ST_T;
+  if (nvalid < ST_T) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = 8 * (r >> 2) + 4 * c.cg + (r & 3);
-    if (t >= nvalid) sc[r] = -INFINITY;
-    mloc = fmaxf(mloc, sc[r]);
+    for (int r = 0; r < 16; ++r) {
+      const int t = 8 * (r >> 2) + 4 * c.cg + (r & 3);
+      if (t >= nvalid) sc[r] = -INFINITY;
+    }
   }
+  float mloc = sc[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sc[r]);
   return mloc;
 }
 
@@ -144,7 +173,7 @@ __device__ __forceinline__ bool attend_pass(const SplitCtx& c, const bf16x8 (&qf
   prologue(c);
   bool ovf = false;
   for (int k = 0; k < c.nst; ++k) {
-    const uint8_t* st = advance(c, k);
+    const lu8* st = advance(c, k);
     f32x16 sc = stage_scores(c, st, qf);
     float mloc = mask_max(c, sc, k);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
@@ -154,21 +183,29 @@ __device__ __forceinline__ bool attend_pass(const SplitCtx& c, const bf16x8 (&qf
     float ls = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const bf16_t pv = (bf16_t)exp2f(fminf(sc[r] - m_ref, HEADROOM));
-      ls += (float)pv;
-      pb[r >> 3][r & 7] = pv;
+      // raw v_exp_f32: results below 2^-126 flush to zero, harmless here
+      const float pv = __builtin_amdgcn_exp2f(fminf(sc[r] - m_ref, HEADROOM));
+      ls += pv;
+      pb[r >> 3][r & 7] = (bf16_t)pv;
     }
     l_run += ls;
 
-    // O^T[c][h] += V^T[c][t] P^T[t][h] for the stage's tokens 16hf..16hf+15
+    // O^T[c][h] += V^T[c][t] P^T[t][h] for the stage's tokens 16hf..16hf+15;
+    // consecutive MFMAs go to different accumulators
+    // The per-stage lane bases are made opaque so that the compiler keeps one
+    // base register each and folds every (cb, hf) offset into the instruction.
+    uint32_t b1 = (uint32_t)(uintptr_t)(st + c.vofs1), b2 = (uint32_t)(uintptr_t)(st + c.vofs2);
+    asm volatile("" : "+v"(b1), "+v"(b2));
+    const lu8* p1 = (const lu8*)(uintptr_t)b1;
+    const lu8* p2 = (const lu8*)(uintptr_t)b2;
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) {
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint8_t* a1 = st + cb * (4 * ST_T * 16) + hf * 256 + c.vofs1;
-        const uint8_t* a2 = st + cb * (4 * ST_T * 16) + hf * 256 + c.vofs2;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
+      for (int cb = 0; cb < 16; ++cb) {
+        const lu8* a1 = p1 + cb * (4 * ST_T * 16) + hf * 256;
+        const lu8* a2 = p2 + cb * (4 * ST_T * 16) + hf * 256;
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)a1);
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)a2);
         const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
         o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s8), pb[hf], o[cb], 0, 0, 0);
       }
@@ -182,7 +219,7 @@ __device__ __forceinline__ float max_pass(const SplitCtx& c, const bf16x8 (&qf)[
   prologue(c);
   float mx = -INFINITY;
   for (int k = 0; k < c.nst; ++k) {
-    const uint8_t* st = advance(c, k);
+    const lu8* st = advance(c, k);
     f32x16 sc = stage_scores(c, st, qf);
     mx = fmaxf(mx, mask_max(c, sc, k));
   }
@@ -192,10 +229,15 @@ __device__ __forceinline__ float max_pass(const SplitCtx& c, const bf16x8 (&qf)[
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
                     const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt,
-                    int max_pages, const int32_t* __restrict__ seqlens, float* __restrict__ opart,
-                    float* __restrict__ lpart) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+                    int max_pages, const int32_t* __restrict__ seqlens, bf16_t* __restrict__ opart,
+                    float* __restrict__ lpart, int32_t* __restrict__ hdr, int batch) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  lu8* lds = (lu8*)lds_raw;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // the split plan, for the combine
+    hdr[HDR_MAGIC] = WS_MAGIC; hdr[HDR_S] = S; hdr[HDR_PPS] = pps; hdr[HDR_BATCH] = batch;
+    hdr[HDR_SQ] = s_q; hdr[HDR_H] = H; hdr[HDR_DC] = DC; hdr[HDR_PDT] = MLA_BF16;
+  }
   const int RB = s_q;
   // The RB row blocks of one (b, s) share blockIdx % 8, i.e. one XCD and its
   // L2, and are dispatched next to each other.
@@ -217,13 +259,13 @@ void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restri
   const int cg = lane >> 5;  // lane half: k-group / token quad in the MFMA layouts
   const int hrow = wave * 32 + (lane & 31);
   const size_t prow = (((size_t)b * S + s) * s_q + j) * H + hrow;
-  float* orow = opart + prow * DC;
+  bf16_t* orow = opart + prow * DC;
 
   if (c.nst == 0) {
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) *(float4*)(orow + 32 * cb + 8 * r4 + 4 * cg) = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int r4 = 0; r4 < 4; ++r4) *(uint2*)(orow + 32 * cb + 8 * r4 + 4 * cg) = make_uint2(0u, 0u);
     if (cg == 0) lpart[prow] = -INFINITY;
     return;
   }
@@ -247,6 +289,11 @@ void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restri
   c.pages = pages;
   c.page_bytes = page_bytes;
   c.bt_row = bt + (size_t)b * max_pages;
+  c.p0 = c.t_begin / PAGE;
+  {
+    const int np = (c.ntok + PAGE - 1) / PAGE;
+    c.bt_lane = lane < np ? c.bt_row[c.p0 + lane] : 0;
+  }
   c.lds = lds;
   c.wave = wave;
   c.lane = lane;
@@ -290,9 +337,12 @@ void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restri
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *(float4*)(orow + 32 * cb + 8 * r4 + 4 * cg) =
-          make_float4(o[cb][4 * r4] * inv, o[cb][4 * r4 + 1] * inv, o[cb][4 * r4 + 2] * inv, o[cb][4 * r4 + 3] * inv);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16_t)(o[cb][4 * r4 + e] * inv);
+      *(bf16x4*)(orow + 32 * cb + 8 * r4 + 4 * cg) = v;
+    }
     __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time through VGPRs
   }
   if (cg == 0) lpart[prow] = m_ref + log2f(l_tot);
@@ -311,10 +361,11 @@ hipError_t fast_attention(const DecodeArgs& a) {
   const int P_items = a.batch * a.S;
   const int RB = a.s_q;
   const int grid = ((P_items + 7) / 8) * 8 * RB;
-  hipLaunchKernelGGL(k_attn_v3_bf16, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split,
+  MLA_TRY(launch(&k_attn_v3_bf16, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split,
                      P_items, (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages,
-                     a.seqlens, (float*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart));
-  return hipGetLastError();
+                     a.seqlens, (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header),
+                     a.batch));
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -230,8 +230,9 @@ __global__ __launch_bounds__(256) void k_combine_generic(int batch, int H, int s
   extern __shared__ float olat[];
   float* wsm = olat + d_c;  // S weights
   const int S = ((const int32_t*)ws)[HDR_S];
+  const bool pbf16 = ((const int32_t*)ws)[HDR_PDT] == MLA_BF16;
   const float* lpart = (const float*)(ws + lpart_off);
-  const float* opart = (const float*)(ws + opart_offset(lpart_off, batch, S, s_q, H));
+  const uint8_t* opart = ws + opart_offset(lpart_off, batch, S, s_q, H);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x, i = row % H, bj = row / H, j = bj % s_q, b = bj / s_q;
   auto prow = [&](int s) { return (((size_t)b * S + s) * s_q + j) * H + i; };
@@ -249,7 +250,8 @@ __global__ __launch_bounds__(256) void k_combine_generic(int batch, int H, int s
   for (int c = tid; c < d_c; c += blockDim.x) {
     float a = 0.0f;
     for (int s = 0; s < S; ++s)
-      if (wsm[s] != 0.0f) a += wsm[s] * opart[prow(s) * d_c + c];
+      if (wsm[s] != 0.0f)
+        a += wsm[s] * (pbf16 ? (float)((const bf16_t*)opart)[prow(s) * d_c + c] : ((const float*)opart)[prow(s) * d_c + c]);
     olat[c] = a * invW;
   }
   __syncthreads();
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(256) void k_combine_generic(int batch, int H, int s
 __global__ void k_write_header(int32_t* hdr, int S, int pps, int batch, int s_q, int H, int d_c) {
   if (threadIdx.x == 0) {
     hdr[HDR_MAGIC] = WS_MAGIC; hdr[HDR_S] = S; hdr[HDR_PPS] = pps; hdr[HDR_BATCH] = batch;
-    hdr[HDR_SQ] = s_q; hdr[HDR_H] = H; hdr[HDR_DC] = d_c;
+    hdr[HDR_SQ] = s_q; hdr[HDR_H] = H; hdr[HDR_DC] = d_c; hdr[HDR_PDT] = MLA_F32;
   }
 }
 
@@ -274,33 +276,33 @@ __global__ void k_write_header(int32_t* hdr, int S, int pps, int batch, int s_q,
 hipError_t generic_append(const AppendArgs& a) {
   const size_t lds = (size_t)(a.g.d_c + a.g.d_rope) * 4;
   if (a.act == MLA_F32)
-    hipLaunchKernelGGL((k_latent_row<float, 0>), dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
+    MLA_TRY(launch(&k_latent_row<float, 0>, dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
                        a.d.rope_theta, (const float*)a.h, (const float*)nullptr, a.seq_id, a.pos,
-                       (const float*)a.W_DKV, (const float*)a.W_KR, a.pages, a.block_table, a.max_pages);
+                       (const float*)a.W_DKV, (const float*)a.W_KR, a.pages, a.block_table, a.max_pages));
   else
-    hipLaunchKernelGGL((k_latent_row<bf16_t, 0>), dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
+    MLA_TRY(launch(&k_latent_row<bf16_t, 0>, dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
                        a.d.rope_theta, (const bf16_t*)a.h, (const bf16_t*)nullptr, a.seq_id, a.pos,
-                       (const bf16_t*)a.W_DKV, (const bf16_t*)a.W_KR, a.pages, a.block_table, a.max_pages);
-  return hipGetLastError();
+                       (const bf16_t*)a.W_DKV, (const bf16_t*)a.W_KR, a.pages, a.block_table, a.max_pages));
+  return hipSuccess;
 }
 
 hipError_t generic_write(const AppendArgs& a) {
   const size_t lds = (size_t)(a.g.d_c + a.g.d_rope) * 4;
   if (a.act == MLA_F32)
-    hipLaunchKernelGGL((k_latent_row<float, 1>), dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
+    MLA_TRY(launch(&k_latent_row<float, 1>, dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
                        a.d.rope_theta, (const float*)a.h, (const float*)a.k_rope, a.seq_id, a.pos,
-                       (const float*)nullptr, (const float*)nullptr, a.pages, a.block_table, a.max_pages);
+                       (const float*)nullptr, (const float*)nullptr, a.pages, a.block_table, a.max_pages));
   else
-    hipLaunchKernelGGL((k_latent_row<bf16_t, 1>), dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
+    MLA_TRY(launch(&k_latent_row<bf16_t, 1>, dim3(a.n_tok), dim3(256), lds, a.stream, a.d.d_model, a.g,
                        a.d.rope_theta, (const bf16_t*)a.h, (const bf16_t*)a.k_rope, a.seq_id, a.pos,
-                       (const bf16_t*)nullptr, (const bf16_t*)nullptr, a.pages, a.block_table, a.max_pages);
-  return hipGetLastError();
+                       (const bf16_t*)nullptr, (const bf16_t*)nullptr, a.pages, a.block_table, a.max_pages));
+  return hipSuccess;
 }
 
 hipError_t write_header(const DecodeArgs& a) {
-  hipLaunchKernelGGL(k_write_header, dim3(1), dim3(64), 0, a.stream, (int32_t*)(a.ws + a.L.header), a.S,
-                     a.pages_per_split, a.batch, a.s_q, a.d.n_heads, a.d.d_c);
-  return hipGetLastError();
+  MLA_TRY(launch(&k_write_header, dim3(1), dim3(64), 0, a.stream, (int32_t*)(a.ws + a.L.header), a.S,
+                     a.pages_per_split, a.batch, a.s_q, a.d.n_heads, a.d.d_c));
+  return hipSuccess;
 }
 
 template <typename T>
@@ -314,19 +316,19 @@ static hipError_t generic_query_t(const DecodeArgs& a) {
   if (a.W_DQ) {
     float* cq = (float*)(a.ws + a.L.cq_part);
     const long n1 = (long)R * d.d_cq;
-    hipLaunchKernelGGL((k_gemm_xwT<T, T>), dim3((unsigned)((n1 + 3) / 4)), dim3(256), 0, a.stream, R, d.d_cq,
-                       d.d_model, (const T*)a.hq, (const T*)a.W_DQ, cq);
-    hipLaunchKernelGGL((k_gemm_xwT<float, T>), dim3((unsigned)((nu + 3) / 4)), dim3(256), 0, a.stream, R,
-                       H * (d.d_head + d.d_rope), d.d_cq, (const float*)cq, (const T*)a.W_UQ, u);
+    MLA_TRY(launch(&k_gemm_xwT<T, T>, dim3((unsigned)((n1 + 3) / 4)), dim3(256), 0, a.stream, R, d.d_cq,
+                       d.d_model, (const T*)a.hq, (const T*)a.W_DQ, cq));
+    MLA_TRY(launch(&k_gemm_xwT<float, T>, dim3((unsigned)((nu + 3) / 4)), dim3(256), 0, a.stream, R,
+                       H * (d.d_head + d.d_rope), d.d_cq, (const float*)cq, (const T*)a.W_UQ, u));
   } else {
-    hipLaunchKernelGGL((k_gemm_xwT<T, T>), dim3((unsigned)((nu + 3) / 4)), dim3(256), 0, a.stream, R,
-                       H * (d.d_head + d.d_rope), d.d_cq, (const T*)a.hq, (const T*)a.W_UQ, u);
+    MLA_TRY(launch(&k_gemm_xwT<T, T>, dim3((unsigned)((nu + 3) / 4)), dim3(256), 0, a.stream, R,
+                       H * (d.d_head + d.d_rope), d.d_cq, (const T*)a.hq, (const T*)a.W_UQ, u));
   }
-  hipLaunchKernelGGL((k_qrope_generic<T>), dim3(R * H), dim3(64), 0, a.stream, H, a.s_q, d.d_head, d.d_rope, d.d_c,
-                     d.rope_theta, scale2, a.seqlens, (const float*)u, qt);
-  hipLaunchKernelGGL((k_absorb_generic<T, T>), dim3(R * H), dim3(256), 0, a.stream, H, d.d_head, d.d_rope, d.d_c,
-                     scale2, (const float*)u, (const T*)a.W_UK, qt);
-  return hipGetLastError();
+  MLA_TRY(launch(&k_qrope_generic<T>, dim3(R * H), dim3(64), 0, a.stream, H, a.s_q, d.d_head, d.d_rope, d.d_c,
+                     d.rope_theta, scale2, a.seqlens, (const float*)u, qt));
+  MLA_TRY(launch(&k_absorb_generic<T, T>, dim3(R * H), dim3(256), 0, a.stream, H, d.d_head, d.d_rope, d.d_c,
+                     scale2, (const float*)u, (const T*)a.W_UK, qt));
+  return hipSuccess;
 }
 
 template <typename T>
@@ -334,10 +336,10 @@ static hipError_t generic_attention_t(const DecodeArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
   const size_t lds = (size_t)(d.d_c + d.d_rope + 256 + 8) * 4;
-  hipLaunchKernelGGL((k_attn_generic<T>), dim3(R * H, a.S), dim3(256), lds, a.stream, H, a.s_q, a.g,
+  MLA_TRY(launch(&k_attn_generic<T>, dim3(R * H, a.S), dim3(256), lds, a.stream, H, a.s_q, a.g,
                      (const T*)(a.ws + a.L.qt), a.pages, a.block_table, a.max_pages, a.seqlens, a.S,
-                     a.pages_per_split, (float*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart));
-  return hipGetLastError();
+                     a.pages_per_split, (float*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart)));
+  return hipSuccess;
 }
 
 hipError_t generic_query(const DecodeArgs& a) {
@@ -347,6 +349,10 @@ hipError_t generic_query(const DecodeArgs& a) {
 }
 
 hipError_t generic_attention(const DecodeArgs& a) {
+  // the header is rewritten so that an attend-only call after a query call
+  // with other arguments still leaves a consistent plan for the combine
+  hipError_t e = write_header(a);
+  if (e != hipSuccess) return e;
   return a.act == MLA_F32 ? generic_attention_t<float>(a) : generic_attention_t<bf16_t>(a);
 }
 
@@ -361,14 +367,14 @@ hipError_t generic_combine(const CombineArgs& a) {
   const int R = a.batch * a.s_q;
   const size_t lds = (size_t)(d.d_c + MAX_SPLITS) * 4;
   if (a.act == MLA_F32)
-    hipLaunchKernelGGL((k_combine_generic<float>), dim3(R * d.n_heads), dim3(256), lds, a.stream, a.batch,
+    MLA_TRY(launch(&k_combine_generic<float>, dim3(R * d.n_heads), dim3(256), lds, a.stream, a.batch,
                        d.n_heads, a.s_q, d.d_head, d.d_c, a.ws, a.L.lpart, (const float*)a.W_UV, (float*)a.out,
-                       a.lse_out);
+                       a.lse_out));
   else
-    hipLaunchKernelGGL((k_combine_generic<bf16_t>), dim3(R * d.n_heads), dim3(256), lds, a.stream, a.batch,
+    MLA_TRY(launch(&k_combine_generic<bf16_t>, dim3(R * d.n_heads), dim3(256), lds, a.stream, a.batch,
                        d.n_heads, a.s_q, d.d_head, d.d_c, a.ws, a.L.lpart, (const bf16_t*)a.W_UV,
-                       (bf16_t*)a.out, a.lse_out);
-  return hipGetLastError();
+                       (bf16_t*)a.out, a.lse_out));
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -14,7 +14,8 @@ namespace mla {
 //   u        : f32 [R][H][d_head+d_rope]   W^UQ c^Q (bf16 q^C for the MFMA path)
 //   qt       : act [R][H][d_c+d_rope]      absorbed, scaled query [q_abs | q^R]
 //   lpart    : f32 [B][S][s_q][H]          per-split log2-sum-exp2 of scores
-//   opart    : f32 [B][S][s_q][H][d_c]     per-split normalised latent outputs
+//   opart    : f32 or bf16 [B][S][s_q][H][d_c]  per-split normalised latent outputs
+//                                        (sized for f32; element type in the header)
 // R = batch * s_q.  Everything up to lpart is independent of the split count
 // S; opart follows lpart, so a kernel that reads S from the header finds it
 // with opart_offset().
@@ -50,7 +51,8 @@ inline WsLayout ws_layout(const mla_dims& d, int act, int batch, int s_q, int S)
 }
 
 // Header fields (int32 indices).
-enum { HDR_MAGIC = 0, HDR_S = 1, HDR_PPS = 2, HDR_BATCH = 3, HDR_SQ = 4, HDR_H = 5, HDR_DC = 6 };
+enum { HDR_MAGIC = 0, HDR_S = 1, HDR_PPS = 2, HDR_BATCH = 3, HDR_SQ = 4, HDR_H = 5, HDR_DC = 6, HDR_PDT = 7 };
+// HDR_PDT: element type of opart, MLA_F32 or MLA_BF16 (the MFMA attention writes bf16)
 
 struct DecodeArgs {
   mla_dims d;
@@ -106,11 +108,14 @@ hipError_t generic_attention(const DecodeArgs& a);   // qt + cache -> per-split 
 hipError_t generic_combine(const CombineArgs& a);
 hipError_t write_header(const DecodeArgs& a);
 
-bool fast_append_supported(const mla_dims& d, int act);
+bool fast_append_supported(const mla_dims& d, int act, int cache_dtype);
+bool fast_append_shape(const mla_dims& d);
 bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q);
 hipError_t fast_append(const AppendArgs& a);
 hipError_t fast_decode(const DecodeArgs& a);
 hipError_t fast_combine(const CombineArgs& a);
 hipError_t fast_attention(const DecodeArgs& a);
+hipError_t fast_query(const DecodeArgs& a);
+hipError_t fast_combine_mfma(const CombineArgs& a);
 
 }  // namespace mla
