@@ -10,7 +10,8 @@ using namespace mla;
 namespace {
 
 constexpr int MAX_S_Q = 8;
-constexpr int TARGET_ITEMS = 512;  // (sequence, row block, split) work items aimed for per decode
+constexpr int TARGET_ITEMS = 256;  // (sequence, query, split) work items aimed for per decode: one per CU
+constexpr int MAX_PAGES_PER_SPLIT = 64;  // caps one item's work so that ragged batches balance
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -120,6 +121,8 @@ int32_t mla_default_splits(const mla_dims* dims, int32_t batch, int32_t s_q, int
   const int row_blocks = (rows + 127) / 128;
   long items = (long)batch * row_blocks;
   int s = (int)((TARGET_ITEMS + items - 1) / items);
+  const int s_cap = (max_pages + MAX_PAGES_PER_SPLIT - 1) / MAX_PAGES_PER_SPLIT;
+  if (s < s_cap) s = s_cap;
   if (s > max_pages) s = max_pages;
   if (s > MAX_SPLITS) s = MAX_SPLITS;
   return s < 1 ? 1 : s;

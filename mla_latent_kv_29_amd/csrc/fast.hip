@@ -14,7 +14,8 @@ bool fast_append_supported(const mla_dims& d, int act, int cache_dtype) {
 }
 
 bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q) {
-  return v3_shape(d) && act == MLA_BF16 && cache_dtype == MLA_BF16 && s_q >= 1 && s_q <= 8;
+  return v3_shape(d) && act == MLA_BF16 && (cache_dtype == MLA_BF16 || cache_dtype == MLA_FP8_E4M3) && s_q >= 1 &&
+         s_q <= 8;
 }
 
 hipError_t fast_decode(const DecodeArgs& a) {

@@ -1,5 +1,5 @@
 // Split-KV MLA decode attention on MFMA for the DeepSeek-V3 shape
-// (d_c 512, d_rope 64, 128 heads, 64-token bf16 pages), gfx950.
+// (d_c 512, d_rope 64, 128 heads, 64-token bf16 or fp8 pages), gfx950.
 //
 // What it computes (absorbed form; DeepSeek-V3 reading lesson, §2.1.1 and
 // Question 2): for every query row (head i, query j) of sequence b and every
@@ -23,6 +23,13 @@
 // 512-wide absorbed part (128 VGPRs) and O (256 AGPRs) fit one wave per SIMD.
 // The chunk-major swizzled page layout (layout.hpp) makes that copy verbatim
 // and both LDS access patterns bank-conflict free.
+//
+// FP8 cache (E4M3 codes with one fp32 scale per token and 1x128 channel tile,
+// lesson §3.3; bf16 k^R): a 4-deep ring of fp8 half-page stages (20 992 B
+// each) is filled the same way; each stage is then widened in LDS, by the
+// whole block, to the bf16 stage image (code * scale, rounded once to bf16),
+// and the bf16 compute above runs on it.  Products stay bf16 x bf16 with fp32
+// accumulation.
 #include "internal.hpp"
 #include "layout.hpp"
 
@@ -36,7 +43,16 @@ constexpr int NST = 3;                     // stages in the LDS ring
 constexpr int ST_BYTES = NCH * ST_T * 16;  // 36 864
 constexpr int QR_OFF = NST * ST_BYTES;     // q^R rows of the 128 heads: 128 x 64 bf16
 constexpr int LDS_BYTES = QR_OFF + H * 64 * 2;  // 126 976
-constexpr float RESCALE_SLACK = 8.0f;      // log2 headroom before O is rescaled
+// FP8 layout: q^R at 0, the bf16 work stage, then the fp8 ring
+constexpr int F8_CODES = 32 * ST_T * 16;   // 16 384: 32 sixteen-channel chunks x 32 tokens
+constexpr int F8_SCALES = ST_T * 16;       // 512: 4 fp32 scales per token
+constexpr int F8_ROPE = 8 * ST_T * 16;     // 4 096: 8 chunks x 32 tokens
+constexpr int F8_BYTES = F8_CODES + F8_SCALES + F8_ROPE;  // 20 992
+constexpr int NST8 = 4;
+constexpr int F8_QR_OFF = 0;
+constexpr int F8_WORK_OFF = H * 64 * 2;
+constexpr int F8_RING_OFF = F8_WORK_OFF + ST_BYTES;
+constexpr int LDS_BYTES_FP8 = F8_RING_OFF + NST8 * F8_BYTES;  // 137 216
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
@@ -77,6 +93,10 @@ struct SplitCtx {
   int wave, lane, cg;
   int kofs_even, kofs_odd, vofs1, vofs2, qr_x;
   const lu8* qr_lds;
+  // fp8 pages: offsets of the scale and rope blocks inside a page, and the
+  // 1 KiB load instructions this wave issues per stage (6 or 5)
+  size_t f8_scale_off, f8_rope_off;
+  int f8_issue;
 };
 
 // S^T[32 tokens][32 heads] of one stage: 36 MFMAs, K fragments prefetched two
@@ -123,7 +143,7 @@ __device__ __forceinline__ const uint8_t* stage_page(const SplitCtx& c, int t0) 
 }
 
 // Issues the first two stages of a pass into the ring.
-__device__ __forceinline__ void prologue(const SplitCtx& c) {
+__device__ __forceinline__ void prologue_bf16(const SplitCtx& c) {
   for (int k = 0; k < 2 && k < c.nst; ++k) {
     const int t0 = c.t_begin + k * ST_T;
     issue_stage(stage_page(c, t0), (t0 / ST_T) & 1, c.lds + k * ST_BYTES, c.wave,
@@ -132,7 +152,7 @@ __device__ __forceinline__ void prologue(const SplitCtx& c) {
 }
 
 // Waits for stage k, then refills the ring slot that stage k-1 used.
-__device__ __forceinline__ const lu8* advance(const SplitCtx& c, int k) {
+__device__ __forceinline__ const lu8* advance_bf16(const SplitCtx& c, int k) {
   if (k + 1 < c.nst) wait_vmcnt<9>();
   else wait_vmcnt<0>();
   __syncthreads();
@@ -142,6 +162,99 @@ __device__ __forceinline__ const lu8* advance(const SplitCtx& c, int k) {
                 c.wave, c.lane);
   }
   return c.lds + (k % NST) * ST_BYTES;
+}
+
+// fp8 half-page stage k: 21 instructions of 1 KiB -- 16 for the codes (chunks
+// 2q, 2q+1), one for the 32 tokens' scales (lanes 0..31), four for the rope
+// chunks -- instruction i issued by wave i % 4.
+__device__ __forceinline__ void issue_fp8(const SplitCtx& c, int k) {
+  const int t0 = c.t_begin + k * ST_T;
+  const int half = (t0 / ST_T) & 1;
+  const uint8_t* page = stage_page(c, t0);
+  lu8* dst = c.lds + F8_RING_OFF + (k % NST8) * F8_BYTES;
+  const int lofs = (c.lane >> 5) * (PAGE * 16) + half * (ST_T * 16) + (c.lane & 31) * 16;
+#pragma unroll
+  for (int n = 0; n < 6; ++n) {
+    const int i = c.wave + 4 * n;
+    if (i < 16) {
+      __builtin_amdgcn_global_load_lds((gbl_void*)(page + (size_t)(2 * i) * (PAGE * 16) + lofs),
+                                       (lds_void*)(dst + i * 1024), 16, 0, 0);
+    } else if (i == 16) {
+      if (c.lane < 32)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(page + c.f8_scale_off + (size_t)(half * ST_T + c.lane) * 16),
+                                         (lds_void*)(dst + F8_CODES), 16, 0, 0);
+    } else if (i < 21) {
+      __builtin_amdgcn_global_load_lds((gbl_void*)(page + c.f8_rope_off + (size_t)(2 * (i - 17)) * (PAGE * 16) + lofs),
+                                       (lds_void*)(dst + F8_CODES + F8_SCALES + (i - 17) * 1024), 16, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void prologue_fp8(const SplitCtx& c) {
+  for (int k = 0; k < NST8 - 1 && k < c.nst; ++k) issue_fp8(c, k);
+}
+
+// Widens fp8 stage k into the bf16 stage image: thread handles token tid%32,
+// bf16 chunks tid/32 + 8n (n < 8) and rope chunk tid/32.
+__device__ __forceinline__ void widen_fp8(const lu8* src, lu8* dst, int tid) {
+  const int t = tid & 31, c0 = tid >> 5;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int c = c0 + 8 * n;  // 8-channel chunk, 0..63
+    const int C8 = c >> 1;     // 16-channel fp8 chunk
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 code =
+        *(__attribute__((address_space(3))) const u32x2*)(src + 16 * (C8 * ST_T + (t ^ (4 * (C8 & 3)))) + 8 * (c & 1));
+    const float sc = *(__attribute__((address_space(3))) const float*)(src + F8_CODES + 16 * t + 4 * (c >> 4));
+    bf16x8 v;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t word = code[w];
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+      v[4 * w + 0] = (bf16_t)(lo[0] * sc);
+      v[4 * w + 1] = (bf16_t)(lo[1] * sc);
+      v[4 * w + 2] = (bf16_t)(hi[0] * sc);
+      v[4 * w + 3] = (bf16_t)(hi[1] * sc);
+    }
+    *(__attribute__((address_space(3))) bf16x8*)(dst + 16 * (c * ST_T + (t ^ (4 * (c & 3))))) = v;
+  }
+  {
+    const int m = c0;  // rope chunk 0..7, same swizzle in source and destination
+    const bf16x8 r = *(lbf16x8*)(src + F8_CODES + F8_SCALES + 16 * (m * ST_T + (t ^ (4 * (m & 3)))));
+    *(__attribute__((address_space(3))) bf16x8*)(dst + 16 * ((64 + m) * ST_T + (t ^ (4 * (m & 3))))) = r;
+  }
+}
+
+// Waits for fp8 stage k, refills the ring slot of stage k-1, widens stage k
+// into the work image (once every wave is done with the previous one).
+__device__ __forceinline__ const lu8* advance_fp8(const SplitCtx& c, int k) {
+  const int after = min(NST8 - 2, c.nst - 1 - k);
+  if (c.f8_issue == 6) {
+    if (after >= 2) wait_vmcnt<12>();
+    else if (after == 1) wait_vmcnt<6>();
+    else wait_vmcnt<0>();
+  } else {
+    if (after >= 2) wait_vmcnt<10>();
+    else if (after == 1) wait_vmcnt<5>();
+    else wait_vmcnt<0>();
+  }
+  __syncthreads();
+  if (k + NST8 - 1 < c.nst) issue_fp8(c, k + NST8 - 1);
+  lu8* work = c.lds + F8_WORK_OFF;
+  widen_fp8(c.lds + F8_RING_OFF + (k % NST8) * F8_BYTES, work, c.wave * 64 + c.lane);
+  __syncthreads();
+  return work;
+}
+
+template <bool FP8>
+__device__ __forceinline__ void prologue(const SplitCtx& c) {
+  if (FP8) prologue_fp8(c);
+  else prologue_bf16(c);
+}
+template <bool FP8>
+__device__ __forceinline__ const lu8* advance(const SplitCtx& c, int k) {
+  return FP8 ? advance_fp8(c, k) : advance_bf16(c, k);
 }
 
 // Masks the scores of tokens past the end of the split (only the last stage
@@ -168,12 +281,13 @@ constexpr float HEADROOM = 96.0f;
 // false, m_ref is set to the first stage's maximum and the return value says
 // whether a later score rose more than HEADROOM above it in some row of the
 // wave; with fixed == true m_ref is the exact maximum of the split.
+template <bool FP8>
 __device__ __forceinline__ bool attend_pass(const SplitCtx& c, const bf16x8 (&qf)[32], bool fixed, float& m_ref,
                                             f32x16 (&o)[16], float& l_run) {
-  prologue(c);
+  prologue<FP8>(c);
   bool ovf = false;
   for (int k = 0; k < c.nst; ++k) {
-    const lu8* st = advance(c, k);
+    const lu8* st = advance<FP8>(c, k);
     f32x16 sc = stage_scores(c, st, qf);
     float mloc = mask_max(c, sc, k);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
@@ -215,22 +329,24 @@ __device__ __forceinline__ bool attend_pass(const SplitCtx& c, const bf16x8 (&qf
 }
 
 // Scores only: the exact row maximum over the split.
+template <bool FP8>
 __device__ __forceinline__ float max_pass(const SplitCtx& c, const bf16x8 (&qf)[32]) {
-  prologue(c);
+  prologue<FP8>(c);
   float mx = -INFINITY;
   for (int k = 0; k < c.nst; ++k) {
-    const lu8* st = advance(c, k);
+    const lu8* st = advance<FP8>(c, k);
     f32x16 sc = stage_scores(c, st, qf);
     mx = fmaxf(mx, mask_max(c, sc, k));
   }
   return fmaxf(mx, __shfl_xor(mx, 32, 64));
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
-                    const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt,
-                    int max_pages, const int32_t* __restrict__ seqlens, bf16_t* __restrict__ opart,
-                    float* __restrict__ lpart, int32_t* __restrict__ hdr, int batch) {
+void k_attn_v3(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
+               const uint8_t* __restrict__ pages, size_t page_bytes, size_t f8_scale_off, size_t f8_rope_off,
+               const int32_t* __restrict__ bt, int max_pages, const int32_t* __restrict__ seqlens,
+               bf16_t* __restrict__ opart, float* __restrict__ lpart, int32_t* __restrict__ hdr, int batch) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lu8* lds = (lu8*)lds_raw;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -283,7 +399,7 @@ void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restri
     const int i = wave + 4 * n;
     const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
     __builtin_amdgcn_global_load_lds((gbl_void*)(qblk + (size_t)h * DKV + DC + 8 * lc),
-                                     (lds_void*)(lds + QR_OFF + i * 1024), 16, 0, 0);
+                                     (lds_void*)(lds + (FP8 ? F8_QR_OFF : QR_OFF) + i * 1024), 16, 0, 0);
   }
 
   c.pages = pages;
@@ -301,7 +417,10 @@ void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restri
   const int tr = lane & 31;
   c.kofs_even = cg * (ST_T * 16) + (tr ^ (4 * cg)) * 16;       // chunk 2kk+cg, kk even
   c.kofs_odd = cg * (ST_T * 16) + (tr ^ (4 * (2 + cg))) * 16;  // chunk 2kk+cg, kk odd
-  c.qr_lds = lds + QR_OFF + hrow * 128;
+  c.qr_lds = lds + (FP8 ? F8_QR_OFF : QR_OFF) + hrow * 128;
+  c.f8_scale_off = f8_scale_off;
+  c.f8_rope_off = f8_rope_off;
+  c.f8_issue = wave == 0 ? 6 : 5;
   c.qr_x = (hrow >> 1) & 7;
   const int g16 = lane >> 4, i16 = lane & 15;
   const int tq = i16 >> 2, qq = i16 & 3;
@@ -321,10 +440,10 @@ void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restri
   bool fixed = false;
 #pragma clang loop unroll(disable)
   for (;;) {
-    const bool ovf = attend_pass(c, qf, fixed, m_ref, o, l_run);
+    const bool ovf = attend_pass<FP8>(c, qf, fixed, m_ref, o, l_run);
     __syncthreads();  // every wave is done with the ring
     if (fixed || !__syncthreads_or(ovf)) break;
-    m_ref = max_pass(c, qf);
+    m_ref = max_pass<FP8>(c, qf);
     __syncthreads();
     fixed = true;
     l_run = 0.0f;
@@ -351,20 +470,21 @@ void k_attn_v3_bf16(int s_q, int S, int pps, int P_items, const bf16_t* __restri
 }  // namespace
 
 hipError_t fast_attention(const DecodeArgs& a) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_v3_bf16, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  const bool fp8 = a.cache_dtype == MLA_FP8_E4M3;
+  auto kern = fp8 ? &k_attn_v3<true> : &k_attn_v3<false>;
+  const int lds = fp8 ? LDS_BYTES_FP8 : LDS_BYTES;
+  static bool attr_set[2] = {false, false};
+  if (!attr_set[fp8]) {
+    MLA_TRY(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    attr_set[fp8] = true;
   }
   const int P_items = a.batch * a.S;
   const int RB = a.s_q;
   const int grid = ((P_items + 7) / 8) * 8 * RB;
-  MLA_TRY(launch(&k_attn_v3_bf16, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split,
-                     P_items, (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages,
-                     a.seqlens, (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header),
-                     a.batch));
+  MLA_TRY(launch(kern, dim3(grid), dim3(256), lds, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
+                 (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.g.fp8_scale_off, a.g.fp8_rope_off,
+                 a.block_table, a.max_pages, a.seqlens, (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart),
+                 (int32_t*)(a.ws + a.L.header), a.batch));
   return hipSuccess;
 }
 

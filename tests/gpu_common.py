@@ -88,7 +88,61 @@ class Case:
             return oracle.decode_from_latents(c, r, hqb, Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], d, Lb,
                                               self.s_q, tau, heads)
         h = to_np(self.h(b, 0, Lb))
-        return oracle.decode_from_h(h, Wn, d, Lb, self.s_q, tau, heads)
+        if not fp8:
+            return oracle.decode_from_h(h, Wn, d, Lb, self.s_q, tau, heads)
+        c, kr = oracle.kv_latents(h, Wn["W_DKV"], Wn["W_KR"], np.arange(Lb), d["rope_theta"])
+        codes, scales = oracle.quantize_tiles(c)
+        c = oracle.dequantize_tiles(codes, scales)
+        kr = to_np(torch.from_numpy(kr).to(torch.bfloat16))   # the cache keeps k^R in bf16
+        hq = h[Lb - self.s_q:Lb]
+        return oracle.decode_from_latents(c, kr, hq, Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], d, Lb,
+                                          self.s_q, tau, heads)
+
+
+def bf16_page_off(t, ch, page_size):
+    """Byte offset of channel ch of token t in a chunk-major bf16 page (16-byte
+    chunks of 8 channels, token slot t ^ 4*(chunk % 4))."""
+    C = ch // 8
+    return 16 * (C * page_size + (t ^ (4 * (C % 4)))) + 2 * (ch % 8)
+
+
+def read_bf16_rows(pages, page_ids, dims):
+    """Cache rows [n_pages*page_size, d_c + d_rope] (float64) of a bf16 cache."""
+    ps, D = dims["page_size"], dims["d_c"] + dims["d_rope"]
+    raw = pages.cpu().numpy()
+    t = np.arange(ps)[:, None]
+    ch = np.arange(D)[None, :]
+    C = ch // 8
+    off = 16 * (C * ps + (t ^ (4 * (C % 4)))) + 2 * (ch % 8)
+    out = []
+    for p in page_ids:
+        b = raw[int(p)]
+        u16 = b[off].astype(np.uint16) | (b[off + 1].astype(np.uint16) << 8)
+        out.append((u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    return np.concatenate(out, 0)
+
+
+def read_fp8_rows(pages, page_ids, dims):
+    """(codes uint8 [n, d_c], scales f32 [n, d_c/128], rope f64 [n, d_rope]) of an fp8 cache."""
+    ps, dc, dr = dims["page_size"], dims["d_c"], dims["d_rope"]
+    raw = pages.cpu().numpy()
+    t = np.arange(ps)[:, None]
+    ch = np.arange(dc)[None, :]
+    C = ch // 16
+    coff = 16 * (C * ps + (t ^ (4 * (C % 4)))) + (ch % 16)
+    s_off = ps * dc
+    r_off = s_off + ps * (dc // 128) * 4
+    m = np.arange(dr)[None, :]
+    Cm = m // 8
+    roff = r_off + 16 * (Cm * ps + (t ^ (4 * (Cm % 4)))) + 2 * (m % 8)
+    codes, scales, rope = [], [], []
+    for p in page_ids:
+        b = raw[int(p)]
+        codes.append(b[coff])
+        scales.append(b[s_off:r_off].view(np.float32).reshape(ps, dc // 128))
+        u16 = b[roff].astype(np.uint16) | (b[roff + 1].astype(np.uint16) << 8)
+        rope.append((u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    return np.concatenate(codes, 0), np.concatenate(scales, 0), np.concatenate(rope, 0)
 
 
 def max_abs(a, b):
