@@ -9,10 +9,13 @@
 //
 // One kernel template: Y[M x N] = X[M x K] . B with B given either as W[N][K]
 // (k contiguous, "X W^T") or as W[K][N] (n contiguous, read with the gfx950
-// transposing LDS load).  64x64 output tile per 256-thread block, 32-deep k
-// steps through an NS-stage LDS ring filled by global_load_lds_dwordx4, four
-// waves of 32x32 (2x2 v_mfma_f32_16x16x32_bf16), optional split-K over
-// blockIdx.z and a batch (head) index in blockIdx.y.
+// transposing LDS load).  64x64 output tile per 256-thread block, 64-deep k
+// steps (whole 128-byte lines of every weight row) through an NS-stage LDS
+// ring filled by global_load_lds_dwordx4, four waves of 32x32 (2x2
+// v_mfma_f32_16x16x32_bf16, two k-halves per step), optional split-K over
+// blockIdx.z and a batch (head) index in blockIdx.y.  The decode GEMMs have
+// only 64-256 activation rows: they stream the weights, so what matters is
+// keeping enough full cache lines in flight per CU.
 #include "internal.hpp"
 
 namespace mla {
@@ -21,8 +24,9 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-constexpr int NS = 6;             // ring depth
-constexpr int TILE_BYTES = 4096;  // 64 rows x 32 k x bf16 (or 32 k x 64 n)
+constexpr int NS = 4;             // ring depth (three k-steps in flight)
+constexpr int BK = 64;
+constexpr int TILE_BYTES = 8192;  // 64 rows x 64 k x bf16 (or 64 k x 64 n)
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -35,32 +39,32 @@ __device__ __forceinline__ void wait_vmcnt() {
 struct GemmArgs {
   int M, N, K;              // per batch
   int mtiles;               // ceil(M / 64)
-  int k_per_split;          // multiple of 32
+  int k_per_split;          // multiple of BK
   const bf16_t* X;          // [batch][M][ldx]
   long ldx, bsx;
   const bf16_t* W;          // W_NK: [batch][N][ldw]; else [batch][K][ldw]
   long ldw, bsw;
 };
 
-// X-like tile: 64 rows x 32 k, row r chunk q (16 B) stored at r*4 + (q ^ ((r>>2)&3)).
-__device__ __forceinline__ int xtile_pos(int r, int q) { return r * 4 + (q ^ ((r >> 2) & 3)); }
-// K-major tile: 32 k-rows x 64 n, row k chunk q (8 n) stored at k*8 + (q ^ swz(k)).
+// Row tile: 64 rows x 64 k, row r chunk q (16 B, 8 k) stored at r*8 + (q ^ (r & 7)).
+__device__ __forceinline__ int xtile_pos(int r, int q) { return r * 8 + (q ^ (r & 7)); }
+// K-major tile: 64 k-rows x 64 n, row k chunk q (8 n) stored at k*8 + (q ^ swz(k)).
 __device__ __forceinline__ int ktile_pos(int k, int q) { return k * 8 + (q ^ (4 * ((k >> 1) & 1)) ^ (2 * ((k >> 3) & 1))); }
 
-// Copies one 64 x 32 row tile (rows r0.., columns k0..) into LDS: 4 instructions of
-// 1 KiB; instruction i covers LDS positions 64i..64i+63.  Rows >= rows_valid
-// read the last valid row (never stored).
+// Copies one 64 x 64 row tile (rows r0.., columns k0..) into LDS: 8 instructions of
+// 1 KiB (8 rows of 128 B each); instruction i covers LDS positions 64i..64i+63.
+// Rows >= rows_valid read the last valid row (never stored).
 __device__ __forceinline__ void load_rows_tile(const bf16_t* base, long ld, int r0, int rows_valid, int k0,
                                                uint8_t* dst, int i, int lane) {
   const int pos = 64 * i + lane;
-  const int r = pos >> 2, phys = pos & 3, q = phys ^ ((r >> 2) & 3);
+  const int r = pos >> 3, phys = pos & 7, q = phys ^ (r & 7);
   int row = r0 + r;
   row = row < rows_valid ? row : rows_valid - 1;
   __builtin_amdgcn_global_load_lds((gbl_void*)(base + (long)row * ld + k0 + 8 * q), (lds_void*)(dst + i * 1024), 16,
                                    0, 0);
 }
 
-// Copies a 32 k x 64 n tile of a K-major matrix into LDS.
+// Copies a 64 k x 64 n tile of a K-major matrix into LDS (8 instructions).
 __device__ __forceinline__ void load_kmajor_tile(const bf16_t* base, long ld, int k0, int n0, uint8_t* dst, int i,
                                                  int lane) {
   const int pos = 64 * i + lane;
@@ -78,17 +82,20 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, Epi epi) {
   const int batch = blockIdx.y / g.mtiles, m0 = (blockIdx.y % g.mtiles) * 64;
   const int kb = blockIdx.z * g.k_per_split;
   const int ke = min(g.K, kb + g.k_per_split);
-  const int nsteps = (ke - kb) / 32;
+  const int nsteps = (ke - kb) / BK;
   const bf16_t* X = g.X + (long)batch * g.bsx;
   const bf16_t* W = g.W + (long)batch * g.bsw;
 
-  // one instruction per wave per tile: X tile (4 instr), W tile (4 instr)
+  // two instructions per wave per tile: X tile (8 instr), W tile (8 instr)
   auto issue = [&](int step) {
     uint8_t* st = lds + (step % NS) * STAGE_BYTES;
-    const int k0 = kb + step * 32;
-    load_rows_tile(X, g.ldx, m0, g.M, k0, st, wave, lane);
-    if (W_NK) load_rows_tile(W, g.ldw, n0, g.N, k0, st + TILE_BYTES, wave, lane);
-    else load_kmajor_tile(W, g.ldw, k0, n0, st + TILE_BYTES, wave, lane);
+    const int k0 = kb + step * BK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      load_rows_tile(X, g.ldx, m0, g.M, k0, st, wave + 4 * h, lane);
+      if (W_NK) load_rows_tile(W, g.ldw, n0, g.N, k0, st + TILE_BYTES, wave + 4 * h, lane);
+      else load_kmajor_tile(W, g.ldw, k0, n0, st + TILE_BYTES, wave + 4 * h, lane);
+    }
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -105,43 +112,45 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, Epi epi) {
     const int after = min(NS - 2, nsteps - 1 - step);
     switch (after) {
       case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<2>(); break;
-      case 2: wait_vmcnt<4>(); break;
-      case 3: wait_vmcnt<6>(); break;
+      case 1: wait_vmcnt<4>(); break;
       default: wait_vmcnt<8>(); break;
     }
     __syncthreads();
     if (step + NS - 1 < nsteps) issue(step + NS - 1);
     const uint8_t* st = lds + (step % NS) * STAGE_BYTES;
-    bf16x8 a[2], b[2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = 32 * wm + 16 * mi + i16;
-      a[mi] = *(const bf16x8*)(st + xtile_pos(r, g16) * 16);
-    }
+    for (int kh = 0; kh < 2; ++kh) {  // two 32-deep MFMA k-steps per stage
+      bf16x8 a[2], b[2];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      if (W_NK) {
-        const int r = 32 * wn + 16 * ni + i16;
-        b[ni] = *(const bf16x8*)(st + TILE_BYTES + xtile_pos(r, g16) * 16);
-      } else {
-        // B[k][n]: lane needs k = 8*g16 + e, n = 32wn + 16ni + i16 (two transposed reads)
-        const int e = i16 >> 2, qq = i16 & 3;
-        const int nq = 32 * wn + 16 * ni + 4 * qq;  // first n of this lane's 4-wide source
-        const int c = nq >> 3, half = (nq >> 2) & 1;
-        const int k1 = 8 * g16 + e, k2 = 8 * g16 + 4 + e;
-        const uint8_t* p1 = st + TILE_BYTES + ktile_pos(k1, c) * 16 + half * 8;
-        const uint8_t* p2 = st + TILE_BYTES + ktile_pos(k2, c) * 16 + half * 8;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p2);
-        const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
-        b[ni] = __builtin_bit_cast(bf16x8, s8);
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = 32 * wm + 16 * mi + i16;
+        a[mi] = *(const bf16x8*)(st + xtile_pos(r, 4 * kh + g16) * 16);
       }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        if (W_NK) {
+          const int r = 32 * wn + 16 * ni + i16;
+          b[ni] = *(const bf16x8*)(st + TILE_BYTES + xtile_pos(r, 4 * kh + g16) * 16);
+        } else {
+          // B[k][n]: lane needs k = 32kh + 8*g16 + e, n = 32wn + 16ni + i16 (two transposed reads)
+          const int e = i16 >> 2, qq = i16 & 3;
+          const int nq = 32 * wn + 16 * ni + 4 * qq;  // first n of this lane's 4-wide source
+          const int c = nq >> 3, half = (nq >> 2) & 1;
+          const int k1 = 32 * kh + 8 * g16 + e, k2 = k1 + 4;
+          const uint8_t* p1 = st + TILE_BYTES + ktile_pos(k1, c) * 16 + half * 8;
+          const uint8_t* p2 = st + TILE_BYTES + ktile_pos(k2, c) * 16 + half * 8;
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p2);
+          const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+          b[ni] = __builtin_bit_cast(bf16x8, s8);
+        }
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
   }
   // C layout: lane holds rows 4*g16 .. +3 of column i16 of each 16x16 block
 #pragma unroll
@@ -234,64 +243,55 @@ __global__ void k_reduce_cq(int R, int N, int splits, const float* part, bf16_t*
   cq[idx] = (bf16_t)s;
 }
 
-// Merge of the per-split attention partials into O_lat (bf16 [R][H][d_c]):
-// weights exp2(lse_s - max_s lse), empty splits (lse = -inf) skipped.
-// Partials are fp32 or bf16 (header).
+// Merge of the per-split attention partials into O_lat (bf16 [R][H][d_c]) and
+// the row's log-sum-exp: weights exp2(lse_s - max_s lse), empty splits
+// (lse = -inf) skipped.  One wave per (row, head); each lane owns 8 channels
+// per pass (16-byte partial reads).  Partials are fp32 or bf16 (header).
 __global__ __launch_bounds__(256) void k_merge(int batch, int H, int s_q, int d_c, const uint8_t* ws,
-                                               size_t lpart_off, bf16_t* olat) {
-  __shared__ float wsm[MAX_SPLITS];
+                                               size_t lpart_off, bf16_t* olat, float* lse_out) {
   const int S = ((const int32_t*)ws)[HDR_S];
   const bool pbf16 = ((const int32_t*)ws)[HDR_PDT] == MLA_BF16;
   const float* lpart = (const float*)(ws + lpart_off);
   const uint8_t* opart = ws + opart_offset(lpart_off, batch, S, s_q, H);
-  const int row = blockIdx.x;  // (b*s_q + j)*H + i
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*s_q + j)*H + i
+  if (row >= batch * s_q * H) return;
   const int i = row % H, bj = row / H, j = bj % s_q, b = bj / s_q;
-  auto prow = [&](int s) { return (((size_t)b * S + s) * s_q + j) * H + i; };
+  const size_t p0 = (((size_t)b * S) * s_q + j) * H + i, pstep = (size_t)s_q * H;  // partial row of split s
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lpart[prow(s)]);
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const float l = lpart[prow(s)];
-    wsm[s] = l == -INFINITY ? 0.0f : exp2f(l - M);
-  }
-  __syncthreads();
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, lpart[p0 + s * pstep]);
+  M = wave_max(M);
   float W = 0.0f;
-  for (int s = 0; s < S; ++s) W += wsm[s];
+  for (int s = lane; s < S; s += 64) {
+    const float l = lpart[p0 + s * pstep];
+    W += l == -INFINITY ? 0.0f : exp2f(l - M);
+  }
+  W = wave_sum(W);
   const float invW = W > 0.0f ? 1.0f / W : 0.0f;
-  for (int c = threadIdx.x * 2; c < d_c; c += blockDim.x * 2) {
-    float a0 = 0.0f, a1 = 0.0f;
+  if (lse_out && lane == 0) lse_out[row] = W > 0.0f ? (M + log2f(W)) * 0.6931471805599453f : -INFINITY;
+  for (int c = 8 * lane; c < d_c; c += 512) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int s = 0; s < S; ++s) {
-      const float w = wsm[s];
-      if (w != 0.0f) {
-        float2 v;
-        if (pbf16) {
-          const bf16_t* p = (const bf16_t*)opart + prow(s) * d_c + c;
-          v = make_float2((float)p[0], (float)p[1]);
-        } else {
-          v = *(const float2*)((const float*)opart + prow(s) * d_c + c);
-        }
-        a0 += w * v.x;
-        a1 += w * v.y;
+      const float l = lpart[p0 + s * pstep];
+      if (l == -INFINITY) continue;
+      const float w = exp2f(l - M);
+      const size_t off = (p0 + s * pstep) * d_c + c;
+      if (pbf16) {
+        const bf16x8 v = *(const bf16x8*)((const bf16_t*)opart + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
+      } else {
+        const f32x4 v0 = *(const f32x4*)((const float*)opart + off);
+        const f32x4 v1 = *(const f32x4*)((const float*)opart + off + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { acc[e] += w * v0[e]; acc[4 + e] += w * v1[e]; }
       }
     }
-    olat[(size_t)row * d_c + c] = (bf16_t)(a0 * invW);
-    olat[(size_t)row * d_c + c + 1] = (bf16_t)(a1 * invW);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16_t)(acc[e] * invW);
+    *(bf16x8*)(olat + (size_t)row * d_c + c) = o;
   }
-}
-
-__global__ void k_lse_out(int batch, int H, int s_q, const uint8_t* ws, size_t lpart_off, float* lse_out) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= batch * s_q * H) return;
-  const int S = ((const int32_t*)ws)[HDR_S];
-  const float* lpart = (const float*)(ws + lpart_off);
-  const int i = row % H, bj = row / H, j = bj % s_q, b = bj / s_q;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lpart[(((size_t)b * S + s) * s_q + j) * H + i]);
-  float W = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float l = lpart[(((size_t)b * S + s) * s_q + j) * H + i];
-    if (l != -INFINITY) W += exp2f(l - M);
-  }
-  lse_out[row] = W > 0.0f ? (M + log2f(W)) * 0.6931471805599453f : -INFINITY;
 }
 
 template <bool W_NK, class Epi>
@@ -306,7 +306,7 @@ GemmArgs gemm_args(int M, int N, int K, const bf16_t* X, long ldx, long bsx, con
   GemmArgs g;
   g.M = M; g.N = N; g.K = K; g.mtiles = (M + 63) / 64;
   int kps = (K + splits - 1) / splits;
-  g.k_per_split = (kps + 31) / 32 * 32;
+  g.k_per_split = (kps + BK - 1) / BK * BK;
   g.X = X; g.ldx = ldx; g.bsx = bsx; g.W = W; g.ldw = ldw; g.bsw = bsw;
   return g;
 }
@@ -320,15 +320,14 @@ hipError_t fast_query(const DecodeArgs& a) {
   const float scale2 = a.scale * LOG2E;
   bf16_t* qt = (bf16_t*)(a.ws + a.L.qt);
   bf16_t* qc = (bf16_t*)(a.ws + a.L.u);  // q^C, bf16 [R][H][d_head]
-  hipError_t e = write_header(a);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   const bf16_t* cq = (const bf16_t*)a.hq;
   if (a.W_DQ) {
     // c^Q = W^DQ h: split K so that the grid covers the GPU
     const int ntile = d.d_cq / 64 * ((R + 63) / 64);
     int splits = (512 + ntile - 1) / ntile;
     splits = splits > KSPLIT_MAX ? KSPLIT_MAX : splits;
-    while (splits > 1 && d.d_model / splits < 128) --splits;
+    while (splits > 1 && d.d_model / splits < 2 * BK) --splits;
     GemmArgs g = gemm_args(R, d.d_cq, d.d_model, (const bf16_t*)a.hq, d.d_model, 0, (const bf16_t*)a.W_DQ,
                            d.d_model, 0, splits);
     splits = (d.d_model + g.k_per_split - 1) / g.k_per_split;
@@ -361,17 +360,12 @@ hipError_t fast_combine_mfma(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
   bf16_t* olat = (bf16_t*)(a.ws + a.L.qt);  // the query buffer is free after the attention
-  MLA_TRY(launch(&k_merge, dim3(R * H), dim3(256), 0, a.stream, a.batch, H, a.s_q, d.d_c, a.ws, a.L.lpart, olat));
+  MLA_TRY(launch(&k_merge, dim3((R * H + 3) / 4), dim3(256), 0, a.stream, a.batch, H, a.s_q, d.d_c, a.ws, a.L.lpart,
+                 olat, a.lse_out));
   hipError_t e;
   GemmArgs g = gemm_args(R, d.d_head, d.d_c, olat, (long)H * d.d_c, d.d_c, (const bf16_t*)a.W_UV, d.d_c,
                          (long)d.d_head * d.d_c, 1);
   e = launch_gemm<true>(g, H, 1, EpiOut{(bf16_t*)a.out, H, d.d_head}, a.stream);
-  if (e != hipSuccess) return e;
-  if (a.lse_out) {
-    const int rows = R * H;
-    MLA_TRY(launch(&k_lse_out, dim3((rows + 255) / 256), dim3(256), 0, a.stream, a.batch, H, a.s_q, a.ws,
-                       a.L.lpart, a.lse_out));
-  }
   return e;
 }
 
