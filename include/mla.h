@@ -39,15 +39,25 @@
  *     behaviour.
  *
  * Cache layout.  Token t of sequence b lives in page block_table[b*max_pages
- * + t/page_size], slot t%page_size.  A page of an F32 or BF16 cache is
- * [page_size][d_c + d_rope] elements, each row c^KV (d_c) then k^R (d_rope,
- * already rotated at the token's position).  A page of an FP8_E4M3 cache is
- *     codes  u8   [page_size][d_c]          (OCP E4M3FN, max 448)
- *     scales f32  [page_size][d_c/128]      (one per 1x128 channel tile)
- *     rope   bf16 [page_size][d_rope]
- * following the lesson's §3.3 "Обучение в FP8": E4M3 for all tensors, one
- * scale per 1x128 activation tile.  Scale s = amax/448 (1 for an all-zero
- * tile), code = round-to-nearest-even(x/s) saturated to +-448, value = code*s.
+ * + t/page_size], slot t%page_size.  Its row is c^KV (d_c channels) then k^R
+ * (d_rope channels, already rotated at the token's position).
+ *   F32 pages:  row-major float [page_size][d_c + d_rope].
+ *   BF16 pages: the rows cut into 16-byte chunks of 8 channels and stored
+ *     chunk-major: channel ch of slot t is the bf16 at byte
+ *         16 * ((ch/8) * page_size + (t ^ x(ch/8))) + 2 * (ch%8),
+ *     x(C) = 4 * ((4 - C%4) % 4)  (0, 12, 8, 4).  (d_c + d_rope) % 8 == 0.
+ *   FP8_E4M3 pages, in this order:
+ *     codes  u8, 16-channel chunks, chunk-major: latent channel ch of slot t
+ *            at byte 16 * ((ch/16) * page_size + (t ^ x(ch/16))) + ch%16;
+ *     scales f32 [page_size][d_c/128] at byte page_size * d_c;
+ *     rope   bf16 k^R at byte page_size * (d_c + 4 * d_c/128), laid out
+ *            like a BF16 page of d_rope channels.
+ *   FP8 follows the lesson's §3.3 "Обучение в FP8": E4M3 for all tensors,
+ *   one scale per 1x128 activation tile.  Scale s = amax/448 (1 for an
+ *   all-zero tile), code = round-to-nearest-even(x/s) saturated to +-448,
+ *   value = code*s.  Requires d_c % 128 == 0 and d_rope % 8 == 0.
+ * The chunk-major pages are what the gfx950 kernels copy to LDS verbatim;
+ * mla_page_bytes() gives a page's size.
  */
 #ifndef MLA_H
 #define MLA_H

@@ -88,6 +88,13 @@ __device__ __forceinline__ void rope_cs(int pos, int m, int d_rope, float theta,
   *c = (float)cs; *s = (float)sn;
 }
 
+// Workgroup barrier for LDS rings filled by global_load_lds.  The caller has
+// already waited (vmcnt) for the loads that must have landed; __syncthreads()
+// would also drain the loads still in flight for later stages, which empties
+// the ring every step.  LDS reads and writes issued before it are complete
+// when any wave passes it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;

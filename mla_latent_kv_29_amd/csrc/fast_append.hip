@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void k_append_v3(int n_tok, int d_model, float
   for (int step = 0; step < nsteps; ++step) {
     if (step + 1 < nsteps) wait_vmcnt<10>();
     else wait_vmcnt<0>();
-    __syncthreads();
+    ring_barrier();
     if (step + NSA - 1 < nsteps) issue(step + NSA - 1);
     const uint8_t* st = lds + (step % NSA) * STA_BYTES;
     bf16x8 a[4];

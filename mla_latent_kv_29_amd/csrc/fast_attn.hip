@@ -155,7 +155,7 @@ __device__ __forceinline__ void prologue_bf16(const SplitCtx& c) {
 __device__ __forceinline__ const lu8* advance_bf16(const SplitCtx& c, int k) {
   if (k + 1 < c.nst) wait_vmcnt<9>();
   else wait_vmcnt<0>();
-  __syncthreads();
+  ring_barrier();
   if (k + 2 < c.nst) {
     const int t0 = c.t_begin + (k + 2) * ST_T;
     issue_stage(stage_page(c, t0), (t0 / ST_T) & 1, c.lds + ((k + 2) % NST) * ST_BYTES,
@@ -204,7 +204,7 @@ __device__ __forceinline__ void widen_fp8(const lu8* src, lu8* dst, int tid) {
     const int C8 = c >> 1;     // 16-channel fp8 chunk
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 code =
-        *(__attribute__((address_space(3))) const u32x2*)(src + 16 * (C8 * ST_T + (t ^ (4 * (C8 & 3)))) + 8 * (c & 1));
+        *(__attribute__((address_space(3))) const u32x2*)(src + 16 * (C8 * ST_T + (t ^ slot_x(C8))) + 8 * (c & 1));
     const float sc = *(__attribute__((address_space(3))) const float*)(src + F8_CODES + 16 * t + 4 * (c >> 4));
     bf16x8 v;
 #pragma unroll
@@ -217,12 +217,12 @@ __device__ __forceinline__ void widen_fp8(const lu8* src, lu8* dst, int tid) {
       v[4 * w + 2] = (bf16_t)(hi[0] * sc);
       v[4 * w + 3] = (bf16_t)(hi[1] * sc);
     }
-    *(__attribute__((address_space(3))) bf16x8*)(dst + 16 * (c * ST_T + (t ^ (4 * (c & 3))))) = v;
+    *(__attribute__((address_space(3))) bf16x8*)(dst + 16 * (c * ST_T + (t ^ slot_x(c)))) = v;
   }
   {
     const int m = c0;  // rope chunk 0..7, same swizzle in source and destination
-    const bf16x8 r = *(lbf16x8*)(src + F8_CODES + F8_SCALES + 16 * (m * ST_T + (t ^ (4 * (m & 3)))));
-    *(__attribute__((address_space(3))) bf16x8*)(dst + 16 * ((64 + m) * ST_T + (t ^ (4 * (m & 3))))) = r;
+    const bf16x8 r = *(lbf16x8*)(src + F8_CODES + F8_SCALES + 16 * (m * ST_T + (t ^ slot_x(m))));
+    *(__attribute__((address_space(3))) bf16x8*)(dst + 16 * ((64 + m) * ST_T + (t ^ slot_x(m)))) = r;
   }
 }
 
@@ -239,11 +239,11 @@ __device__ __forceinline__ const lu8* advance_fp8(const SplitCtx& c, int k) {
     else if (after == 1) wait_vmcnt<5>();
     else wait_vmcnt<0>();
   }
-  __syncthreads();
+  ring_barrier();
   if (k + NST8 - 1 < c.nst) issue_fp8(c, k + NST8 - 1);
   lu8* work = c.lds + F8_WORK_OFF;
   widen_fp8(c.lds + F8_RING_OFF + (k % NST8) * F8_BYTES, work, c.wave * 64 + c.lane);
-  __syncthreads();
+  ring_barrier();
   return work;
 }
 
@@ -415,8 +415,8 @@ void k_attn_v3(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ 
   c.lane = lane;
   c.cg = cg;
   const int tr = lane & 31;
-  c.kofs_even = cg * (ST_T * 16) + (tr ^ (4 * cg)) * 16;       // chunk 2kk+cg, kk even
-  c.kofs_odd = cg * (ST_T * 16) + (tr ^ (4 * (2 + cg))) * 16;  // chunk 2kk+cg, kk odd
+  c.kofs_even = cg * (ST_T * 16) + (tr ^ slot_x(cg)) * 16;       // chunk 2kk+cg, kk even
+  c.kofs_odd = cg * (ST_T * 16) + (tr ^ slot_x(2 + cg)) * 16;  // chunk 2kk+cg, kk odd
   c.qr_lds = lds + (FP8 ? F8_QR_OFF : QR_OFF) + hrow * 128;
   c.f8_scale_off = f8_scale_off;
   c.f8_rope_off = f8_rope_off;
@@ -426,7 +426,7 @@ void k_attn_v3(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ 
   const int tq = i16 >> 2, qq = i16 & 3;
   // V^T reads: chunk C = 4cb + 2(g16&1) + (qq>>1), so C&3 is lane-constant
   const int cl = 2 * (g16 & 1) + (qq >> 1);
-  const int cx = 4 * (cl & 3);
+  const int cx = slot_x(cl);
   c.vofs1 = cl * (ST_T * 16) + ((4 * (g16 >> 1) + tq) ^ cx) * 16 + (qq & 1) * 8;
   c.vofs2 = cl * (ST_T * 16) + ((8 + 4 * (g16 >> 1) + tq) ^ cx) * 16 + (qq & 1) * 8;
 
@@ -469,7 +469,7 @@ void k_attn_v3(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ 
 
 }  // namespace
 
-hipError_t fast_attention(const DecodeArgs& a) {
+hipError_t fast_attention_v1(const DecodeArgs& a) {
   const bool fp8 = a.cache_dtype == MLA_FP8_E4M3;
   auto kern = fp8 ? &k_attn_v3<true> : &k_attn_v3<false>;
   const int lds = fp8 ? LDS_BYTES_FP8 : LDS_BYTES;

@@ -1,0 +1,556 @@
+// Split-KV MLA decode attention on MFMA for the DeepSeek-V3 shape
+// (d_c 512, d_rope 64, 128 heads, 64-token bf16 pages), gfx950.
+//
+// What it computes (absorbed form; DeepSeek-V3 reading lesson, §2.1.1 and
+// Question 2): for every query row (head i, query j) of sequence b and every
+// cached token t visible to it inside this split,
+//     s_t = qt_i . [c_t ; k^R_t]      (qt = tau*log2(e)*[W^UK_i^T q^C_i ; q^R_i])
+// exp2-domain softmax weights, and O_i = sum_t p_t c_t / sum_t p_t (the
+// attention-weighted latent; W^UV is applied later by the combine).
+//
+// Work item = (sequence b, split s, query j): all 128 heads over the split's
+// tokens.  Four waves, one per SIMD, split the two products differently:
+//   * scores: wave w owns heads 32w..32w+31.  S^T[16 tokens][16 heads]
+//     blocks = K . Q^T with v_mfma_f32_16x16x32_bf16 (each K fragment read
+//     from LDS feeds two of them); the wave's 512-wide absorbed query rows
+//     sit in 128 VGPRs, the 64-wide RoPE rows of all heads in LDS.
+//   * P.V: wave w owns latent channels 128w..128w+127 of all 128 heads.
+//     O^T[128 ch][128 heads] += V^T . P^T with v_mfma_f32_32x32x16_bf16 into
+//     all 256 AGPRs; V^T comes from the staged tokens with the transposing
+//     ds_read_b64_tr_b16, P^T from an LDS buffer that every wave writes its
+//     heads' weights to.
+// Splitting P.V by channel means each wave reads only a quarter of V.  A
+// step covers two 16-token stages: the scores of stages 2m, 2m+1 and the P.V
+// of stages 2m-2, 2m-1 run between the same two barriers, so one barrier per
+// 32 tokens publishes both the new stages and the previous weights.
+//
+// The score MFMAs are written as inline asm with VGPR accumulators: with O
+// holding every AGPR, compiler-selected MFMAs would put the scores in AGPRs
+// too and shuttle O through VGPRs each step.  Their one hazard the compiler
+// cannot see -- a VALU read of an accumulator right after the MFMA that
+// writes it -- is covered by s_nop wait states after each chain's last MFMA.
+//
+// Cache tokens stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+// staging) through a 7-slot ring of 16-token stages: two being scored, two
+// in P.V, three in flight.  The chunk-major swizzled page layout makes that
+// copy verbatim and every LDS access pattern bank-conflict free.
+//
+// Softmax reference: the first step's row maximum, with 96 log2 units of
+// headroom, so O is never rescaled.  If a later score exceeds it by more than
+// the headroom the item is redone against the exact maximum (scores-only
+// pass first).
+#include "internal.hpp"
+#include "layout.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int H = 128, DC = 512, DKV = 576, PAGE = 64;
+constexpr int NW = 4;                      // waves per block
+constexpr int T = 16;                      // tokens per stage
+constexpr int NCH = DKV / 8;               // 72 sixteen-byte chunks per token
+constexpr int ST_BYTES = NCH * T * 16;     // 18 432
+constexpr int NST = 7;                     // ring slots
+constexpr int P_OFF = NST * ST_BYTES;      // 129 024: two P buffers of two stages
+constexpr int P_STAGE = H * T * 2;         // 4 096
+constexpr int P_BYTES = 2 * P_STAGE;       // 8 192
+constexpr int QR_OFF = P_OFF + 2 * P_BYTES;  // RoPE query rows: 128 x 64 bf16
+constexpr int L_OFF = QR_OFF + H * 64 * 2;   // per-head softmax sums at the end
+constexpr int LDS_BYTES = L_OFF + H * 4;     // 162 304
+
+typedef __attribute__((address_space(3))) uint8_t lu8;
+typedef __attribute__((address_space(3))) const bf16x8 lbf16x8;
+typedef __attribute__((address_space(3))) i16x4 li16x4;
+
+// One wave-wide 1 KiB copy HBM -> LDS: lane l moves 16 bytes from
+// sbase + voff(l) to lds_addr + 16 l.  sbase and lds_addr are wave-uniform.
+// Written as inline asm so that the compiler does not track these copies: it
+// would otherwise make every later LDS read wait for all of them, draining
+// the ring each step.  Completion is waited for explicitly (wait_vmcnt)
+// before the barrier that publishes a stage.  Nothing else in this kernel
+// uses M0.
+__device__ __forceinline__ void dma_1k(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct Ctx {
+  const uint8_t* pages;
+  size_t page_bytes;
+  const int32_t* bt_row;
+  int p0, bt_lane;
+  int t_begin, ntok, nst, nsteps;
+  lu8* lds;
+  uint32_t lds_addr;
+  int wave, lane;
+  uint32_t dma_ofs;           // lane part of a stage copy
+  uint32_t koff;              // K fragment of the scores MFMA
+  uint32_t qr_ofs0, qr_ofs1;  // RoPE query fragments (k-steps 16, 17)
+  uint32_t vofs1, vofs2;      // V^T transposing reads (wave's first channel block)
+  uint32_t pw_ofs, pr_ofs;    // P write (scores layout) / read (P.V layout)
+};
+
+__device__ __forceinline__ int wrap(int x) { return x >= NST ? x - NST : x; }
+
+__device__ __forceinline__ const uint8_t* stage_page(const Ctx& c, int t0) {
+  const int idx = t0 / PAGE - c.p0;
+  const int page = __builtin_amdgcn_readfirstlane(idx < 64 ? __builtin_amdgcn_readlane(c.bt_lane, idx) : c.bt_row[t0 / PAGE]);
+  return c.pages + (size_t)page * c.page_bytes;
+}
+
+// Stage i (tokens t_begin + 16 i ..) into ring slot `slot`: 18 wave-
+// instructions of 1 KiB (four 256-byte chunk runs each); wave w issues w,
+// w+4, ... -- five on waves 0-1, four on waves 2-3.
+__device__ __forceinline__ void issue_stage(const Ctx& c, int i, int slot) {
+  if (i >= c.nst) return;
+  const int t0 = c.t_begin + i * T;
+  const uint8_t* src = stage_page(c, t0) + ((t0 / T) & 3) * (T * 16);
+  const uint32_t dst = c.lds_addr + slot * ST_BYTES;
+#pragma unroll
+  for (int n = 0; n < 5; ++n) {
+    const int ii = c.wave + NW * n;
+    if (ii < NCH / 4) dma_1k(src + 4096 * ii, c.dma_ofs, dst + 1024 * ii);
+  }
+}
+
+// A stage copy prepared for issue one instruction at a time, so that the
+// copies can be spread between matrix instructions: a wave whose copies wait
+// for the address unit cannot issue anything else meanwhile.
+struct StageCopy {
+  const uint8_t* src;  // nullptr: nothing to copy
+  uint32_t dst;
+};
+__device__ __forceinline__ StageCopy plan_stage(const Ctx& c, int i, int slot) {
+  StageCopy s;
+  s.src = nullptr;
+  s.dst = c.lds_addr + slot * ST_BYTES;
+  if (i < c.nst) {
+    const int t0 = c.t_begin + i * T;
+    s.src = stage_page(c, t0) + ((t0 / T) & 3) * (T * 16);
+  }
+  return s;
+}
+// Instruction n (0..4) of this wave's share of a stage copy.
+__device__ __forceinline__ void copy_part(const Ctx& c, const StageCopy& s, int n) {
+  const int ii = c.wave + NW * n;
+  if (s.src != nullptr && ii < NCH / 4) dma_1k(s.src + 4096 * ii, c.dma_ofs, s.dst + 1024 * ii);
+}
+
+// Before step m: stages 2m and 2m+1 have landed once at most the copies of
+// stage 2m+2 (issued one step earlier) are outstanding.
+__device__ __forceinline__ void wait_step(const Ctx& c, int m) {
+  if (2 * m + 2 < c.nst) {
+    if (c.wave < 2) wait_vmcnt<5>();
+    else wait_vmcnt<4>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// Score MFMA with a VGPR accumulator (see the file comment).
+__device__ __forceinline__ f32x4 mfma_s0(bf16x8 a, bf16x8 b) {
+  f32x4 c;
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ f32x4 mfma_s(bf16x8 a, bf16x8 b, f32x4 c) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+// Last MFMA of a chain: 12 wait states before anything may read the result.
+__device__ __forceinline__ f32x4 mfma_s_last(bf16x8 a, bf16x8 b, f32x4 c) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+
+// S^T[16 tokens][16 heads] for stages A, B x head blocks 0, 1: 72 MFMAs in
+// four chains; every K fragment feeds two.  The K fragments of k-step ks+KD
+// are read while k-step ks multiplies; sched_barrier keeps that order (the
+// scheduler would otherwise sink each read to its use).
+constexpr int KD = 4;
+__device__ __forceinline__ bf16x8 rope_q(const Ctx& c, int ks, int hb) {
+  return *(lbf16x8*)(c.lds + QR_OFF + (ks == 16 ? c.qr_ofs0 : c.qr_ofs1) + 16 * 128 * hb);
+}
+__device__ __forceinline__ void step_scores(const Ctx& c, const lu8* stA, const lu8* stB, const bf16x8 (&qf)[16][2],
+                                            f32x4 (&sc)[2][2], const StageCopy& cx, const StageCopy& cy) {
+  const lu8* ka = stA + c.koff;
+  const lu8* kb = stB + c.koff;
+  bf16x8 fa[KD], fb[KD];
+#pragma unroll
+  for (int d = 0; d < KD; ++d) {
+    fa[d] = *(lbf16x8*)(ka + 1024 * d);
+    fb[d] = *(lbf16x8*)(kb + 1024 * d);
+  }
+  bf16x8 r0[2], r1[2];
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    if (ks == 12) {  // RoPE query fragments for k-steps 16, 17
+      r0[0] = rope_q(c, 16, 0); r0[1] = rope_q(c, 16, 1);
+      r1[0] = rope_q(c, 17, 0); r1[1] = rope_q(c, 17, 1);
+    }
+    const bf16x8 a = fa[ks % KD], b = fb[ks % KD];
+    const bf16x8 q0 = ks < 16 ? qf[ks][0] : (ks == 16 ? r0[0] : r1[0]);
+    const bf16x8 q1 = ks < 16 ? qf[ks][1] : (ks == 16 ? r0[1] : r1[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks == 0) {
+      sc[0][0] = mfma_s0(a, q0);
+      sc[0][1] = mfma_s0(a, q1);
+      sc[1][0] = mfma_s0(b, q0);
+      sc[1][1] = mfma_s0(b, q1);
+    } else if (ks < 17) {
+      sc[0][0] = mfma_s(a, q0, sc[0][0]);
+      sc[0][1] = mfma_s(a, q1, sc[0][1]);
+      sc[1][0] = mfma_s(b, q0, sc[1][0]);
+      sc[1][1] = mfma_s(b, q1, sc[1][1]);
+    } else {
+      sc[0][0] = mfma_s_last(a, q0, sc[0][0]);
+      sc[0][1] = mfma_s_last(a, q1, sc[0][1]);
+      sc[1][0] = mfma_s_last(b, q0, sc[1][0]);
+      sc[1][1] = mfma_s_last(b, q1, sc[1][1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks + KD < 18) {
+      fa[ks % KD] = *(lbf16x8*)(ka + 1024 * (ks + KD));
+      fb[ks % KD] = *(lbf16x8*)(kb + 1024 * (ks + KD));
+    }
+    // the next two stages' copies go out between these MFMAs: the first at
+    // k-steps 1..5, the second at 6..10
+    if (ks >= 1 && ks <= 5) copy_part(c, cx, ks - 1);
+    if (ks >= 6 && ks <= 10) copy_part(c, cy, ks - 6);
+  }
+}
+
+// Lane layout of S^T: head 16w + lane%16, tokens 4*(lane/16) + r.  Masks
+// tokens past the end of the split (nvalid may be <= 0: a padding stage).
+__device__ __forceinline__ void mask(const Ctx& c, f32x4& s, int nvalid) {
+  if (nvalid < T) {
+    const int tb = 4 * (c.lane >> 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (tb + r >= nvalid) s[r] = -INFINITY;
+  }
+}
+
+constexpr float HEADROOM = 96.0f;
+
+// Maximum over the lanes l, l^16 (permlane16 swap leaves the two values of
+// each pair in the two results) and over l, l^32.
+__device__ __forceinline__ float max_x16(float m) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float m) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Softmax weights of stages 2m, 2m+1 from their (masked) scores; the weights
+// go to P buffer m&1 as bf16.  Lane: heads 32w + 16hb + lane%16 (hb = 0, 1).
+__device__ __forceinline__ void weights_step(const Ctx& c, int m, const f32x4 (&sc)[2][2], bool fixed,
+                                             float (&m_ref)[2], float (&m_all)[2], float (&l_run)[2], bool& ovf) {
+  lu8* pbuf = c.lds + P_OFF + (m & 1) * P_BYTES + c.pw_ofs;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const f32x4 sA = sc[0][hb], sB = sc[1][hb];
+    float mloc =
+        fmaxf(fmaxf(fmaxf(sA[0], sA[1]), fmaxf(sA[2], sA[3])), fmaxf(fmaxf(sB[0], sB[1]), fmaxf(sB[2], sB[3])));
+    mloc = max_x32(max_x16(mloc));
+    m_all[hb] = fmaxf(m_all[hb], mloc);
+    if (!fixed && m == 0) m_ref[hb] = mloc;
+    ovf |= mloc > m_ref[hb] + HEADROOM;
+    bf16x4 pa, pb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // raw v_exp_f32: results below 2^-126 flush to zero, harmless here
+      const float xa = __builtin_amdgcn_exp2f(fminf(sA[r] - m_ref[hb], HEADROOM));
+      const float xb = __builtin_amdgcn_exp2f(fminf(sB[r] - m_ref[hb], HEADROOM));
+      l_run[hb] += xa + xb;
+      pa[r] = (bf16_t)xa;
+      pb[r] = (bf16_t)xb;
+    }
+    *(__attribute__((address_space(3))) bf16x4*)(pbuf + 512 * hb) = pa;
+    *(__attribute__((address_space(3))) bf16x4*)(pbuf + 512 * hb + P_STAGE) = pb;
+  }
+}
+
+// O^T[128 channels][128 heads] += V^T . P^T for two stages: 32 MFMAs.  All
+// 24 LDS reads are issued first.
+__device__ __forceinline__ void pv_step(const Ctx& c, const lu8* stA, const lu8* stB, const lu8* pb,
+                                        f32x16 (&o)[4][4]) {
+  bf16x8 v[2][4], p[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const lu8* st = j ? stB : stA;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(st + c.vofs1 + 1024 * i));
+      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(st + c.vofs2 + 1024 * i));
+      const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+      v[j][i] = __builtin_bit_cast(bf16x8, s8);
+    }
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) p[j][hb] = *(lbf16x8*)(pb + j * P_STAGE + 1024 * hb);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[j][i], p[j][hb], o[i][hb], 0, 0, 0);
+}
+
+// Zeroes the latent part of the tokens past the end of the split in its last
+// stage, so that whatever bytes the page holds there cannot turn a zero
+// weight into NaN in P.V.  Runs after the barrier that publishes the stage
+// and before the one that precedes its P.V.
+__device__ __forceinline__ void zero_tail(const Ctx& c, int slot) {
+  const int nvalid = c.ntok - (c.nst - 1) * T;
+  if (nvalid >= T) return;
+  lu8* st = c.lds + slot * ST_BYTES;
+  const int tid = c.wave * 64 + c.lane;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int idx = tid + 256 * n;  // 64 latent chunks x 16 token slots
+    const int C = idx >> 4, t = idx & 15;
+    if (t >= nvalid) *(__attribute__((address_space(3))) bf16x8*)(st + 256 * C + 16 * (t ^ slot_x(C))) = bf16x8{};
+  }
+}
+
+// The pass over the split.  Step m: score MFMAs of stages 2m, 2m+1 (with the
+// copies of stages 2m+3, 2m+4 into the slots of 2m-4, 2m-3 between them),
+// then the P.V MFMAs of stages 2m-2, 2m-1, then the softmax of 2m, 2m+1 (its
+// VALU work overlaps the P.V MFMAs still in the matrix pipe).  A missing
+// second stage is scored from the first one's slot with every token masked.  m_all collects the exact maximum of each of the wave's heads; the
+// return value says whether some score exceeded the reference by more than
+// the headroom (only possible with fixed == false).
+template <bool WITH_PV>
+__device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2], bool fixed, float (&m_ref)[2],
+                                         float (&m_all)[2], float (&l_run)[2], f32x16 (&o)[4][4]) {
+  issue_stage(c, 1, 1);  // stage 0 is already on its way
+  issue_stage(c, 2, 2);
+  bool ovf = false;
+  int sa = 0;  // slot of stage 2m
+  for (int m = 0; m <= c.nsteps; ++m) {
+    if (m < c.nsteps) wait_step(c, m);
+    ring_barrier();
+    // copies of stages 2m+3, 2m+4 go out between the score MFMAs
+    const StageCopy cx = plan_stage(c, 2 * m + 3, wrap(sa + 3));
+    const StageCopy cy = plan_stage(c, 2 * m + 4, wrap(sa + 4));
+    f32x4 sc[2][2];
+    if (m < c.nsteps) {
+      const int sb = 2 * m + 1 < c.nst ? wrap(sa + 1) : sa;
+      if (WITH_PV && (c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
+      step_scores(c, c.lds + sa * ST_BYTES, c.lds + sb * ST_BYTES, qf, sc, cx, cy);
+      const int nv = c.ntok - 2 * m * T;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        mask(c, sc[0][hb], nv);
+        mask(c, sc[1][hb], nv - T);
+      }
+    }
+    if (WITH_PV && m > 0) {
+      const int pa = wrap(sa + 5), pb = 2 * m - 1 < c.nst ? wrap(sa + 6) : pa;
+      pv_step(c, c.lds + pa * ST_BYTES, c.lds + pb * ST_BYTES, c.lds + P_OFF + ((m - 1) & 1) * P_BYTES + c.pr_ofs, o);
+    }
+    if (m < c.nsteps) weights_step(c, m, sc, fixed, m_ref, m_all, l_run, ovf);
+    sa = wrap(sa + 2);
+  }
+  return ovf;
+}
+
+// Normalised partial output of the item: O / l per head (bf16) and the
+// per-head log2-sum-exp2 m_ref + log2(l).
+__device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4], const float (&m_ref)[2],
+                                          const float (&l_run)[2], bf16_t* opart, float* lpart, size_t prow0) {
+  const int lane = c.lane, wave = c.wave;
+  const int g = lane >> 4, hq = 32 * wave + (lane & 15);
+  // per-head sums of the weights: the 4 token groups of a head are lanes i16 + 16g
+  float* lsum = (float*)(c.lds + L_OFF);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float l_tot = l_run[hb] + __shfl_xor(l_run[hb], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (g == 0) {
+      lsum[hq + 16 * hb] = l_tot;
+      lpart[prow0 + hq + 16 * hb] = m_ref[hb] + log2f(l_tot);
+    }
+  }
+  __syncthreads();
+
+  // O^T lane layout: head 32 hb + lane%32, channels 32 cb + 8 (r/4) + 4 (lane/32) + r%4
+  const int n = lane & 31, cg = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int h = 32 * hb + n;
+    const float inv = 1.0f / lsum[h];
+    bf16_t* orow = opart + (prow0 + h) * DC + 128 * wave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16_t)(o[i][hb][4 * r4 + e] * inv);
+        *(bf16x4*)(orow + 32 * i + 8 * r4 + 4 * cg) = v;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
+                const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt, int max_pages,
+                const int32_t* __restrict__ seqlens, bf16_t* __restrict__ opart, float* __restrict__ lpart,
+                int32_t* __restrict__ hdr, int batch) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  lu8* lds = (lu8*)lds_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // the split plan, for the combine
+    hdr[HDR_MAGIC] = WS_MAGIC; hdr[HDR_S] = S; hdr[HDR_PPS] = pps; hdr[HDR_BATCH] = batch;
+    hdr[HDR_SQ] = s_q; hdr[HDR_H] = H; hdr[HDR_DC] = DC; hdr[HDR_PDT] = MLA_BF16;
+  }
+  // Blocks are dealt to the 8 XCDs round-robin (blockIdx % 8).  Work items
+  // (b, s) are numbered so that each XCD takes a contiguous run: the splits
+  // of one sequence then share that XCD's L2 (its query rows are fetched from
+  // HBM once), and the s_q query rows of one item are dispatched together.
+  const int RB = s_q;
+  const int n_per = (P_items + 7) / 8;
+  const int u = blockIdx.x / 8;
+  const int p = (blockIdx.x % 8) * n_per + u / RB;
+  const int j = u % RB;
+  if (u / RB >= n_per || p >= P_items) return;
+  const int b = p / S, s = p % S;
+
+  const int L = seqlens[b];
+  int vis = L > 0 ? L - s_q + j + 1 : 0;
+  vis = vis < 0 ? 0 : vis;
+  Ctx c;
+  c.t_begin = s * pps * PAGE;
+  const int t_end = min(vis, c.t_begin + pps * PAGE);
+  c.ntok = t_end > c.t_begin ? t_end - c.t_begin : 0;
+  c.nst = (c.ntok + T - 1) / T;
+  c.nsteps = (c.nst + 1) / 2;
+
+  const size_t prow0 = (((size_t)b * S + s) * s_q + j) * H;  // partial row of head 0
+  if (c.nst == 0) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    for (int i = threadIdx.x; i < H * DC / 8; i += 256) *(u32x4*)(opart + prow0 * DC + 8 * i) = u32x4{0, 0, 0, 0};
+    if (threadIdx.x < H) lpart[prow0 + threadIdx.x] = -INFINITY;
+    return;
+  }
+
+  const int g = lane >> 4, i16 = lane & 15;
+  const int hq = 32 * wave + i16;  // head of this lane in head block 0 of the scores layout
+  const bf16_t* qblk = qt + (size_t)(b * s_q + j) * H * DKV;
+
+  c.pages = pages;
+  c.page_bytes = page_bytes;
+  c.bt_row = bt + (size_t)b * max_pages;
+  c.p0 = c.t_begin / PAGE;
+  {
+    const int np = (c.ntok + PAGE - 1) / PAGE;
+    c.bt_lane = lane < np ? c.bt_row[c.p0 + lane] : 0;
+  }
+  c.lds = lds;
+  c.lds_addr = (uint32_t)(uintptr_t)lds;
+  c.wave = wave;
+  c.lane = lane;
+  c.dma_ofs = (uint32_t)(g * 1024 + i16 * 16);
+  // RoPE rows of all heads to LDS: row h at QR_OFF + 128h, its eight 16-byte
+  // chunks permuted by (h/2)%8 (conflict-free B-operand reads).
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i = wave + NW * n;
+    const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
+    dma_1k((const uint8_t*)qblk, (uint32_t)((h * DKV + DC + 8 * lc) * 2), c.lds_addr + QR_OFF + i * 1024);
+  }
+  issue_stage(c, 0, 0);
+  // Absorbed query rows as B operands: lane holds qt[hq + 16 hb][32 ks + 8 g .. +8].
+  bf16x8 qf[16][2];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) qf[ks][hb] = *(const bf16x8*)(qblk + (size_t)(hq + 16 * hb) * DKV + 32 * ks + 8 * g);
+  wait_vmcnt<0>();  // the compiler's own loads are then known complete
+
+  // K fragment: token i16, chunk 4 ks + g (chunk % 4 = g)
+  c.koff = (uint32_t)(256 * g + 16 * (i16 ^ slot_x(g)));
+  // (head block 1, heads hq + 16, sits 16 rows further with the same permutation)
+  c.qr_ofs0 = (uint32_t)(hq * 128 + 16 * ((0 + g) ^ ((hq >> 1) & 7)));
+  c.qr_ofs1 = (uint32_t)(hq * 128 + 16 * ((4 + g) ^ ((hq >> 1) & 7)));
+  {
+    // V^T[32 ch][16 tokens] of channel block 4w (+1, +2, +3): chunk 4cb + cl,
+    // lane group layout of the transposing read
+    const int tq = i16 >> 2, qq = i16 & 3;
+    const int cl = 2 * (g & 1) + (qq >> 1);
+    c.vofs1 = (uint32_t)(4096 * wave + 256 * cl + 16 * ((4 * (g >> 1) + tq) ^ slot_x(cl)) + 8 * (qq & 1));
+    c.vofs2 = (uint32_t)(4096 * wave + 256 * cl + 16 * ((8 + 4 * (g >> 1) + tq) ^ slot_x(cl)) + 8 * (qq & 1));
+  }
+  {
+    // P row of head h (one per stage): 16 bf16 weights in token order 0-3,
+    // 8-11, 4-7, 12-15 (the k order of the transposed V^T fragment), 16-byte
+    // halves swapped when bit 3 of h is set.  Writer: tokens 4g..4g+3 of head
+    // hq (head hq + 16 is 512 bytes further, same swap).
+    const int pos = ((g & 1) << 1) | (g >> 1);
+    c.pw_ofs = (uint32_t)(hq * 32 + 16 * ((pos >> 1) ^ ((hq >> 3) & 1)) + 8 * (pos & 1));
+    const int n = lane & 31;  // reader: head 32 hb + n, half lane/32
+    c.pr_ofs = (uint32_t)(n * 32 + 16 * ((lane >> 5) ^ ((n >> 3) & 1)));
+  }
+
+  f32x16 o[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_all[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+  // Normally one pass.  If some score rose more than 2^96 above the first
+  // step's maximum, a scores-only pass collects the exact maximum and the
+  // item is done again against it.
+  bool fixed = false;
+#pragma clang loop unroll(disable)
+  for (;;) {
+    const bool ovf = run_pass<true>(c, qf, fixed, m_ref, m_all, l_run, o);
+    __syncthreads();  // every wave is done with the ring
+    if (fixed || !__syncthreads_or(ovf)) break;
+    issue_stage(c, 0, 0);
+    m_all[0] = m_all[1] = -INFINITY;
+    run_pass<false>(c, qf, true, m_ref, m_all, l_run, o);
+    __syncthreads();
+    m_ref[0] = m_all[0];
+    m_ref[1] = m_all[1];
+    issue_stage(c, 0, 0);
+    fixed = true;
+    l_run[0] = l_run[1] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
+  }
+  write_out(c, o, m_ref, l_run, opart, lpart, prow0);
+}
+
+}  // namespace
+
+hipError_t fast_attention_b(const DecodeArgs& a) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    MLA_TRY(hipFuncSetAttribute((const void*)&k_attn_v3b, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES));
+    attr_set = true;
+  }
+  const int P_items = a.batch * a.S;
+  const int grid = ((P_items + 7) / 8) * 8 * a.s_q;
+  MLA_TRY(launch(&k_attn_v3b, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
+                 (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages, a.seqlens,
+                 (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch));
+  return hipSuccess;
+}
+
+}  // namespace mla

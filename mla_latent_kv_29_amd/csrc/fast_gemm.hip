@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, Epi epi) {
       case 1: wait_vmcnt<4>(); break;
       default: wait_vmcnt<8>(); break;
     }
-    __syncthreads();
+    ring_barrier();
     if (step + NS - 1 < nsteps) issue(step + NS - 1);
     const uint8_t* st = lds + (step % NS) * STAGE_BYTES;
 #pragma unroll

@@ -99,11 +99,16 @@ class Case:
                                           self.s_q, tau, heads)
 
 
+def slot_x(C):
+    """Token-slot XOR of chunk C in a chunk-major page: 0, 12, 8, 4 for C % 4 = 0..3."""
+    return 4 * ((4 - C % 4) % 4)
+
+
 def bf16_page_off(t, ch, page_size):
     """Byte offset of channel ch of token t in a chunk-major bf16 page (16-byte
-    chunks of 8 channels, token slot t ^ 4*(chunk % 4))."""
+    chunks of 8 channels, token slot t ^ slot_x(chunk))."""
     C = ch // 8
-    return 16 * (C * page_size + (t ^ (4 * (C % 4)))) + 2 * (ch % 8)
+    return 16 * (C * page_size + (t ^ slot_x(C))) + 2 * (ch % 8)
 
 
 def read_bf16_rows(pages, page_ids, dims):
@@ -113,7 +118,7 @@ def read_bf16_rows(pages, page_ids, dims):
     t = np.arange(ps)[:, None]
     ch = np.arange(D)[None, :]
     C = ch // 8
-    off = 16 * (C * ps + (t ^ (4 * (C % 4)))) + 2 * (ch % 8)
+    off = 16 * (C * ps + (t ^ slot_x(C))) + 2 * (ch % 8)
     out = []
     for p in page_ids:
         b = raw[int(p)]
@@ -129,12 +134,12 @@ def read_fp8_rows(pages, page_ids, dims):
     t = np.arange(ps)[:, None]
     ch = np.arange(dc)[None, :]
     C = ch // 16
-    coff = 16 * (C * ps + (t ^ (4 * (C % 4)))) + (ch % 16)
+    coff = 16 * (C * ps + (t ^ slot_x(C))) + (ch % 16)
     s_off = ps * dc
     r_off = s_off + ps * (dc // 128) * 4
     m = np.arange(dr)[None, :]
     Cm = m // 8
-    roff = r_off + 16 * (Cm * ps + (t ^ (4 * (Cm % 4)))) + 2 * (m % 8)
+    roff = r_off + 16 * (Cm * ps + (t ^ slot_x(Cm))) + 2 * (m % 8)
     codes, scales, rope = [], [], []
     for p in page_ids:
         b = raw[int(p)]
