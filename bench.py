@@ -12,6 +12,7 @@ attention (mla_decode_attend): its duration is taken with HIP events around
 that call on the stream it runs on, inside the timed region.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -44,6 +45,36 @@ def algorithmic(spec, dims, lengths):
     o_flops = 2 * R * H * dh * dc
     return dict(step_bytes=cache + w_bytes + io_bytes, step_flops=attn_flops + q_flops + o_flops,
                 attn_bytes=cache, attn_flops=attn_flops)
+
+
+# Sources that define the attention kernel of each cache type; a traffic
+# figure measured with hardware counters is reported only while they are
+# unchanged since the measurement.
+ATTN_SOURCES = {"bf16": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
+                "fp8": ["fast_attn.hip", "layout.hpp", "common.hpp"]}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+
+
+def attn_source_sha(cache):
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES.get(cache, []):
+        with open(os.path.join(ROOT, "mla_latent_kv_29_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, cache):
+    """HBM bytes per attention launch from the committed counter measurement
+    (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known size), or None if
+    there is none for this workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha256") != attn_source_sha(cache):
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=16):
@@ -91,6 +122,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="copies of cache+weights rotated across steps")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain elementwise copy of MIB MiB three times (untimed), as the "
+                         "reference for hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -155,6 +189,15 @@ def main():
         if e is not None:
             e[3].record(stream)
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -194,7 +237,8 @@ def main():
                    "s_q": s_q, "cache": spec["cache"], "splits": sess.num_splits,
                    "cached_tokens": int(tokens), "rotation_sets": len(sets)},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                     "traffic": None, "kernel": "k_attn_v3_bf16 (mla_decode_attend)",
+                     "traffic": measured_traffic(args.workload, spec["cache"]),
+                     "kernel": ("k_attn_v3b" if spec["cache"] == "bf16" else "k_attn_v3<fp8>") + " (mla_decode_attend)",
                      "attn_ms_mean": float(np.mean(a_ms))},
         "step_roofline": {"t_bound_us": t_bound * 1e6, "frac": t_bound / (ms_per_step * 1e-3),
                           "step_bytes": alg["step_bytes"], "step_flops": alg["step_flops"]},
