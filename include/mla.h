@@ -174,9 +174,10 @@ MLA_API int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq,
 
 /* The two halves of mla_decode, for callers that want to schedule or time
  * them separately (same arguments and validation as mla_decode):
- * mla_decode_query runs the query projection and absorption and records the
- * split plan in ws; mla_decode_attend then runs the split-KV attention over
- * the cache using the queries in ws.  mla_decode == query then attend.      */
+ * mla_decode_query runs the query projection and absorption into ws;
+ * mla_decode_attend then runs the split-KV attention over the cache using
+ * the queries in ws and records the split plan there for mla_combine.
+ * mla_decode == query then attend.                                          */
 MLA_API int mla_decode_query(const mla_dims* dims, int32_t act_dtype, const void* hq,
                int32_t batch, int32_t s_q, const void* W_DQ, const void* W_UQ,
                const void* W_UK, const mla_cache* cache,
