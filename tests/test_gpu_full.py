@@ -1,0 +1,106 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (its seeds, lengths, block tables and default split count), on sampled
+sequences and heads that the float64 oracle computes one by one.
+
+The oracle rebuilds each sampled sequence's latents from its hidden states
+(chunked, so a 131072-token sequence never needs its whole h in float64) and
+decodes the sampled heads from them; nothing it uses comes from the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_29_amd import inputs
+from mla_latent_kv_29_amd.session import DecodeSession
+from gpu_common import DEV, tau_of, to_np, max_abs
+
+pytestmark = pytest.mark.gpu
+
+HEADS = [0, 45, 127]
+
+
+def full_session(name):
+    spec = inputs.WORKLOADS[name]
+    dims, wl = spec["dims"], spec["index"]
+    tdt = inputs.torch_dtype(spec["act"])
+    lengths = inputs.seqlens(spec["lengths"], spec["batch"], 0, wl)
+    table, pool = inputs.block_table(lengths, dims["page_size"], spec["table"], 0, wl)
+    W = inputs.weights(dims, spec["sigma"], tdt, DEV, 0, wl)
+    sess = DecodeSession(dims, spec["act"], spec["cache"], lengths, table, pool, spec["s_q"], 0, DEV)
+    gen_h = lambda b, t0, t1: inputs.hidden(dims, b, t0, t1, tdt, DEV, 0, wl)
+    sess.build_from_h(gen_h, W, chunk=32768)
+    s_q = spec["s_q"]
+    hq = torch.cat([gen_h(b, int(Lb) - s_q, int(Lb)) for b, Lb in enumerate(lengths)], 0).contiguous()
+    torch.cuda.synchronize()
+    return spec, dims, lengths, W, sess, gen_h, hq
+
+
+def oracle_latents(dims, Wn, gen_h, b, Lb, chunk=8192):
+    """c^KV [Lb, d_c] and k^R [Lb, d_rope] of sequence b in float64, chunk by chunk."""
+    cs, rs = [], []
+    for t0 in range(0, Lb, chunk):
+        t1 = min(Lb, t0 + chunk)
+        h = to_np(gen_h(b, t0, t1))
+        c, r = oracle.kv_latents(h, Wn["W_DKV"], Wn["W_KR"], np.arange(t0, t1), dims["rope_theta"])
+        cs.append(c)
+        rs.append(r)
+    return np.concatenate(cs, 0), np.concatenate(rs, 0)
+
+
+def bf16_round(x):
+    return to_np(torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16))
+
+
+def check(name, samples, kappas):
+    spec, dims, lengths, W, sess, gen_h, hq = full_session(name)
+    s_q = spec["s_q"]
+    fp8 = spec["cache"] == "fp8"
+    Wn = {k: to_np(v) for k, v in W.items()}
+    lat = {}
+    for b in samples:
+        Lb = int(lengths[b])
+        c, r = oracle_latents(dims, Wn, gen_h, b, Lb)
+        if fp8:
+            codes, scales = oracle.quantize_tiles(c)
+            lat[b] = (c, r, oracle.dequantize_tiles(codes, scales), bf16_round(r))
+        else:
+            lat[b] = (c, r, None, None)
+    hqn = to_np(hq)
+    for kappa in kappas:
+        tau = kappa * tau_of(dims)
+        out, lse = sess.decode(hq, W, tau)
+        torch.cuda.synchronize()
+        out, lse = to_np(out), to_np(lse)
+        for b in samples:
+            Lb = int(lengths[b])
+            c, r, cq, rq = lat[b]
+            hqb = hqn[b * s_q:(b + 1) * s_q]
+            args = (Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], dims, Lb, s_q, tau, HEADS)
+            o_ref, l_ref = oracle.decode_from_latents(c, r, hqb, *args)
+            got, got_l = out[b][:, HEADS], lse[b][:, HEADS]
+            tol = (5e-2 if fp8 else 2e-2) * float(np.max(np.abs(o_ref)))
+            err = max_abs(got, o_ref)
+            assert err <= tol, (name, b, Lb, kappa, err, tol)
+            assert max_abs(got_l, l_ref) <= (5e-2 if fp8 else 2e-2) * max(1.0, float(np.max(np.abs(l_ref)))), (name, b, kappa)
+            if fp8:
+                o_q, _ = oracle.decode_from_latents(cq, rq, hqb, *args)
+                assert max_abs(got, o_q) <= 2e-2 * float(np.max(np.abs(o_q))), (name, b, kappa, "emulated")
+
+
+def test_full_v3_bf16_b64_l4096():
+    check("v3_bf16_b64_l4096", [0, 37, 63], [1.0, 56.0])
+
+
+def test_full_v3_bf16_b128_var32k_paged():
+    lengths = inputs.seqlens(inputs.WORKLOADS["v3_bf16_b128_var32k_paged"]["lengths"], 128, 0, 2)
+    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 5})
+    check("v3_bf16_b128_var32k_paged", picks, [1.0, 56.0])
+
+
+def test_full_v3_bf16_b4_l128k():
+    check("v3_bf16_b4_l128k", [3], [1.0, 56.0])
+
+
+def test_full_v3_fp8_b128_l8192_sq2():
+    check("v3_fp8_b128_l8192_sq2", [0, 127], [1.0, 56.0])

@@ -98,3 +98,27 @@ def test_v3_score_far_above_first_stage_max():
     o, l = case.oracle(0, tau, hq=hq)
     assert max_abs(out[0], o) <= TOL_BF16 * float(np.abs(o).max())
     assert abs(lse[0, 0, 0] - l[0, 0]) <= 1e-2 * abs(l[0, 0])
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_v3_bf16_bytes_past_the_end_are_ignored(splits):
+    """Page slots past a sequence's length hold NaN bf16 patterns (0xFFFF):
+    the tokens they would be are not visible, so the output must not change."""
+    from gpu_common import bf16_page_off
+    case = Case(V3, "bf16", "bf16", [300, 129, 64], s_q=1, table="shuffled", wl=1, num_splits=splits)
+    ps, D = V3["page_size"], V3["d_c"] + V3["d_rope"]
+    t = np.arange(ps)[:, None]
+    ch = np.arange(D)[None, :]
+    raw = case.sess.pages.cpu().numpy()
+    for b, Lb in enumerate(case.lengths):
+        last = int(case.bt[b, (int(Lb) - 1) // ps])
+        tail = t[int(Lb) % ps:] if Lb % ps else t[:0]
+        off = bf16_page_off(tail, ch, ps)
+        raw[last, off.ravel()] = 0xFF
+        raw[last, off.ravel() + 1] = 0xFF
+    case.sess.pages.copy_(torch.from_numpy(raw))
+    torch.cuda.synchronize()
+    tau = tau_of(V3) * 56.0
+    out, lse, _ = case.run(tau)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    check_all(case, out, lse, tau, TOL_BF16)
