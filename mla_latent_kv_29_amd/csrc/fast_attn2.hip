@@ -22,7 +22,9 @@
 // Splitting P.V by channel means each wave reads only a quarter of V.  A
 // step covers two 16-token stages: the scores of stages 2m, 2m+1 and the P.V
 // of stages 2m-2, 2m-1 run between the same two barriers, so one barrier per
-// 32 tokens publishes both the new stages and the previous weights.
+// 32 tokens publishes both the new stages and the previous weights.  The
+// softmax VALU work is interleaved one slot at a time with the P.V MFMAs, so
+// it issues while the matrix unit is busy.
 //
 // The score MFMAs are written as inline asm with VGPR accumulators: with O
 // holding every AGPR, compiler-selected MFMAs would put the scores in AGPRs
@@ -36,9 +38,12 @@
 // copy verbatim and every LDS access pattern bank-conflict free.
 //
 // Softmax reference: the first step's row maximum, with 96 log2 units of
-// headroom, so O is never rescaled.  If a later score exceeds it by more than
-// the headroom the item is redone against the exact maximum (scores-only
-// pass first).
+// headroom, so O is never rescaled.  The pass also collects the exact row
+// maximum.  If some score exceeded the reference by more than the headroom,
+// the item records that maximum in the workspace, and a second launch of
+// the kernel (every other item returns at once) redoes it against it.  One
+// copy of the pass per kernel keeps register allocation simple.
+#include <utility>
 #include "internal.hpp"
 #include "layout.hpp"
 
@@ -219,8 +224,8 @@ __device__ __forceinline__ void step_scores(const Ctx& c, const lu8* stA, const 
       fa[ks % KD] = *(lbf16x8*)(ka + 1024 * (ks + KD));
       fb[ks % KD] = *(lbf16x8*)(kb + 1024 * (ks + KD));
     }
-    // the next two stages' copies go out between these MFMAs: the first at
-    // k-steps 1..5, the second at 6..10
+    // the next two stages' copies go out between these MFMAs, early in the
+    // step: the first at k-steps 1..5, the second at 6..10
     if (ks >= 1 && ks <= 5) copy_part(c, cx, ks - 1);
     if (ks >= 6 && ks <= 10) copy_part(c, cy, ks - 6);
   }
@@ -250,39 +255,78 @@ __device__ __forceinline__ float max_x32(float m) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Softmax weights of stages 2m, 2m+1 from their (masked) scores; the weights
-// go to P buffer m&1 as bf16.  Lane: heads 32w + 16hb + lane%16 (hb = 0, 1).
-__device__ __forceinline__ void weights_step(const Ctx& c, int m, const f32x4 (&sc)[2][2], bool fixed,
-                                             float (&m_ref)[2], float (&m_all)[2], float (&l_run)[2], bool& ovf) {
-  lu8* pbuf = c.lds + P_OFF + (m & 1) * P_BYTES + c.pw_ofs;
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const f32x4 sA = sc[0][hb], sB = sc[1][hb];
-    float mloc =
-        fmaxf(fmaxf(fmaxf(sA[0], sA[1]), fmaxf(sA[2], sA[3])), fmaxf(fmaxf(sB[0], sB[1]), fmaxf(sB[2], sB[3])));
-    mloc = max_x32(max_x16(mloc));
-    m_all[hb] = fmaxf(m_all[hb], mloc);
-    if (!fixed && m == 0) m_ref[hb] = mloc;
-    ovf |= mloc > m_ref[hb] + HEADROOM;
-    bf16x4 pa, pb;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // raw v_exp_f32: results below 2^-126 flush to zero, harmless here
-      const float xa = __builtin_amdgcn_exp2f(fminf(sA[r] - m_ref[hb], HEADROOM));
-      const float xb = __builtin_amdgcn_exp2f(fminf(sB[r] - m_ref[hb], HEADROOM));
-      l_run[hb] += xa + xb;
-      pa[r] = (bf16_t)xa;
-      pb[r] = (bf16_t)xb;
-    }
-    *(__attribute__((address_space(3))) bf16x4*)(pbuf + 512 * hb) = pa;
-    *(__attribute__((address_space(3))) bf16x4*)(pbuf + 512 * hb + P_STAGE) = pb;
+// P.V MFMAs of stages 2m-2, 2m-1 interleaved with the softmax of this
+// step's (masked) scores: the VALU instructions issue while each MFMA
+// occupies the matrix unit.  The 32 slots are generated at compile time and
+// sched_barrier pins their order.  Weights go to P buffer m&1 as bf16; lane
+// heads 32w + 16hb + lane%16 (hb = 0, 1).
+struct PvwState {
+  const Ctx& c;
+  int m;
+  const f32x4 (&sc)[2][2];
+  const bf16x8 (&v)[2][4];
+  const bf16x8 (&p)[2][4];
+  f32x16 (&o)[4][4];
+  bool fixed;
+  float (&m_ref)[2];
+  float (&m_all)[2];
+  float (&l_run)[2];
+  bool& ovf;
+  lu8* pw;
+  float ml[2];
+  f32x4 xa[2];
+};
+
+template <int K>
+__device__ __forceinline__ void pvw_slot(PvwState& st) {
+  {
+    constexpr int j = K >> 4, hb = (K >> 2) & 3, i = K & 3;
+    st.o[i][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.v[j][i], st.p[j][hb], st.o[i][hb], 0, 0, 0);
   }
+  if constexpr (K < 10) {
+    constexpr int h = K / 5, part = K % 5;
+    const f32x4 sA = st.sc[0][h], sB = st.sc[1][h];
+    if constexpr (part == 0) {
+      st.ml[h] = fmaxf(fmaxf(fmaxf(sA[0], sA[1]), fmaxf(sA[2], sA[3])), fmaxf(fmaxf(sB[0], sB[1]), fmaxf(sB[2], sB[3])));
+    } else if constexpr (part == 1) {
+      st.ml[h] = max_x16(st.ml[h]);
+    } else if constexpr (part == 2) {
+      st.ml[h] = max_x32(st.ml[h]);
+      st.m_all[h] = fmaxf(st.m_all[h], st.ml[h]);
+      if (!st.fixed && st.m == 0) st.m_ref[h] = st.ml[h];
+      st.ovf |= st.ml[h] > st.m_ref[h] + HEADROOM;
+    } else if constexpr (part == 3) {
+      // raw v_exp_f32: results below 2^-126 flush to zero, harmless here; a
+      // score above the headroom only occurs in a pass that is redone
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.xa[h][r] = __builtin_amdgcn_exp2f(sA[r] - st.m_ref[h]);
+    } else {
+      f32x4 xb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xb[r] = __builtin_amdgcn_exp2f(sB[r] - st.m_ref[h]);
+      const f32x4 xa = st.xa[h];
+      st.l_run[h] += (xa[0] + xa[1]) + (xa[2] + xa[3]) + (xb[0] + xb[1]) + (xb[2] + xb[3]);
+      bf16x4 pa, pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pa[r] = (bf16_t)xa[r];
+        pb[r] = (bf16_t)xb[r];
+      }
+      *(__attribute__((address_space(3))) bf16x4*)(st.pw + 512 * h) = pa;
+      *(__attribute__((address_space(3))) bf16x4*)(st.pw + 512 * h + P_STAGE) = pb;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// O^T[128 channels][128 heads] += V^T . P^T for two stages: 32 MFMAs.  All
-// 24 LDS reads are issued first.
-__device__ __forceinline__ void pv_step(const Ctx& c, const lu8* stA, const lu8* stB, const lu8* pb,
-                                        f32x16 (&o)[4][4]) {
+template <int... K>
+__device__ __forceinline__ void pvw_slots(PvwState& st, std::integer_sequence<int, K...>) {
+  (pvw_slot<K>(st), ...);
+}
+
+__device__ __forceinline__ void pv_weights_step(const Ctx& c, int m, const f32x4 (&sc)[2][2], const lu8* stA,
+                                                const lu8* stB, const lu8* prd, f32x16 (&o)[4][4], bool fixed,
+                                                float (&m_ref)[2], float (&m_all)[2], float (&l_run)[2], bool& ovf) {
   bf16x8 v[2][4], p[2][4];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -295,15 +339,12 @@ __device__ __forceinline__ void pv_step(const Ctx& c, const lu8* stA, const lu8*
       v[j][i] = __builtin_bit_cast(bf16x8, s8);
     }
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) p[j][hb] = *(lbf16x8*)(pb + j * P_STAGE + 1024 * hb);
+    for (int hb = 0; hb < 4; ++hb) p[j][hb] = *(lbf16x8*)(prd + j * P_STAGE + 1024 * hb);
   }
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[j][i], p[j][hb], o[i][hb], 0, 0, 0);
+  PvwState st{c, m, sc, v, p, o, fixed, m_ref, m_all, l_run, ovf, c.lds + P_OFF + (m & 1) * P_BYTES + c.pw_ofs,
+              {0.0f, 0.0f}, {}};
+  pvw_slots(st, std::make_integer_sequence<int, 32>{});
 }
 
 // Zeroes the latent part of the tokens past the end of the split in its last
@@ -323,30 +364,41 @@ __device__ __forceinline__ void zero_tail(const Ctx& c, int slot) {
   }
 }
 
-// The pass over the split.  Step m: score MFMAs of stages 2m, 2m+1 (with the
-// copies of stages 2m+3, 2m+4 into the slots of 2m-4, 2m-3 between them),
-// then the P.V MFMAs of stages 2m-2, 2m-1, then the softmax of 2m, 2m+1 (its
-// VALU work overlaps the P.V MFMAs still in the matrix pipe).  A missing
-// second stage is scored from the first one's slot with every token masked.  m_all collects the exact maximum of each of the wave's heads; the
-// return value says whether some score exceeded the reference by more than
-// the headroom (only possible with fixed == false).
-template <bool WITH_PV>
+// The pass over the split.  Step m: score MFMAs of stages 2m, 2m+1 with the
+// copies of stages 2m+3, 2m+4 (into the slots of 2m-4, 2m-3) between them,
+// then the P.V of stages 2m-2, 2m-1 interleaved with the softmax of 2m, 2m+1.  Step 0 has no
+// P.V: it multiplies zero weights (P buffer 1 starts zeroed) with the RoPE
+// query rows standing in for V; after the last scores, all-(-inf) scores give
+// zero weights.  So one copy of the step code serves every step.  A missing
+// second stage is scored from the first one's slot with every token masked.
+// m_all collects the exact maximum of each of the wave's heads; the return
+// value says whether a score exceeded the reference by more than the
+// headroom (only possible with fixed == false).
 __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2], bool fixed, float (&m_ref)[2],
                                          float (&m_all)[2], float (&l_run)[2], f32x16 (&o)[4][4]) {
   issue_stage(c, 1, 1);  // stage 0 is already on its way
   issue_stage(c, 2, 2);
+  {
+    const int tid = c.wave * 64 + c.lane;
+    *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * tid) = bf16x8{};
+    *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * (tid + 256)) = bf16x8{};
+  }
   bool ovf = false;
   int sa = 0;  // slot of stage 2m
   for (int m = 0; m <= c.nsteps; ++m) {
     if (m < c.nsteps) wait_step(c, m);
     ring_barrier();
-    // copies of stages 2m+3, 2m+4 go out between the score MFMAs
+    const int pa = wrap(sa + 5), pb = 2 * m - 1 < c.nst ? wrap(sa + 6) : pa;
+    const lu8* va = m > 0 ? c.lds + pa * ST_BYTES : c.lds + QR_OFF;
+    const lu8* vb = m > 0 ? c.lds + pb * ST_BYTES : c.lds + QR_OFF;
+    const lu8* prd = c.lds + P_OFF + ((m - 1) & 1) * P_BYTES + c.pr_ofs;
+    // copies of stages 2m+3, 2m+4 (none past the last step)
     const StageCopy cx = plan_stage(c, 2 * m + 3, wrap(sa + 3));
     const StageCopy cy = plan_stage(c, 2 * m + 4, wrap(sa + 4));
     f32x4 sc[2][2];
     if (m < c.nsteps) {
       const int sb = 2 * m + 1 < c.nst ? wrap(sa + 1) : sa;
-      if (WITH_PV && (c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
+      if ((c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
       step_scores(c, c.lds + sa * ST_BYTES, c.lds + sb * ST_BYTES, qf, sc, cx, cy);
       const int nv = c.ntok - 2 * m * T;
 #pragma unroll
@@ -354,12 +406,11 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2]
         mask(c, sc[0][hb], nv);
         mask(c, sc[1][hb], nv - T);
       }
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) sc[0][hb] = sc[1][hb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
-    if (WITH_PV && m > 0) {
-      const int pa = wrap(sa + 5), pb = 2 * m - 1 < c.nst ? wrap(sa + 6) : pa;
-      pv_step(c, c.lds + pa * ST_BYTES, c.lds + pb * ST_BYTES, c.lds + P_OFF + ((m - 1) & 1) * P_BYTES + c.pr_ofs, o);
-    }
-    if (m < c.nsteps) weights_step(c, m, sc, fixed, m_ref, m_all, l_run, ovf);
+    pv_weights_step(c, m, sc, va, vb, prd, o, fixed, m_ref, m_all, l_run, ovf);
     sa = wrap(sa + 2);
   }
   return ovf;
@@ -408,12 +459,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
                 const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt, int max_pages,
                 const int32_t* __restrict__ seqlens, bf16_t* __restrict__ opart, float* __restrict__ lpart,
-                int32_t* __restrict__ hdr, int batch) {
+                int32_t* __restrict__ hdr, int batch, int32_t* __restrict__ ovf_flag, float* __restrict__ amax,
+                int fixup) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lu8* lds = (lu8*)lds_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
-  if (blockIdx.x == 0 && threadIdx.x == 0) {  // the split plan, for the combine
+  if (!fixup && blockIdx.x == 0 && threadIdx.x == 0) {  // the split plan, for the combine
     hdr[HDR_MAGIC] = WS_MAGIC; hdr[HDR_S] = S; hdr[HDR_PPS] = pps; hdr[HDR_BATCH] = batch;
     hdr[HDR_SQ] = s_q; hdr[HDR_H] = H; hdr[HDR_DC] = DC; hdr[HDR_PDT] = MLA_BF16;
   }
@@ -439,8 +491,11 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   c.nst = (c.ntok + T - 1) / T;
   c.nsteps = (c.nst + 1) / 2;
 
-  const size_t prow0 = (((size_t)b * S + s) * s_q + j) * H;  // partial row of head 0
+  const size_t item = ((size_t)b * S + s) * s_q + j;
+  const size_t prow0 = item * H;  // partial row of head 0
+  if (fixup && ovf_flag[item] == 0) return;  // second launch: only items that overflowed
   if (c.nst == 0) {
+    if (threadIdx.x == 0) ovf_flag[item] = 0;
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     for (int i = threadIdx.x; i < H * DC / 8; i += 256) *(u32x4*)(opart + prow0 * DC + 8 * i) = u32x4{0, 0, 0, 0};
     if (threadIdx.x < H) lpart[prow0 + threadIdx.x] = -INFINITY;
@@ -511,30 +566,21 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
   float m_ref[2] = {-INFINITY, -INFINITY}, m_all[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-  // Normally one pass.  If some score rose more than 2^96 above the first
-  // step's maximum, a scores-only pass collects the exact maximum and the
-  // item is done again against it.
-  bool fixed = false;
-#pragma clang loop unroll(disable)
-  for (;;) {
-    const bool ovf = run_pass<true>(c, qf, fixed, m_ref, m_all, l_run, o);
-    __syncthreads();  // every wave is done with the ring
-    if (fixed || !__syncthreads_or(ovf)) break;
-    issue_stage(c, 0, 0);
-    m_all[0] = m_all[1] = -INFINITY;
-    run_pass<false>(c, qf, true, m_ref, m_all, l_run, o);
-    __syncthreads();
-    m_ref[0] = m_all[0];
-    m_ref[1] = m_all[1];
-    issue_stage(c, 0, 0);
-    fixed = true;
-    l_run[0] = l_run[1] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
+  if (fixup) {  // the exact maximum found by the first launch
+    m_ref[0] = amax[prow0 + hq];
+    m_ref[1] = amax[prow0 + hq + 16];
   }
+  const bool ovf = run_pass(c, qf, fixup != 0, m_ref, m_all, l_run, o);
+  __syncthreads();  // every wave is done with the ring
   write_out(c, o, m_ref, l_run, opart, lpart, prow0);
+  if (!fixup) {
+    const bool any = __syncthreads_or(ovf);
+    if (any && g == 0) {
+      amax[prow0 + hq] = m_all[0];
+      amax[prow0 + hq + 16] = m_all[1];
+    }
+    if (threadIdx.x == 0) ovf_flag[item] = any ? 1 : 0;
+  }
 }
 
 }  // namespace
@@ -547,9 +593,12 @@ hipError_t fast_attention_b(const DecodeArgs& a) {
   }
   const int P_items = a.batch * a.S;
   const int grid = ((P_items + 7) / 8) * 8 * a.s_q;
-  MLA_TRY(launch(&k_attn_v3b, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
-                 (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages, a.seqlens,
-                 (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch));
+  // second launch: items whose scores outgrew the first step's reference
+  for (int fixup = 0; fixup < 2; ++fixup)
+    MLA_TRY(launch(&k_attn_v3b, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
+                   (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages, a.seqlens,
+                   (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch,
+                   (int32_t*)(a.ws + a.L.ovf), (float*)(a.ws + a.L.amax), fixup));
   return hipSuccess;
 }
 
