@@ -88,6 +88,17 @@ __device__ __forceinline__ void rope_cs(int pos, int m, int d_rope, float theta,
   *c = (float)cs; *s = (float)sn;
 }
 
+// The same rotation from a precomputed frequency w = theta^(-2m/d_rope)
+// (double): the angle pos*w is reduced modulo 2 pi in double, so that the
+// single-precision sincos of the remainder keeps full accuracy at any
+// position, at a fraction of the cost of the double-precision functions.
+__device__ __forceinline__ void rope_cs_w(int pos, double w, float* c, float* s) {
+  const double x = (double)pos * w;
+  const double k = rint(x * 0.15915494309189535);           // 1 / (2 pi)
+  const double r = fma(-k, 1.2246467991473532e-16, fma(-k, 6.283185307179586, x));  // 2 pi = hi + lo
+  sincosf((float)r, s, c);
+}
+
 // Workgroup barrier for LDS rings filled by global_load_lds.  The caller has
 // already waited (vmcnt) for the loads that must have landed; __syncthreads()
 // would also drain the loads still in flight for later stages, which empties

@@ -40,9 +40,12 @@
 // Softmax reference: the first step's row maximum, with 96 log2 units of
 // headroom, so O is never rescaled.  The pass also collects the exact row
 // maximum.  If some score exceeded the reference by more than the headroom,
-// the item records that maximum in the workspace, and a second launch of
-// the kernel (every other item returns at once) redoes it against it.  One
-// copy of the pass per kernel keeps register allocation simple.
+// the block runs the pass again against that maximum.  Both passes are one
+// runtime loop over the same code: a second copy of the pass would not fit
+// the register file.
+//
+// The normalised partial rows leave through LDS so that each store writes a
+// whole 1 KiB row.
 #include <utility>
 #include "internal.hpp"
 #include "layout.hpp"
@@ -267,7 +270,6 @@ struct PvwState {
   const bf16x8 (&v)[2][4];
   const bf16x8 (&p)[2][4];
   f32x16 (&o)[4][4];
-  bool fixed;
   float (&m_ref)[2];
   float (&m_all)[2];
   float (&l_run)[2];
@@ -293,7 +295,9 @@ __device__ __forceinline__ void pvw_slot(PvwState& st) {
     } else if constexpr (part == 2) {
       st.ml[h] = max_x32(st.ml[h]);
       st.m_all[h] = fmaxf(st.m_all[h], st.ml[h]);
-      if (!st.fixed && st.m == 0) st.m_ref[h] = st.ml[h];
+      // the reference: the first step's maximum, or the exact maximum
+      // already in m_ref when the pass is redone (it is never smaller)
+      if (st.m == 0) st.m_ref[h] = fmaxf(st.m_ref[h], st.ml[h]);
       st.ovf |= st.ml[h] > st.m_ref[h] + HEADROOM;
     } else if constexpr (part == 3) {
       // raw v_exp_f32: results below 2^-126 flush to zero, harmless here; a
@@ -325,7 +329,7 @@ __device__ __forceinline__ void pvw_slots(PvwState& st, std::integer_sequence<in
 }
 
 __device__ __forceinline__ void pv_weights_step(const Ctx& c, int m, const f32x4 (&sc)[2][2], const lu8* stA,
-                                                const lu8* stB, const lu8* prd, f32x16 (&o)[4][4], bool fixed,
+                                                const lu8* stB, const lu8* prd, f32x16 (&o)[4][4],
                                                 float (&m_ref)[2], float (&m_all)[2], float (&l_run)[2], bool& ovf) {
   bf16x8 v[2][4], p[2][4];
 #pragma unroll
@@ -342,7 +346,7 @@ __device__ __forceinline__ void pv_weights_step(const Ctx& c, int m, const f32x4
     for (int hb = 0; hb < 4; ++hb) p[j][hb] = *(lbf16x8*)(prd + j * P_STAGE + 1024 * hb);
   }
   __builtin_amdgcn_sched_barrier(0);
-  PvwState st{c, m, sc, v, p, o, fixed, m_ref, m_all, l_run, ovf, c.lds + P_OFF + (m & 1) * P_BYTES + c.pw_ofs,
+  PvwState st{c, m, sc, v, p, o, m_ref, m_all, l_run, ovf, c.lds + P_OFF + (m & 1) * P_BYTES + c.pw_ofs,
               {0.0f, 0.0f}, {}};
   pvw_slots(st, std::make_integer_sequence<int, 32>{});
 }
@@ -374,15 +378,14 @@ __device__ __forceinline__ void zero_tail(const Ctx& c, int slot) {
 // m_all collects the exact maximum of each of the wave's heads; the return
 // value says whether a score exceeded the reference by more than the
 // headroom (only possible with fixed == false).
-__device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2], bool fixed, float (&m_ref)[2],
+__device__ __forceinline__ void zero_p1(const Ctx& c) {
+  const int tid = c.wave * 64 + c.lane;
+  *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * tid) = bf16x8{};
+  *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * (tid + 256)) = bf16x8{};
+}
+__device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2], float (&m_ref)[2],
                                          float (&m_all)[2], float (&l_run)[2], f32x16 (&o)[4][4]) {
-  issue_stage(c, 1, 1);  // stage 0 is already on its way
-  issue_stage(c, 2, 2);
-  {
-    const int tid = c.wave * 64 + c.lane;
-    *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * tid) = bf16x8{};
-    *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * (tid + 256)) = bf16x8{};
-  }
+  zero_p1(c);
   bool ovf = false;
   int sa = 0;  // slot of stage 2m
   for (int m = 0; m <= c.nsteps; ++m) {
@@ -410,7 +413,7 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2]
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) sc[0][hb] = sc[1][hb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
-    pv_weights_step(c, m, sc, va, vb, prd, o, fixed, m_ref, m_all, l_run, ovf);
+    pv_weights_step(c, m, sc, va, vb, prd, o, m_ref, m_all, l_run, ovf);
     sa = wrap(sa + 2);
   }
   return ovf;
@@ -435,13 +438,15 @@ __device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4],
   }
   __syncthreads();
 
+  // The rows go out through LDS (the ring is free by now): row h at 1024 h,
+  // 16-byte chunk C at 16 (C ^ h%16), so that the register-layout writes
+  // spread over the banks and every global store writes one whole 1 KiB row.
   // O^T lane layout: head 32 hb + lane%32, channels 32 cb + 8 (r/4) + 4 (lane/32) + r%4
   const int n = lane & 31, cg = lane >> 5;
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const int h = 32 * hb + n;
     const float inv = 1.0f / lsum[h];
-    bf16_t* orow = opart + (prow0 + h) * DC + 128 * wave;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -449,9 +454,17 @@ __device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4],
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (bf16_t)(o[i][hb][4 * r4 + e] * inv);
-        *(bf16x4*)(orow + 32 * i + 8 * r4 + 4 * cg) = v;
+        const int C = 16 * wave + 4 * i + r4;
+        *(__attribute__((address_space(3))) bf16x4*)(c.lds + 1024 * h + 16 * (C ^ (h & 15)) + 8 * cg) = v;
       }
     }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int k = 0; k < H / NW; ++k) {
+    const int h = NW * k + wave;
+    const bf16x8 v = *(lbf16x8*)(c.lds + 1024 * h + 16 * (lane ^ (h & 15)));
+    *(bf16x8*)(opart + (prow0 + h) * DC + 8 * lane) = v;
   }
 }
 
@@ -459,13 +472,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
                 const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt, int max_pages,
                 const int32_t* __restrict__ seqlens, bf16_t* __restrict__ opart, float* __restrict__ lpart,
-                int32_t* __restrict__ hdr, int batch, int32_t* __restrict__ ovf_flag, float* __restrict__ amax,
-                int fixup) {
+                int32_t* __restrict__ hdr, int batch) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lu8* lds = (lu8*)lds_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
-  if (!fixup && blockIdx.x == 0 && threadIdx.x == 0) {  // the split plan, for the combine
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // the split plan, for the combine
     hdr[HDR_MAGIC] = WS_MAGIC; hdr[HDR_S] = S; hdr[HDR_PPS] = pps; hdr[HDR_BATCH] = batch;
     hdr[HDR_SQ] = s_q; hdr[HDR_H] = H; hdr[HDR_DC] = DC; hdr[HDR_PDT] = MLA_BF16;
   }
@@ -493,9 +505,7 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
 
   const size_t item = ((size_t)b * S + s) * s_q + j;
   const size_t prow0 = item * H;  // partial row of head 0
-  if (fixup && ovf_flag[item] == 0) return;  // second launch: only items that overflowed
   if (c.nst == 0) {
-    if (threadIdx.x == 0) ovf_flag[item] = 0;
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     for (int i = threadIdx.x; i < H * DC / 8; i += 256) *(u32x4*)(opart + prow0 * DC + 8 * i) = u32x4{0, 0, 0, 0};
     if (threadIdx.x < H) lpart[prow0 + threadIdx.x] = -INFINITY;
@@ -521,20 +531,23 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   c.dma_ofs = (uint32_t)(g * 1024 + i16 * 16);
   // RoPE rows of all heads to LDS: row h at QR_OFF + 128h, its eight 16-byte
   // chunks permuted by (h/2)%8 (conflict-free B-operand reads).
+  // the first three stages go out before anything waits
+  issue_stage(c, 0, 0);
+  issue_stage(c, 1, 1);
+  issue_stage(c, 2, 2);
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int i = wave + NW * n;
     const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
     dma_1k((const uint8_t*)qblk, (uint32_t)((h * DKV + DC + 8 * lc) * 2), c.lds_addr + QR_OFF + i * 1024);
   }
-  issue_stage(c, 0, 0);
   // Absorbed query rows as B operands: lane holds qt[hq + 16 hb][32 ks + 8 g .. +8].
   bf16x8 qf[16][2];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) qf[ks][hb] = *(const bf16x8*)(qblk + (size_t)(hq + 16 * hb) * DKV + 32 * ks + 8 * g);
-  wait_vmcnt<0>();  // the compiler's own loads are then known complete
+  wait_vmcnt<0>();  // the compiler's own loads are then known complete (and stages 0-2 have landed)
 
   // K fragment: token i16, chunk 4 ks + g (chunk % 4 = g)
   c.koff = (uint32_t)(256 * g + 16 * (i16 ^ slot_x(g)));
@@ -561,26 +574,28 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   }
 
   f32x16 o[4][4];
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_all[2], l_run[2];
+  // A second pass, against the exact maximum, only if a score outgrew the
+  // first step's reference.  Both passes run the same code (a runtime loop,
+  // nothing to specialise on), so the step code exists once.
+#pragma clang loop unroll(disable)
+  for (int pass = 0;; ++pass) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
-  float m_ref[2] = {-INFINITY, -INFINITY}, m_all[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-  if (fixup) {  // the exact maximum found by the first launch
-    m_ref[0] = amax[prow0 + hq];
-    m_ref[1] = amax[prow0 + hq + 16];
+      for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
+    m_all[0] = m_all[1] = -INFINITY;
+    l_run[0] = l_run[1] = 0.0f;
+    const bool ovf = run_pass(c, qf, m_ref, m_all, l_run, o);
+    const bool again = __syncthreads_or(ovf);  // also: every wave is done with the ring
+    if (pass > 0 || !again) break;
+    m_ref[0] = m_all[0];
+    m_ref[1] = m_all[1];
+    issue_stage(c, 0, 0);
+    issue_stage(c, 1, 1);
+    issue_stage(c, 2, 2);
   }
-  const bool ovf = run_pass(c, qf, fixup != 0, m_ref, m_all, l_run, o);
-  __syncthreads();  // every wave is done with the ring
   write_out(c, o, m_ref, l_run, opart, lpart, prow0);
-  if (!fixup) {
-    const bool any = __syncthreads_or(ovf);
-    if (any && g == 0) {
-      amax[prow0 + hq] = m_all[0];
-      amax[prow0 + hq + 16] = m_all[1];
-    }
-    if (threadIdx.x == 0) ovf_flag[item] = any ? 1 : 0;
-  }
 }
 
 }  // namespace
@@ -593,13 +608,9 @@ hipError_t fast_attention_b(const DecodeArgs& a) {
   }
   const int P_items = a.batch * a.S;
   const int grid = ((P_items + 7) / 8) * 8 * a.s_q;
-  // second launch: items whose scores outgrew the first step's reference
-  for (int fixup = 0; fixup < 2; ++fixup)
-    MLA_TRY(launch(&k_attn_v3b, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
-                   (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages, a.seqlens,
-                   (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch,
-                   (int32_t*)(a.ws + a.L.ovf), (float*)(a.ws + a.L.amax), fixup));
-  return hipSuccess;
+  return launch(&k_attn_v3b, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
+                (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages, a.seqlens,
+                (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch);
 }
 
 }  // namespace mla

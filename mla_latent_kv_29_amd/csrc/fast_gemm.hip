@@ -16,6 +16,7 @@
 // blockIdx.z and a batch (head) index in blockIdx.y.  The decode GEMMs have
 // only 64-256 activation rows: they stream the weights, so what matters is
 // keeping enough full cache lines in flight per CU.
+#include <math.h>
 #include "internal.hpp"
 
 namespace mla {
@@ -182,7 +183,8 @@ struct EpiUQ {
   bf16_t* qt;
   const int32_t* seqlens;
   int H, d_head, d_rope, d_c, s_q;
-  float theta, scale2;
+  float scale2;
+  double freq[32];  // theta^(-2m/d_rope) of RoPE pair m
   __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
     const int w = d_head + d_rope;
     const int i = col / w, d = col % w;
@@ -203,7 +205,7 @@ struct EpiUQ {
       int p = seqlens[b] - s_q + j;
       p = p < 0 ? 0 : p;
       float cs, sn;
-      rope_cs(p, m, d_rope, theta, &cs, &sn);
+      rope_cs_w(p, freq[m], &cs, &sn);
       const float x0 = odd ? other : v[r], x1 = odd ? v[r] : other;
       const float y = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
       qt[((long)rr * H + i) * (d_c + d_rope) + d_c + (d - d_head)] = (bf16_t)(scale2 * y);
@@ -317,6 +319,7 @@ GemmArgs gemm_args(int M, int N, int K, const bf16_t* X, long ldx, long bsx, con
 hipError_t fast_query(const DecodeArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
+  if (skinny_query_supported(d, R)) return skinny_query(a);
   const float scale2 = a.scale * LOG2E;
   bf16_t* qt = (bf16_t*)(a.ws + a.L.qt);
   bf16_t* qc = (bf16_t*)(a.ws + a.L.u);  // q^C, bf16 [R][H][d_head]
@@ -342,7 +345,8 @@ hipError_t fast_query(const DecodeArgs& a) {
   }
   {
     GemmArgs g = gemm_args(R, H * (d.d_head + d.d_rope), d.d_cq, cq, d.d_cq, 0, (const bf16_t*)a.W_UQ, d.d_cq, 0, 1);
-    EpiUQ epi{qc, qt, a.seqlens, H, d.d_head, d.d_rope, d.d_c, a.s_q, d.rope_theta, scale2};
+    EpiUQ epi{qc, qt, a.seqlens, H, d.d_head, d.d_rope, d.d_c, a.s_q, scale2, {}};
+    for (int m = 0; m < d.d_rope / 2; ++m) epi.freq[m] = pow((double)d.rope_theta, -2.0 * m / d.d_rope);
     e = launch_gemm<true>(g, 1, 1, epi, a.stream);
     if (e != hipSuccess) return e;
   }

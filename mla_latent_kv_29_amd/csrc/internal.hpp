@@ -16,8 +16,6 @@ namespace mla {
 //   lpart    : f32 [B][S][s_q][H]          per-split log2-sum-exp2 of scores
 //   opart    : f32 or bf16 [B][S][s_q][H][d_c]  per-split normalised latent outputs
 //                                        (sized for f32; element type in the header)
-//   ovf      : i32 [B][S][s_q]           MFMA attention: item needs its exact-maximum pass
-//   amax     : f32 [B][S][s_q][H]        MFMA attention: exact score maximum of such an item
 // R = batch * s_q.  Everything up to lpart is independent of the split count
 // S; opart follows lpart, so a kernel that reads S from the header finds it
 // with opart_offset().
@@ -27,7 +25,7 @@ constexpr int WS_HEADER_INTS = 64;
 constexpr int32_t WS_MAGIC = 0x4d4c4144;  // "MLAD"
 
 struct WsLayout {
-  size_t header, cq_part, cq, u, qt, opart, lpart, ovf, amax, total;
+  size_t header, cq_part, cq, u, qt, opart, lpart, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -48,8 +46,6 @@ inline WsLayout ws_layout(const mla_dims& d, int act, int batch, int s_q, int S)
   w.qt = o;      o = align256(o + R * H * (d.d_c + d.d_rope) * es);
   w.lpart = o;   o = align256(o + (size_t)batch * S * s_q * H * 4);
   w.opart = o;   o = align256(o + (size_t)batch * S * s_q * H * d.d_c * 4);
-  w.ovf = o;     o = align256(o + (size_t)batch * S * s_q * 4);
-  w.amax = o;    o = align256(o + (size_t)batch * S * s_q * H * 4);
   w.total = o;
   return w;
 }
@@ -123,5 +119,7 @@ hipError_t fast_attention_b(const DecodeArgs& a);
 hipError_t fast_attention_v1(const DecodeArgs& a);
 hipError_t fast_query(const DecodeArgs& a);
 hipError_t fast_combine_mfma(const CombineArgs& a);
+bool skinny_query_supported(const mla_dims& d, int R);
+hipError_t skinny_query(const DecodeArgs& a);
 
 }  // namespace mla
