@@ -493,11 +493,36 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   if (u / RB >= n_per || p >= P_items) return;
   const int b = p / S, s = p % S;
 
+  const int g = lane >> 4, i16 = lane & 15;
+  const int hq = 32 * wave + i16;  // head of this lane in head block 0 of the scores layout
+  const bf16_t* qblk = qt + (size_t)(b * s_q + j) * H * DKV;
+  const int32_t* bt_row = bt + (size_t)b * max_pages;
+  const int p0 = s * pps;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  // Everything that needs only the block index goes out at once: the length
+  // and the split's page ids side by side, then the query rows; the stage
+  // copies follow as soon as the length and the page ids are in.
   const int L = seqlens[b];
+  const int bt_lane = lane < pps && p0 + lane < max_pages ? bt_row[p0 + lane] : 0;
+  // RoPE rows of all heads to LDS: row h at QR_OFF + 128h, its eight 16-byte
+  // chunks permuted by (h/2)%8 (conflict-free B-operand reads).
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i = wave + NW * n;
+    const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
+    dma_1k((const uint8_t*)qblk, (uint32_t)((h * DKV + DC + 8 * lc) * 2), lds_addr + QR_OFF + i * 1024);
+  }
+  // Absorbed query rows as B operands: lane holds qt[hq + 16 hb][32 ks + 8 g .. +8].
+  bf16x8 qf[16][2];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) qf[ks][hb] = *(const bf16x8*)(qblk + (size_t)(hq + 16 * hb) * DKV + 32 * ks + 8 * g);
+
   int vis = L > 0 ? L - s_q + j + 1 : 0;
   vis = vis < 0 ? 0 : vis;
   Ctx c;
-  c.t_begin = s * pps * PAGE;
+  c.t_begin = p0 * PAGE;
   const int t_end = min(vis, c.t_begin + pps * PAGE);
   c.ntok = t_end > c.t_begin ? t_end - c.t_begin : 0;
   c.nst = (c.ntok + T - 1) / T;
@@ -509,44 +534,24 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     for (int i = threadIdx.x; i < H * DC / 8; i += 256) *(u32x4*)(opart + prow0 * DC + 8 * i) = u32x4{0, 0, 0, 0};
     if (threadIdx.x < H) lpart[prow0 + threadIdx.x] = -INFINITY;
+    wait_vmcnt<0>();  // nothing in flight into LDS when the block leaves
     return;
   }
 
-  const int g = lane >> 4, i16 = lane & 15;
-  const int hq = 32 * wave + i16;  // head of this lane in head block 0 of the scores layout
-  const bf16_t* qblk = qt + (size_t)(b * s_q + j) * H * DKV;
-
   c.pages = pages;
   c.page_bytes = page_bytes;
-  c.bt_row = bt + (size_t)b * max_pages;
-  c.p0 = c.t_begin / PAGE;
-  {
-    const int np = (c.ntok + PAGE - 1) / PAGE;
-    c.bt_lane = lane < np ? c.bt_row[c.p0 + lane] : 0;
-  }
+  c.bt_row = bt_row;
+  c.p0 = p0;
+  c.bt_lane = bt_lane;
   c.lds = lds;
-  c.lds_addr = (uint32_t)(uintptr_t)lds;
+  c.lds_addr = lds_addr;
   c.wave = wave;
   c.lane = lane;
   c.dma_ofs = (uint32_t)(g * 1024 + i16 * 16);
-  // RoPE rows of all heads to LDS: row h at QR_OFF + 128h, its eight 16-byte
-  // chunks permuted by (h/2)%8 (conflict-free B-operand reads).
   // the first three stages go out before anything waits
   issue_stage(c, 0, 0);
   issue_stage(c, 1, 1);
   issue_stage(c, 2, 2);
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int i = wave + NW * n;
-    const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
-    dma_1k((const uint8_t*)qblk, (uint32_t)((h * DKV + DC + 8 * lc) * 2), c.lds_addr + QR_OFF + i * 1024);
-  }
-  // Absorbed query rows as B operands: lane holds qt[hq + 16 hb][32 ks + 8 g .. +8].
-  bf16x8 qf[16][2];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) qf[ks][hb] = *(const bf16x8*)(qblk + (size_t)(hq + 16 * hb) * DKV + 32 * ks + 8 * g);
   wait_vmcnt<0>();  // the compiler's own loads are then known complete (and stages 0-2 have landed)
 
   // K fragment: token i16, chunk 4 ks + g (chunk % 4 = g)
