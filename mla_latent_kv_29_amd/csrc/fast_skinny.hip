@@ -63,7 +63,13 @@ struct XPlain {  // X[batch][M][ldx] (bf16)
 // waves for its column pairs and hands them to the epilogue.
 template <int WPB, int NB>
 struct SkPlan {
-  static constexpr int NBR = WPB * 64 * (NB * 16 + 4) * 4 <= 144 * 1024 ? NB : NB / 2;
+  static constexpr int bytes(int nbr) { return (WPB * 64 * (nbr * 16 + 4) + (nbr == NB ? 0 : 64 * (NB * 16 + 2))) * 4; }
+  static constexpr int pick() {
+    for (int nbr = NB; nbr > 1; --nbr)
+      if (NB % nbr == 0 && bytes(nbr) <= 160 * 1024) return nbr;
+    return 1;
+  }
+  static constexpr int NBR = pick();  // column blocks per reduction round
   static constexpr int LDN = NBR * 16 + 4;
   static constexpr int SLAB = 64 * LDN;  // floats per wave
   // with several rounds the sums wait in a final tile [64 m][NB*16 + 2] for
