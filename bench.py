@@ -80,7 +80,7 @@ def measured_traffic(workload, cache):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=16):
+def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=64):
     """The float64 oracle (decode from cached latents, explicit per-head k^C and
     v^C) on a bounded sample of sequences of the same workload; cached
     tokens/s = sum of sample lengths / oracle time."""
