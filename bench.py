@@ -54,7 +54,7 @@ def algorithmic(spec, dims, lengths):
 # figure measured with hardware counters is reported only while they are
 # unchanged since the measurement.
 ATTN_SOURCES = {"bf16": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
-                "fp8": ["fast_attn.hip", "layout.hpp", "common.hpp"]}
+                "fp8": ["fast_attn2.hip", "layout.hpp", "common.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
 
@@ -242,7 +242,7 @@ def main():
                    "cached_tokens": int(tokens), "rotation_sets": len(sets)},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": measured_traffic(args.workload, spec["cache"]),
-                     "kernel": ("k_attn_v3b" if spec["cache"] == "bf16" else "k_attn_v3<fp8>") + " (mla_decode_attend)",
+                     "kernel": ("k_attn_v3b<false>" if spec["cache"] == "bf16" else "k_attn_v3b<true>") + " (mla_decode_attend)",
                      "attn_ms_mean": float(np.mean(a_ms))},
         "step_roofline": {"t_bound_us": t_bound * 1e6, "frac": t_bound / (ms_per_step * 1e-3),
                           "step_bytes": alg["step_bytes"], "step_flops": alg["step_flops"]},

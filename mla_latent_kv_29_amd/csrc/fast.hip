@@ -1,6 +1,5 @@
 // Dispatch of the MFMA path for the DeepSeek-V3 MLA shape (d_c 512, d_rope
 // 64, 128 heads of 128, 64-token pages, bf16 activations).
-#include <stdlib.h>
 #include "internal.hpp"
 
 namespace mla {
@@ -25,10 +24,7 @@ hipError_t fast_decode(const DecodeArgs& a) {
   return fast_attention(a);
 }
 
-hipError_t fast_attention(const DecodeArgs& a) {
-  if (a.cache_dtype == MLA_BF16 && !getenv("MLA_ATTN_V1")) return fast_attention_b(a);
-  return fast_attention_v1(a);
-}
+hipError_t fast_attention(const DecodeArgs& a) { return fast_attention_b(a); }
 
 hipError_t fast_combine(const CombineArgs& a) { return fast_combine_mfma(a); }
 

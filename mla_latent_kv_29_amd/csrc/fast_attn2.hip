@@ -1,5 +1,5 @@
 // Split-KV MLA decode attention on MFMA for the DeepSeek-V3 shape
-// (d_c 512, d_rope 64, 128 heads, 64-token bf16 pages), gfx950.
+// (d_c 512, d_rope 64, 128 heads, 64-token bf16 or fp8 pages), gfx950.
 //
 // What it computes (absorbed form; DeepSeek-V3 reading lesson, §2.1.1 and
 // Question 2): for every query row (head i, query j) of sequence b and every
@@ -37,6 +37,15 @@
 // in P.V, three in flight.  The chunk-major swizzled page layout makes that
 // copy verbatim and every LDS access pattern bank-conflict free.
 //
+// FP8 cache (E4M3 codes with one fp32 scale per token and 1x128 channel tile,
+// lesson §3.3; bf16 k^R): the copies land in a 5-slot ring of fp8 stages
+// (three in flight), and after the step's first barrier the block widens the
+// two stages it is about to score into bf16 images (code * scale, rounded
+// once to bf16) in a 4-slot ring; a second barrier publishes them, and the
+// bf16 step code above runs unchanged.  Products stay bf16 x bf16 with fp32
+// accumulation.  The fp8 copies are issued in the widening phase rather than
+// between the score MFMAs, which keeps the step loop free of spills.
+//
 // Softmax reference: the first step's row maximum, with 96 log2 units of
 // headroom, so O is never rescaled.  The pass also collects the exact row
 // maximum.  If some score exceeded the reference by more than the headroom,
@@ -58,13 +67,33 @@ constexpr int NW = 4;                      // waves per block
 constexpr int T = 16;                      // tokens per stage
 constexpr int NCH = DKV / 8;               // 72 sixteen-byte chunks per token
 constexpr int ST_BYTES = NCH * T * 16;     // 18 432
-constexpr int NST = 7;                     // ring slots
-constexpr int P_OFF = NST * ST_BYTES;      // 129 024: two P buffers of two stages
 constexpr int P_STAGE = H * T * 2;         // 4 096
 constexpr int P_BYTES = 2 * P_STAGE;       // 8 192
-constexpr int QR_OFF = P_OFF + 2 * P_BYTES;  // RoPE query rows: 128 x 64 bf16
-constexpr int L_OFF = QR_OFF + H * 64 * 2;   // per-head softmax sums at the end
-constexpr int LDS_BYTES = L_OFF + H * 4;     // 162 304
+// fp8 stage in LDS: the 16 tokens' E4M3 codes (32 sixteen-channel chunks x 16
+// slots), their bf16 k^R (8 eight-channel chunks x 16 slots), then their fp32
+// scales (4 per token); in page order, so one 1 KiB copy instruction n lands
+// at 1024 n.
+constexpr int F8_ST = 8192 + 2048 + 256;   // 10 496
+constexpr int F8_ROPE = 8192, F8_SCALES = 10240;
+// the same three blocks inside a 64-token fp8 page
+constexpr int F8_PG_SCALES = PAGE * DC, F8_PG_ROPE = F8_PG_SCALES + PAGE * (DC / 128) * 4;  // 32 768, 33 792
+
+// LDS layout.  bf16 cache: a 7-slot ring of 16-token stages.  fp8 cache: the
+// copies land in a 5-slot ring of fp8 stages, and each stage is widened to
+// its bf16 image in a 4-slot ring (two being scored, two in P.V).  Then two
+// P buffers, the RoPE query rows (128 x 64 bf16) and the per-head sums.
+template <bool F8>
+struct Lay {
+  static constexpr int NST = F8 ? 4 : 7;                 // bf16 stage slots
+  static constexpr int NF8 = F8 ? 5 : 0;                 // fp8 stage slots
+  static constexpr int F8_OFF = NST * ST_BYTES;          // 73 728 (fp8 ring)
+  static constexpr int P_OFF = F8_OFF + NF8 * F8_ST;     // 129 024 | 126 208
+  static constexpr int QR_OFF = P_OFF + 2 * P_BYTES;
+  static constexpr int L_OFF = QR_OFF + H * 64 * 2;
+  static constexpr int LDS_BYTES = L_OFF + H * 4;        // 162 304 | 159 488
+  static constexpr int COPIES = F8 ? 11 : NCH / 4;       // 1 KiB copy instructions per stage
+};
+static_assert(Lay<false>::LDS_BYTES <= 160 * 1024 && Lay<true>::LDS_BYTES <= 160 * 1024, "LDS");
 
 typedef __attribute__((address_space(3))) uint8_t lu8;
 typedef __attribute__((address_space(3))) const bf16x8 lbf16x8;
@@ -104,7 +133,9 @@ struct Ctx {
   uint32_t pw_ofs, pr_ofs;    // P write (scores layout) / read (P.V layout)
 };
 
-__device__ __forceinline__ int wrap(int x) { return x >= NST ? x - NST : x; }
+template <bool F8>
+__device__ __forceinline__ int wrap(int x) { return x >= Lay<F8>::NST ? x - Lay<F8>::NST : x; }
+__device__ __forceinline__ int wrap5(int x) { return x >= 5 ? x - 5 : x; }
 
 __device__ __forceinline__ const uint8_t* stage_page(const Ctx& c, int t0) {
   const int idx = t0 / PAGE - c.p0;
@@ -112,18 +143,36 @@ __device__ __forceinline__ const uint8_t* stage_page(const Ctx& c, int t0) {
   return c.pages + (size_t)page * c.page_bytes;
 }
 
-// Stage i (tokens t_begin + 16 i ..) into ring slot `slot`: 18 wave-
-// instructions of 1 KiB (four 256-byte chunk runs each); wave w issues w,
-// w+4, ... -- five on waves 0-1, four on waves 2-3.
+// Copy instruction ii of a stage whose quarter-page base is src (the page
+// plus 256 bytes per earlier 16-token quarter) into the stage at dst.  bf16:
+// 18 instructions of four 256-byte chunk runs.  fp8: 8 of codes, 2 of k^R, and
+// the 256 bytes of scales on lanes 0-15.
+template <bool F8>
+__device__ __forceinline__ void copy_1k(const Ctx& c, const uint8_t* src, uint32_t dst, int ii) {
+  if constexpr (!F8) {
+    dma_1k(src + 4096 * ii, c.dma_ofs, dst + 1024 * ii);
+  } else {
+    const uint8_t* s = ii < 8 ? src + 4096 * ii : ii < 10 ? src + F8_PG_ROPE + 4096 * (ii - 8) : src + F8_PG_SCALES;
+    if (ii < 10 || c.lane < 16) dma_1k(s, c.dma_ofs, dst + 1024 * ii);
+  }
+}
+template <bool F8>
+__device__ __forceinline__ uint32_t stage_dst(const Ctx& c, int slot) {
+  return c.lds_addr + (F8 ? Lay<F8>::F8_OFF + slot * F8_ST : slot * ST_BYTES);
+}
+
+// Stage i (tokens t_begin + 16 i ..) into ring slot `slot` (fp8: the fp8
+// ring); wave w issues copy instructions w, w+4, ...
+template <bool F8>
 __device__ __forceinline__ void issue_stage(const Ctx& c, int i, int slot) {
   if (i >= c.nst) return;
   const int t0 = c.t_begin + i * T;
   const uint8_t* src = stage_page(c, t0) + ((t0 / T) & 3) * (T * 16);
-  const uint32_t dst = c.lds_addr + slot * ST_BYTES;
+  const uint32_t dst = stage_dst<F8>(c, slot);
 #pragma unroll
   for (int n = 0; n < 5; ++n) {
     const int ii = c.wave + NW * n;
-    if (ii < NCH / 4) dma_1k(src + 4096 * ii, c.dma_ofs, dst + 1024 * ii);
+    if (ii < Lay<F8>::COPIES) copy_1k<F8>(c, src, dst, ii);
   }
 }
 
@@ -134,10 +183,11 @@ struct StageCopy {
   const uint8_t* src;  // nullptr: nothing to copy
   uint32_t dst;
 };
+template <bool F8>
 __device__ __forceinline__ StageCopy plan_stage(const Ctx& c, int i, int slot) {
   StageCopy s;
   s.src = nullptr;
-  s.dst = c.lds_addr + slot * ST_BYTES;
+  s.dst = stage_dst<F8>(c, slot);
   if (i < c.nst) {
     const int t0 = c.t_begin + i * T;
     s.src = stage_page(c, t0) + ((t0 / T) & 3) * (T * 16);
@@ -145,17 +195,24 @@ __device__ __forceinline__ StageCopy plan_stage(const Ctx& c, int i, int slot) {
   return s;
 }
 // Instruction n (0..4) of this wave's share of a stage copy.
+template <bool F8>
 __device__ __forceinline__ void copy_part(const Ctx& c, const StageCopy& s, int n) {
   const int ii = c.wave + NW * n;
-  if (s.src != nullptr && ii < NCH / 4) dma_1k(s.src + 4096 * ii, c.dma_ofs, s.dst + 1024 * ii);
+  if (s.src != nullptr && ii < Lay<F8>::COPIES) copy_1k<F8>(c, s.src, s.dst, ii);
 }
 
 // Before step m: stages 2m and 2m+1 have landed once at most the copies of
 // stage 2m+2 (issued one step earlier) are outstanding.
+template <bool F8>
 __device__ __forceinline__ void wait_step(const Ctx& c, int m) {
   if (2 * m + 2 < c.nst) {
-    if (c.wave < 2) wait_vmcnt<5>();
-    else wait_vmcnt<4>();
+    if constexpr (F8) {  // 11 copies: three on waves 0-2, two on wave 3
+      if (c.wave < 3) wait_vmcnt<3>();
+      else wait_vmcnt<2>();
+    } else {  // 18 copies: five on waves 0-1, four on waves 2-3
+      if (c.wave < 2) wait_vmcnt<5>();
+      else wait_vmcnt<4>();
+    }
   } else {
     wait_vmcnt<0>();
   }
@@ -182,9 +239,11 @@ __device__ __forceinline__ f32x4 mfma_s_last(bf16x8 a, bf16x8 b, f32x4 c) {
 // are read while k-step ks multiplies; sched_barrier keeps that order (the
 // scheduler would otherwise sink each read to its use).
 constexpr int KD = 4;
+template <bool F8>
 __device__ __forceinline__ bf16x8 rope_q(const Ctx& c, int ks, int hb) {
-  return *(lbf16x8*)(c.lds + QR_OFF + (ks == 16 ? c.qr_ofs0 : c.qr_ofs1) + 16 * 128 * hb);
+  return *(lbf16x8*)(c.lds + Lay<F8>::QR_OFF + (ks == 16 ? c.qr_ofs0 : c.qr_ofs1) + 16 * 128 * hb);
 }
+template <bool F8>
 __device__ __forceinline__ void step_scores(const Ctx& c, const lu8* stA, const lu8* stB, const bf16x8 (&qf)[16][2],
                                             f32x4 (&sc)[2][2], const StageCopy& cx, const StageCopy& cy) {
   const lu8* ka = stA + c.koff;
@@ -199,8 +258,8 @@ __device__ __forceinline__ void step_scores(const Ctx& c, const lu8* stA, const 
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
     if (ks == 12) {  // RoPE query fragments for k-steps 16, 17
-      r0[0] = rope_q(c, 16, 0); r0[1] = rope_q(c, 16, 1);
-      r1[0] = rope_q(c, 17, 0); r1[1] = rope_q(c, 17, 1);
+      r0[0] = rope_q<F8>(c, 16, 0); r0[1] = rope_q<F8>(c, 16, 1);
+      r1[0] = rope_q<F8>(c, 17, 0); r1[1] = rope_q<F8>(c, 17, 1);
     }
     const bf16x8 a = fa[ks % KD], b = fb[ks % KD];
     const bf16x8 q0 = ks < 16 ? qf[ks][0] : (ks == 16 ? r0[0] : r1[0]);
@@ -229,8 +288,10 @@ __device__ __forceinline__ void step_scores(const Ctx& c, const lu8* stA, const 
     }
     // the next two stages' copies go out between these MFMAs, early in the
     // step: the first at k-steps 1..5, the second at 6..10
-    if (ks >= 1 && ks <= 5) copy_part(c, cx, ks - 1);
-    if (ks >= 6 && ks <= 10) copy_part(c, cy, ks - 6);
+    if constexpr (!F8) {  // (the fp8 copies go out in the widening phase)
+      if (ks >= 1 && ks <= 5) copy_part<F8>(c, cx, ks - 1);
+      if (ks >= 6 && ks <= 10) copy_part<F8>(c, cy, ks - 6);
+    }
   }
 }
 
@@ -328,6 +389,7 @@ __device__ __forceinline__ void pvw_slots(PvwState& st, std::integer_sequence<in
   (pvw_slot<K>(st), ...);
 }
 
+template <bool F8>
 __device__ __forceinline__ void pv_weights_step(const Ctx& c, int m, const f32x4 (&sc)[2][2], const lu8* stA,
                                                 const lu8* stB, const lu8* prd, f32x16 (&o)[4][4],
                                                 float (&m_ref)[2], float (&m_all)[2], float (&l_run)[2], bool& ovf) {
@@ -346,7 +408,7 @@ __device__ __forceinline__ void pv_weights_step(const Ctx& c, int m, const f32x4
     for (int hb = 0; hb < 4; ++hb) p[j][hb] = *(lbf16x8*)(prd + j * P_STAGE + 1024 * hb);
   }
   __builtin_amdgcn_sched_barrier(0);
-  PvwState st{c, m, sc, v, p, o, m_ref, m_all, l_run, ovf, c.lds + P_OFF + (m & 1) * P_BYTES + c.pw_ofs,
+  PvwState st{c, m, sc, v, p, o, m_ref, m_all, l_run, ovf, c.lds + Lay<F8>::P_OFF + (m & 1) * P_BYTES + c.pw_ofs,
               {0.0f, 0.0f}, {}};
   pvw_slots(st, std::make_integer_sequence<int, 32>{});
 }
@@ -378,31 +440,83 @@ __device__ __forceinline__ void zero_tail(const Ctx& c, int slot) {
 // m_all collects the exact maximum of each of the wave's heads; the return
 // value says whether a score exceeded the reference by more than the
 // headroom (only possible with fixed == false).
+template <bool F8>
 __device__ __forceinline__ void zero_p1(const Ctx& c) {
   const int tid = c.wave * 64 + c.lane;
-  *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * tid) = bf16x8{};
-  *(__attribute__((address_space(3))) bf16x8*)(c.lds + P_OFF + P_BYTES + 16 * (tid + 256)) = bf16x8{};
+  *(__attribute__((address_space(3))) bf16x8*)(c.lds + Lay<F8>::P_OFF + P_BYTES + 16 * tid) = bf16x8{};
+  *(__attribute__((address_space(3))) bf16x8*)(c.lds + Lay<F8>::P_OFF + P_BYTES + 16 * (tid + 256)) = bf16x8{};
 }
+
+// fp8: widens stage slot `fs` of the fp8 ring into the bf16 image in slot
+// `bs`: code * scale, rounded once to bf16 (products then stay bf16 x bf16
+// with fp32 accumulation); k^R is copied.  Thread: token tid%16, 8-channel
+// chunks tid/16 + 16 j (scale tile j), and k^R chunk tid/16 on threads < 128.
+__device__ __forceinline__ void widen_stage(const Ctx& c, int fs, int bs) {
+  const int tid = c.wave * 64 + c.lane, t = tid & 15, cq = tid >> 4;
+  // chunks cq + 16 j share the slot permutation (x depends on the chunk mod
+  // 4), so one source and one destination offset serve all four
+  const int dofs = 256 * cq + 16 * (t ^ slot_x(cq));
+  const lu8* f8 = c.lds + Lay<true>::F8_OFF + fs * F8_ST;
+  const lu8* src = f8 + 256 * (cq >> 1) + 16 * (t ^ slot_x(cq >> 1)) + 8 * (cq & 1);
+  const lu8* scl = f8 + F8_SCALES + 16 * t;
+  lu8* dst = c.lds + bs * ST_BYTES + dofs;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // 8-channel chunk cq + 16 j = 16-channel chunk cq/2 + 8 j, scale tile j
+    const u32x2 code = *(__attribute__((address_space(3))) const u32x2*)(src + 2048 * j);
+    const float sc = *(__attribute__((address_space(3))) const float*)(scl + 4 * j);
+    bf16x8 v;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[w], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[w], true);
+      v[4 * w + 0] = (bf16_t)(lo[0] * sc);
+      v[4 * w + 1] = (bf16_t)(lo[1] * sc);
+      v[4 * w + 2] = (bf16_t)(hi[0] * sc);
+      v[4 * w + 3] = (bf16_t)(hi[1] * sc);
+    }
+    *(__attribute__((address_space(3))) bf16x8*)(dst + 4096 * j) = v;
+  }
+  // k^R chunk cq (threads < 128): the same slot order in both (x(64 + m) = x(m))
+  if (tid < 128) *(__attribute__((address_space(3))) bf16x8*)(dst + 256 * 64) = *(lbf16x8*)(f8 + F8_ROPE + dofs);
+}
+template <bool F8>
 __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2], float (&m_ref)[2],
                                          float (&m_all)[2], float (&l_run)[2], f32x16 (&o)[4][4]) {
-  zero_p1(c);
+  using Ly = Lay<F8>;
+  zero_p1<F8>(c);
   bool ovf = false;
   int sa = 0;  // slot of stage 2m
+  int fa = 0;  // fp8: fp8-ring slot of stage 2m
   for (int m = 0; m <= c.nsteps; ++m) {
-    if (m < c.nsteps) wait_step(c, m);
+    if (m < c.nsteps) wait_step<F8>(c, m);
     ring_barrier();
-    const int pa = wrap(sa + 5), pb = 2 * m - 1 < c.nst ? wrap(sa + 6) : pa;
-    const lu8* va = m > 0 ? c.lds + pa * ST_BYTES : c.lds + QR_OFF;
-    const lu8* vb = m > 0 ? c.lds + pb * ST_BYTES : c.lds + QR_OFF;
-    const lu8* prd = c.lds + P_OFF + ((m - 1) & 1) * P_BYTES + c.pr_ofs;
+    if constexpr (F8) {
+      // this step's two stages into the bf16 slots freed by the last P.V
+      if (m < c.nsteps) {
+        widen_stage(c, fa, sa);
+        if (2 * m + 1 < c.nst) widen_stage(c, wrap5(fa + 1), wrap<F8>(sa + 1));
+      }
+      // copies of stages 2m+3, 2m+4 into the fp8 slots widened last step
+      issue_stage<F8>(c, 2 * m + 3, wrap5(fa + 3));
+      issue_stage<F8>(c, 2 * m + 4, wrap5(fa + 4));
+      ring_barrier();
+    }
+    const int pa = wrap<F8>(sa + Ly::NST - 2), pb = 2 * m - 1 < c.nst ? wrap<F8>(sa + Ly::NST - 1) : pa;
+    const lu8* va = m > 0 ? c.lds + pa * ST_BYTES : c.lds + Ly::QR_OFF;
+    const lu8* vb = m > 0 ? c.lds + pb * ST_BYTES : c.lds + Ly::QR_OFF;
+    const lu8* prd = c.lds + Ly::P_OFF + ((m - 1) & 1) * P_BYTES + c.pr_ofs;
     // copies of stages 2m+3, 2m+4 (none past the last step)
-    const StageCopy cx = plan_stage(c, 2 * m + 3, wrap(sa + 3));
-    const StageCopy cy = plan_stage(c, 2 * m + 4, wrap(sa + 4));
+    StageCopy cx{nullptr, 0}, cy{nullptr, 0};
+    if constexpr (!F8) {
+      cx = plan_stage<F8>(c, 2 * m + 3, wrap<F8>(sa + 3));
+      cy = plan_stage<F8>(c, 2 * m + 4, wrap<F8>(sa + 4));
+    }
     f32x4 sc[2][2];
     if (m < c.nsteps) {
-      const int sb = 2 * m + 1 < c.nst ? wrap(sa + 1) : sa;
+      const int sb = 2 * m + 1 < c.nst ? wrap<F8>(sa + 1) : sa;
       if ((c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
-      step_scores(c, c.lds + sa * ST_BYTES, c.lds + sb * ST_BYTES, qf, sc, cx, cy);
+      step_scores<F8>(c, c.lds + sa * ST_BYTES, c.lds + sb * ST_BYTES, qf, sc, cx, cy);
       const int nv = c.ntok - 2 * m * T;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
@@ -413,20 +527,22 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2]
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) sc[0][hb] = sc[1][hb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
-    pv_weights_step(c, m, sc, va, vb, prd, o, m_ref, m_all, l_run, ovf);
-    sa = wrap(sa + 2);
+    pv_weights_step<F8>(c, m, sc, va, vb, prd, o, m_ref, m_all, l_run, ovf);
+    sa = wrap<F8>(sa + 2);
+    if constexpr (F8) fa = wrap5(fa + 2);
   }
   return ovf;
 }
 
 // Normalised partial output of the item: O / l per head (bf16) and the
 // per-head log2-sum-exp2 m_ref + log2(l).
+template <bool F8>
 __device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4], const float (&m_ref)[2],
                                           const float (&l_run)[2], bf16_t* opart, float* lpart, size_t prow0) {
   const int lane = c.lane, wave = c.wave;
   const int g = lane >> 4, hq = 32 * wave + (lane & 15);
   // per-head sums of the weights: the 4 token groups of a head are lanes i16 + 16g
-  float* lsum = (float*)(c.lds + L_OFF);
+  float* lsum = (float*)(c.lds + Lay<F8>::L_OFF);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     float l_tot = l_run[hb] + __shfl_xor(l_run[hb], 16, 64);
@@ -468,6 +584,7 @@ __device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4],
   }
 }
 
+template <bool F8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
                 const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt, int max_pages,
@@ -510,7 +627,7 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   for (int n = 0; n < 4; ++n) {
     const int i = wave + NW * n;
     const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
-    dma_1k((const uint8_t*)qblk, (uint32_t)((h * DKV + DC + 8 * lc) * 2), lds_addr + QR_OFF + i * 1024);
+    dma_1k((const uint8_t*)qblk, (uint32_t)((h * DKV + DC + 8 * lc) * 2), lds_addr + Lay<F8>::QR_OFF + i * 1024);
   }
   // Absorbed query rows as B operands: lane holds qt[hq + 16 hb][32 ks + 8 g .. +8].
   bf16x8 qf[16][2];
@@ -549,9 +666,9 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   c.lane = lane;
   c.dma_ofs = (uint32_t)(g * 1024 + i16 * 16);
   // the first three stages go out before anything waits
-  issue_stage(c, 0, 0);
-  issue_stage(c, 1, 1);
-  issue_stage(c, 2, 2);
+  issue_stage<F8>(c, 0, 0);
+  issue_stage<F8>(c, 1, 1);
+  issue_stage<F8>(c, 2, 2);
   wait_vmcnt<0>();  // the compiler's own loads are then known complete (and stages 0-2 have landed)
 
   // K fragment: token i16, chunk 4 ks + g (chunk % 4 = g)
@@ -591,31 +708,42 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
       for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
     m_all[0] = m_all[1] = -INFINITY;
     l_run[0] = l_run[1] = 0.0f;
-    const bool ovf = run_pass(c, qf, m_ref, m_all, l_run, o);
+    const bool ovf = run_pass<F8>(c, qf, m_ref, m_all, l_run, o);
     const bool again = __syncthreads_or(ovf);  // also: every wave is done with the ring
     if (pass > 0 || !again) break;
     m_ref[0] = m_all[0];
     m_ref[1] = m_all[1];
-    issue_stage(c, 0, 0);
-    issue_stage(c, 1, 1);
-    issue_stage(c, 2, 2);
+    issue_stage<F8>(c, 0, 0);
+    issue_stage<F8>(c, 1, 1);
+    issue_stage<F8>(c, 2, 2);
   }
-  write_out(c, o, m_ref, l_run, opart, lpart, prow0);
+  write_out<F8>(c, o, m_ref, l_run, opart, lpart, prow0);
 }
 
 }  // namespace
 
-hipError_t fast_attention_b(const DecodeArgs& a) {
-  static bool attr_set = false;
+template <bool F8>
+static hipError_t launch_attn(const DecodeArgs& a) {
+  constexpr int lds = Lay<F8>::LDS_BYTES;
+  static bool attr_set = false;  // one flag per instantiation
   if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)&k_attn_v3b, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES));
+    MLA_TRY(hipFuncSetAttribute((const void*)&k_attn_v3b<F8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
     attr_set = true;
   }
   const int P_items = a.batch * a.S;
   const int grid = ((P_items + 7) / 8) * 8 * a.s_q;
-  return launch(&k_attn_v3b, dim3(grid), dim3(256), LDS_BYTES, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
+  return launch(&k_attn_v3b<F8>, dim3(grid), dim3(256), lds, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
                 (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages, a.seqlens,
                 (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch);
+}
+
+hipError_t fast_attention_b(const DecodeArgs& a) {
+  if (a.cache_dtype == MLA_FP8_E4M3) {
+    // the page geometry the fp8 stage copies are compiled for
+    if (a.g.fp8_scale_off != (size_t)F8_PG_SCALES || a.g.fp8_rope_off != (size_t)F8_PG_ROPE) return hipErrorInvalidValue;
+    return launch_attn<true>(a);
+  }
+  return launch_attn<false>(a);
 }
 
 }  // namespace mla

@@ -116,7 +116,6 @@ hipError_t fast_decode(const DecodeArgs& a);
 hipError_t fast_combine(const CombineArgs& a);
 hipError_t fast_attention(const DecodeArgs& a);
 hipError_t fast_attention_b(const DecodeArgs& a);
-hipError_t fast_attention_v1(const DecodeArgs& a);
 hipError_t fast_query(const DecodeArgs& a);
 hipError_t fast_combine_mfma(const CombineArgs& a);
 bool skinny_query_supported(const mla_dims& d, int R);
