@@ -79,3 +79,38 @@ def test_fp8_planted_decode_vs_emulated_oracle():
     for b in range(2):
         o_q, _ = case.oracle(b, tau, hq=hq, fp8=True)
         assert max_abs(out[b], o_q) <= 2e-2 * float(np.abs(o_q).max())
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_fp8_bytes_past_the_end_are_ignored(splits):
+    """Page slots past a sequence's length hold NaN patterns in all three
+    blocks (E4M3 code 0xFF, fp32 scale 0xFFFFFFFF, bf16 k^R 0xFFFF): those
+    tokens are not visible, so the output must stay finite and unchanged."""
+    from gpu_common import slot_x
+    case = Case(V3, "bf16", "fp8", [300, 129, 64], s_q=1, table="shuffled", wl=4, num_splits=splits)
+    ps, dc, dr = V3["page_size"], V3["d_c"], V3["d_rope"]
+    s_off = ps * dc
+    r_off = s_off + ps * (dc // 128) * 4
+    raw = case.sess.pages.cpu().numpy()
+    for b, Lb in enumerate(case.lengths):
+        if Lb % ps == 0:
+            continue
+        last = int(case.bt[b, (int(Lb) - 1) // ps])
+        t = np.arange(int(Lb) % ps, ps)[:, None]
+        ch = np.arange(dc)[None, :]
+        C = ch // 16
+        raw[last, (16 * (C * ps + (t ^ slot_x(C))) + ch % 16).ravel()] = 0xFF
+        raw[last, (s_off + 16 * t + np.arange(16)[None, :]).ravel()] = 0xFF
+        m = np.arange(dr)[None, :]
+        Cm = m // 8
+        roff = (r_off + 16 * (Cm * ps + (t ^ slot_x(Cm))) + 2 * (m % 8)).ravel()
+        raw[last, roff] = 0xFF
+        raw[last, roff + 1] = 0xFF
+    case.sess.pages.copy_(torch.from_numpy(raw))
+    torch.cuda.synchronize()
+    tau = tau_of(V3) * 56.0
+    out, lse, _ = case.run(tau)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    for b in range(3):
+        o_q, _ = case.oracle(b, tau, fp8=True)
+        assert max_abs(out[b], o_q) <= 2e-2 * float(np.abs(o_q).max()), b
