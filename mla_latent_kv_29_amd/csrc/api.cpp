@@ -11,7 +11,7 @@ namespace {
 
 constexpr int MAX_S_Q = 8;
 constexpr int TARGET_ITEMS = 256;  // (sequence, query, split) work items aimed for per decode: one per CU
-constexpr int MAX_PAGES_PER_SPLIT = 64;  // caps one item's work so that ragged batches balance
+constexpr int MAX_PAGES_PER_SPLIT = 32;  // caps one item's work (2048 tokens) so that ragged batches balance
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 

@@ -647,9 +647,7 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
 
   const size_t item = ((size_t)b * S + s) * s_q + j;
   const size_t prow0 = item * H;  // partial row of head 0
-  if (c.nst == 0) {
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    for (int i = threadIdx.x; i < H * DC / 8; i += 256) *(u32x4*)(opart + prow0 * DC + 8 * i) = u32x4{0, 0, 0, 0};
+  if (c.nst == 0) {  // an empty split: lse = -inf, which the merge skips without reading its rows
     if (threadIdx.x < H) lpart[prow0 + threadIdx.x] = -INFINITY;
     wait_vmcnt<0>();  // nothing in flight into LDS when the block leaves
     return;
