@@ -40,6 +40,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 struct GemmArgs {
   int M, N, K;              // per batch
   int mtiles;               // ceil(M / 64)
+  int xcd_map;              // column tiles a multiple of 8: keep a tile's row tiles on one XCD
   int k_per_split;          // multiple of BK
   const bf16_t* X;          // [batch][M][ldx]
   long ldx, bsx;
@@ -79,8 +80,21 @@ template <bool W_NK, class Epi>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, Epi epi) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE_BYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 64;
-  const int batch = blockIdx.y / g.mtiles, m0 = (blockIdx.y % g.mtiles) * 64;
+  // The row tiles of one column tile are neighbours in the dispatch order, so
+  // that its weight tiles are fetched from HBM once and then hit in cache;
+  // blocks are dealt to the 8 XCDs round-robin, so with xcd_map they also
+  // share one L2 (blockIdx.x % 8 picks the XCD).
+  int nt, mt;
+  if (g.xcd_map) {
+    const int loc = blockIdx.x >> 3;
+    mt = loc % g.mtiles;
+    nt = (loc / g.mtiles) * 8 + (blockIdx.x & 7);
+  } else {
+    mt = blockIdx.x % g.mtiles;
+    nt = blockIdx.x / g.mtiles;
+  }
+  const int n0 = nt * 64;
+  const int batch = blockIdx.y, m0 = mt * 64;
   const int kb = blockIdx.z * g.k_per_split;
   const int ke = min(g.K, kb + g.k_per_split);
   const int nsteps = (ke - kb) / BK;
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(256) void k_merge(int batch, int H, int s_q, int d_
 
 template <bool W_NK, class Epi>
 hipError_t launch_gemm(const GemmArgs& g, int batch, int splits, const Epi& epi, hipStream_t st) {
-  dim3 grid(g.N / 64, g.mtiles * batch, splits);
+  dim3 grid((g.N / 64) * g.mtiles, batch, splits);
   MLA_TRY(launch(&k_gemm<W_NK, Epi>, grid, dim3(256), 0, st, g, epi));
   return hipSuccess;
 }
@@ -307,6 +321,7 @@ GemmArgs gemm_args(int M, int N, int K, const bf16_t* X, long ldx, long bsx, con
                    int splits) {
   GemmArgs g;
   g.M = M; g.N = N; g.K = K; g.mtiles = (M + 63) / 64;
+  g.xcd_map = (N / 64) % 8 == 0;
   int kps = (K + splits - 1) / splits;
   g.k_per_split = (kps + BK - 1) / BK * BK;
   g.X = X; g.ldx = ldx; g.bsx = bsx; g.W = W; g.ldw = ldw; g.bsw = bsw;
