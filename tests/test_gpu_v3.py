@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from mla_latent_kv_29_amd import inputs
-from gpu_common import Case, tau_of, max_abs
+from gpu_common import Case, tau_of, max_abs, to_np, DEV
 
 pytestmark = pytest.mark.gpu
 V3 = inputs.V3_DIMS
@@ -122,3 +122,22 @@ def test_v3_bf16_bytes_past_the_end_are_ignored(splits):
     out, lse, _ = case.run(tau)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     check_all(case, out, lse, tau, TOL_BF16)
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_v3_bf16_compressed_query_input(s_q):
+    """W_DQ = NULL: the caller passes c^Q = W^DQ h (here the float64 oracle's,
+    rounded to bf16) instead of h; the output matches the oracle decoded
+    from h."""
+    case = Case(V3, "bf16", "bf16", [300, 129, 70], s_q=s_q, table="shuffled", wl=1, num_splits=2)
+    tau = tau_of(V3)
+    Wn = case.weights_np()
+    hq = case.hq()
+    cq = torch.from_numpy(to_np(hq) @ Wn["W_DQ"].T).to(torch.bfloat16).to(DEV).contiguous()
+    out, lse = case.sess.decode(cq, case.W, tau, use_dq=False)
+    torch.cuda.synchronize()
+    out, lse = to_np(out), to_np(lse)
+    for b in range(3):
+        o, l = case.oracle(b, tau)
+        assert max_abs(out[b], o) <= TOL_BF16 * float(np.abs(o).max()), b
+        assert max_abs(lse[b], l) <= TOL_BF16 * max(1.0, float(np.abs(l).max())), b
