@@ -287,16 +287,36 @@ __global__ __launch_bounds__(256) void k_merge(int batch, int H, int s_q, int d_
   if (lse_out && lane == 0) lse_out[row] = W > 0.0f ? (M + log2f(W)) * 0.6931471805599453f : -INFINITY;
   for (int c = 8 * lane; c < d_c; c += 512) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s = 0; s < S; ++s) {
-      const float l = lpart[p0 + s * pstep];
-      if (l == -INFINITY) continue;
-      const float w = exp2f(l - M);
-      const size_t off = (p0 + s * pstep) * d_c + c;
-      if (pbf16) {
-        const bf16x8 v = *(const bf16x8*)((const bf16_t*)opart + off);
+    if (pbf16) {
+      // Lane t of a chunk of 64 splits holds split t's weight; the rows of 8
+      // splits are loaded together (a long split list would otherwise pay
+      // one memory latency per split).  Empty splits are never read.
+      for (int s0 = 0; s0 < S; s0 += 64) {
+        const int n = min(64, S - s0);
+        const float lt = lane < n ? lpart[p0 + (size_t)(s0 + lane) * pstep] : -INFINITY;
+        const float wt = lt == -INFINITY ? 0.0f : exp2f(lt - M);
+        for (int u0 = 0; u0 < n; u0 += 8) {
+          float w[8];
+          bf16x8 v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
-      } else {
+          for (int u = 0; u < 8; ++u) {
+            w[u] = __shfl(wt, u0 + u, 64);  // 0 past the chunk (lanes >= n hold 0)
+            v[u] = bf16x8{};
+            if (w[u] != 0.0f)
+              v[u] = *(const bf16x8*)((const bf16_t*)opart + (p0 + (size_t)(s0 + u0 + u) * pstep) * d_c + c);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += w[u] * (float)v[u][e];
+        }
+      }
+    } else {
+      for (int s = 0; s < S; ++s) {
+        const float l = lpart[p0 + s * pstep];
+        if (l == -INFINITY) continue;
+        const float w = exp2f(l - M);
+        const size_t off = (p0 + s * pstep) * d_c + c;
         const f32x4 v0 = *(const f32x4*)((const float*)opart + off);
         const f32x4 v1 = *(const f32x4*)((const float*)opart + off + 4);
 #pragma unroll
