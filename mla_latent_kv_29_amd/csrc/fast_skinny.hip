@@ -183,52 +183,72 @@ __global__ __launch_bounds__(256) void k_reduce_rows(int MN, int KG, const float
   *(bf16x4*)(y + i) = o;
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
+
 // ------------------------------------------------------------ W^UQ + absorption
 // One block per (head i, half e of d_c), 8 waves:
 //   1. u_i = W^UQ_i c^Q for the head's 128 content rows and the 32 RoPE rows
-//      of half e (16 pairs), K = d_cq split over the waves as in k_skinny;
-//      the content sums, rounded to bf16, stay in LDS as the q^C_i tile, the
-//      RoPE pairs are rotated at the row's position, scaled by tau log2 e and
-//      written to the tail of qt.
-//   2. qt_i[:, 256e .. 256e+255] = tau log2 e q^C_i W^UK_i[:, 256e ..], with
-//      the W^UK tile copied to LDS (global_load_lds) while phase 1 streams.
+//      of half e (16 pairs).  The content sums, rounded to bf16, stay in LDS
+//      as the q^C_i tile; the RoPE pairs are rotated at the row's position,
+//      scaled by tau log2 e and written to the tail of qt.
+//   2. qt_i[:, 256e .. 256e+255] = tau log2 e q^C_i W^UK_i[:, 256e ..].
 // Both halves of a head read the same content rows of W^UQ; the two blocks
 // are placed on one XCD, so the second read is served by that XCD's L2.
-// Per block: 491 KiB of W^UQ (393 KiB shared with the partner), 64 KiB of
-// W^UK and c^Q (64 x 1536 bf16) from L2.  One launch instead of a W^UQ GEMM
-// plus an absorption kernel, and q^C never leaves the CU.
 //
-// W^UK_i[128 k][512 n] in LDS as 64-column tiles [128 k][64 n]: row k chunk
-// q (8 n) at k*8 + (q ^ swz(k)) -- the layout whose transposing reads are
-// bank-conflict free.
+// Weights reach LDS through global_load_lds in units of 24 KiB (16 weight
+// rows x half of d_cq), every wave-instruction reading whole 512-byte runs
+// of two rows: a CU keeps more bytes in flight this way than with loads of
+// 16 rows x 64 bytes straight into MFMA operands.  A ring of five unit
+// slots holds four units in flight while one is multiplied.  The 23 units
+// are the 20 of W^UQ (column block nb = u/2, K half u%2) and then W^UK_i's
+// half-e tile (64 KiB), which so lands in slots 0-2, i.e. in one piece at the
+// ring's start.  Wave w = 2 rb + kq multiplies rows 16 rb .. +15 of c^Q (held
+// in registers) with k-quarter kq of each unit; the two k-quarters of a row
+// block meet through a 1 KiB slab.
+//
+// W^UQ unit layout: wave-instruction j (0..23) covers rows 2(j/3), 2(j/3)+1
+// and 16-byte chunks 32(j%3) .. +31 of the unit's 96; chunk c of row r sits
+// at slot c ^ (r & 15) of its run (conflict-free MFMA operand reads).
+// W^UK tile: 64-column tiles [128 k][64 n], row k chunk q (8 n) at
+// k*8 + (q ^ swz(k)), the layout whose transposing reads are conflict free.
 __device__ __forceinline__ int ab_pos(int k, int q) { return k * 8 + (q ^ (4 * ((k >> 1) & 1)) ^ (2 * ((k >> 3) & 1))); }
 
 constexpr int AB_DH = 128;                     // d_head (k of the absorption)
 constexpr int AB_NCOL = 256;                   // absorbed columns per block (half of d_c)
 constexpr int AB_TILE = AB_DH * 64 * 2;        // one 64-column W^UK tile, bytes
-constexpr int UA_WAVES = 8, UA_KS = 6;         // K = 8 waves x 6 k-steps x 32 = d_cq
-constexpr int UA_DCQ = UA_WAVES * UA_KS * 32;  // 1536
+constexpr int UA_WAVES = 8;
+constexpr int UA_DCQ = 1536;                   // d_cq
 constexpr int UA_NOPE_NB = AB_DH / 16;         // content column blocks (8)
 constexpr int UA_NB = UA_NOPE_NB + 2;          // + two RoPE column blocks (32 columns)
-constexpr int UA_DEPTH = 4;                    // column blocks of W^UQ loads in flight
-constexpr int UA_LDN = 2 * 16 + 4;             // slab row, floats (two column blocks per round)
-constexpr int UA_SLAB = 64 * UA_LDN;           // floats per wave
+constexpr int UA_UNIT = 16 * UA_DCQ;           // bytes of a unit: 16 rows x half of d_cq
+constexpr int UA_QUNITS = 2 * UA_NB;           // W^UQ units
+constexpr int UA_UNITS = UA_QUNITS + 3;        // + the W^UK tile (24 + 24 + 16 KiB)
+constexpr int UA_SLOTS = 5;
+constexpr int UA_KS = UA_DCQ / 2 / 2 / 32;     // k-steps of a wave per unit (12)
 constexpr int UA_QC_LD = AB_DH + 8;            // q^C tile row, bf16 (rows 16 bytes apart in the banks)
-constexpr int UA_QC_OFF = UA_WAVES * UA_SLAB * 4;
-constexpr int UA_W_OFF = UA_QC_OFF + 64 * UA_QC_LD * 2;
-constexpr int UA_LDS = UA_W_OFF + 4 * AB_TILE;
+constexpr int UA_QC_OFF = UA_SLOTS * UA_UNIT;
+constexpr int UA_SLAB_OFF = UA_QC_OFF + 64 * UA_QC_LD * 2;
+constexpr int UA_LDS = UA_SLAB_OFF + 2 * 4 * 1024;
+constexpr int UA_STAGE_OFF = 3 * UA_UNIT;      // output staging: slots 3-4, free once W^UQ is done
 static_assert(UA_LDS <= 160 * 1024, "LDS");
-static_assert(UA_W_OFF % 1024 == 0, "W^UK tile alignment");
-static_assert(64 * AB_NCOL * 2 <= UA_QC_OFF, "output staging fits in the slabs");
+static_assert(4 * AB_TILE <= UA_STAGE_OFF && 3 * UA_UNIT == 72 * 1024, "W^UK tile in slots 0-2");
+static_assert(UA_STAGE_OFF + 64 * AB_NCOL * 2 <= UA_QC_OFF, "output staging in slots 3-4");
+static_assert((UA_QUNITS + 0) % UA_SLOTS == 0, "the W^UK units start at slot 0");
 
 typedef __attribute__((address_space(3))) uint8_t lu8;
+typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
 
 // One 1 KiB wave-instruction of a global -> LDS copy (16 bytes a lane at
 // gbase + voff, to LDS lds_addr + 16 lane).  Issued from asm: the compiler
 // cannot tell where such a copy lands, so for the builtin it waits for every
 // outstanding load before any later LDS access, which would drain the weight
-// stream at each reduction round.  The caller waits (vmcnt) before reading
-// the copy.  Nothing else in k_uq_absorb uses M0.
+// stream at each step.  The caller waits (vmcnt) before reading the copy.
+// Nothing else in k_uq_absorb uses M0.
 __device__ __forceinline__ void ua_dma(const void* gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_addr)
                : "memory");
@@ -246,153 +266,195 @@ struct UaArgs {
   double freq[MAX_ROPE_PAIRS];  // theta^(-2p/d_rope) of RoPE pair p
 };
 
+struct UaCtx {
+  const bf16_t *wq, *wk;  // W^UQ_i, W^UK_i half e
+  uint32_t ring;          // LDS address of the ring
+  int wave, lane, e;
+};
+
+// Unit u into its ring slot: this wave's 3 (the last W^UK unit: 2) of the
+// unit's wave-instructions.
+__device__ __forceinline__ void ua_issue(const UaCtx& c, int u) {
+  if (u >= UA_UNITS) return;
+  if (u < UA_QUNITS) {
+    const int nb = u >> 1, kh = u & 1;
+    const int row0 = nb < UA_NOPE_NB ? 16 * nb : AB_DH + 32 * c.e + 16 * (nb - UA_NOPE_NB);
+    const uint32_t dst = c.ring + (u % UA_SLOTS) * UA_UNIT;
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      const int j = c.wave + 8 * jj;
+      const int r = 2 * (j / 3) + (c.lane >> 5), s = 32 * (j % 3) + (c.lane & 31);
+      const int ch = s ^ (r & 15);
+      ua_dma(c.wq, (uint32_t)(((row0 + r) * UA_DCQ + kh * (UA_DCQ / 2) + 8 * ch) * 2), dst + 1024 * j);
+    }
+  } else {
+    // W^UK instruction ii (0..63): tile t = ii/16, k-rows 8(ii%16) .. +7
+    const int n = u == UA_UNITS - 1 ? 2 : 3;
+    for (int jj = 0; jj < n; ++jj) {
+      const int ii = 24 * (u - UA_QUNITS) + c.wave + 8 * jj;
+      const int t = ii >> 4, i = ii & 15;
+      const int pos = 64 * i + c.lane, k = pos >> 3, phys = pos & 7;
+      const int q = phys ^ (4 * ((k >> 1) & 1)) ^ (2 * ((k >> 3) & 1));
+      ua_dma(c.wk, (uint32_t)((k * 2 * AB_NCOL + 64 * t + 8 * q) * 2), c.ring + 1024 * ii);
+    }
+  }
+}
+
 __global__ __launch_bounds__(UA_WAVES * 64) void k_uq_absorb(UaArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-  float* slab = (float*)lds;
-  bf16_t* qct = (bf16_t*)(lds + UA_QC_OFF);
-  uint8_t* wt = lds + UA_W_OFF;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  lu8* lds = (lu8*)lds_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 4, i16 = lane & 15;
+  const int rb = wave >> 1, kq = wave & 1;
   // Blocks are dealt to the 8 XCDs round-robin: XCD x runs blocks x, x + 8,
   // ...; its consecutive pairs of those are the two halves of one head.
-  const int xcd = blockIdx.x & 7, u = blockIdx.x >> 3;
-  const int head = xcd * (gridDim.x >> 4) + (u >> 1), e = u & 1;
-  const int wd = AB_DH + a.d_rope;
+  const int xcd = blockIdx.x & 7, ub = blockIdx.x >> 3;
+  const int head = xcd * (gridDim.x >> 4) + (ub >> 1), e = ub & 1;
 
-  // Issue order: the W^UK copy, then the c^Q rows, then the first UA_DEPTH
-  // column blocks of W^UQ.  Loads complete in issue order, so the wait for
-  // any weight block also covers everything issued before it.
+  // The row's position and its lane's four RoPE frequencies (pairs of
+  // columns 32e + 16j + 4g, +2 for j = 0, 1), for the RoPE epilogue; then
+  // the first four units, then the c^Q rows 16 rb + i16 (clamped: rows past
+  // M are computed, never stored), k = 768 kh + 384 kq + 32 ks + 8 g .. +7.
+  const int m = 16 * rb + i16;
+  const int sl = m < a.M ? a.seqlens[m / a.s_q] : 0;
+  double fr[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fr[j][h] = a.freq[16 * e + 8 * j + 2 * g + h];
+  UaCtx c;
+  c.wq = a.Wuq + (long)head * (AB_DH + a.d_rope) * UA_DCQ;
+  c.wk = a.Wuk + (long)head * AB_DH * a.d_c + AB_NCOL * e;
+  c.ring = (uint32_t)(uintptr_t)lds;
+  c.wave = wave;
+  c.lane = lane;
+  c.e = e;
+  for (int u = 0; u < UA_SLOTS - 1; ++u) ua_issue(c, u);
+
+  bf16x8 xf[2][UA_KS];
   {
-    const bf16_t* Wk = a.Wuk + (long)head * AB_DH * a.d_c + AB_NCOL * e;
-    const uint32_t wt_addr = (uint32_t)(uintptr_t)(lu8*)wt;
+    const bf16_t* x = a.X + (long)min(m, a.M - 1) * UA_DCQ + 384 * kq + 8 * g;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {  // 64 KiB as 64 wave-instructions of 1 KiB (8 k-rows x 128 B of a tile)
-      const int ii = wave + 8 * n;
-      const int t = ii >> 4, i = ii & 15;
-      const int pos = 64 * i + lane, k = pos >> 3, phys = pos & 7;
-      const int q = phys ^ (4 * ((k >> 1) & 1)) ^ (2 * ((k >> 3) & 1));
-      ua_dma(Wk, (uint32_t)((k * a.d_c + 64 * t + 8 * q) * 2), wt_addr + t * AB_TILE + i * 1024);
-    }
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int ks = 0; ks < UA_KS; ++ks) xf[kh][ks] = *(const bf16x8*)(x + 768 * kh + 32 * ks);
   }
-  bf16x8 xf[4][UA_KS];
-  XPlain{a.X, UA_DCQ, 0}.load<UA_KS>(0, wave * UA_KS * 32 + 8 * g, i16, g, wave, a.M, xf);
-  __builtin_amdgcn_sched_barrier(0);
-  // W^UQ rows of column block nb (lane row i16) from this wave's K-slice
-  const bf16_t* Wq = a.Wuq + (long)head * wd * UA_DCQ + wave * UA_KS * 32 + 8 * g;
-  auto wrow = [&](int nb) -> const bf16_t* {
-    const int r = nb < UA_NOPE_NB ? 16 * nb : AB_DH + 32 * e + 16 * (nb - UA_NOPE_NB);
-    return Wq + (long)(r + i16) * UA_DCQ;
-  };
-  bf16x8 wf[UA_DEPTH][UA_KS];
-#pragma unroll
-  for (int d = 0; d < UA_DEPTH; ++d)
-#pragma unroll
-    for (int ks = 0; ks < UA_KS; ++ks) wf[d][ks] = *(const bf16x8*)(wrow(d) + 32 * ks);
+  __builtin_amdgcn_sched_barrier(0);  // every load of the prologue is out before anything waits
+  wait_vmcnt0();  // all of the above (and units 0-3) have landed: no later wait of the compiler's drains the ring
 
-  float* mine = slab + wave * UA_SLAB;
+  // LDS offsets of this lane's A fragments (row i16, chunk 48 kq + 4 ks + g)
+  uint32_t aoff[UA_KS];
 #pragma unroll
-  for (int nb = 0; nb < UA_NB; ++nb) {
-    // the MFMAs of block nb, then the loads of block nb + UA_DEPTH, kept in
-    // this order so that UA_DEPTH - 1 blocks stay in flight meanwhile
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[4];
+  for (int ks = 0; ks < UA_KS; ++ks) {
+    const int ch = 48 * kq + 4 * ks + g, s = ch ^ i16;
+    aoff[ks] = (uint32_t)(1024 * (3 * (i16 >> 1) + (s >> 5)) + 512 * (i16 & 1) + 16 * (s & 31));
+  }
+  int ps = m < a.M ? sl - a.s_q + m % a.s_q : 0;
+  ps = ps < 0 ? 0 : ps;
+  lu8* slab = lds + UA_SLAB_OFF;
+  lu8* qct = lds + UA_QC_OFF;  // q^C tile [64 m][UA_QC_LD] bf16
+
+  // Column block nb's epilogue (waves kq = 0): the pair's sum, then the q^C
+  // tile (content) or the rotated RoPE pairs (qt tail).  Lane holds columns
+  // 16 nb + 4g + r (r = 0..3) of row m.
+  auto epilogue = [&](int nb, const f32x4& acc) {
+    const f32x4 v = acc + *(const __attribute__((address_space(3))) f32x4*)(slab + ((nb & 1) * 4 + rb) * 1024 + 16 * lane);
+    if (nb < UA_NOPE_NB) {
+      bf16x4 o;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{};
+      for (int r = 0; r < 4; ++r) o[r] = (bf16_t)v[r];
+      *(__attribute__((address_space(3))) bf16x4*)(qct + (m * UA_QC_LD + 16 * nb + 4 * g) * 2) = o;
+    } else if (m < a.M) {
+      const int j = nb - UA_NOPE_NB;
+      bf16x4 o;
 #pragma unroll
-    for (int ks = 0; ks < UA_KS; ++ks) {
-      const bf16x8 w = wf[nb % UA_DEPTH][ks];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xf[mb][ks], acc[mb], 0, 0, 0);
-    }
-    if (nb + UA_DEPTH < UA_NB) {
-#pragma unroll
-      for (int ks = 0; ks < UA_KS; ++ks) wf[nb % UA_DEPTH][ks] = *(const bf16x8*)(wrow(nb + UA_DEPTH) + 32 * ks);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // C = u^T: lane holds column 16 nb + 4g + r (r = 0..3) of row m = 16 mb + i16
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) *(f32x4*)(mine + (16 * mb + i16) * UA_LDN + 16 * (nb & 1) + 4 * g) = acc[mb];
-    if (nb & 1) {
-      ring_barrier();  // every wave's slab holds column blocks nb-1, nb
-      const int cb = nb - 1;
-      for (int p = threadIdx.x; p < 16 * 64; p += UA_WAVES * 64) {
-        const int m = p >> 4, c = 2 * (p & 15);
-        float2 v = *(const float2*)(slab + m * UA_LDN + c);
-#pragma unroll
-        for (int w = 1; w < UA_WAVES; ++w) {
-          const float2 t = *(const float2*)(slab + w * UA_SLAB + m * UA_LDN + c);
-          v.x += t.x;
-          v.y += t.y;
-        }
-        if (cb < UA_NOPE_NB) {
-          *(bf16x2*)(qct + m * UA_QC_LD + 16 * cb + c) = bf16x2{(bf16_t)v.x, (bf16_t)v.y};
-        } else if (m < a.M) {
-          const int d = 32 * e + 16 * (cb - UA_NOPE_NB) + c;  // RoPE column (pair d/2)
-          const int b = m / a.s_q, j = m % a.s_q;
-          int ps = a.seqlens[b] - a.s_q + j;
-          ps = ps < 0 ? 0 : ps;
-          float cs, sn;
-          rope_cs_w(ps, a.freq[d >> 1], &cs, &sn);
-          *(bf16x2*)(a.qt + ((long)m * a.H + head) * (a.d_c + a.d_rope) + a.d_c + d) =
-              bf16x2{(bf16_t)(a.scale2 * (v.x * cs - v.y * sn)), (bf16_t)(a.scale2 * (v.x * sn + v.y * cs))};
-        }
+      for (int h = 0; h < 2; ++h) {
+        float cs, sn;
+        rope_cs_w(ps, fr[j][h], &cs, &sn);
+        o[2 * h] = (bf16_t)(a.scale2 * (v[2 * h] * cs - v[2 * h + 1] * sn));
+        o[2 * h + 1] = (bf16_t)(a.scale2 * (v[2 * h] * sn + v[2 * h + 1] * cs));
       }
-      ring_barrier();  // the slabs are free again; the q^C columns are in LDS
+      *(bf16x4*)(a.qt + ((long)m * a.H + head) * (a.d_c + a.d_rope) + a.d_c + 32 * e + 16 * j + 4 * g) = o;
+    }
+  };
+
+  f32x4 acc = f32x4{};
+#pragma unroll 1
+  for (int nb = 0; nb < UA_NB; ++nb) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int u = 2 * nb + kh;
+      // this wave's copies of unit u have landed (younger: units u+1 .. u+3,
+      // three instructions each but for the last W^UK unit's two)
+      if (u == UA_QUNITS - 1) wait_vmcnt<8>(); else wait_vmcnt<9>();
+      ring_barrier();  // everyone's copies of unit u are in; everyone is done with unit u-1 and the slab
+      ua_issue(c, u + UA_SLOTS - 1);  // into unit u-1's slot
+      if (kh == 0) {
+        if (nb > 0 && kq == 0) epilogue(nb - 1, acc);
+        acc = f32x4{};
+      }
+      const lu8* sb = lds + (u % UA_SLOTS) * UA_UNIT;
+#pragma unroll
+      for (int ks = 0; ks < UA_KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const lbf16x8*)(sb + aoff[ks]), xf[kh][ks], acc, 0, 0, 0);
+      if (kh == 1 && kq == 1) *(__attribute__((address_space(3))) f32x4*)(slab + ((nb & 1) * 4 + rb) * 1024 + 16 * lane) = acc;
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the W^UK copy (issued first) has landed
-  __syncthreads();
+  wait_vmcnt0();  // the W^UK units
+  ring_barrier();
+  if (kq == 0) epilogue(UA_NB - 1, acc);
+  ring_barrier();  // the q^C tile is complete
 
   // 2. absorption, K = d_head: wave w computes columns 32w .. 32w+31 of the
   // block's 256 for all 64 rows.  A = q^C rows from the tile; B[k][n] from two
   // transposing reads of 4 k-rows each.
+  bf16x8 qf[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      xf[mb][ks] = *(const __attribute__((address_space(3))) bf16x8*)((const __attribute__((address_space(3))) uint8_t*)qct +
-                                                                      ((16 * mb + i16) * UA_QC_LD + 32 * ks + 8 * g) * 2);
-  f32x4 acc[4][2];
+      qf[mb][ks] = *(const lbf16x8*)(qct + ((16 * mb + i16) * UA_QC_LD + 32 * ks + 8 * g) * 2);
+  f32x4 ab[4][2];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb][0] = acc[mb][1] = f32x4{};
+  for (int mb = 0; mb < 4; ++mb) ab[mb][0] = ab[mb][1] = f32x4{};
   const int e4 = i16 >> 2, qq = i16 & 3;
 #pragma unroll
   for (int nbi = 0; nbi < 2; ++nbi) {
     const int nloc = 32 * wave + 16 * nbi;
     const int t = nloc >> 6, nq = (nloc & 63) + 4 * qq;
-    const int c = nq >> 3, half = (nq >> 2) & 1;
-    const uint8_t* tb = wt + t * AB_TILE + half * 8;
+    const int cc = nq >> 3, half = (nq >> 2) & 1;
+    const lu8* tb = lds + t * AB_TILE + half * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int k1 = 32 * ks + 8 * g + e4, k2 = k1 + 4;
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(tb + ab_pos(k1, c) * 16));
-      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(tb + ab_pos(k2, c) * 16));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(tb + ab_pos(k1, cc) * 16));
+      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(tb + ab_pos(k2, cc) * 16));
       const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
       const bf16x8 bw = __builtin_bit_cast(bf16x8, s8);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb][nbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[mb][ks], bw, acc[mb][nbi], 0, 0, 0);
+      for (int mb = 0; mb < 4; ++mb) ab[mb][nbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mb][ks], bw, ab[mb][nbi], 0, 0, 0);
     }
   }
-  // Output rows staged in the (free) slab area as [64 m][256 n] bf16, 16-byte
-  // chunk j of row m at j ^ (m & 31); C lane layout: rows m = 16 mb + 4 g + r,
-  // column n = 32 w + 16 nbi + i16.
-  bf16_t* st = (bf16_t*)lds;
+  // Output rows staged (slots 3-4) as [64 m][256 n] bf16, 16-byte chunk j of
+  // row m at j ^ (m & 31); C lane layout: rows m = 16 mb + 4 g + r, column
+  // n = 32 w + 16 nbi + i16.
+  __attribute__((address_space(3))) bf16_t* st = (__attribute__((address_space(3))) bf16_t*)(lds + UA_STAGE_OFF);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nbi = 0; nbi < 2; ++nbi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = 16 * mb + 4 * g + r, n = 32 * wave + 16 * nbi + i16;
-        st[m * AB_NCOL + 8 * ((n >> 3) ^ (m & 31)) + (n & 7)] = (bf16_t)(a.scale2 * acc[mb][nbi][r]);
+        const int mm = 16 * mb + 4 * g + r, n = 32 * wave + 16 * nbi + i16;
+        st[mm * AB_NCOL + 8 * ((n >> 3) ^ (mm & 31)) + (n & 7)] = (bf16_t)(a.scale2 * ab[mb][nbi][r]);
       }
   __syncthreads();
   for (int p = threadIdx.x; p < 64 * 32; p += UA_WAVES * 64) {
-    const int m = p >> 5, j = p & 31;
-    if (m < a.M)
-      *(bf16x8*)(a.qt + ((long)m * a.H + head) * (a.d_c + a.d_rope) + AB_NCOL * e + 8 * j) =
-          *(const bf16x8*)(st + m * AB_NCOL + 8 * (j ^ (m & 31)));
+    const int mm = p >> 5, j = p & 31;
+    if (mm < a.M)
+      *(bf16x8*)(a.qt + ((long)mm * a.H + head) * (a.d_c + a.d_rope) + AB_NCOL * e + 8 * j) =
+          *(const __attribute__((address_space(3))) bf16x8*)(st + mm * AB_NCOL + 8 * (j ^ (mm & 31)));
   }
 }
 
