@@ -111,6 +111,14 @@ __device__ __forceinline__ void dma_1k(const uint8_t* sbase, uint32_t voff, uint
                : "memory");
 }
 
+// The same with M0 = lds_base + OFS (one scalar add instead of an address
+// computation and a move per copy).
+template <int OFS>
+__device__ __forceinline__ void dma_1k_at(const uint8_t* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base), "i"(OFS)
+               : "memory", "scc");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -127,6 +135,7 @@ struct Ctx {
   uint32_t lds_addr;
   int wave, lane;
   uint32_t dma_ofs;           // lane part of a stage copy
+  uint32_t dma_ofs_w;         // bf16: the same plus this wave's first copy (4096 * wave)
   uint32_t koff;              // K fragment of the scores MFMA
   uint32_t qr_ofs0, qr_ofs1;  // RoPE query fragments (k-steps 16, 17)
   uint32_t vofs1, vofs2;      // V^T transposing reads (wave's first channel block)
@@ -187,7 +196,7 @@ template <bool F8>
 __device__ __forceinline__ StageCopy plan_stage(const Ctx& c, int i, int slot) {
   StageCopy s;
   s.src = nullptr;
-  s.dst = stage_dst<F8>(c, slot);
+  s.dst = stage_dst<F8>(c, slot) + (F8 ? 0 : 1024 * c.wave);  // bf16: this wave's first copy
   if (i < c.nst) {
     const int t0 = c.t_begin + i * T;
     s.src = stage_page(c, t0) + ((t0 / T) & 3) * (T * 16);
@@ -195,10 +204,22 @@ __device__ __forceinline__ StageCopy plan_stage(const Ctx& c, int i, int slot) {
   return s;
 }
 // Instruction n (0..4) of this wave's share of a stage copy.
-template <bool F8>
-__device__ __forceinline__ void copy_part(const Ctx& c, const StageCopy& s, int n) {
-  const int ii = c.wave + NW * n;
-  if (s.src != nullptr && ii < Lay<F8>::COPIES) copy_1k<F8>(c, s.src, s.dst, ii);
+// bf16: copy ii = wave + 4n reads src + 4096 ii into dst + 1024 ii; the
+// wave's part sits in dma_ofs_w and s.dst, n's part in the offsets below.
+template <int N>
+__device__ __forceinline__ void copy_part(const Ctx& c, const StageCopy& s) {
+  static_assert(Lay<false>::COPIES == 18, "five copies on waves 0-1, four on waves 2-3");
+  if (s.src != nullptr && (N < 4 || c.wave < 2)) dma_1k_at<4096 * N>(s.src, c.dma_ofs_w + 16384 * N, s.dst);
+}
+// n is a constant once the k-step loop is unrolled
+__device__ __forceinline__ void copy_at(const Ctx& c, const StageCopy& s, int n) {
+  switch (n) {
+    case 0: copy_part<0>(c, s); break;
+    case 1: copy_part<1>(c, s); break;
+    case 2: copy_part<2>(c, s); break;
+    case 3: copy_part<3>(c, s); break;
+    default: copy_part<4>(c, s); break;
+  }
 }
 
 // Before step m: stages 2m and 2m+1 have landed once at most the copies of
@@ -289,8 +310,8 @@ __device__ __forceinline__ void step_scores(const Ctx& c, const lu8* stA, const 
     // the next two stages' copies go out between these MFMAs, early in the
     // step: the first at k-steps 1..5, the second at 6..10
     if constexpr (!F8) {  // (the fp8 copies go out in the widening phase)
-      if (ks >= 1 && ks <= 5) copy_part<F8>(c, cx, ks - 1);
-      if (ks >= 6 && ks <= 10) copy_part<F8>(c, cy, ks - 6);
+      if (ks >= 1 && ks <= 5) copy_at(c, cx, ks - 1);
+      if (ks >= 6 && ks <= 10) copy_at(c, cy, ks - 6);
     }
   }
 }
@@ -308,21 +329,38 @@ __device__ __forceinline__ void mask(const Ctx& c, f32x4& s, int nvalid) {
 
 constexpr float HEADROOM = 96.0f;
 
+// Maxima as single instructions: fmaxf on values the compiler cannot prove
+// quiet (the scores come from inline asm) costs two extra canonicalising
+// instructions per call.  Scores are finite or -inf.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Maximum over the lanes l, l^16 (permlane16 swap leaves the two values of
 // each pair in the two results) and over l, l^32.
 __device__ __forceinline__ float max_x16(float m) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_x32(float m) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // P.V MFMAs of stages 2m-2, 2m-1 interleaved with the softmax of this
 // step's (masked) scores: the VALU instructions issue while each MFMA
-// occupies the matrix unit.  The 32 slots are generated at compile time and
-// sched_barrier pins their order.  Weights go to P buffer m&1 as bf16; lane
+// occupies the matrix unit.  A wave issues about one instruction per four
+// cycles and a 32x32x16 MFMA keeps the unit busy for 32, so the softmax is
+// cut into 12 items of a few instructions, spread over the 32 slots
+// (generated at compile time; sched_barrier pins their order); head blocks
+// 0 and 1 alternate, which also spaces each item from the one it needs.  Weights go to P buffer m&1 as bf16; lane
 // heads 32w + 16hb + lane%16 (hb = 0, 1).
 struct PvwState {
   const Ctx& c;
@@ -337,7 +375,7 @@ struct PvwState {
   bool& ovf;
   lu8* pw;
   float ml[2];
-  f32x4 xa[2];
+  f32x4 xa[2], xb[2];
 };
 
 template <int K>
@@ -346,30 +384,32 @@ __device__ __forceinline__ void pvw_slot(PvwState& st) {
     constexpr int j = K >> 4, hb = (K >> 2) & 3, i = K & 3;
     st.o[i][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.v[j][i], st.p[j][hb], st.o[i][hb], 0, 0, 0);
   }
-  if constexpr (K < 10) {
-    constexpr int h = K / 5, part = K % 5;
+  // item i (0..11) sits in slot 8i/3: part i/2 of head block i%2
+  constexpr int item = (3 * K + 7) / 8;
+  if constexpr (item < 12 && (8 * item) / 3 == K) {
+    constexpr int h = item & 1, part = item >> 1;
     const f32x4 sA = st.sc[0][h], sB = st.sc[1][h];
     if constexpr (part == 0) {
-      st.ml[h] = fmaxf(fmaxf(fmaxf(sA[0], sA[1]), fmaxf(sA[2], sA[3])), fmaxf(fmaxf(sB[0], sB[1]), fmaxf(sB[2], sB[3])));
+      st.ml[h] = vmax(vmax3(sA[0], sA[1], sA[2]), vmax3(sA[3], sB[0], vmax3(sB[1], sB[2], sB[3])));
     } else if constexpr (part == 1) {
       st.ml[h] = max_x16(st.ml[h]);
     } else if constexpr (part == 2) {
       st.ml[h] = max_x32(st.ml[h]);
-      st.m_all[h] = fmaxf(st.m_all[h], st.ml[h]);
+      st.m_all[h] = vmax(st.m_all[h], st.ml[h]);
       // the reference: the first step's maximum, or the exact maximum
       // already in m_ref when the pass is redone (it is never smaller)
-      if (st.m == 0) st.m_ref[h] = fmaxf(st.m_ref[h], st.ml[h]);
+      if (st.m == 0) st.m_ref[h] = vmax(st.m_ref[h], st.ml[h]);
       st.ovf |= st.ml[h] > st.m_ref[h] + HEADROOM;
     } else if constexpr (part == 3) {
       // raw v_exp_f32: results below 2^-126 flush to zero, harmless here; a
       // score above the headroom only occurs in a pass that is redone
 #pragma unroll
       for (int r = 0; r < 4; ++r) st.xa[h][r] = __builtin_amdgcn_exp2f(sA[r] - st.m_ref[h]);
-    } else {
-      f32x4 xb;
+    } else if constexpr (part == 4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xb[r] = __builtin_amdgcn_exp2f(sB[r] - st.m_ref[h]);
-      const f32x4 xa = st.xa[h];
+      for (int r = 0; r < 4; ++r) st.xb[h][r] = __builtin_amdgcn_exp2f(sB[r] - st.m_ref[h]);
+    } else {
+      const f32x4 xa = st.xa[h], xb = st.xb[h];
       st.l_run[h] += (xa[0] + xa[1]) + (xa[2] + xa[3]) + (xb[0] + xb[1]) + (xb[2] + xb[3]);
       bf16x4 pa, pb;
 #pragma unroll
@@ -409,7 +449,7 @@ __device__ __forceinline__ void pv_weights_step(const Ctx& c, int m, const f32x4
   }
   __builtin_amdgcn_sched_barrier(0);
   PvwState st{c, m, sc, v, p, o, m_ref, m_all, l_run, ovf, c.lds + Lay<F8>::P_OFF + (m & 1) * P_BYTES + c.pw_ofs,
-              {0.0f, 0.0f}, {}};
+              {0.0f, 0.0f}, {}, {}};
   pvw_slots(st, std::make_integer_sequence<int, 32>{});
 }
 
@@ -663,6 +703,7 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   c.wave = wave;
   c.lane = lane;
   c.dma_ofs = (uint32_t)(g * 1024 + i16 * 16);
+  c.dma_ofs_w = c.dma_ofs + 4096u * (uint32_t)wave;
   // the first three stages go out before anything waits
   issue_stage<F8>(c, 0, 0);
   issue_stage<F8>(c, 1, 1);

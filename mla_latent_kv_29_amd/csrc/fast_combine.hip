@@ -1,0 +1,267 @@
+// Combine for at most 64 query rows (gfx950): the merge of the attention's
+// per-split partials and the W^UV projection in one kernel.
+//
+// What it computes (DeepSeek-V3 reading lesson, §2.1.1 Question 2, and the
+// split-KV merge of its decode discussion): for query row r and head i,
+//     O_lat = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),  M = max_s lse_s
+// over the splits s that saw at least one token (lse_s = -inf marks an empty
+// split, whose rows are never read), rounded to bf16, and then
+//     out[r][i] = W^UV_i O_lat        (W^UV_i: [d_head][d_c], d_c contiguous)
+// plus the row's natural-log LSE when asked for.
+//
+// One block per (head i, block of 32 rows), eight waves.  W^UV_i (128 KiB)
+// streams HBM -> LDS with global_load_lds while the waves merge their rows
+// (wave w: rows w, w+8, w+16, w+24; lane l: channels 8l .. 8l+7, so each
+// partial-row load is one contiguous 1 KiB wave access, and the rows of up
+// to eight splits of all four rows are in flight together).  The merged rows
+// land in LDS as bf16, and the 32 x 128 output tile is one MFMA pass over
+// d_c.  The two row blocks of a head run on one XCD, so W^UV_i comes from HBM
+// once.  O_lat never leaves the CU, and the merge and the projection are one
+// launch instead of two.
+//
+// LDS: O_lat tile [32 rows][512] then W^UV_i [128 n][512 k], bf16 rows of
+// 1 KiB whose 16-byte chunk q sits at slot q ^ (row & 15): the MFMA operand
+// reads (16 rows, one chunk each) hit 16 distinct bank groups.
+#include "internal.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int CB_DC = 512, CB_DV = 128, CB_ROWS = 32, CB_WAVES = 8;
+constexpr int CB_W_OFF = CB_ROWS * CB_DC * 2;          // 32 KiB
+constexpr int CB_LDS = CB_W_OFF + CB_DV * CB_DC * 2;   // 160 KiB
+static_assert(CB_LDS <= 160 * 1024, "LDS");
+
+typedef __attribute__((address_space(3))) uint8_t lu8;
+typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
+
+// One 1 KiB wave-instruction of a global -> LDS copy (16 bytes a lane at
+// gbase + voff to LDS lds_addr + 16 lane), from asm so that the compiler's
+// wait accounting leaves it alone; the kernel waits for it explicitly.
+// Nothing else in k_merge_uv uses M0.
+__device__ __forceinline__ void cb_dma(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+struct CbArgs {
+  int batch, s_q, H, R;
+  const uint8_t* ws;
+  size_t lpart_off;
+  const bf16_t* Wuv;  // [H][d_head][d_c]
+  bf16_t* out;        // [R][H][d_head]
+  float* lse_out;     // [R][H] or null
+};
+
+__global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  lu8* lds = (lu8*)lds_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i16 = lane & 15;
+  // blocks are dealt to the 8 XCDs round-robin; the row blocks of a head are
+  // consecutive blocks of one XCD
+  const int nrb = (a.R + CB_ROWS - 1) / CB_ROWS;
+  const int lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);  // each XCD: a contiguous run
+  const int head = lin / nrb, rb = lin % nrb;
+
+  // W^UV_i rows to LDS first: the split weights below are one latency-bound
+  // round trip (header, then the lse values), which the copy overlaps (the
+  // compiler's wait for those loads covers the copy too, as loads complete
+  // in order).  Row n = instruction n (16 per wave), chunk q of the row at
+  // slot q ^ (n & 15), i.e. lane l reads chunk l ^ (n & 15).
+  {
+    const bf16_t* W = a.Wuv + (size_t)head * CB_DV * CB_DC;
+    const uint32_t wt = (uint32_t)(uintptr_t)(lds + CB_W_OFF);
+#pragma unroll
+    for (int jj = 0; jj < CB_DV / CB_WAVES; ++jj) {
+      const int n = wave + CB_WAVES * jj;
+      cb_dma(W, (uint32_t)((n * CB_DC + 8 * (lane ^ (n & 15))) * 2), wt + 1024 * n);
+    }
+  }
+
+  // 1. merge: wave w, rows w + 8i of the block; lane l, channels 8l .. +7
+  const int32_t* hdr = (const int32_t*)a.ws;
+  const int S = hdr[HDR_S];
+  const bool pbf16 = hdr[HDR_PDT] == MLA_BF16;
+  const float* lpart = (const float*)(a.ws + a.lpart_off);
+  const uint8_t* opart = a.ws + opart_offset(a.lpart_off, a.batch, S, a.s_q, a.H);
+  const size_t pstep = (size_t)a.s_q * a.H;  // partial row stride between splits
+  size_t p0[4];
+  float M[4], invW[4], wt0[4];
+  bool live[4];
+  // lse of split `lane` for the four rows at once (one round trip), then the
+  // maxima and sums (splits 64.. only when there are more than 64)
+  float lt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = CB_ROWS * rb + wave + CB_WAVES * i;
+    live[i] = row < a.R;
+    const int b = live[i] ? row / a.s_q : 0, j = live[i] ? row % a.s_q : 0;
+    p0[i] = (((size_t)b * S) * a.s_q + j) * a.H + head;
+    lt[i] = live[i] && lane < S ? lpart[p0[i] + (size_t)lane * pstep] : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = lt[i];
+    if (live[i])
+      for (int s = 64 + lane; s < S; s += 64) m = fmaxf(m, lpart[p0[i] + s * pstep]);
+    M[i] = wmax(m);
+    // lane t's weight of split t (0 for empty splits, whose rows are never read)
+    wt0[i] = lt[i] == -INFINITY ? 0.0f : exp2f(lt[i] - M[i]);
+    float w = wt0[i];
+    if (live[i])
+      for (int s = 64 + lane; s < S; s += 64) {
+        const float l = lpart[p0[i] + s * pstep];
+        w += l == -INFINITY ? 0.0f : exp2f(l - M[i]);
+      }
+    const float W = wsum(w);
+    invW[i] = W > 0.0f ? 1.0f / W : 0.0f;
+    if (a.lse_out && live[i] && lane == 0) {
+      const int row = CB_ROWS * rb + wave + CB_WAVES * i;
+      a.lse_out[(size_t)row * a.H + head] = W > 0.0f ? (M[i] + log2f(W)) * 0.6931471805599453f : -INFINITY;
+    }
+  }
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+  if (pbf16) {
+    // Splits four at a time, the loads of all four rows together; lane t of
+    // a 64-split group holds split t's weight.
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int n = min(64, S - s0);
+      float wt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (s0 == 0) {
+          wt[i] = wt0[i];
+        } else {  // more than 64 splits
+          const float l = live[i] && lane < n ? lpart[p0[i] + (size_t)(s0 + lane) * pstep] : -INFINITY;
+          wt[i] = l == -INFINITY ? 0.0f : exp2f(l - M[i]);
+        }
+      }
+      for (int u0 = 0; u0 < n; u0 += 4) {
+        float w[4][4];
+        bf16x8 v[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            w[i][uu] = __shfl(wt[i], u0 + uu, 64);  // 0 past the group (lanes >= n hold 0)
+            v[i][uu] = bf16x8{};
+            if (w[i][uu] != 0.0f)
+              v[i][uu] = *(const bf16x8*)((const bf16_t*)opart + (p0[i] + (size_t)(s0 + u0 + uu) * pstep) * CB_DC + 8 * lane);
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][e] += w[i][uu] * (float)v[i][uu][e];
+      }
+    }
+  } else {
+    // fp32 partials (written by the portable attention)
+    for (int i = 0; i < 4; ++i) {
+      if (!live[i]) continue;
+      for (int s = 0; s < S; ++s) {
+        const float l = lpart[p0[i] + s * pstep];
+        if (l == -INFINITY) continue;
+        const float w = exp2f(l - M[i]);
+        const float* src = (const float*)opart + (p0[i] + s * pstep) * CB_DC + 8 * lane;
+        const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[i][e] += w * x0[e];
+          acc[i][4 + e] += w * x1[e];
+        }
+      }
+    }
+  }
+  // merged rows (bf16) to the O_lat tile; rows past R are zero
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wave + CB_WAVES * i;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16_t)(acc[i][e] * invW[i]);
+    *(lbf16x8*)(lds + 1024 * m + 16 * (lane ^ (m & 15))) = o;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W^UV copies
+  __syncthreads();
+
+  // 2. out tile [32 m][128 n] = O_lat W^UV_i^T: wave w, row block w&1,
+  // column blocks 2(w>>1), 2(w>>1)+1; K = d_c in 16 k-steps.
+  const int mb = wave & 1, nb0 = 2 * (wave >> 1);
+  f32x4 c[2] = {f32x4{}, f32x4{}};
+  {
+    const int ma = 16 * mb + i16;
+    const lu8* arow = lds + 1024 * ma;
+    const lu8* brow0 = lds + CB_W_OFF + 1024 * (16 * nb0 + i16);
+    const lu8* brow1 = brow0 + 1024 * 16;
+    // (rows 16nb + i16 all have (row & 15) == i16)
+#pragma unroll
+    for (int ks = 0; ks < CB_DC / 32; ++ks) {
+      const int slot = (4 * ks + g) ^ i16;
+      const bf16x8 av = *(const lbf16x8*)(arow + 16 * slot);
+      const bf16x8 b0 = *(const lbf16x8*)(brow0 + 16 * slot);
+      const bf16x8 b1 = *(const lbf16x8*)(brow1 + 16 * slot);
+      c[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, av, c[0], 0, 0, 0);
+      c[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, av, c[1], 0, 0, 0);
+    }
+  }
+  // C = out^T tile: lane holds columns n = 16 nb + 4g + r (r = 0..3) of row
+  // m = 16 mb + i16.  Staged in the (dead) O_lat tile as [32 m][128 n] bf16,
+  // then one 16-byte store per thread.
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bf16x4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = (bf16_t)c[t][r];
+    const int m = 16 * mb + i16, n = 16 * (nb0 + t) + 4 * g;
+    *(__attribute__((address_space(3))) bf16x4*)(lds + (m * CB_DV + n) * 2) = o;
+  }
+  __syncthreads();
+  {
+    const int m = threadIdx.x >> 4, q = threadIdx.x & 15;  // 32 rows x 16 chunks
+    const int row = CB_ROWS * rb + m;
+    if (row < a.R)
+      *(bf16x8*)(a.out + ((size_t)row * a.H + head) * CB_DV + 8 * q) = *(const lbf16x8*)(lds + (m * CB_DV + 8 * q) * 2);
+  }
+}
+
+}  // namespace
+
+bool merge_uv_supported(const mla_dims& d, int R) {
+  return R >= 1 && R <= 2 * CB_ROWS && d.d_c == CB_DC && d.d_head == CB_DV;
+}
+
+// Merge + W^UV for R <= 64 rows: grid H x ceil(R / 32).
+hipError_t merge_uv(const CombineArgs& a) {
+  const int R = a.batch * a.s_q, H = a.d.n_heads;
+  const int nrb = (R + CB_ROWS - 1) / CB_ROWS;
+  if ((H * nrb) % 8 != 0) return hipErrorInvalidValue;
+  CbArgs cb{a.batch, a.s_q, H, R, a.ws, a.L.lpart, (const bf16_t*)a.W_UV, (bf16_t*)a.out, a.lse_out};
+  static bool attr_set = false;
+  if (!attr_set) {
+    MLA_TRY(hipFuncSetAttribute((const void*)&k_merge_uv, hipFuncAttributeMaxDynamicSharedMemorySize, CB_LDS));
+    attr_set = true;
+  }
+  return launch(&k_merge_uv, dim3(H * nrb), dim3(CB_WAVES * 64), CB_LDS, a.stream, cb);
+}
+
+}  // namespace mla

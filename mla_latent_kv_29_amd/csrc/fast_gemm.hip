@@ -394,10 +394,12 @@ hipError_t fast_query(const DecodeArgs& a) {
   return e;
 }
 
-// Combine on MFMA: merge the splits into O_lat, then out_i = W^UV_i O_lat_i.
+// Combine on MFMA: merge the splits into O_lat, then out_i = W^UV_i O_lat_i
+// (one fused kernel for at most 64 rows).
 hipError_t fast_combine_mfma(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
+  if (merge_uv_supported(d, R)) return merge_uv(a);
   bf16_t* olat = (bf16_t*)(a.ws + a.L.qt);  // the query buffer is free after the attention
   MLA_TRY(launch(&k_merge, dim3((R * H + 3) / 4), dim3(256), 0, a.stream, a.batch, H, a.s_q, d.d_c, a.ws, a.L.lpart,
                  olat, a.lse_out));

@@ -120,5 +120,7 @@ hipError_t fast_query(const DecodeArgs& a);
 hipError_t fast_combine_mfma(const CombineArgs& a);
 bool skinny_query_supported(const mla_dims& d, int R);
 hipError_t skinny_query(const DecodeArgs& a);
+bool merge_uv_supported(const mla_dims& d, int R);
+hipError_t merge_uv(const CombineArgs& a);
 
 }  // namespace mla
