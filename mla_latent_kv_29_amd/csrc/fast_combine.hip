@@ -138,7 +138,34 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
-  if (pbf16) {
+  if (pbf16 && !live[1]) {
+    // One row on this wave (at most 8 rows per block): sixteen splits in
+    // flight at a time instead of four, so that a long split list costs a
+    // quarter of the memory round trips.
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int n = min(64, S - s0);
+      float wt = wt0[0];
+      if (s0 > 0) {  // more than 64 splits
+        const float l = live[0] && lane < n ? lpart[p0[0] + (size_t)(s0 + lane) * pstep] : -INFINITY;
+        wt = l == -INFINITY ? 0.0f : exp2f(l - M[0]);
+      }
+      for (int u0 = 0; u0 < n; u0 += 16) {
+        float w[16];
+        bf16x8 v[16];
+#pragma unroll
+        for (int uu = 0; uu < 16; ++uu) {
+          w[uu] = __shfl(wt, u0 + uu, 64);  // 0 past the group (lanes >= n hold 0)
+          v[uu] = bf16x8{};
+          if (w[uu] != 0.0f)
+            v[uu] = *(const bf16x8*)((const bf16_t*)opart + (p0[0] + (size_t)(s0 + u0 + uu) * pstep) * CB_DC + 8 * lane);
+        }
+#pragma unroll
+        for (int uu = 0; uu < 16; ++uu)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[0][e] += w[uu] * (float)v[uu][e];
+      }
+    }
+  } else if (pbf16) {
     // Splits four at a time, the loads of all four rows together; lane t of
     // a 64-split group holds split t's weight.
     for (int s0 = 0; s0 < S; s0 += 64) {

@@ -141,3 +141,14 @@ def test_v3_bf16_compressed_query_input(s_q):
         o, l = case.oracle(b, tau)
         assert max_abs(out[b], o) <= TOL_BF16 * float(np.abs(o).max()), b
         assert max_abs(lse[b], l) <= TOL_BF16 * max(1.0, float(np.abs(l).max())), b
+
+
+def test_v3_bf16_many_rows_two_row_blocks():
+    """48 query rows (24 sequences x 2 queries): the combine's second row block
+    is partly empty and each wave merges several rows; ragged lengths down to
+    two tokens (the two new ones) and three splits."""
+    lengths = [2, 2, 65, 300, 129, 64, 17, 200, 33, 250, 80, 5, 140, 96, 63, 190, 7, 111, 222, 40, 66, 130, 3, 280]
+    case = Case(V3, "bf16", "bf16", lengths, s_q=2, table="shuffled", wl=1, num_splits=3)
+    tau = tau_of(V3)
+    out, lse, _ = case.run(tau)
+    check_all(case, out, lse, tau, TOL_BF16, heads=[0, 77, 127])
