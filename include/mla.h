@@ -1,6 +1,6 @@
 /*
  * mla.h -- C ABI of the MI355X (gfx950) Multi-head Latent Attention decode
- * library (libmla.so).
+ * library (libmla.so), with a prefill entry point.
  *
  * What it computes.  DeepSeek-V3's MLA, as the DeepSeek-V3 reading lesson
  * "Читаем техотчёт DeepSeek-V3 вместе" (ai.flicky.cc), section 2.1.1 "MLA: что
@@ -202,6 +202,32 @@ MLA_API int mla_decode_attend(const mla_dims* dims, int32_t act_dtype, const voi
 MLA_API int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch,
                 int32_t s_q, const void* ws, size_t ws_bytes, const void* W_UV,
                 void* out, float* lse_out, void* stream);
+
+/* Prefill (the non-absorbed form of the lesson's §2.1.1 for many new tokens
+ * at once): n_seq fresh sequences packed back to back in
+ *   h [n_tok, d_model] (BF16): sequence b is rows cu_seqlens[b] ..
+ *     cu_seqlens[b+1]-1, and its token t sits at position t;
+ *   cu_seqlens int32 [n_seq + 1] device, cu_seqlens[0] = 0, non-decreasing,
+ *     cu_seqlens[n_seq] = n_tok, no sequence longer than max_seqlen (host);
+ *   W_DQ [d_cq, d_model], W_UQ [n_heads*(d_head+d_rope), d_cq],
+ *   W_UK, W_UV [n_heads*d_head, d_c], W_DKV [d_c, d_model],
+ *   W_KR [d_rope, d_model] (BF16, the layouts of mla_decode/mla_cache_append).
+ * For every token j and head i it computes, with explicit per-head keys
+ * k_{t,i} = [W^UK_i c^KV_t ; k^R_t] and values v_{t,i} = W^UV_i c^KV_t,
+ *   out[j][i] = sum over t <= j of softmax_t(softmax_scale * q_{j,i}.k_{t,i}) v_{t,i}
+ * into out [n_tok, n_heads, d_head] (BF16) and the natural-log log-sum-exp
+ * into lse_out [n_tok, n_heads] fp32 (or NULL), with fp32 accumulation.  The
+ * cache is not written: mla_cache_append stores the same tokens' latents.
+ * ws [ws_bytes >= mla_prefill_workspace_bytes(...)] holds the projections.
+ * Supported: BF16 activations at the DeepSeek-V3 head shape (128 heads of
+ * d_head 128, d_rope 64, d_c 512); anything else returns
+ * MLA_ERR_UNSUPPORTED.  n_tok == 0 is a no-op.                              */
+MLA_API size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t n_tok);
+MLA_API int mla_prefill(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok,
+                int32_t n_seq, const int32_t* cu_seqlens, int32_t max_seqlen,
+                const void* W_DQ, const void* W_UQ, const void* W_UK, const void* W_UV,
+                const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
+                float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code.                                      */
 MLA_API const char* mla_status_str(int status);

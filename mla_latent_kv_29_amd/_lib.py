@@ -17,7 +17,7 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
-           "mla_status_str", "mla_last_hip_error", "mla_version")
+           "mla_prefill_workspace_bytes", "mla_prefill", "mla_status_str", "mla_last_hip_error", "mla_version")
 
 
 class mla_dims(ctypes.Structure):
@@ -61,6 +61,8 @@ def _load():
         "mla_decode_query": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
         "mla_decode_attend": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
         "mla_combine": (ctypes.c_int, [D, I32, I32, I32, P, SZ, P, P, P, P]),
+        "mla_prefill_workspace_bytes": (SZ, [D, I32, I32]),
+        "mla_prefill": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
         "mla_last_hip_error": (ctypes.c_char_p, []),
@@ -187,4 +189,18 @@ def mla_combine(dims, act_dtype, batch, s_q, ws, ws_bytes, W_UV, out, lse_out=No
                           _ptr(W_UV), _ptr(out), _ptr(lse_out), _stream(stream))
     if check:
         _check("mla_combine", st)
+    return st
+
+
+def mla_prefill_workspace_bytes(dims, act_dtype, n_tok):
+    return int(_lib.mla_prefill_workspace_bytes(ctypes.byref(dims), int(act_dtype), int(n_tok)))
+
+
+def mla_prefill(dims, act_dtype, h, n_tok, n_seq, cu_seqlens, max_seqlen, W_DQ, W_UQ, W_UK, W_UV, W_DKV, W_KR,
+                softmax_scale, out, lse_out, ws, ws_bytes, stream=None, check=True):
+    st = _lib.mla_prefill(ctypes.byref(dims), int(act_dtype), _ptr(h), int(n_tok), int(n_seq), _ptr(cu_seqlens),
+                          int(max_seqlen), _ptr(W_DQ), _ptr(W_UQ), _ptr(W_UK), _ptr(W_UV), _ptr(W_DKV), _ptr(W_KR),
+                          float(softmax_scale), _ptr(out), _ptr(lse_out), _ptr(ws), int(ws_bytes), _stream(stream))
+    if check:
+        _check("mla_prefill", st)
     return st

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 SOURCES = ["api.cpp", "generic.hip", "fast.hip", "fast_attn2.hip", "fast_gemm.hip", "fast_skinny.hip",
-           "fast_append.hip", "fast_combine.hip"]
+           "fast_append.hip", "fast_combine.hip", "fast_prefill.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-result", "-fvisibility=hidden"]

@@ -12,6 +12,7 @@ namespace {
 constexpr int MAX_S_Q = 8;
 constexpr int TARGET_ITEMS = 256;  // (sequence, query, split) work items aimed for per decode: one per CU
 constexpr int MAX_PAGES_PER_SPLIT = 32;  // caps one item's work (2048 tokens) so that ragged batches balance
+constexpr int MAX_PREFILL_TOKENS = 1 << 17;  // keeps every per-head byte offset of the prefill workspace in 32 bits
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -213,6 +214,39 @@ int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t 
   if (!force_generic() && fast_decode_supported(*dims, act_dtype, MLA_BF16, s_q)) e = fast_combine(a);
   else e = generic_combine(a);
   return hip_status(e);
+}
+
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t n_tok) {
+  if (check_dims(dims) || !valid_act(act_dtype) || n_tok < 0 || n_tok > MAX_PREFILL_TOKENS) return 0;
+  return prefill_layout(*dims, n_tok).total;
+}
+
+int mla_prefill(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok, int32_t n_seq,
+                const int32_t* cu_seqlens, int32_t max_seqlen, const void* W_DQ, const void* W_UQ, const void* W_UK,
+                const void* W_UV, const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
+                float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
+  if (n_tok < 0 || n_tok > MAX_PREFILL_TOKENS || n_seq < 1 || n_seq > 65535 || max_seqlen < 1) return MLA_ERR_DIMS;
+  if (n_tok == 0) return MLA_OK;
+  if (!prefill_supported(*dims, act_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (!h || !cu_seqlens || !W_DQ || !W_UQ || !W_UK || !W_UV || !W_DKV || !W_KR || !out || !ws) return MLA_ERR_NULL;
+  const void* ptrs[] = {h, cu_seqlens, W_DQ, W_UQ, W_UK, W_UV, W_DKV, W_KR, out, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_ALIGN;
+  if (lse_out && ((uintptr_t)lse_out & 3)) return MLA_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f)) return MLA_ERR_DIMS;
+  const PrefillLayout L = prefill_layout(*dims, n_tok);
+  if (ws_bytes < L.total) return MLA_ERR_WORKSPACE;
+  PrefillArgs a;
+  a.d = *dims; a.h = (const bf16_t*)h; a.n_tok = n_tok; a.n_seq = n_seq; a.max_seqlen = max_seqlen;
+  a.cu_seqlens = cu_seqlens;
+  a.W_DQ = (const bf16_t*)W_DQ; a.W_UQ = (const bf16_t*)W_UQ; a.W_UK = (const bf16_t*)W_UK;
+  a.W_UV = (const bf16_t*)W_UV; a.W_DKV = (const bf16_t*)W_DKV; a.W_KR = (const bf16_t*)W_KR;
+  a.scale = softmax_scale; a.out = (bf16_t*)out; a.lse_out = lse_out; a.ws = (uint8_t*)ws; a.L = L;
+  a.stream = (hipStream_t)stream;
+  return hip_status(fast_prefill(a));
 }
 
 const char* mla_status_str(int s) {

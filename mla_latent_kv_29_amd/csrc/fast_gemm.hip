@@ -394,6 +394,141 @@ hipError_t fast_query(const DecodeArgs& a) {
   return e;
 }
 
+// ------------------------------------------------------------ prefill
+// The projections of the non-absorbed prefill (lesson §2.1.1: c^KV, k^R,
+// c^Q, q; k^C = W^UK c^KV and v^C = W^UV c^KV explicitly per head), one
+// general GEMM each, with the layout the causal attention kernel reads.
+
+namespace {
+
+// Position of token t in its sequence: t - cu_seqlens[b] for the b with
+// cu_seqlens[b] <= t < cu_seqlens[b + 1] (binary search).
+__global__ void k_positions(const int32_t* __restrict__ cu, int n_seq, int n_tok, int32_t* __restrict__ pos) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tok) return;
+  int lo = 0, hi = n_seq;  // cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  pos[t] = t - cu[lo];
+}
+
+// Y[row][col] (bf16, row stride ld)
+struct EpiRowStore {
+  bf16_t* y;
+  int ld;
+  __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (row + r < M) y[(long)(row + r) * ld + col] = (bf16_t)v[r];
+  }
+};
+
+// k^R = RoPE(W^KR h) at the row's position; columns (2m, 2m+1) are a pair in
+// neighbouring lanes.
+struct EpiRopeRows {
+  bf16_t* y;
+  int ld;
+  const int32_t* pos;
+  double freq[32];
+  __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
+    const int m = col >> 1;
+    const bool odd = col & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float other = __shfl_xor(v[r], 1, 64);
+      const int rr = row + r;
+      if (rr >= M) continue;
+      float cs, sn;
+      rope_cs_w(pos[rr], freq[m], &cs, &sn);
+      const float x0 = odd ? other : v[r], x1 = odd ? v[r] : other;
+      y[(long)rr * ld + col] = (bf16_t)(odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn);
+    }
+  }
+};
+
+// q = W^UQ c^Q, column n = (d_head + d_rope) i + d -> q[i][row][d] scaled by
+// tau log2(e), the RoPE columns rotated at the row's position first.  A
+// 16-column block is all content or all RoPE (d_head % 16 == 0), so the
+// branch is wave-uniform.
+struct EpiPrefillQ {
+  bf16_t* q;
+  int n_tok, d_head, d_rope;
+  const int32_t* pos;
+  float scale2;
+  double freq[32];
+  __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
+    const int w = d_head + d_rope;
+    const int i = col / w, d = col % w;
+    bf16_t* qi = q + (long)i * n_tok * w;
+    if (d < d_head) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (row + r < M) qi[(long)(row + r) * w + d] = (bf16_t)(scale2 * v[r]);
+      return;
+    }
+    const int m = (d - d_head) >> 1;
+    const bool odd = (d - d_head) & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float other = __shfl_xor(v[r], 1, 64);
+      const int rr = row + r;
+      if (rr >= M) continue;
+      float cs, sn;
+      rope_cs_w(pos[rr], freq[m], &cs, &sn);
+      const float x0 = odd ? other : v[r], x1 = odd ? v[r] : other;
+      qi[(long)rr * w + d] = (bf16_t)(scale2 * (odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn));
+    }
+  }
+};
+
+// k^C or v^C: column n = d_head i + d -> y[i][row][d]
+struct EpiHeadMajor {
+  bf16_t* y;
+  int n_tok, d_head;
+  __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
+    const int i = col / d_head, d = col % d_head;
+    bf16_t* yi = y + (long)i * n_tok * d_head;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (row + r < M) yi[(long)(row + r) * d_head + d] = (bf16_t)v[r];
+  }
+};
+
+}  // namespace
+
+hipError_t prefill_projections(const PrefillArgs& a) {
+  const mla_dims& d = a.d;
+  const int n = a.n_tok, H = d.n_heads, w = d.d_head + d.d_rope;
+  int32_t* pos = (int32_t*)(a.ws + a.L.pos);
+  bf16_t* ckv = (bf16_t*)(a.ws + a.L.ckv);
+  bf16_t* kr = (bf16_t*)(a.ws + a.L.kr);
+  bf16_t* cq = (bf16_t*)(a.ws + a.L.cq);
+  bf16_t* q = (bf16_t*)(a.ws + a.L.q);
+  bf16_t* kc = (bf16_t*)(a.ws + a.L.kc);
+  bf16_t* vc = (bf16_t*)(a.ws + a.L.vc);
+  MLA_TRY(launch(&k_positions, dim3((n + 255) / 256), dim3(256), 0, a.stream, a.cu_seqlens, a.n_seq, n, pos));
+  double freq[32] = {};
+  for (int m = 0; m < d.d_rope / 2; ++m) freq[m] = pow((double)d.rope_theta, -2.0 * m / d.d_rope);
+  GemmArgs g = gemm_args(n, d.d_c, d.d_model, a.h, d.d_model, 0, a.W_DKV, d.d_model, 0, 1);
+  MLA_TRY(launch_gemm<true>(g, 1, 1, EpiRowStore{ckv, d.d_c}, a.stream));
+  g = gemm_args(n, d.d_rope, d.d_model, a.h, d.d_model, 0, a.W_KR, d.d_model, 0, 1);
+  EpiRopeRows er{kr, d.d_rope, pos, {}};
+  for (int m = 0; m < 32; ++m) er.freq[m] = freq[m];
+  MLA_TRY(launch_gemm<true>(g, 1, 1, er, a.stream));
+  g = gemm_args(n, d.d_cq, d.d_model, a.h, d.d_model, 0, a.W_DQ, d.d_model, 0, 1);
+  MLA_TRY(launch_gemm<true>(g, 1, 1, EpiRowStore{cq, d.d_cq}, a.stream));
+  g = gemm_args(n, H * w, d.d_cq, cq, d.d_cq, 0, a.W_UQ, d.d_cq, 0, 1);
+  EpiPrefillQ eq{q, n, d.d_head, d.d_rope, pos, a.scale * LOG2E, {}};
+  for (int m = 0; m < 32; ++m) eq.freq[m] = freq[m];
+  MLA_TRY(launch_gemm<true>(g, 1, 1, eq, a.stream));
+  g = gemm_args(n, H * d.d_head, d.d_c, ckv, d.d_c, 0, a.W_UK, d.d_c, 0, 1);
+  MLA_TRY(launch_gemm<true>(g, 1, 1, EpiHeadMajor{kc, n, d.d_head}, a.stream));
+  g = gemm_args(n, H * d.d_head, d.d_c, ckv, d.d_c, 0, a.W_UV, d.d_c, 0, 1);
+  return launch_gemm<true>(g, 1, 1, EpiHeadMajor{vc, n, d.d_head}, a.stream);
+}
+
 // Combine on MFMA: merge the splits into O_lat, then out_i = W^UV_i O_lat_i
 // (one fused kernel for at most 64 rows).
 hipError_t fast_combine_mfma(const CombineArgs& a) {

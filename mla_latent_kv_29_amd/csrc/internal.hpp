@@ -99,6 +99,47 @@ struct AppendArgs {
   hipStream_t stream;
 };
 
+// Prefill workspace (every region 256-byte aligned), n = n_tok:
+//   pos : int32 [n]                token position within its sequence
+//   ckv : bf16  [n][d_c]           c^KV = W^DKV h
+//   kr  : bf16  [n][d_rope]        k^R = RoPE(W^KR h)
+//   cq  : bf16  [n][d_cq]          c^Q = W^DQ h
+//   q   : bf16  [H][n][d_head + d_rope]  [q^C ; RoPE(q^R)] * tau * log2(e)
+//   kc  : bf16  [H][n][d_head]     k^C = W^UK c^KV (explicit, per head)
+//   vc  : bf16  [H][n][d_head]     v^C = W^UV c^KV
+struct PrefillLayout {
+  size_t pos, ckv, kr, cq, q, kc, vc, total;
+};
+
+inline PrefillLayout prefill_layout(const mla_dims& d, int n_tok) {
+  const size_t n = (size_t)n_tok, H = d.n_heads;
+  PrefillLayout w;
+  size_t o = 0;
+  w.pos = o; o = align256(o + n * 4);
+  w.ckv = o; o = align256(o + n * d.d_c * 2);
+  w.kr = o;  o = align256(o + n * d.d_rope * 2);
+  w.cq = o;  o = align256(o + n * d.d_cq * 2);
+  w.q = o;   o = align256(o + H * n * (d.d_head + d.d_rope) * 2);
+  w.kc = o;  o = align256(o + H * n * d.d_head * 2);
+  w.vc = o;  o = align256(o + H * n * d.d_head * 2);
+  w.total = o;
+  return w;
+}
+
+struct PrefillArgs {
+  mla_dims d;
+  const bf16_t* h;  // [n_tok][d_model]
+  int n_tok, n_seq, max_seqlen;
+  const int32_t* cu_seqlens;  // [n_seq + 1]
+  const bf16_t *W_DQ, *W_UQ, *W_UK, *W_UV, *W_DKV, *W_KR;
+  float scale;                // softmax scale tau
+  bf16_t* out;                // [n_tok][H][d_head]
+  float* lse_out;             // [n_tok][H] or null
+  uint8_t* ws;
+  PrefillLayout L;
+  hipStream_t stream;
+};
+
 // Launchers (return the first HIP error of the enqueue, hipSuccess otherwise).
 hipError_t generic_append(const AppendArgs& a);
 hipError_t generic_write(const AppendArgs& a);
@@ -122,5 +163,9 @@ bool skinny_query_supported(const mla_dims& d, int R);
 hipError_t skinny_query(const DecodeArgs& a);
 bool merge_uv_supported(const mla_dims& d, int R);
 hipError_t merge_uv(const CombineArgs& a);
+bool prefill_supported(const mla_dims& d, int act);
+hipError_t prefill_projections(const PrefillArgs& a);  // positions, c^KV, k^R, c^Q, q, k^C, v^C
+hipError_t prefill_attention(const PrefillArgs& a);    // causal attention over q, k, v -> out, lse
+hipError_t fast_prefill(const PrefillArgs& a);
 
 }  // namespace mla

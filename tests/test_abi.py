@@ -125,3 +125,37 @@ def test_append_and_combine_argument_errors():
     assert m.mla_combine(d, m.MLA_BF16, 2, 1, FAKE, 1 << 34, None, FAKE, None, stream=0, check=False) == \
         L.MLA_ERR_NULL
     assert m.mla_combine(d, m.MLA_BF16, 0, 1, None, 0, None, None, None, stream=0, check=False) == L.MLA_OK
+
+
+def test_prefill_workspace_and_argument_errors():
+    d = _dims()
+    w1 = m.mla_prefill_workspace_bytes(d, m.MLA_BF16, 1)
+    w100 = m.mla_prefill_workspace_bytes(d, m.MLA_BF16, 100)
+    # per token: position, c^KV, k^R, c^Q, q, k^C and v^C (bf16), 256-byte aligned regions
+    per_tok = 4 + 2 * (512 + 64 + 1536 + 128 * 192 + 2 * 128 * 128)
+    assert w100 >= 100 * per_tok and w100 < 100 * per_tok + 7 * 256
+    assert 0 < w1 < w100
+    assert m.mla_prefill_workspace_bytes(d, m.MLA_BF16, -1) == 0
+
+    def call(**o):
+        a = dict(act=m.MLA_BF16, h=FAKE, n=100, ns=2, cu=FAKE, mx=64, wuv=FAKE, out=FAKE, lse=None, ws=FAKE,
+                 wsb=w100, dims=d, tau=0.1)
+        a.update(o)
+        return m.mla_prefill(a["dims"], a["act"], a["h"], a["n"], a["ns"], a["cu"], a["mx"], FAKE, FAKE, FAKE,
+                             a["wuv"], FAKE, FAKE, a["tau"], a["out"], a["lse"], a["ws"], a["wsb"], stream=0,
+                             check=False)
+
+    assert call(n=0) == L.MLA_OK                                   # no-op
+    assert call(act=7) == L.MLA_ERR_DTYPE
+    assert call(ns=0) == L.MLA_ERR_DIMS
+    assert call(mx=0) == L.MLA_ERR_DIMS
+    assert call(n=-3) == L.MLA_ERR_DIMS
+    assert call(h=None) == L.MLA_ERR_NULL
+    assert call(cu=None) == L.MLA_ERR_NULL
+    assert call(wuv=None) == L.MLA_ERR_NULL
+    assert call(out=FAKE + 8) == L.MLA_ERR_ALIGN
+    assert call(lse=FAKE + 2) == L.MLA_ERR_ALIGN
+    assert call(wsb=w100 - 1) == L.MLA_ERR_WORKSPACE
+    assert call(tau=0.0) == L.MLA_ERR_DIMS
+    assert call(act=m.MLA_F32) == L.MLA_ERR_UNSUPPORTED             # bf16 activations only
+    assert call(dims=m.make_dims(inputs.TINY_DIMS)) == L.MLA_ERR_UNSUPPORTED

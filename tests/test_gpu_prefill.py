@@ -1,0 +1,78 @@
+"""Parity of the causal prefill (mla_prefill) with the float64 oracle.
+
+The oracle's decode of a sequence with s_q equal to its length is exactly the
+prefill of that sequence: every token is a query at its own position and sees
+tokens 0..j, with explicit per-head k^C = W^UK c^KV and v^C = W^UV c^KV (the
+non-absorbed form).  Inputs are the seeded hidden states and weights of the
+decode tests, sequences packed back to back.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mla_latent_kv_29_amd as m
+from mla_latent_kv_29_amd import inputs
+from gpu_common import DEV, tau_of, to_np, max_abs
+
+pytestmark = pytest.mark.gpu
+
+V3 = inputs.V3_DIMS
+TOL_BF16 = 2e-2
+HEADS = [0, 57, 127]
+
+
+def run_prefill(lengths, kappa, seed=0, wl=3, sigma=0.006, lse=True):
+    dims = V3
+    W = inputs.weights(dims, sigma, torch.bfloat16, DEV, seed, wl)
+    hs = [inputs.hidden(dims, b, 0, int(L), torch.bfloat16, DEV, seed, wl) for b, L in enumerate(lengths)]
+    h = torch.cat(hs, 0).contiguous()
+    n = h.shape[0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=DEV)
+    d = m.make_dims(dims)
+    wsb = m.mla_prefill_workspace_bytes(d, m.MLA_BF16, n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    out = torch.full((n, dims["n_heads"], dims["d_head"]), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse_t = torch.full((n, dims["n_heads"]), float("nan"), dtype=torch.float32, device=DEV) if lse else None
+    tau = kappa * tau_of(dims)
+    m.mla_prefill(d, m.MLA_BF16, h, n, len(lengths), cu, int(max(lengths)), W["W_DQ"], W["W_UQ"], W["W_UK"],
+                  W["W_UV"], W["W_DKV"], W["W_KR"], tau, out, lse_t, ws, wsb)
+    torch.cuda.synchronize()
+    return dims, W, hs, to_np(out), (to_np(lse_t) if lse else None), tau
+
+
+def check(lengths, kappa, heads=HEADS):
+    dims, W, hs, out, lse, tau = run_prefill(lengths, kappa)
+    Wn = {k: to_np(v) for k, v in W.items()}
+    row = 0
+    for b, L in enumerate(lengths):
+        L = int(L)
+        o_ref, l_ref = oracle.decode_from_h(to_np(hs[b]), Wn, dims, L, L, tau, heads)
+        got = out[row:row + L][:, heads]
+        ref = float(np.max(np.abs(o_ref)))
+        err = max_abs(got, o_ref)
+        assert err <= TOL_BF16 * ref, (b, L, kappa, err, ref)
+        gl = lse[row:row + L][:, heads]
+        assert max_abs(gl, l_ref) <= TOL_BF16 * max(1.0, float(np.max(np.abs(l_ref)))), (b, L, kappa)
+        row += L
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("kappa", [1.0, 56.0])
+def test_prefill_ragged_sequences(kappa):
+    """One token, exactly one tile, three tiles with a ragged tail, one tile plus one."""
+    check([1, 64, 190, 65], kappa)
+
+
+def test_prefill_long_sequence_streams_many_key_tiles():
+    """640 tokens: ten query tiles, the last of which streams ten key tiles
+    through the two LDS buffers; plus a short neighbour."""
+    check([640, 3], 1.0)
+
+
+def test_prefill_rows_past_the_end_are_not_written():
+    """Query rows of a block beyond its sequence are computed on clamped rows
+    and never stored: the next sequence's rows come out right (covered above),
+    and no output row is left unwritten (no NaN survives the fill)."""
+    dims, W, hs, out, lse, tau = run_prefill([5, 70, 1], 1.0)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
