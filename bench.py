@@ -115,6 +115,102 @@ def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=64):
             "host_cpus": os.cpu_count(), "cpu_model": platform.processor() or platform.machine()}
 
 
+def prefill_algorithmic(dims, lengths):
+    """FLOPs of one prefill: the causal attention (query-key pairs with
+    t <= j, q.k over d_head + d_rope and p.v over d_head, per head) and the
+    projections (c^KV, k^R, c^Q, q, k^C, v^C)."""
+    H, dh, dr, dc, dq, d = (dims[k] for k in ("n_heads", "d_head", "d_rope", "d_c", "d_cq", "d_model"))
+    L = [int(x) for x in lengths]
+    n = sum(L)
+    pairs = sum(x * (x + 1) // 2 for x in L)
+    attn = pairs * H * 2 * ((dh + dr) + dh)
+    proj = 2 * n * (dc * d + dr * d + dq * d + H * (dh + dr) * dq + 2 * H * dh * dc)
+    return attn, proj
+
+
+def run_prefill(args, name):
+    """Prefill workload: one step = mla_prefill_project + mla_prefill_attend
+    over the packed sequences; the attention (the dominant kernel) is timed
+    with HIP events around its call on its stream, every step."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_29_amd import inputs
+    from mla_latent_kv_29_amd import _lib as L
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    spec = inputs.PREFILL_WORKLOADS[name]
+    dims, wl = spec["dims"], spec["index"]
+    tdt = inputs.torch_dtype(spec["act"])
+    lengths = inputs.seqlens(spec["lengths"], spec["batch"], 0, wl)
+    W = inputs.weights(dims, spec["sigma"], tdt, dev, 0, wl)
+    h = torch.cat([inputs.hidden(dims, b, 0, int(Lb), tdt, dev, 0, wl) for b, Lb in enumerate(lengths)], 0)
+    h = h.contiguous()
+    n = int(h.shape[0])
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=dev)
+    c = L.make_dims(dims)
+    wsb = L.mla_prefill_workspace_bytes(c, L.MLA_BF16, n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty((n, dims["n_heads"], dims["d_head"]), dtype=tdt, device=dev)
+    lse = torch.empty((n, dims["n_heads"]), dtype=torch.float32, device=dev)
+    tau = 1.0 / math.sqrt(dims["d_head"] + dims["d_rope"])
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    pargs = (c, L.MLA_BF16, h, n, len(lengths), cu, int(max(lengths)), W["W_DQ"], W["W_UQ"], W["W_UK"], W["W_UV"],
+             W["W_DKV"], W["W_KR"], tau, out, lse, ws, wsb, sp)
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        L.mla_prefill_project(*pargs)
+        if e is not None:
+            e[1].record(stream)
+        L.mla_prefill_attend(*pargs)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    a_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_per_step = wall / args.steps * 1e3
+    attn_flops, proj_flops = prefill_algorithmic(dims, lengths)
+    attn_s = float(np.mean(a_ms)) * 1e-3
+    achieved = attn_flops / attn_s / 1e12
+    t_bound = (attn_flops + proj_flops) / MFMA_BF16_PEAK
+    res = {
+        "metric": f"MLA prefill tokens/s + % MFMA roofline, {spec['batch']} x {spec['lengths'][1]} tokens bf16, 1 GPU",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec["act"],
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,sigma^2) weights at DeepSeek-V3 MLA shapes)",
+        "config": {"workload": name, "batch": int(spec["batch"]), "seq_len": int(spec["lengths"][1]),
+                   "tokens": n},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved * 1e12 / MFMA_BF16_PEAK, "traffic": None,
+                     "kernel": "k_prefill_attn (mla_prefill_attend)", "attn_ms_mean": float(np.mean(a_ms)),
+                     "attn_flops": attn_flops},
+        "step_roofline": {"t_bound_us": t_bound * 1e6, "frac": t_bound / (ms_per_step * 1e-3),
+                          "step_flops": attn_flops + proj_flops},
+        "phases_ms": {"project": float(np.median(p_ms)), "attend": float(np.median(a_ms))},
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,9 +231,13 @@ def main():
               f"share at its real shape and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
+    from mla_latent_kv_29_amd import inputs
+    if args.workload in inputs.PREFILL_WORKLOADS:
+        run_prefill(args, args.workload)
+        return
+
     import numpy as np
     import torch
-    from mla_latent_kv_29_amd import inputs
     from mla_latent_kv_29_amd import _lib as L
     from mla_latent_kv_29_amd.session import DecodeSession
 

@@ -229,6 +229,22 @@ MLA_API int mla_prefill(const mla_dims* dims, int32_t act_dtype, const void* h, 
                 const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
                 float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of mla_prefill (same arguments and validation), for callers
+ * that schedule or time them separately: mla_prefill_project computes the
+ * token positions, c^KV, k^R, c^Q, q, k^C and v^C into ws; mla_prefill_attend
+ * then runs the causal attention from ws into out and lse_out.
+ * mla_prefill == project then attend on the same stream.                    */
+MLA_API int mla_prefill_project(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok,
+                int32_t n_seq, const int32_t* cu_seqlens, int32_t max_seqlen,
+                const void* W_DQ, const void* W_UQ, const void* W_UK, const void* W_UV,
+                const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
+                float* lse_out, void* ws, size_t ws_bytes, void* stream);
+MLA_API int mla_prefill_attend(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok,
+                int32_t n_seq, const int32_t* cu_seqlens, int32_t max_seqlen,
+                const void* W_DQ, const void* W_UQ, const void* W_UK, const void* W_UV,
+                const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
+                float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code.                                      */
 MLA_API const char* mla_status_str(int status);
 

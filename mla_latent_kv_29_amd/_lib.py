@@ -17,7 +17,8 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
-           "mla_prefill_workspace_bytes", "mla_prefill", "mla_status_str", "mla_last_hip_error", "mla_version")
+           "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
+           "mla_status_str", "mla_last_hip_error", "mla_version")
 
 
 class mla_dims(ctypes.Structure):
@@ -63,6 +64,8 @@ def _load():
         "mla_combine": (ctypes.c_int, [D, I32, I32, I32, P, SZ, P, P, P, P]),
         "mla_prefill_workspace_bytes": (SZ, [D, I32, I32]),
         "mla_prefill": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
+        "mla_prefill_project": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
+        "mla_prefill_attend": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
         "mla_last_hip_error": (ctypes.c_char_p, []),
@@ -196,11 +199,24 @@ def mla_prefill_workspace_bytes(dims, act_dtype, n_tok):
     return int(_lib.mla_prefill_workspace_bytes(ctypes.byref(dims), int(act_dtype), int(n_tok)))
 
 
-def mla_prefill(dims, act_dtype, h, n_tok, n_seq, cu_seqlens, max_seqlen, W_DQ, W_UQ, W_UK, W_UV, W_DKV, W_KR,
-                softmax_scale, out, lse_out, ws, ws_bytes, stream=None, check=True):
-    st = _lib.mla_prefill(ctypes.byref(dims), int(act_dtype), _ptr(h), int(n_tok), int(n_seq), _ptr(cu_seqlens),
-                          int(max_seqlen), _ptr(W_DQ), _ptr(W_UQ), _ptr(W_UK), _ptr(W_UV), _ptr(W_DKV), _ptr(W_KR),
-                          float(softmax_scale), _ptr(out), _ptr(lse_out), _ptr(ws), int(ws_bytes), _stream(stream))
+def _prefill_call(name, dims, act_dtype, h, n_tok, n_seq, cu_seqlens, max_seqlen, W_DQ, W_UQ, W_UK, W_UV, W_DKV,
+                  W_KR, softmax_scale, out, lse_out, ws, ws_bytes, stream=None, check=True):
+    st = getattr(_lib, name)(ctypes.byref(dims), int(act_dtype), _ptr(h), int(n_tok), int(n_seq), _ptr(cu_seqlens),
+                             int(max_seqlen), _ptr(W_DQ), _ptr(W_UQ), _ptr(W_UK), _ptr(W_UV), _ptr(W_DKV),
+                             _ptr(W_KR), float(softmax_scale), _ptr(out), _ptr(lse_out), _ptr(ws), int(ws_bytes),
+                             _stream(stream))
     if check:
-        _check("mla_prefill", st)
+        _check(name, st)
     return st
+
+
+def mla_prefill(*args, **kw):
+    return _prefill_call("mla_prefill", *args, **kw)
+
+
+def mla_prefill_project(*args, **kw):
+    return _prefill_call("mla_prefill_project", *args, **kw)
+
+
+def mla_prefill_attend(*args, **kw):
+    return _prefill_call("mla_prefill_attend", *args, **kw)

@@ -221,10 +221,15 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int3
   return prefill_layout(*dims, n_tok).total;
 }
 
-int mla_prefill(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok, int32_t n_seq,
-                const int32_t* cu_seqlens, int32_t max_seqlen, const void* W_DQ, const void* W_UQ, const void* W_UK,
-                const void* W_UV, const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
-                float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+enum PrefillPart { PREFILL_ALL, PREFILL_PROJECT, PREFILL_ATTEND };
+
+int prefill_common(PrefillPart part, const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok,
+                   int32_t n_seq, const int32_t* cu_seqlens, int32_t max_seqlen, const void* W_DQ, const void* W_UQ,
+                   const void* W_UK, const void* W_UV, const void* W_DKV, const void* W_KR, float softmax_scale,
+                   void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
@@ -246,8 +251,28 @@ int mla_prefill(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t 
   a.W_UV = (const bf16_t*)W_UV; a.W_DKV = (const bf16_t*)W_DKV; a.W_KR = (const bf16_t*)W_KR;
   a.scale = softmax_scale; a.out = (bf16_t*)out; a.lse_out = lse_out; a.ws = (uint8_t*)ws; a.L = L;
   a.stream = (hipStream_t)stream;
-  return hip_status(fast_prefill(a));
+  switch (part) {
+    case PREFILL_PROJECT: return hip_status(prefill_projections(a));
+    case PREFILL_ATTEND: return hip_status(prefill_attention(a));
+    default: return hip_status(fast_prefill(a));
+  }
 }
+}  // namespace
+
+extern "C" {
+
+#define MLA_PREFILL_ARGS                                                                                          \
+  const mla_dims *dims, int32_t act_dtype, const void *h, int32_t n_tok, int32_t n_seq, const int32_t *cu_seqlens, \
+      int32_t max_seqlen, const void *W_DQ, const void *W_UQ, const void *W_UK, const void *W_UV,                 \
+      const void *W_DKV, const void *W_KR, float softmax_scale, void *out, float *lse_out, void *ws,            \
+      size_t ws_bytes, void *stream
+#define MLA_PREFILL_PASS                                                                                        \
+  dims, act_dtype, h, n_tok, n_seq, cu_seqlens, max_seqlen, W_DQ, W_UQ, W_UK, W_UV, W_DKV, W_KR, softmax_scale, \
+      out, lse_out, ws, ws_bytes, stream
+
+int mla_prefill(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_ALL, MLA_PREFILL_PASS); }
+int mla_prefill_project(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_PROJECT, MLA_PREFILL_PASS); }
+int mla_prefill_attend(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_ATTEND, MLA_PREFILL_PASS); }
 
 const char* mla_status_str(int s) {
   switch (s) {

@@ -35,6 +35,12 @@ WORKLOADS = {
                                   lengths=("fixed", 8192), table="inorder", sigma=0.006),
 }
 
+# Prefill of fresh sequences (mla_prefill): batch sequences of the given lengths, packed.
+PREFILL_WORKLOADS = {
+    "prefill_v3_bf16_b4_l4096": dict(index=5, dims=V3_DIMS, act="bf16", batch=4, lengths=("fixed", 4096),
+                                     sigma=0.006),
+}
+
 TENSORS = {"W_DKV": 1, "W_KR": 2, "W_DQ": 3, "W_UQ": 4, "W_UK": 5, "W_UV": 6, "h": 7, "len": 8, "table": 9,
            "latent": 10, "rope": 11}
 
