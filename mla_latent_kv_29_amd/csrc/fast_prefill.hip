@@ -9,30 +9,35 @@
 // and lse_{j,i} (natural log).  q arrives pre-scaled by tau log2(e), so the
 // softmax runs in the exp2 domain.
 //
-// Work item = (sequence, head, tile of 64 query rows); four waves of 16 rows.
+// Work item = (sequence, head, tile of 128 query rows); four waves of 32 rows.
 // Per 64-key tile (keys up to the tile's last query):
-//   S^T[16 keys][16 queries] blocks = K . Q^T with v_mfma_f32_16x16x32_bf16:
+//   S^T[32 keys][32 queries] blocks = K . Q^T with v_mfma_f32_32x32x16_bf16:
 //     K fragments from LDS (192-wide rows: k^C of the head, then k^R), the
-//     wave's Q^T fragments in 24 VGPRs for the whole kernel.
-//   Online softmax (running row maximum m and sum l): a lane holds four keys
-//     of one query per 16-key block, so the row maximum needs two lane swaps;
-//     O is rescaled by 2^(m_old - m_new) when the maximum moves.
-//   O^T[16 channels][16 queries] += V^T . P^T: P^T is the S^T register
-//     layout itself (keys 4g..4g+3 of two 16-key blocks make a lane's eight
-//     k-slots), and the transposing LDS read delivers V^T in the same key
-//     order, so P never leaves the registers.
+//     wave's Q^T fragments in 48 VGPRs for the whole kernel.  A 1 KiB K
+//     fragment feeds 16384 multiply-adds (32 queries), which keeps the LDS
+//     reads of four waves within what the LDS delivers.
+//   Online softmax (running row maximum m and sum l): a lane holds sixteen
+//     keys of one query per 32-key block, so the row maximum needs one lane
+//     swap; O is rescaled by 2^(m_old - m_new) only when some row's maximum
+//     moved.
+//   O^T[32 channels][32 queries] += V^T . P^T: P^T is the S^T register layout
+//     itself (keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key step make the eight
+//     k-slots of half-wave h), and two transposing LDS reads deliver V^T in
+//     the same key order, so P never leaves the registers.
 // K and V tiles stream HBM/L2 -> LDS with global_load_lds into two 40 KiB
 // buffers (one tile in flight while the other is multiplied); at 80 KiB a
 // block, two blocks share a CU, i.e. two waves per SIMD.  The LDS layouts
-// (16-byte chunk q of row r at slot q ^ f(r)) make the K fragment reads and
-// the transposing V reads bank-conflict free.
+// (16-byte chunk q of row r at slot q ^ f(r)) spread the K fragment reads and
+// the transposing V reads over the banks.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace mla {
 namespace {
 
 constexpr int PH = 128, PDH = 128, PDR = 64, PDQK = PDH + PDR;  // heads, d_head (= d_v), d_rope, q.k width
-constexpr int BQ = 64, BKT = 64;                                 // query rows per block, keys per tile
+constexpr int BQ = 128, BKT = 64;                                // query rows per block, keys per tile
 constexpr int KC_BYTES = BKT * PDH * 2;                          // 16 KiB
 constexpr int KR_BYTES = BKT * PDR * 2;                          // 8 KiB
 constexpr int V_BYTES = BKT * PDH * 2;                           // 16 KiB
@@ -62,10 +67,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Slot of 16-byte chunk c of tile row r: k^C rows (256 B), k^R rows (128 B),
-// V rows (256 B).
+// V rows (256 B).  The V swizzle gives the four key rows that one
+// transposing read of 32 lanes touches four disjoint groups of four slots.
 __device__ __forceinline__ int kc_slot(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int kr_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
-__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3) + 8 * ((r >> 2) & 1); }
+__device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
 
 struct PaArgs {
   const bf16_t* q;   // [H][n_tok][192], pre-scaled by tau log2(e)
@@ -78,28 +84,61 @@ struct PaArgs {
   float* lse;        // [n_tok][H] or null
 };
 
+// Per-lane byte offsets of this wave's tile copies, the same for every tile
+// and every copy of a kind (the swizzle depends on row bits that the copy
+// index does not change): k^C copy j (rows 4j + lane/16), k^R copy j (rows
+// 8j + lane/8), V copy j (rows 4j + lane/16).
+struct TileOffsets {
+  uint32_t kc, kr, v;
+};
+__device__ __forceinline__ TileOffsets tile_offsets(int wave, int lane) {
+  TileOffsets t;
+  t.kc = (uint32_t)(((lane >> 4) * PDH + 8 * ((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15))) * 2);
+  t.kr = (uint32_t)(((lane >> 3) * PDR + 8 * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7))) * 2);
+  t.v = (uint32_t)(((lane >> 4) * PDH + 8 * ((lane & 15) ^ v_swz(lane >> 4))) * 2);
+  return t;
+}
+
 // Tile kt (keys 64 kt .. +63 of the sequence, clamped to its last token) into
-// stage buffer `buf`: wave w issues copies w, w+4, ..., w+36 of the 40
-// (0-15 k^C rows, 16-23 k^R rows, 24-39 V rows).
+// stage buffer `buf`.  Of the 40 copies (0-15 k^C rows, 16-23 k^R rows, 24-39
+// V rows) wave w issues w, w+4, ..., w+36: copies n = 0-3 of the wave are
+// k^C, 4-5 k^R, 6-9 V, whatever w is.  A tile inside the sequence needs no
+// clamping: its copies take the per-lane offsets above and the tile's
+// position in the scalar base; the sequence's last tile clamps rows.
 __device__ __forceinline__ void issue_tile(const bf16_t* kc_h, const bf16_t* vc_h, const bf16_t* kr, int start,
-                                           int len, int kt, uint32_t buf, int wave, int lane) {
+                                           int len, int kt, uint32_t buf, int wave, int lane, const TileOffsets& to) {
   const int k0 = kt * BKT;
+  if (k0 + BKT <= len) {
+    const uint8_t* kcb = (const uint8_t*)kc_h + (size_t)(start + k0 + 4 * wave) * PDH * 2;
+    const uint8_t* krb = (const uint8_t*)kr + (size_t)(start + k0 + 8 * wave) * PDR * 2;
+    const uint8_t* vb = (const uint8_t*)vc_h + (size_t)(start + k0 + 4 * wave) * PDH * 2;
+    const uint32_t lb = buf + 1024 * wave;
 #pragma unroll
-  for (int n = 0; n < 10; ++n) {
-    const int j = wave + 4 * n;  // wave-uniform
-    if (j < 16) {
-      const int r = 4 * j + (lane >> 4), c = kc_slot(r, lane & 15);
-      const int key = min(k0 + r, len - 1);
-      pa_dma(kc_h, (uint32_t)(((start + key) * PDH + 8 * c) * 2), buf + 1024 * j);
-    } else if (j < 24) {
-      const int jj = j - 16, r = 8 * jj + (lane >> 3), c = kr_slot(r, lane & 7);
-      const int key = min(k0 + r, len - 1);
-      pa_dma(kr, (uint32_t)(((start + key) * PDR + 8 * c) * 2), buf + KC_BYTES + 1024 * jj);
-    } else {
-      const int jj = j - 24, r = 4 * jj + (lane >> 4), c = (lane & 15) ^ v_swz(r);
-      const int key = min(k0 + r, len - 1);
-      pa_dma(vc_h, (uint32_t)(((start + key) * PDH + 8 * c) * 2), buf + KC_BYTES + KR_BYTES + 1024 * jj);
-    }
+    for (int n = 0; n < 4; ++n) pa_dma(kcb + 16 * n * PDH * 2, to.kc, lb + 4096 * n);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) pa_dma(krb + 32 * n * PDR * 2, to.kr, lb + KC_BYTES + 4096 * n);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) pa_dma(vb + 16 * n * PDH * 2, to.v, lb + KC_BYTES + KR_BYTES + 4096 * n);
+    return;
+  }
+  const uint32_t lb = buf + 1024 * wave;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int r = 4 * (wave + 4 * n) + (lane >> 4), c = kc_slot(r, lane & 15);
+    const int key = min(k0 + r, len - 1);
+    pa_dma(kc_h, (uint32_t)(((start + key) * PDH + 8 * c) * 2), lb + 4096 * n);
+  }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int r = 8 * (wave + 4 * n) + (lane >> 3), c = kr_slot(r, lane & 7);
+    const int key = min(k0 + r, len - 1);
+    pa_dma(kr, (uint32_t)(((start + key) * PDR + 8 * c) * 2), lb + KC_BYTES + 4096 * n);
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int r = 4 * (wave + 4 * n) + (lane >> 4), c = (lane & 15) ^ v_swz(r);
+    const int key = min(k0 + r, len - 1);
+    pa_dma(vc_h, (uint32_t)(((start + key) * PDH + 8 * c) * 2), lb + KC_BYTES + KR_BYTES + 4096 * n);
   }
 }
 
@@ -114,120 +153,169 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
   lu8* lds = (lu8*)lds_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, i16 = lane & 15;
+  const int l32 = lane & 31, hw = lane >> 5;  // 32x32 MFMA lane layout: row/column l32, k-half hw
   const int b = blockIdx.y, h = blockIdx.z;
   const int start = a.cu[b], len = a.cu[b + 1] - start;
   const int qt = a.qtiles - 1 - (int)blockIdx.x;  // the longest (last) query tiles first
   const int q0 = qt * BQ;
   if (q0 >= len) return;
-  const int ntiles = qt + 1;  // causal: keys 0 .. q0 + 63
+  const int ntiles = (min(len, q0 + BQ) - 1) / BKT + 1;  // causal: keys up to the block's last query
   const bf16_t* kc_h = a.kc + (size_t)h * a.n_tok * PDH;
   const bf16_t* vc_h = a.vc + (size_t)h * a.n_tok * PDH;
   const uint32_t ring = (uint32_t)(uintptr_t)lds;
 
-  // Q^T fragments (B operand): query row q0 + 16 wave + i16 (clamped: rows
-  // past the sequence are computed and never stored), k = 32 ks + 8 g.
-  const int qrow = q0 + 16 * wave + i16;
-  bf16x8 qf[6];
+  // Q^T fragments (B operand): query row q0 + 32 wave + l32 (clamped: rows
+  // past the sequence are computed and never stored), k = 16 ks + 8 hw.
+  const int wq0 = q0 + 32 * wave;  // this wave's first query
+  const int qrow = wq0 + l32;
+  bf16x8 qf[12];
   {
-    const bf16_t* qp = a.q + ((size_t)h * a.n_tok + start + min(qrow, len - 1)) * PDQK + 8 * g;
+    const bf16_t* qp = a.q + ((size_t)h * a.n_tok + start + min(qrow, len - 1)) * PDQK + 8 * hw;
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) qf[ks] = *(const bf16x8*)(qp + 32 * ks);
+    for (int ks = 0; ks < 12; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
   }
   wait_vmcnt<0>();  // the compiler's loads are done before the copies go out
-  issue_tile(kc_h, vc_h, a.kr, start, len, 0, ring, wave, lane);
-  if (ntiles > 1) issue_tile(kc_h, vc_h, a.kr, start, len, 1, ring + STAGE, wave, lane);
+  const TileOffsets to = tile_offsets(wave, lane);
+  issue_tile(kc_h, vc_h, a.kr, start, len, 0, ring, wave, lane, to);
+  if (ntiles > 1) issue_tile(kc_h, vc_h, a.kr, start, len, 1, ring + STAGE, wave, lane, to);
 
-  f32x4 o[8];
+  f32x16 o[4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4{};
-  float m = -INFINITY, l = 0.0f;  // running maximum (all of the lane's row) and this lane's partial sum
-  // V^T transposing reads: lane (e, qq) of group g addresses key row 4g + e
-  // (+16 for the second read), channels 16 db + 4 qq .. +3
-  const int e = i16 >> 2, qq = i16 & 3;
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.0f;  // row maximum in use (log2 domain) and this lane's partial sum
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // LDS byte addresses of the lane's reads in stage 0 (the stage, the key
+  // block and the key step become instruction offsets):
+  //  K: k-step ks (16-wide slice 16 ks .. of the 192-wide key row, this
+  //     lane's half 8 hw ..) of key row l32;
+  //  V^T: 16-lane group G = lane/16 covers channels 32 db + 16 (G & 1) ..
+  //     +15 for k-half G/2 (= hw); lane (e, qq) of the group addresses key
+  //     row 4 hw + e (+ 16 kk, + 8), channels +4 qq .. +3.
+  uint32_t ka[12], va[4];
+  {
+    const uint32_t base = (uint32_t)(uintptr_t)lds;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = base + l32 * 256 + 16 * kc_slot(l32, 2 * ks + hw);
+#pragma unroll
+    for (int ks = 8; ks < 12; ++ks) ka[ks] = base + KC_BYTES + l32 * 128 + 16 * kr_slot(l32, 2 * (ks - 8) + hw);
+    const int e = (lane & 15) >> 2, qq = lane & 3, gsub = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      va[db] = base + KC_BYTES + KR_BYTES + (4 * hw + e) * 256 + 16 * ((4 * db + 2 * gsub + (qq >> 1)) ^ v_swz(e)) +
+               8 * (qq & 1);
+  }
+
+  // One key tile kt in stage buffer STG (compile-time, so every LDS offset is
+  // an immediate).
+  auto tile = [&](auto stg, int kt) {
+    constexpr int STG = decltype(stg)::value;
     if (kt == 0 && ntiles > 1) wait_vmcnt<10>();  // tile 1 may stay in flight
     else wait_vmcnt<0>();
     ring_barrier();  // tile kt is in; every wave is done with tile kt-1, whose buffer takes tile kt+1
-    if (kt >= 1 && kt + 1 < ntiles) issue_tile(kc_h, vc_h, a.kr, start, len, kt + 1, ring + ((kt + 1) & 1) * STAGE, wave, lane);
-    const lu8* st = lds + (kt & 1) * STAGE;
+    if (kt >= 1 && kt + 1 < ntiles)
+      issue_tile(kc_h, vc_h, a.kr, start, len, kt + 1, ring + (1 - STG) * STAGE, wave, lane, to);
+    const int k0 = kt * BKT;
+    if (k0 > wq0 + 31) return;  // every key of the tile is after every query of this wave
 
-    // S^T blocks: keys 16 nb + 4g + r of this lane's query i16
-    f32x4 s[4];
+    // S^T blocks: lane holds keys 32 kb + 8 j + 4 hw + i (VGPR 4j + i) of
+    // query l32.  The two key blocks alternate (two independent chains) and
+    // the K fragments are read four MFMAs ahead.
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      constexpr int D = 4;
+      auto rd = [&](int t) -> bf16x8 {
+        const int ks = t >> 1, kb = t & 1;
+        const uint32_t off = STG * STAGE + (ks < 8 ? kb * 8192 : kb * 4096);
+        return *(const lbf16x8*)(ka[ks] + off);
+      };
+      bf16x8 kf[D];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int r = 16 * nb + i16;
-      f32x4 acc = f32x4{};
+      for (int t = 0; t < D; ++t) kf[t] = rd(t);
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
-        const lu8* p = ks < 4 ? st + r * 256 + 16 * kc_slot(r, 4 * ks + g)
-                              : st + KC_BYTES + r * 128 + 16 * kr_slot(r, 4 * (ks - 4) + g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const lbf16x8*)p, qf[ks], acc, 0, 0, 0);
+      for (int t = 0; t < 24; ++t) {
+        s[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % D], qf[t >> 1], s[t & 1], 0, 0, 0);
+        if (t + D < 24) kf[t % D] = rd(t + D);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads D steps ahead
       }
-      s[nb] = acc;
     }
-    if (kt == qt) {  // the diagonal tile: keys after the query are masked
+    if (k0 + BKT - 1 > wq0) {  // some key of the tile is after some query of the wave
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (q0 + 16 * nb + 4 * g + r > qrow) s[nb][r] = -INFINITY;
+        for (int v = 0; v < 16; ++v)
+          if (k0 + 32 * kb + 8 * (v >> 2) + 4 * hw + (v & 3) > qrow) s[kb][v] = -INFINITY;
     }
-    // online softmax
-    float mt = vmax3(vmax3(s[0][0], s[0][1], s[0][2]), vmax3(s[0][3], s[1][0], s[1][1]), vmax3(s[1][2], s[1][3], s[2][0]));
-    mt = vmax3(mt, vmax3(s[2][1], s[2][2], s[2][3]), vmax3(s[3][0], s[3][1], vmax3(s[3][2], s[3][3], s[3][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    // Online softmax with a lazily raised maximum: p = 2^(s - m) with the m
+    // in use, which moves (and O and the sum are rescaled) only when some
+    // score exceeds it by more than 2^8; every p stays below 256, and the
+    // result o / l is the same for any m.
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; v += 4) mt = vmax3(mt, vmax3(s[kb][v], s[kb][v + 1], s[kb][v + 2]), s[kb][v + 3]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);  // finite: every query sees key 0 in tile 0
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
+    if (__any(mt > m + 8.0f)) {  // tile 0 always: m is -inf and every query sees key 0
+      const float mn = mt > m + 8.0f ? mt : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      m = mn;
+    }
     float ls = 0.0f;
-    bf16x8 pb[2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[nb][r] - mn);
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][v] - m);
+        s[kb][v] = p;
         ls += p;
-        pb[nb >> 1][4 * (nb & 1) + r] = (bf16_t)p;
       }
-    l = l * alpha + ls;
+    l += ls;
+    // O^T += V^T P^T, k-step kk = keys 16 kk .. +15 of the tile: half-wave hw
+    // holds keys 16kk + 4hw + 0..3 (VGPRs 4j0..) and 16kk + 8 + 4hw + 0..3
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] *= alpha;
-    // O^T += V^T P^T: k-step kk covers keys 32 kk .. +31 in the order of the
-    // S^T registers (keys 32kk + 4g + 0..3, then 32kk + 16 + 4g + 0..3)
-    const lu8* vt = st + KC_BYTES + KR_BYTES;
+    for (int kk = 0; kk < 4; ++kk) {
+      const int kb = kk >> 1, j0 = 2 * (kk & 1);
+      bf16x8 pb;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int r1 = 32 * kk + 4 * g + e, r2 = r1 + 16;
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = (bf16_t)s[kb][4 * j0 + i];
+        pb[4 + i] = (bf16_t)s[kb][4 * j0 + 4 + i];
+      }
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int c = 2 * db + (qq >> 1), half = qq & 1;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(vt + r1 * 256 + 16 * (c ^ v_swz(r1)) + 8 * half));
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(vt + r2 * 256 + 16 * (c ^ v_swz(r2)) + 8 * half));
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t off = STG * STAGE + kk * 4096;
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(va[db] + off));
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(va[db] + off + 2048));
         const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s8), pb[kk], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s8), pb, o[db], 0, 0, 0);
       }
     }
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < ntiles) tile(std::integral_constant<int, 1>{}, kt + 1);
   }
   wait_vmcnt<0>();  // nothing in flight into LDS when the block leaves
 
-  // O^T lane layout: channels 16 db + 4 g + r of query i16; the row's sum is
-  // spread over the four lanes i16 + 16 g'
-  float lt = l + __shfl_xor(l, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  // O^T lane layout: channels 32 db + 8 j + 4 hw + i (VGPR 4j + i) of query
+  // l32; the row's sum is split over the lanes l32 and l32 + 32
+  const float lt = l + __shfl_xor(l, 32, 64);
   if (qrow < len) {
     const float inv = 1.0f / lt;
-    bf16_t* op = a.out + ((size_t)(start + qrow) * PH + h) * PDH + 4 * g;
+    bf16_t* op = a.out + ((size_t)(start + qrow) * PH + h) * PDH + 4 * hw;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      bf16x4 v;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (bf16_t)(o[db][r] * inv);
-      *(bf16x4*)(op + 16 * db) = v;
-    }
-    if (a.lse && g == 0) a.lse[(size_t)(start + qrow) * PH + h] = (m + __log2f(lt)) * 0.6931471805599453f;
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (bf16_t)(o[db][4 * j + i] * inv);
+        *(bf16x4*)(op + 32 * db + 8 * j) = v;
+      }
+    if (a.lse && hw == 0) a.lse[(size_t)(start + qrow) * PH + h] = (m + __log2f(lt)) * 0.6931471805599453f;
   }
 }
 
