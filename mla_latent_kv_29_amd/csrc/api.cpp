@@ -1,6 +1,7 @@
 // C-ABI entry points of libmla.so: argument validation, split planning,
 // workspace layout and dispatch to the kernel launchers.  Nothing here
 // allocates device memory or synchronises.
+#include <algorithm>
 #include <stdlib.h>
 #include <string.h>
 #include "internal.hpp"
@@ -245,7 +246,8 @@ int prefill_common(PrefillPart part, const mla_dims* dims, int32_t act_dtype, co
   const PrefillLayout L = prefill_layout(*dims, n_tok);
   if (ws_bytes < L.total) return MLA_ERR_WORKSPACE;
   PrefillArgs a;
-  a.d = *dims; a.h = (const bf16_t*)h; a.n_tok = n_tok; a.n_seq = n_seq; a.max_seqlen = max_seqlen;
+  // no sequence is longer than all tokens together
+  a.d = *dims; a.h = (const bf16_t*)h; a.n_tok = n_tok; a.n_seq = n_seq; a.max_seqlen = std::min(max_seqlen, n_tok);
   a.cu_seqlens = cu_seqlens;
   a.W_DQ = (const bf16_t*)W_DQ; a.W_UQ = (const bf16_t*)W_UQ; a.W_UK = (const bf16_t*)W_UK;
   a.W_UV = (const bf16_t*)W_UV; a.W_DKV = (const bf16_t*)W_DKV; a.W_KR = (const bf16_t*)W_KR;

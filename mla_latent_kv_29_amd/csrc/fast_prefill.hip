@@ -10,6 +10,8 @@
 // softmax runs in the exp2 domain.
 //
 // Work item = (sequence, head, tile of 128 query rows); four waves of 32 rows.
+// All query tiles of one (sequence, head) run on one XCD together, so the K
+// and V tiles that they all stream come from that XCD's L2.
 // Per 64-key tile (keys up to the tile's last query):
 //   S^T[32 keys][32 queries] blocks = K . Q^T with v_mfma_f32_32x32x16_bf16:
 //     K fragments from LDS (192-wide rows: k^C of the head, then k^R), the
@@ -29,6 +31,7 @@
 // block, two blocks share a CU, i.e. two waves per SIMD.  The LDS layouts
 // (16-byte chunk q of row r at slot q ^ f(r)) spread the K fragment reads and
 // the transposing V reads over the banks.
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -79,7 +82,7 @@ struct PaArgs {
   const bf16_t* vc;  // [H][n_tok][128]
   const bf16_t* kr;  // [n_tok][64]
   const int32_t* cu; // [n_seq + 1]
-  int n_tok, qtiles;
+  int n_tok, qtiles, n_seq;
   bf16_t* out;       // [n_tok][H][128]
   float* lse;        // [n_tok][H] or null
 };
@@ -154,9 +157,16 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hw = lane >> 5;  // 32x32 MFMA lane layout: row/column l32, k-half hw
-  const int b = blockIdx.y, h = blockIdx.z;
+  // Work item w = (pair (head, sequence), query tile): workgroups reach the
+  // eight XCDs round-robin, so item w runs on XCD w / (G / 8) when block
+  // L = 8 (w mod G/8) + XCD.  All query tiles of a (head, sequence) then run
+  // on one XCD at about the same time and re-read its K and V tiles from
+  // that XCD's L2.  Within a pair the longest (last) query tiles go first.
+  const int G = (int)gridDim.x, per = G >> 3;  // G = qtiles * n_seq * 128, a multiple of 8
+  const int w = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+  const int pair = w / a.qtiles, b = pair % a.n_seq, h = pair / a.n_seq;
   const int start = a.cu[b], len = a.cu[b + 1] - start;
-  const int qt = a.qtiles - 1 - (int)blockIdx.x;  // the longest (last) query tiles first
+  const int qt = a.qtiles - 1 - (w - pair * a.qtiles);
   const int q0 = qt * BQ;
   if (q0 >= len) return;
   const int ntiles = (min(len, q0 + BQ) - 1) / BKT + 1;  // causal: keys up to the block's last query
@@ -329,13 +339,20 @@ bool prefill_supported(const mla_dims& d, int act) {
 hipError_t prefill_attention(const PrefillArgs& a) {
   const int qtiles = (a.max_seqlen + BQ - 1) / BQ;
   PaArgs pa{(const bf16_t*)(a.ws + a.L.q), (const bf16_t*)(a.ws + a.L.kc), (const bf16_t*)(a.ws + a.L.vc),
-            (const bf16_t*)(a.ws + a.L.kr), a.cu_seqlens, a.n_tok, qtiles, a.out, a.lse_out};
+            (const bf16_t*)(a.ws + a.L.kr), a.cu_seqlens, a.n_tok, qtiles, a.n_seq, a.out, a.lse_out};
   static bool attr_set = false;
   if (!attr_set) {
     MLA_TRY(hipFuncSetAttribute((const void*)&k_prefill_attn, hipFuncAttributeMaxDynamicSharedMemorySize, PA_LDS));
     attr_set = true;
   }
-  return launch(&k_prefill_attn, dim3(qtiles, a.n_seq, PH), dim3(256), PA_LDS, a.stream, pa);
+  // at most 2^30 workgroups a launch: sequences in chunks
+  const int chunk = std::max(1, (1 << 30) / (qtiles * PH));
+  for (int s0 = 0; s0 < a.n_seq; s0 += chunk) {
+    pa.cu = a.cu_seqlens + s0;
+    pa.n_seq = std::min(chunk, a.n_seq - s0);
+    MLA_TRY(launch(&k_prefill_attn, dim3(qtiles * pa.n_seq * PH), dim3(256), PA_LDS, a.stream, pa));
+  }
+  return hipSuccess;
 }
 
 hipError_t fast_prefill(const PrefillArgs& a) {
