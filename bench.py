@@ -54,7 +54,8 @@ def algorithmic(spec, dims, lengths):
 # figure measured with hardware counters is reported only while they are
 # unchanged since the measurement.
 ATTN_SOURCES = {"bf16": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
-                "fp8": ["fast_attn2.hip", "layout.hpp", "common.hpp"]}
+                "fp8": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
+                "prefill": ["fast_prefill.hip", "internal.hpp", "common.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
 
@@ -128,6 +129,22 @@ def prefill_algorithmic(dims, lengths):
     return attn, proj
 
 
+def copy_calibration(mib, dev):
+    """A plain elementwise copy of `mib` MiB (read once, written once), run
+    three times untimed: the known-size reference that scales the hardware
+    byte counters of a profiled run."""
+    if mib <= 0:
+        return
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_prefill(args, name):
     """Prefill workload: one step = mla_prefill_project + mla_prefill_attend
     over the packed sequences; the attention (the dominant kernel) is timed
@@ -170,6 +187,7 @@ def run_prefill(args, name):
         if e is not None:
             e[2].record(stream)
 
+    copy_calibration(args.copy_calibration, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -201,7 +219,7 @@ def run_prefill(args, name):
         "config": {"workload": name, "batch": int(spec["batch"]), "seq_len": int(spec["lengths"][1]),
                    "tokens": n},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved * 1e12 / MFMA_BF16_PEAK, "traffic": None,
+                     "frac": achieved * 1e12 / MFMA_BF16_PEAK, "traffic": measured_traffic(name, "prefill"),
                      "kernel": "k_prefill_attn (mla_prefill_attend)", "attn_ms_mean": float(np.mean(a_ms)),
                      "attn_flops": attn_flops},
         "step_roofline": {"t_bound_us": t_bound * 1e6, "frac": t_bound / (ms_per_step * 1e-3),
@@ -293,14 +311,7 @@ def main():
         if e is not None:
             e[3].record(stream)
 
-    if args.copy_calibration > 0:
-        n = args.copy_calibration * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration, dev)
 
     for i in range(args.warmup):
         step(i)
