@@ -57,6 +57,7 @@ ATTN_SOURCES = {"bf16": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
                 "fp8": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
                 "prefill": ["fast_prefill.hip", "internal.hpp", "common.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+MTP_ACCEPTANCE = 0.85  # second-token acceptance of MTP drafts, lower end of the pages' 85-90%
 
 
 def attn_source_sha(cache):
@@ -329,7 +330,9 @@ def main():
     alg = algorithmic(spec, dims, lengths)
 
     attn_s = float(np.mean(a_ms)) * 1e-3
-    if spec["cache"] == "fp8":
+    # the attention's roof is the larger of its byte time and its MFMA time
+    # (bf16 at one query row: bytes; fp8 or several query rows: MFMA)
+    if alg["attn_flops"] / MFMA_BF16_PEAK > alg["attn_bytes"] / HBM_PEAK:
         bound, achieved, peak, unit = "mfma", alg["attn_flops"] / attn_s / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", alg["attn_bytes"] / attn_s / 1e9, HBM_PEAK / 1e9, "GB/s"
@@ -361,6 +364,12 @@ def main():
                       "combine": float(np.median(c_ms))},
         "cache_build_s": build_s,
     }
+    if s_q > 1:
+        # the verify step checks s_q - 1 drafts; expected emitted tokens at the
+        # pages' 85% acceptance
+        tps = L.mla_mtp_tokens_per_step(MTP_ACCEPTANCE, s_q - 1)
+        res["mtp_verify"] = {"depth": s_q - 1, "acceptance": MTP_ACCEPTANCE, "tokens_per_step": tps,
+                             "generated_tokens_per_s": spec["batch"] * tps / (ms_per_step * 1e-3)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, dims, W, gen_h, lengths, args.cpu_budget)
     print(json.dumps(res))

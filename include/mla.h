@@ -143,6 +143,17 @@ MLA_API int mla_cache_write(const mla_dims* dims, int32_t act_dtype, const void*
 MLA_API int32_t mla_default_splits(const mla_dims* dims, int32_t batch, int32_t s_q,
                            int32_t max_pages);
 
+/* Speculative verify with multi-token prediction ("Читаем техотчёт
+ * DeepSeek-V3 вместе", §2.2 Multi-Token Prediction, and the tokens_per_step
+ * exercise of its practice part): a decode step with s_q = 1 + depth query
+ * rows per sequence checks `depth` chained drafts, and the k-th draft counts
+ * only if every earlier one was accepted, each with probability
+ * `acceptance`.  Returns the expected number of tokens such a step emits,
+ * 1 + acceptance + ... + acceptance^depth; NaN if acceptance is outside
+ * [0, 1] or depth is outside 0..7 (s_q is at most 8).  Host arithmetic only:
+ * no device, no stream.                                                      */
+MLA_API double mla_mtp_tokens_per_step(double acceptance, int32_t depth);
+
 /* Workspace bytes needed by mla_decode/mla_combine for these sizes
  * (num_splits >= 1; 0 for invalid arguments).                               */
 MLA_API size_t mla_workspace_bytes(const mla_dims* dims, int32_t act_dtype,

@@ -18,7 +18,7 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
-           "mla_status_str", "mla_last_hip_error", "mla_version")
+           "mla_mtp_tokens_per_step", "mla_status_str", "mla_last_hip_error", "mla_version")
 
 
 class mla_dims(ctypes.Structure):
@@ -66,6 +66,7 @@ def _load():
         "mla_prefill": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_prefill_project": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_prefill_attend": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
+        "mla_mtp_tokens_per_step": (ctypes.c_double, [ctypes.c_double, I32]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
         "mla_last_hip_error": (ctypes.c_char_p, []),
@@ -123,6 +124,10 @@ def _check(fn, st):
 
 def mla_page_bytes(dims, cache_dtype):
     return int(_lib.mla_page_bytes(ctypes.byref(dims), int(cache_dtype)))
+
+
+def mla_mtp_tokens_per_step(acceptance, depth):
+    return float(_lib.mla_mtp_tokens_per_step(float(acceptance), int(depth)))
 
 
 def mla_default_splits(dims, batch, s_q, max_pages):

@@ -2,6 +2,7 @@
 // workspace layout and dispatch to the kernel launchers.  Nothing here
 // allocates device memory or synchronises.
 #include <algorithm>
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 #include "internal.hpp"
@@ -275,6 +276,14 @@ extern "C" {
 int mla_prefill(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_ALL, MLA_PREFILL_PASS); }
 int mla_prefill_project(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_PROJECT, MLA_PREFILL_PASS); }
 int mla_prefill_attend(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_ATTEND, MLA_PREFILL_PASS); }
+
+double mla_mtp_tokens_per_step(double acceptance, int32_t depth) {
+  if (!(acceptance >= 0.0 && acceptance <= 1.0) || depth < 0 || depth > MAX_S_Q - 1) return NAN;
+  // Horner form of 1 + a + ... + a^depth: the draft chain's survival probabilities
+  double t = 1.0;
+  for (int k = 0; k < depth; ++k) t = 1.0 + acceptance * t;
+  return t;
+}
 
 const char* mla_status_str(int s) {
   switch (s) {

@@ -21,7 +21,7 @@ TINY_DIMS = dict(d_model=256, n_heads=4, d_head=32, d_rope=16, d_c=64, d_cq=96, 
 V3_DIMS = dict(d_model=7168, n_heads=128, d_head=128, d_rope=64, d_c=512, d_cq=1536, page_size=64,
                rope_theta=10000.0)
 
-# The five decode workloads: a tiny float32 one, then DeepSeek-V3 shapes.
+# The decode workloads: a tiny float32 one, then DeepSeek-V3 shapes.
 WORKLOADS = {
     "tiny_f32_b2_l256": dict(index=0, dims=TINY_DIMS, act="f32", cache="f32", batch=2, s_q=1,
                              lengths=("fixed", 256), table="inorder", sigma=0.02),
@@ -33,6 +33,9 @@ WORKLOADS = {
                              lengths=("fixed", 131072), table="inorder", sigma=0.006),
     "v3_fp8_b128_l8192_sq2": dict(index=4, dims=V3_DIMS, act="bf16", cache="fp8", batch=128, s_q=2,
                                   lengths=("fixed", 8192), table="inorder", sigma=0.006),
+    # speculative verify of three chained MTP drafts (s_q = 1 + 3)
+    "v3_bf16_b64_l4096_sq4": dict(index=6, dims=V3_DIMS, act="bf16", cache="bf16", batch=64, s_q=4,
+                                  lengths=("fixed", 4096), table="inorder", sigma=0.006),
 }
 
 # Prefill of fresh sequences (mla_prefill): batch sequences of the given lengths, packed.

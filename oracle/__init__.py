@@ -16,6 +16,8 @@ Sources (cited by page title and section, never by file position):
 * "Báo cáo Kỹ thuật DeepSeek-V3" (xyznot.com paper summary), "Phương pháp",
   item 1 "Multi-head Latent Attention (MLA)" -- the same equations with the
   compressed query c^Q.
+* The same lesson, section 2.2 "Multi-Token Prediction" and the
+  `tokens_per_step` docstring of its practice part -- the verify-step model.
 
 Parity status per function is listed in each module header.
 """
@@ -25,6 +27,7 @@ from .fp8 import (e4m3_decode, e4m3_encode, e4m3_values, e5m2_decode,
                   quantize_tiles, dequantize_tiles)
 from .sizes import (cache_values_per_token, mha_values_per_token, cache_bytes,
                     mla_params_per_layer)
+from .mtp import tokens_per_step
 
 __all__ = [
     "rope", "kv_latents", "queries", "attend_nonabsorbed", "attend_absorbed",
@@ -32,5 +35,5 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "e4m3_values", "e5m2_decode",
     "quantize_tiles", "dequantize_tiles",
     "cache_values_per_token", "mha_values_per_token", "cache_bytes",
-    "mla_params_per_layer",
+    "mla_params_per_layer", "tokens_per_step",
 ]

@@ -159,3 +159,15 @@ def test_prefill_workspace_and_argument_errors():
     assert call(tau=0.0) == L.MLA_ERR_DIMS
     assert call(act=m.MLA_F32) == L.MLA_ERR_UNSUPPORTED             # bf16 activations only
     assert call(dims=m.make_dims(inputs.TINY_DIMS)) == L.MLA_ERR_UNSUPPORTED
+
+
+def test_mtp_tokens_per_step_matches_oracle():
+    """Host arithmetic of the C ABI against the oracle's enumeration; invalid
+    arguments give NaN."""
+    import math
+    import oracle
+    for depth in range(0, 8):
+        for a in (0.0, 0.5, 0.85, 0.9, 1.0):
+            assert abs(m.mla_mtp_tokens_per_step(a, depth) - oracle.tokens_per_step(a, depth)) < 1e-12
+    for a, depth in ((-0.1, 1), (1.1, 1), (float("nan"), 1), (0.5, -1), (0.5, 8)):
+        assert math.isnan(m.mla_mtp_tokens_per_step(a, depth))

@@ -59,7 +59,7 @@ def test_bf16_append_rows_match_oracle_latents():
         assert max_abs(rows, ref) <= 1e-2 * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("s_q,kappa,splits", [(2, 1.0, 2), (2, 56.0, 3), (1, 56.0, 1)])
+@pytest.mark.parametrize("s_q,kappa,splits", [(2, 1.0, 2), (2, 56.0, 3), (1, 56.0, 1), (4, 56.0, 2)])
 def test_fp8_decode_parity(s_q, kappa, splits):
     case = Case(V3, "bf16", "fp8", [300, 65, 128], s_q=s_q, table="shuffled", wl=4, num_splits=splits)
     tau = tau_of(V3) * kappa

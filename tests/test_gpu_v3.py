@@ -63,6 +63,26 @@ def test_v3_bf16_causal_two_queries(s_q):
     check_all(case, out, lse, tau, TOL_BF16)
 
 
+@pytest.mark.parametrize("s_q", [3, 4, 8])
+def test_v3_bf16_deeper_mtp_verify(s_q):
+    """Verify of s_q - 1 chained drafts: s_q causal query rows per sequence.
+    The last sequence holds exactly s_q tokens, so its first query sees one."""
+    case = Case(V3, "bf16", "bf16", [200, 65, s_q], s_q=s_q, table="shuffled", wl=6, num_splits=2)
+    tau = tau_of(V3) * 56.0
+    out, lse, _ = case.run(tau)
+    check_all(case, out, lse, tau, TOL_BF16)
+
+
+def test_v3_bf16_verify_more_than_64_rows():
+    """9 sequences x 8 query rows = 72 rows: the query projection and the
+    combine take their many-row kernels; default split plan."""
+    lengths = [70 + 37 * i for i in range(9)]
+    case = Case(V3, "bf16", "bf16", lengths, s_q=8, table="shuffled", wl=6)
+    tau = tau_of(V3) * 20.0
+    out, lse, _ = case.run(tau)
+    check_all(case, out, lse, tau, TOL_BF16, heads=[0, 63, 127])
+
+
 def test_v3_planted_latents_sharp():
     """Cache written directly (std 0.5, the scale of W^DKV h at these
     weights), queries from h; sharpened softmax."""

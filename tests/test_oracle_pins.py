@@ -346,3 +346,38 @@ def test_brute_force_loops_tiny():
                for t in range(L)) for a in range(dh)]
     np.testing.assert_allclose(o[0, i], out, rtol=1e-11, atol=1e-13)
     assert abs(lse[0, i] - (mx + math.log(z))) < 1e-12
+
+
+# ---------------------------------------------------------------- MTP verify model
+
+def test_tokens_per_step_matches_printed_numbers():
+    """Depth-1 MTP at 85% and 90% acceptance gives the 1.85 and 1.9 tokens per
+    step that the lesson prints (section 2.2, quiz item 5, summary)."""
+    g = json.load(open(os.path.join(GOLD, "mtp_tokens_per_step.json")))
+    for row in g["printed"]:
+        assert abs(oracle.tokens_per_step(row["acceptance"], row["depth"]) - row["tokens_per_step"]) < 1e-12
+
+
+@pytest.mark.parametrize("depth", [0, 1, 2, 3, 7])
+def test_tokens_per_step_limits_and_geometric_series(depth):
+    """Acceptance 0: only the main model's token; acceptance 1: every draft
+    counts; in between, the k-th draft survives with probability a^k, so the
+    mean is the geometric series 1 + a + ... + a^depth."""
+    assert oracle.tokens_per_step(0.0, depth) == 1.0
+    assert oracle.tokens_per_step(1.0, depth) == 1.0 + depth
+    for a in (0.3, 0.85, 0.97):
+        series = sum(a ** k for k in range(depth + 1))
+        assert abs(oracle.tokens_per_step(a, depth) - series) < 1e-12
+
+
+def test_tokens_per_step_by_simulation():
+    """A Monte Carlo run of the draft chain (accept each draft with
+    probability a, stop at the first rejection) agrees within 4 standard
+    errors."""
+    rng = np.random.default_rng(7)
+    a, depth, n = 0.8, 4, 200000
+    acc = rng.random((n, depth)) < a
+    first_reject = np.where(acc.all(1), depth, np.argmin(acc, 1))
+    emitted = 1 + first_reject
+    se = emitted.std() / np.sqrt(n)
+    assert abs(emitted.mean() - oracle.tokens_per_step(a, depth)) < 4 * se
