@@ -22,7 +22,7 @@ Sources (cited by page title and section, never by file position):
 Parity status per function is listed in each module header.
 """
 from .mla import (rope, kv_latents, queries, attend_nonabsorbed, attend_absorbed,
-                  decode_from_latents, decode_from_h, softmax_lse)
+                  decode_from_latents, decode_from_h, softmax_lse, output_projection)
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_values, e5m2_decode,
                   quantize_tiles, dequantize_tiles)
 from .sizes import (cache_values_per_token, mha_values_per_token, cache_bytes,
@@ -31,7 +31,7 @@ from .mtp import tokens_per_step
 
 __all__ = [
     "rope", "kv_latents", "queries", "attend_nonabsorbed", "attend_absorbed",
-    "decode_from_latents", "decode_from_h", "softmax_lse",
+    "decode_from_latents", "decode_from_h", "softmax_lse", "output_projection",
     "e4m3_decode", "e4m3_encode", "e4m3_values", "e5m2_decode",
     "quantize_tiles", "dequantize_tiles",
     "cache_values_per_token", "mha_values_per_token", "cache_bytes",

@@ -14,6 +14,8 @@ primitive used):
   v^C = W^UV c^KV, built EXPLICITLY per head (§2.1.1) -- no absorption here.
 * Scaled softmax attention over the visible tokens (the pages print the score
   q^T k but not the softmax; the plain reading of "multi-head attention").
+* Output projection W^O of the concatenated heads (the W_O shape of the
+  attention_params docstring; its result is the u_t of §2.1.2).
 
 `attend_absorbed` is a second, independent route through the same maths (the
 absorption of W^UK into the query from §2.1.1 Question 2, and W^UV applied after
@@ -195,3 +197,19 @@ def decode_from_h(h, W, dims, seqlen, s_q, tau, heads=None, chunk=4096):
     hq = np.asarray(h[seqlen - s_q:seqlen], dtype=np.float64)
     return decode_from_latents(c, kr, hq, W.get("W_DQ"), W["W_UQ"], W["W_UK"],
                                W["W_UV"], dims, seqlen, s_q, tau, heads)
+
+
+def output_projection(o, W_O):
+    """Attention output of the layer for rows of per-head outputs.
+
+    o has shape [R, H, d_head]; W_O is stored [out, in] = [d_model,
+    H * d_head] (the practice section's attention_params docstring gives W_O
+    as heads*d_head x d).  The heads of a row are concatenated in head order,
+    d_head innermost, and projected: y_r = W^O [o_{r,1}; ...; o_{r,H}]
+    (shape [R, d_model]).  This is the u_t that the MoE layer of §2.1.2
+    takes as input; no residual or norm is printed, so none is added.
+    """
+    o = np.asarray(o, dtype=np.float64)
+    R = o.shape[0]
+    cat = o.reshape(R, -1)
+    return cat @ np.asarray(W_O, dtype=np.float64).T

@@ -381,3 +381,30 @@ def test_tokens_per_step_by_simulation():
     emitted = 1 + first_reject
     se = emitted.std() / np.sqrt(n)
     assert abs(emitted.mean() - oracle.tokens_per_step(a, depth)) < 4 * se
+
+
+# ---------------------------------------------------------------- W^O
+
+def test_output_projection_brute_force_and_head_order():
+    """y[r][n] = sum over heads i and channels a of W_O[n][i*d_head + a] *
+    o[r][i][a], by explicit loops; a W_O that picks one head's block returns
+    exactly that head (pins the head-major concatenation); an identity W_O
+    (d_model = H * d_head) returns the concatenated heads."""
+    rng = np.random.default_rng(11)
+    R, H, dh, dm = 3, 4, 5, 7
+    o = rng.normal(size=(R, H, dh))
+    W = rng.normal(size=(dm, H * dh))
+    y = oracle.output_projection(o, W)
+    assert y.shape == (R, dm)
+    for r in range(R):
+        for n in range(dm):
+            ref = 0.0
+            for i in range(H):
+                for a in range(dh):
+                    ref += W[n][i * dh + a] * o[r][i][a]
+            assert abs(y[r][n] - ref) < 1e-12
+    for i in range(H):
+        P = np.zeros((dh, H * dh))
+        P[:, i * dh:(i + 1) * dh] = np.eye(dh)
+        np.testing.assert_array_equal(oracle.output_projection(o, P), o[:, i, :])
+    np.testing.assert_array_equal(oracle.output_projection(o, np.eye(H * dh)), o.reshape(R, H * dh))
