@@ -146,6 +146,116 @@ def copy_calibration(mib, dev):
     del src, dst
 
 
+def run_layers(args, name):
+    """Layer-stack workload: one step = for every layer, mla_decode_query +
+    mla_decode_attend + mla_combine + mla_output_project, each layer with its
+    own paged cache (built from the same hidden states through its own W^DKV,
+    W^KR) and its own weights.  Every layer takes the same seeded query rows:
+    no norm, residual or MoE sits between the layers on this path, so the
+    values feeding each layer are synthetic either way."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_29_amd import inputs
+    from mla_latent_kv_29_amd import _lib as L
+    from mla_latent_kv_29_amd.session import DecodeSession
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    spec = inputs.LAYER_WORKLOADS[name]
+    dims, wl, n_layers = spec["dims"], spec["index"], spec["layers"]
+    tdt = inputs.torch_dtype(spec["act"])
+    lengths = inputs.seqlens(spec["lengths"], spec["batch"], 0, wl)
+    table, pool = inputs.block_table(lengths, dims["page_size"], spec["table"], 0, wl)
+    gen_h = lambda b, t0, t1: inputs.hidden(dims, b, t0, t1, tdt, dev, 0, wl)
+    s_q, batch = spec["s_q"], spec["batch"]
+    tau = 1.0 / math.sqrt(dims["d_head"] + dims["d_rope"])
+    layers = []
+    t0 = time.perf_counter()
+    for li in range(n_layers):
+        W = inputs.weights(dims, spec["sigma"], tdt, dev, li, wl)
+        W["W_O"] = inputs.out_weight(dims, spec["sigma"], tdt, dev, li, wl)
+        sess = DecodeSession(dims, spec["act"], spec["cache"], lengths, table, pool, s_q, 0, dev)
+        sess.build_from_h(gen_h, W, chunk=32768)
+        del W["W_DKV"], W["W_KR"]  # cache projections: not part of a decode step
+        layers.append((sess, W))
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    hq = torch.cat([gen_h(b, int(Lb) - s_q, int(Lb)) for b, Lb in enumerate(lengths)], 0).contiguous()
+    R = batch * s_q
+    y = torch.empty((R, dims["d_model"]), dtype=tdt, device=dev)
+    c = layers[0][0].cdims
+    act = layers[0][0].act
+    owsb = L.mla_output_project_workspace_bytes(c, act, R)
+    ows = torch.empty(max(owsb, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def layer(sess, W, e=None):
+        dargs = (c, act, hq, batch, s_q, W["W_DQ"], W["W_UQ"], W["W_UK"], sess.cache, sess.block_table,
+                 sess.max_pages, sess.seqlens, tau, sess.num_splits, sess.ws, sess.ws_bytes, sp)
+        L.mla_decode_query(*dargs)
+        if e is not None:
+            e[0].record(stream)
+        L.mla_decode_attend(*dargs)
+        if e is not None:
+            e[1].record(stream)
+        L.mla_combine(c, act, batch, s_q, sess.ws, sess.ws_bytes, W["W_UV"], sess.out, sess.lse, sp)
+        L.mla_output_project(c, act, R, sess.out, W["W_O"], y, ows, owsb, sp)
+
+    def step(ev=None):
+        for li, (sess, W) in enumerate(layers):
+            layer(sess, W, None if ev is None else ev[li])
+
+    sampled = set(range(0, args.steps, max(1, args.steps // 4)))
+    evs = {i: [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in layers] for i in sampled}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    a_ms = [e[0].elapsed_time(e[1]) for i in sampled for e in evs[i]]
+    ms_per_step = wall / args.steps * 1e3
+    alg = algorithmic(spec, dims, lengths)
+    attn_s = float(np.mean(a_ms)) * 1e-3
+    tokens = float(np.sum(lengths))
+    wo_bytes = 2 * dims["d_model"] * dims["n_heads"] * dims["d_head"]
+    tok_bytes = (dims["d_c"] + dims["d_rope"]) * 2
+    # one layer: the decode step's bytes and flops plus W^O (weights, y rows)
+    layer_bytes = alg["step_bytes"] + wo_bytes + 2 * R * dims["d_model"]
+    layer_flops = alg["step_flops"] + 2 * R * dims["d_model"] * dims["n_heads"] * dims["d_head"]
+    t_bound = n_layers * max(layer_bytes / HBM_PEAK, layer_flops / MFMA_BF16_PEAK)
+    res = {
+        "metric": f"MLA decode through {n_layers} attention layers (W^O included): cached token-layers/s",
+        "value": tokens * n_layers / (ms_per_step * 1e-3),
+        "unit": "cached-token-layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec["act"],
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,sigma^2) weights per layer at DeepSeek-V3 MLA shapes)",
+        "config": {"workload": name, "batch": batch, "seq_len": spec["lengths"][1], "s_q": s_q,
+                   "layers": n_layers, "cache": spec["cache"], "splits": layers[0][0].num_splits},
+        "roofline": {"bound": "hbm", "achieved": alg["attn_bytes"] / attn_s / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": alg["attn_bytes"] / attn_s / HBM_PEAK, "traffic": None,
+                     "kernel": "k_attn_v3b<false> (mla_decode_attend), every layer", "attn_ms_mean": attn_s * 1e3},
+        "step_roofline": {"t_bound_us": t_bound * 1e6, "frac": t_bound / (ms_per_step * 1e-3),
+                          "layer_bytes": layer_bytes, "layer_flops": layer_flops},
+        "sequences_tokens_per_s": batch * s_q / (ms_per_step * 1e-3),
+        "ms_per_layer": ms_per_step / n_layers,
+        "cache_bytes_per_token_all_layers": n_layers * tok_bytes,
+        "cache_bytes_total": int(tokens) * n_layers * tok_bytes,
+        "cache_build_s": build_s,
+    }
+    print(json.dumps(res))
+
+
 def run_prefill(args, name):
     """Prefill workload: one step = mla_prefill_project + mla_prefill_attend
     over the packed sequences; the attention (the dominant kernel) is timed
@@ -253,6 +363,9 @@ def main():
     from mla_latent_kv_29_amd import inputs
     if args.workload in inputs.PREFILL_WORKLOADS:
         run_prefill(args, args.workload)
+        return
+    if args.workload in inputs.LAYER_WORKLOADS:
+        run_layers(args, args.workload)
         return
 
     import numpy as np

@@ -143,6 +143,28 @@ MLA_API int mla_cache_write(const mla_dims* dims, int32_t act_dtype, const void*
 MLA_API int32_t mla_default_splits(const mla_dims* dims, int32_t batch, int32_t s_q,
                            int32_t max_pages);
 
+/* Output projection of the attention layer: for each of `rows` rows,
+ *     y_r = W^O [o_{r,1}; o_{r,2}; ...; o_{r,H}]
+ * (the W_O of the attention_params docstring of "Читаем техотчёт
+ * DeepSeek-V3 вместе", practice part, heads*d_head x d; its result is the
+ * u_t that the MoE layer of §2.1.2 takes as input; no residual or norm).
+ *   o   [rows, n_heads*d_head] (act_dtype), heads concatenated in head order
+ *       with d_head innermost: exactly the out tensor of mla_combine
+ *       [batch, s_q, H, d_head] with rows = batch*s_q.
+ *   W_O [d_model, n_heads*d_head] (act_dtype, stored [out, in]).
+ *   y   [rows, d_model] (act_dtype), written.
+ *   ws  device workspace of mla_output_project_workspace_bytes() bytes
+ *       (fp32 partial sums; may be NULL when that is 0), 16-byte aligned.
+ * act_dtype MLA_F32 or MLA_BF16; rows in 0..131072 (0 does nothing).  All
+ * device pointers 16-byte aligned and caller-owned.  Errors: MLA_ERR_NULL,
+ * MLA_ERR_DTYPE, MLA_ERR_DIMS, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP;
+ * nothing is enqueued on an error other than MLA_ERR_HIP.                   */
+MLA_API size_t mla_output_project_workspace_bytes(const mla_dims* dims, int32_t act_dtype,
+                                                  int32_t rows);
+MLA_API int mla_output_project(const mla_dims* dims, int32_t act_dtype, int32_t rows,
+                               const void* o, const void* W_O, void* y, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* Speculative verify with multi-token prediction ("Читаем техотчёт
  * DeepSeek-V3 вместе", §2.2 Multi-Token Prediction, and the tokens_per_step
  * exercise of its practice part): a decode step with s_q = 1 + depth query

@@ -18,7 +18,8 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
-           "mla_mtp_tokens_per_step", "mla_status_str", "mla_last_hip_error", "mla_version")
+           "mla_output_project_workspace_bytes", "mla_output_project", "mla_mtp_tokens_per_step",
+           "mla_status_str", "mla_last_hip_error", "mla_version")
 
 
 class mla_dims(ctypes.Structure):
@@ -66,6 +67,8 @@ def _load():
         "mla_prefill": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_prefill_project": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_prefill_attend": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
+        "mla_output_project_workspace_bytes": (SZ, [D, I32, I32]),
+        "mla_output_project": (ctypes.c_int, [D, I32, I32, P, P, P, P, SZ, P]),
         "mla_mtp_tokens_per_step": (ctypes.c_double, [ctypes.c_double, I32]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
@@ -124,6 +127,18 @@ def _check(fn, st):
 
 def mla_page_bytes(dims, cache_dtype):
     return int(_lib.mla_page_bytes(ctypes.byref(dims), int(cache_dtype)))
+
+
+def mla_output_project_workspace_bytes(dims, act, rows):
+    return int(_lib.mla_output_project_workspace_bytes(ctypes.byref(dims), int(act), int(rows)))
+
+
+def mla_output_project(dims, act, rows, o, W_O, y, ws, ws_bytes, stream=None, check=True):
+    st = _lib.mla_output_project(ctypes.byref(dims), int(act), int(rows), _ptr(o), _ptr(W_O), _ptr(y), _ptr(ws),
+                                 int(ws_bytes), _stream(stream))
+    if check:
+        _check("mla_output_project", st)
+    return st
 
 
 def mla_mtp_tokens_per_step(acceptance, depth):

@@ -14,6 +14,7 @@ namespace {
 constexpr int MAX_S_Q = 8;
 constexpr int TARGET_ITEMS = 256;  // (sequence, query, split) work items aimed for per decode: one per CU
 constexpr int MAX_PAGES_PER_SPLIT = 32;  // caps one item's work (2048 tokens) so that ragged batches balance
+constexpr int MAX_OUT_ROWS = 1 << 17;  // rows of one output projection
 constexpr int MAX_PREFILL_TOKENS = 1 << 17;  // keeps every per-head byte offset of the prefill workspace in 32 bits
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -276,6 +277,29 @@ extern "C" {
 int mla_prefill(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_ALL, MLA_PREFILL_PASS); }
 int mla_prefill_project(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_PROJECT, MLA_PREFILL_PASS); }
 int mla_prefill_attend(MLA_PREFILL_ARGS) { return prefill_common(PREFILL_ATTEND, MLA_PREFILL_PASS); }
+
+size_t mla_output_project_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t rows) {
+  if (check_dims(dims) || !valid_act(act_dtype) || rows < 0 || rows > MAX_OUT_ROWS) return 0;
+  return out_proj_ws_bytes(act_dtype, rows, dims->d_model, dims->n_heads * dims->d_head);
+}
+
+int mla_output_project(const mla_dims* dims, int32_t act_dtype, int32_t rows, const void* o, const void* W_O,
+                       void* y, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
+  if (rows < 0 || rows > MAX_OUT_ROWS) return MLA_ERR_DIMS;
+  if (rows == 0) return MLA_OK;
+  if (!o || !W_O || !y) return MLA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(W_O) || !aligned16(y)) return MLA_ERR_ALIGN;
+  OutProjArgs a;
+  a.rows = rows; a.N = dims->d_model; a.K = dims->n_heads * dims->d_head; a.act = act_dtype;
+  a.o = o; a.W_O = W_O; a.y = y; a.ws = (uint8_t*)ws; a.stream = (hipStream_t)stream;
+  const size_t need = out_proj_ws_bytes(act_dtype, rows, a.N, a.K);
+  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return MLA_ERR_ALIGN;
+  return hip_status(force_generic() ? generic_out_project(a) : out_project(a));
+}
 
 double mla_mtp_tokens_per_step(double acceptance, int32_t depth) {
   if (!(acceptance >= 0.0 && acceptance <= 1.0) || depth < 0 || depth > MAX_S_Q - 1) return NAN;

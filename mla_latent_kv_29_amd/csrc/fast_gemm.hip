@@ -16,6 +16,7 @@
 // blockIdx.z and a batch (head) index in blockIdx.y.  The decode GEMMs have
 // only 64-256 activation rows: they stream the weights, so what matters is
 // keeping enough full cache lines in flight per CU.
+#include <algorithm>
 #include <math.h>
 #include "internal.hpp"
 
@@ -531,6 +532,40 @@ hipError_t prefill_projections(const PrefillArgs& a) {
 
 // Combine on MFMA: merge the splits into O_lat, then out_i = W^UV_i O_lat_i
 // (one fused kernel for at most 64 rows).
+// ------------------------------------------------------------ W^O
+int out_proj_splits(int act, int rows, int N, int K) {
+  if (act != MLA_BF16 || rows < 1) return 0;
+  if (skinny_out_supported(rows, N, K)) return K / 1024;
+  if (N % 64 || K % BK) return 0;
+  // general GEMM: split K until about 1024 blocks, at most 8 splits
+  const long tiles = (long)((rows + 63) / 64) * (N / 64);
+  const int want = (int)std::min<long>(8, std::max<long>(1, (1024 + tiles - 1) / tiles));
+  return std::min(want, K / BK);
+}
+
+// fp32 partials of the MFMA path, and never less than the fp32 result of
+// the generic path for bf16 (which MLA_FORCE_GENERIC may select).
+size_t out_proj_ws_bytes(int act, int rows, int N, int K) {
+  if (rows < 1 || act == MLA_F32) return 0;
+  const int s = out_proj_splits(act, rows, N, K);
+  return (size_t)std::max(s, 1) * rows * N * 4;
+}
+
+// y = W^O o: the skinny kernel for at most 64 rows, the general GEMM (split
+// over K into fp32 partials when the tiles alone do not fill the chip)
+// otherwise, the generic kernel for other shapes and for fp32.
+hipError_t out_project(const OutProjArgs& a) {
+  const int s = out_proj_splits(a.act, a.rows, a.N, a.K);
+  if (s == 0) return generic_out_project(a);
+  if (skinny_out_supported(a.rows, a.N, a.K)) return skinny_out(a, s);
+  GemmArgs g = gemm_args(a.rows, a.N, a.K, (const bf16_t*)a.o, a.K, 0, (const bf16_t*)a.W_O, a.K, 0, s);
+  if (s == 1) return launch_gemm<true>(g, 1, 1, EpiRowStore{(bf16_t*)a.y, a.N}, a.stream);
+  float* part = (float*)a.ws;
+  MLA_TRY(launch_gemm<true>(g, 1, s, EpiPartial{part, a.N, (long)a.rows * a.N}, a.stream));
+  return launch(&k_reduce_cq, dim3((a.rows * a.N + 255) / 256), dim3(256), 0, a.stream, a.rows, a.N, s,
+                (const float*)part, (bf16_t*)a.y);
+}
+
 hipError_t fast_combine_mfma(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;

@@ -15,6 +15,7 @@
 //              partial sums meet in LDS (one slab per wave, summed by the
 //              epilogue threads).  A grid dimension over K (k-groups) writes
 //              fp32 partials that k_reduce_rows sums.
+//              The same kernel streams W^O (y = W^O o, K = H d_head).
 //   k_uq_absorb  q_i = W^UQ_i c^Q for one head (the same split of K over
 //              the waves), then qt_i = tau log2(e) q^C_i . W^UK_i with
 //              W^UK_i[d_head][d_c] (n contiguous) in LDS, read by the
@@ -478,6 +479,23 @@ hipError_t launch_skinny(const SkArgs& a, const XSrc& xs, int n_groups, int k_gr
 bool skinny_query_supported(const mla_dims& d, int R) {
   return R >= 1 && R <= 64 && d.d_model % 896 == 0 && d.d_model / 896 <= KSPLIT_MAX && d.d_cq == UA_DCQ &&
          d.d_head == AB_DH && d.d_c == 2 * AB_NCOL && d.d_rope == 64 && d.n_heads % 4 == 0;
+}
+
+// W^O: 4 waves x 8 k-steps = 1024 k per k-group, 4 column blocks of 16 per
+// block (64 columns), three of them loading ahead; 70 KiB of LDS, so two
+// blocks share a CU and one's reduction overlaps the other's loads.
+bool skinny_out_supported(int rows, int N, int K) {
+  return rows >= 1 && rows <= 64 && N % 64 == 0 && K % 1024 == 0 && K / 1024 <= 64;
+}
+
+hipError_t skinny_out(const OutProjArgs& a, int kgroups) {
+  SkArgs s{a.rows, 1024, (const bf16_t*)a.W_O, a.K, 0};
+  XPlain xs{(const bf16_t*)a.o, a.K, 0};
+  float* part = (float*)a.ws;
+  MLA_TRY((launch_skinny<4, 8, 4, 3>(s, xs, a.N / 64, kgroups, 1, EpiKPart{part, a.rows, a.N}, a.stream)));
+  const int MN = a.rows * a.N;
+  return launch(&k_reduce_rows, dim3((MN / 4 + 255) / 256), dim3(256), 0, a.stream, MN, kgroups, (const float*)part,
+                (bf16_t*)a.y);
 }
 
 // c^Q = W^DQ h (k-groups + reduction), then W^UQ with RoPE and the

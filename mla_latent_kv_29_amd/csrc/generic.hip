@@ -362,6 +362,27 @@ hipError_t generic_decode(const DecodeArgs& a) {
   return generic_attention(a);
 }
 
+// fp32 -> bf16 (round to nearest even), elementwise.
+__global__ __launch_bounds__(256) void k_f32_to_bf16(long n, const float* __restrict__ x, bf16_t* __restrict__ y) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = (bf16_t)x[i];
+}
+
+// y = W^O o on the VALU: one wave per output element, fp32 accumulation;
+// bf16 results go through an fp32 buffer in the workspace.
+hipError_t generic_out_project(const OutProjArgs& a) {
+  const long MN = (long)a.rows * a.N;
+  const dim3 grid((unsigned)((MN + 3) / 4));
+  if (a.act == MLA_F32)
+    return launch(&k_gemm_xwT<float, float>, grid, dim3(256), 0, a.stream, a.rows, a.N, a.K, (const float*)a.o,
+                  (const float*)a.W_O, (float*)a.y);
+  float* tmp = (float*)a.ws;
+  MLA_TRY(launch(&k_gemm_xwT<bf16_t, bf16_t>, grid, dim3(256), 0, a.stream, a.rows, a.N, a.K,
+                 (const bf16_t*)a.o, (const bf16_t*)a.W_O, tmp));
+  return launch(&k_f32_to_bf16, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, a.stream, MN,
+                (const float*)tmp, (bf16_t*)a.y);
+}
+
 hipError_t generic_combine(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q;

@@ -140,6 +140,21 @@ struct PrefillArgs {
   hipStream_t stream;
 };
 
+// Output projection y = W^O [o_1; ...; o_H] for `rows` rows.
+struct OutProjArgs {
+  int rows, N, K;  // N = d_model, K = H * d_head
+  int act;         // MLA_F32 or MLA_BF16 (o, W_O and y)
+  const void* o;   // [rows][K]
+  const void* W_O; // [N][K]
+  void* y;         // [rows][N]
+  uint8_t* ws;     // fp32 partials (out_proj_ws_bytes)
+  hipStream_t stream;
+};
+// Plan of the bf16 MFMA path: k-groups of the skinny kernel (rows <= 64) or
+// K splits of the general GEMM; 0 when the shape takes the generic path.
+int out_proj_splits(int act, int rows, int N, int K);
+size_t out_proj_ws_bytes(int act, int rows, int N, int K);
+
 // Launchers (return the first HIP error of the enqueue, hipSuccess otherwise).
 hipError_t generic_append(const AppendArgs& a);
 hipError_t generic_write(const AppendArgs& a);
@@ -167,5 +182,9 @@ bool prefill_supported(const mla_dims& d, int act);
 hipError_t prefill_projections(const PrefillArgs& a);  // positions, c^KV, k^R, c^Q, q, k^C, v^C
 hipError_t prefill_attention(const PrefillArgs& a);    // causal attention over q, k, v -> out, lse
 hipError_t fast_prefill(const PrefillArgs& a);
+bool skinny_out_supported(int rows, int N, int K);
+hipError_t skinny_out(const OutProjArgs& a, int kgroups);  // rows <= 64: k-groups + their sum
+hipError_t generic_out_project(const OutProjArgs& a);
+hipError_t out_project(const OutProjArgs& a);
 
 }  // namespace mla

@@ -38,6 +38,13 @@ WORKLOADS = {
                                   lengths=("fixed", 4096), table="inorder", sigma=0.006),
 }
 
+# Decode through a stack of attention layers, each with its own cache and
+# weights (W^O included): the per-layer cache of the whole model.
+LAYER_WORKLOADS = {
+    "v3_bf16_b64_l4096_61layers": dict(index=8, dims=V3_DIMS, act="bf16", cache="bf16", batch=64, s_q=1,
+                                       lengths=("fixed", 4096), table="inorder", sigma=0.006, layers=61),
+}
+
 # Prefill of fresh sequences (mla_prefill): batch sequences of the given lengths, packed.
 PREFILL_WORKLOADS = {
     "prefill_v3_bf16_b4_l4096": dict(index=5, dims=V3_DIMS, act="bf16", batch=4, lengths=("fixed", 4096),
@@ -45,7 +52,7 @@ PREFILL_WORKLOADS = {
 }
 
 TENSORS = {"W_DKV": 1, "W_KR": 2, "W_DQ": 3, "W_UQ": 4, "W_UK": 5, "W_UV": 6, "h": 7, "len": 8, "table": 9,
-           "latent": 10, "rope": 11}
+           "latent": 10, "rope": 11, "W_O": 12, "o": 13}
 
 
 def seed_of(seed, workload_index, tensor, b=0, block=0):
@@ -82,6 +89,18 @@ def weights(dims, sigma, dtype, device, seed=0, workload_index=0):
     """Weights N(0, sigma^2), stored [out, in] in `dtype`."""
     return {k: normal(s, sigma, seed_of(seed, workload_index, k), device, dtype)
             for k, s in weight_shapes(dims).items()}
+
+
+def out_weight(dims, sigma, dtype, device, seed=0, workload_index=0):
+    """W^O ~ N(0, sigma^2), stored [out, in] = [d_model, n_heads * d_head]."""
+    shape = (dims["d_model"], dims["n_heads"] * dims["d_head"])
+    return normal(shape, sigma, seed_of(seed, workload_index, "W_O"), device, dtype)
+
+
+def head_outputs(dims, rows, std, dtype, device, seed=0, workload_index=0):
+    """Per-head attention outputs o ~ N(0, std^2), [rows, n_heads, d_head]."""
+    shape = (rows, dims["n_heads"], dims["d_head"])
+    return normal(shape, std, seed_of(seed, workload_index, "o"), device, dtype)
 
 
 def hidden(dims, b, t0, t1, dtype, device, seed=0, workload_index=0):

@@ -171,3 +171,36 @@ def test_mtp_tokens_per_step_matches_oracle():
             assert abs(m.mla_mtp_tokens_per_step(a, depth) - oracle.tokens_per_step(a, depth)) < 1e-12
     for a, depth in ((-0.1, 1), (1.1, 1), (float("nan"), 1), (0.5, -1), (0.5, 8)):
         assert math.isnan(m.mla_mtp_tokens_per_step(a, depth))
+
+
+def test_output_project_workspace_and_argument_errors():
+    d = _dims()
+    K, N = 128 * 128, 7168
+    # at most 64 rows: 16 k-groups of 1024 fp32 partials; more rows: K splits of the general GEMM
+    assert m.mla_output_project_workspace_bytes(d, m.MLA_BF16, 1) == 16 * 1 * N * 4
+    assert m.mla_output_project_workspace_bytes(d, m.MLA_BF16, 64) == 16 * 64 * N * 4
+    assert m.mla_output_project_workspace_bytes(d, m.MLA_BF16, 72) == 5 * 72 * N * 4
+    assert m.mla_output_project_workspace_bytes(d, m.MLA_BF16, 4096) == 4096 * N * 4
+    assert m.mla_output_project_workspace_bytes(d, m.MLA_F32, 10) == 0
+    assert m.mla_output_project_workspace_bytes(d, m.MLA_BF16, -1) == 0
+    assert m.mla_output_project_workspace_bytes(d, 9, 10) == 0
+    w = m.mla_output_project_workspace_bytes(d, m.MLA_BF16, 10)
+
+    def call(**o):
+        a = dict(act=m.MLA_BF16, rows=10, o=FAKE, w=FAKE, y=FAKE, ws=FAKE, wsb=w)
+        a.update(o)
+        return m.mla_output_project(d, a["act"], a["rows"], a["o"], a["w"], a["y"], a["ws"], a["wsb"], stream=0,
+                                    check=False)
+
+    assert call(rows=0) == L.MLA_OK                               # no-op
+    assert call(act=7) == L.MLA_ERR_DTYPE
+    assert call(act=m.MLA_FP8_E4M3) == L.MLA_ERR_DTYPE
+    assert call(rows=-1) == L.MLA_ERR_DIMS
+    assert call(rows=(1 << 17) + 1) == L.MLA_ERR_DIMS
+    assert call(o=None) == L.MLA_ERR_NULL
+    assert call(w=None) == L.MLA_ERR_NULL
+    assert call(y=None) == L.MLA_ERR_NULL
+    assert call(y=FAKE + 8) == L.MLA_ERR_ALIGN
+    assert call(ws=None) == L.MLA_ERR_WORKSPACE
+    assert call(wsb=w - 1) == L.MLA_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == L.MLA_ERR_ALIGN
