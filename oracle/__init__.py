@@ -24,7 +24,8 @@ Parity status per function is listed in each module header.
 from .mla import (rope, kv_latents, queries, attend_nonabsorbed, attend_absorbed,
                   decode_from_latents, decode_from_h, softmax_lse, output_projection)
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_values, e5m2_decode,
-                  quantize_tiles, dequantize_tiles)
+                  quantize_tiles, dequantize_tiles, quantize_blocks, dequantize_blocks,
+                  gemm_block_scaled)
 from .sizes import (cache_values_per_token, mha_values_per_token, cache_bytes,
                     mla_params_per_layer)
 from .mtp import tokens_per_step
@@ -33,7 +34,7 @@ __all__ = [
     "rope", "kv_latents", "queries", "attend_nonabsorbed", "attend_absorbed",
     "decode_from_latents", "decode_from_h", "softmax_lse", "output_projection",
     "e4m3_decode", "e4m3_encode", "e4m3_values", "e5m2_decode",
-    "quantize_tiles", "dequantize_tiles",
+    "quantize_tiles", "dequantize_tiles", "quantize_blocks", "dequantize_blocks", "gemm_block_scaled",
     "cache_values_per_token", "mha_values_per_token", "cache_bytes",
     "mla_params_per_layer", "tokens_per_step",
 ]

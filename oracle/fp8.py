@@ -10,6 +10,10 @@ The codec is built from the format definition: every code is decoded by its
 bit fields, and encoding is "nearest representable value, ties to the code
 with an even mantissa, saturate at +-448" by search over the decoded table.
 
+Block quantisation of weights (item 2: 128 x 128 blocks) applies the same
+rule to each block; the block-scaled GEMM (items 2-3) multiplies the
+dequantised activations (1 x 128 tiles) and weights.
+
 Tile quantisation (a reading of item 2 for the latent cache): for each token
 and each group of 128 consecutive channels, scale s = amax/448 computed in
 float32 (s = 1 when amax = 0), code = encode(float32(x) / s) in float32, and the
@@ -89,3 +93,51 @@ def dequantize_tiles(codes, scales, tile=128):
     n, d = codes.shape
     v = e4m3_decode(codes).reshape(n, d // tile, tile)
     return (v * np.asarray(scales, dtype=np.float64)[:, :, None]).reshape(n, d)
+
+
+def quantize_blocks(w, block=128):
+    """Per-block E4M3 quantisation of a weight w [n, k] (k % block == 0):
+    one scale per block x block block (§3.3 item 2: weights in 128 x 128
+    blocks, each group with its own scale), the last row-block cut short when
+    n % block != 0.  The rule inside a block is the tile rule above: s =
+    amax/448 in float32 (1 for an all-zero block), code = encode(float32(x) /
+    s).
+
+    Returns (codes uint8 [n, k], scales float32 [ceil(n / block), k / block]).
+    """
+    w32 = np.asarray(w, dtype=np.float64).astype(np.float32)
+    n, k = w32.shape
+    assert k % block == 0
+    nb, kb = -(-n // block), k // block
+    codes = np.zeros((n, k), dtype=np.uint8)
+    scales = np.zeros((nb, kb), dtype=np.float32)
+    for i in range(nb):
+        for j in range(kb):
+            blk = w32[i * block:(i + 1) * block, j * block:(j + 1) * block]
+            amax = np.float32(np.abs(blk).max())
+            s = amax / np.float32(E4M3_MAX) if amax > 0 else np.float32(1.0)
+            scales[i, j] = s
+            codes[i * block:(i + 1) * block, j * block:(j + 1) * block] = e4m3_encode(
+                (blk / s).astype(np.float32).astype(np.float64))
+    return codes, scales
+
+
+def dequantize_blocks(codes, scales, block=128):
+    """codes [n, k] uint8, scales [ceil(n / block), k / block] -> float64 code * scale."""
+    n, k = codes.shape
+    s = np.repeat(np.repeat(np.asarray(scales, dtype=np.float64), block, 0)[:n], block, 1)
+    return e4m3_decode(codes) * s
+
+
+def gemm_block_scaled(x, w_codes, w_scales, block=128):
+    """Y = Q(x) . Q(w)^T of the pages' FP8 GEMM (§3.3 items 2-3): the
+    activations x [m, k] quantised in 1 x 128 tiles, the weight given as
+    128 x 128-block codes and scales, the product of the dequantised values
+    summed exactly (float64).  The per-128 promotion of item 3 is how a
+    device keeps this sum accurate; in exact arithmetic it is this sum.
+
+    Returns (y float64 [m, n], x_codes, x_scales)."""
+    xc, xs = quantize_tiles(x, block)
+    xq = dequantize_tiles(xc, xs, block)
+    wq = dequantize_blocks(w_codes, w_scales, block)
+    return xq @ wq.T, xc, xs

@@ -408,3 +408,76 @@ def test_output_projection_brute_force_and_head_order():
         P[:, i * dh:(i + 1) * dh] = np.eye(dh)
         np.testing.assert_array_equal(oracle.output_projection(o, P), o[:, i, :])
     np.testing.assert_array_equal(oracle.output_projection(o, np.eye(H * dh)), o.reshape(R, H * dh))
+
+
+# ---------------------------------------------------------------- FP8 weight blocks and the block-scaled GEMM
+
+def test_weight_blocks_reduce_to_the_tile_rule():
+    """A 128 x 128 block is quantised exactly like one tile holding all of its
+    values (the pinned 1 x 128 rule with the tile widened); the short last
+    row-block (n = 200: rows 128..199) likewise."""
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.02, (200, 256))
+    codes, scales = oracle.quantize_blocks(w)
+    assert codes.shape == (200, 256) and scales.shape == (2, 2)
+    for i, (r0, r1) in enumerate(((0, 128), (128, 200))):
+        for j in range(2):
+            blk = w[r0:r1, 128 * j:128 * (j + 1)]
+            c1, s1 = oracle.quantize_tiles(blk.reshape(1, -1), tile=blk.size)
+            assert s1[0, 0] == scales[i, j]
+            np.testing.assert_array_equal(c1.reshape(blk.shape), codes[r0:r1, 128 * j:128 * (j + 1)])
+
+
+def test_weight_blocks_scale_error_bound_and_outlier_isolation():
+    """amax of every block decodes to +-448 x scale; the dequantised weight is
+    within half an E4M3 step (2^-4 relative; 2^-10 x scale absolute near 0);
+    a power-of-two factor on one block changes only that block's scale; an
+    outlier spoils only its own block (§3.3 item 2)."""
+    rng = np.random.default_rng(4)
+    w = rng.normal(0, 0.01, (256, 384))
+    codes, scales = oracle.quantize_blocks(w)
+    deq = oracle.dequantize_blocks(codes, scales)
+    s_full = np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)
+    assert np.all(np.abs(deq - w) <= np.maximum(np.abs(w) * 2.0 ** -4, s_full * 2.0 ** -10) * (1 + 1e-9))
+    for i in range(2):
+        for j in range(3):
+            blk = oracle.e4m3_decode(codes[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)])
+            assert np.abs(blk).max() == 448.0
+    w2 = w.copy()
+    w2[128:256, 0:128] *= 4.0
+    c2, s2 = oracle.quantize_blocks(w2)
+    np.testing.assert_array_equal(c2, codes)
+    assert s2[1, 0] == 4 * scales[1, 0] and np.all(np.delete(s2.ravel(), 3) == np.delete(scales.ravel(), 3))
+    w3 = w.copy()
+    w3[5, 300] = 50.0
+    c3, s3 = oracle.quantize_blocks(w3)
+    changed = np.argwhere(s3 != scales)
+    assert changed.tolist() == [[0, 2]]
+    mask = np.ones_like(codes, dtype=bool)
+    mask[0:128, 256:384] = False
+    np.testing.assert_array_equal(c3[mask], codes[mask])
+
+
+def test_block_scaled_gemm_by_promoted_partial_sums():
+    """Y by the route of §3.3 item 3 written out: for every 128-wide k-block
+    the integer-grid partial sum of code values is scaled by the activation
+    tile's and the weight block's scales and promoted into the running sum;
+    equals the oracle's dequantise-then-multiply, and stays within the FP8
+    error bound of the unquantised product."""
+    rng = np.random.default_rng(5)
+    m, n, k = 3, 130, 384
+    x = rng.normal(0, 1.0, (m, k))
+    w = rng.normal(0, 0.02, (n, k))
+    wc, ws = oracle.quantize_blocks(w)
+    y, xc, xs = oracle.gemm_block_scaled(x, wc, ws)
+    xv, wv = oracle.e4m3_decode(xc), oracle.e4m3_decode(wc)
+    for r in range(m):
+        for c in range(n):
+            acc = 0.0
+            for kb in range(k // 128):
+                part = float(np.dot(xv[r, 128 * kb:128 * (kb + 1)], wv[c, 128 * kb:128 * (kb + 1)]))
+                acc += part * float(xs[r, kb]) * float(ws[c // 128, kb])
+            assert abs(acc - y[r, c]) <= 1e-12 * max(1.0, abs(acc))
+    exact = x @ w.T
+    bound = (np.abs(x) @ np.abs(w).T) * (2 * 2.0 ** -4 + 2.0 ** -8) + 1e-6
+    assert np.all(np.abs(y - exact) <= bound)
