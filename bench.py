@@ -256,6 +256,88 @@ def run_layers(args, name):
     print(json.dumps(res))
 
 
+def run_fp8_proj(args, name):
+    """FP8 projection workload: one step = mla_fp8_gemm for every MLA weight
+    of a layer (W^O included) at the decode row count, the weights quantised
+    once beforehand in 128 x 128 blocks (three copies rotated, so that no step
+    finds them in the 256 MB MALL).  The W^O call, the largest, is timed with
+    HIP events on its stream every step."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_29_amd import inputs
+    from mla_latent_kv_29_amd import _lib as L
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    spec = inputs.FP8_WORKLOADS[name]
+    M, wl = spec["rows"], spec["index"]
+    sets = []
+    for r in range(max(1, args.rotate)):
+        one = []
+        for pname, N, K in inputs.FP8_PROJECTIONS:
+            X, W = inputs.gemm_operands(M, N, K, spec["sigma"], torch.bfloat16, dev, r, wl)
+            codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            scales = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=dev)
+            L.mla_fp8_quantize_weight(W, N, K, codes, scales)
+            del W
+            one.append((pname, N, K, X, codes, scales, torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        sets.append(one)
+    wsb = max(L.mla_fp8_gemm_workspace_bytes(M, N, K) for _, N, K in inputs.FP8_PROJECTIONS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+
+    def step(i, e=None):
+        for pname, N, K, X, codes, scales, Y in sets[i % len(sets)]:
+            if e is not None and pname == "W_O":
+                e[0].record(stream)
+            L.mla_fp8_gemm(M, N, K, X, codes, scales, Y, ws, wsb, sp)
+            if e is not None and pname == "W_O":
+                e[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    wo_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    def alg_bytes(N, K):  # weight codes and scales, activations in, results out
+        return N * K + (N + 127) // 128 * (K // 128) * 4 + 2 * M * K + 2 * M * N
+
+    step_bytes = sum(alg_bytes(N, K) for _, N, K in inputs.FP8_PROJECTIONS)
+    wo_bytes = alg_bytes(7168, 16384)
+    achieved = wo_bytes / (wo_ms * 1e-3) / 1e9
+    res = {
+        "metric": f"FP8 block-scaled MLA projection GEMMs at {M} rows (E4M3, 128x128 weight blocks, 1x128 "
+                  f"activation tiles): algorithmic GB/s + % HBM roofline, 1 GPU",
+        "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,sigma^2) weights at DeepSeek-V3 MLA shapes)",
+        "config": {"workload": name, "rows": M, "weights": [p[0] for p in inputs.FP8_PROJECTIONS],
+                   "rotation_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved * 1e9 / HBM_PEAK, "traffic": None,
+                     "kernel": "mla_fp8_gemm on W^O (k_quant_x + k_skinny_f8 + k_reduce_rows)", "call_ms_mean": wo_ms},
+        "step_roofline": {"t_bound_us": step_bytes / HBM_PEAK * 1e6, "frac": step_bytes / HBM_PEAK / (ms_per_step * 1e-3),
+                          "step_bytes": step_bytes},
+    }
+    print(json.dumps(res))
+
+
 def run_prefill(args, name):
     """Prefill workload: one step = mla_prefill_project + mla_prefill_attend
     over the packed sequences; the attention (the dominant kernel) is timed
@@ -366,6 +448,9 @@ def main():
         return
     if args.workload in inputs.LAYER_WORKLOADS:
         run_layers(args, args.workload)
+        return
+    if args.workload in inputs.FP8_WORKLOADS:
+        run_fp8_proj(args, args.workload)
         return
 
     import numpy as np

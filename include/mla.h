@@ -165,6 +165,34 @@ MLA_API int mla_output_project(const mla_dims* dims, int32_t act_dtype, int32_t 
                                const void* o, const void* W_O, void* y, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* FP8 projection GEMMs with fine-grained scaling ("Читаем техотчёт
+ * DeepSeek-V3 вместе", §3.3 "Обучение в FP8", items 2-4; the same scheme in
+ * the "Báo cáo Kỹ thuật DeepSeek-V3" summary): E4M3 everywhere, weights in
+ * 128 x 128 blocks and activations in 1 x 128 tiles, each group with its
+ * own fp32 scale s = amax / 448 (1 for an all-zero group), code =
+ * round-to-nearest-even(x / s) saturated at +-448, and every 128-wide
+ * partial sum scaled and accumulated in fp32.
+ *
+ * mla_fp8_quantize_weight: W [N, K] bf16 (stored [out, in], 16-byte
+ *   aligned) -> codes [N, K] uint8 (E4M3FN, 16-byte aligned) and scales
+ *   [ceil(N/128), K/128] fp32 (4-byte aligned); the last row-block is
+ *   shorter when N % 128 != 0.  N % 16 == 0 and K % 128 == 0 (else
+ *   MLA_ERR_UNSUPPORTED), N and K at most 65536.
+ * mla_fp8_gemm: Y [M, N] (bf16) = Q(X) . Q(W)^T for X [M, K] bf16, the
+ *   weight as quantised above; X is quantised in 1 x 128 tiles (64 rows at
+ *   a time) into the workspace.  N % 16 == 0 and K % 512 == 0 (else
+ *   MLA_ERR_UNSUPPORTED); M in 0..131072 (0 does nothing); ws (16-byte
+ *   aligned) holds mla_fp8_gemm_workspace_bytes() bytes: the activation
+ *   codes and scales of one 64-row chunk and the fp32 partial sums.  Made
+ *   for decode-sized M: every 64 rows stream the weight once.
+ * Errors as for the other calls; nothing is enqueued on an error other than
+ * MLA_ERR_HIP.  Device pointers, caller-owned, no allocation.               */
+MLA_API int mla_fp8_quantize_weight(const void* W, int32_t N, int32_t K, void* codes,
+                                    float* scales, void* stream);
+MLA_API size_t mla_fp8_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
+MLA_API int mla_fp8_gemm(int32_t M, int32_t N, int32_t K, const void* X, const void* W_codes,
+                         const float* W_scales, void* Y, void* ws, size_t ws_bytes, void* stream);
+
 /* Speculative verify with multi-token prediction ("Читаем техотчёт
  * DeepSeek-V3 вместе", §2.2 Multi-Token Prediction, and the tokens_per_step
  * exercise of its practice part): a decode step with s_q = 1 + depth query

@@ -11,13 +11,15 @@ from . import _lib
 from ._lib import (mla_page_bytes, mla_cache_append, mla_cache_write, mla_default_splits,
                    mla_workspace_bytes, mla_decode, mla_decode_query, mla_decode_attend, mla_combine,
                    mla_prefill_workspace_bytes, mla_prefill, mla_prefill_project, mla_prefill_attend,
-                   mla_output_project_workspace_bytes, mla_output_project, mla_mtp_tokens_per_step,
+                   mla_output_project_workspace_bytes, mla_output_project, mla_fp8_quantize_weight,
+                   mla_fp8_gemm_workspace_bytes, mla_fp8_gemm, mla_mtp_tokens_per_step,
                    status_str, version, make_dims,
                    MLAError, MLA_F32, MLA_BF16, MLA_FP8_E4M3)
 
 __all__ = ["mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
-           "mla_output_project_workspace_bytes", "mla_output_project", "mla_mtp_tokens_per_step",
+           "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
+           "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
            "status_str", "version", "make_dims",
            "MLAError", "MLA_F32", "MLA_BF16", "MLA_FP8_E4M3"]

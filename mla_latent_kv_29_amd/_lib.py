@@ -18,7 +18,8 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
-           "mla_output_project_workspace_bytes", "mla_output_project", "mla_mtp_tokens_per_step",
+           "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
+           "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
            "mla_status_str", "mla_last_hip_error", "mla_version")
 
 
@@ -69,6 +70,9 @@ def _load():
         "mla_prefill_attend": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_output_project_workspace_bytes": (SZ, [D, I32, I32]),
         "mla_output_project": (ctypes.c_int, [D, I32, I32, P, P, P, P, SZ, P]),
+        "mla_fp8_quantize_weight": (ctypes.c_int, [P, I32, I32, P, P, P]),
+        "mla_fp8_gemm_workspace_bytes": (SZ, [I32, I32, I32]),
+        "mla_fp8_gemm": (ctypes.c_int, [I32, I32, I32, P, P, P, P, P, SZ, P]),
         "mla_mtp_tokens_per_step": (ctypes.c_double, [ctypes.c_double, I32]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
@@ -138,6 +142,25 @@ def mla_output_project(dims, act, rows, o, W_O, y, ws, ws_bytes, stream=None, ch
                                  int(ws_bytes), _stream(stream))
     if check:
         _check("mla_output_project", st)
+    return st
+
+
+def mla_fp8_quantize_weight(W, N, K, codes, scales, stream=None, check=True):
+    st = _lib.mla_fp8_quantize_weight(_ptr(W), int(N), int(K), _ptr(codes), _ptr(scales), _stream(stream))
+    if check:
+        _check("mla_fp8_quantize_weight", st)
+    return st
+
+
+def mla_fp8_gemm_workspace_bytes(M, N, K):
+    return int(_lib.mla_fp8_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def mla_fp8_gemm(M, N, K, X, W_codes, W_scales, Y, ws, ws_bytes, stream=None, check=True):
+    st = _lib.mla_fp8_gemm(int(M), int(N), int(K), _ptr(X), _ptr(W_codes), _ptr(W_scales), _ptr(Y), _ptr(ws),
+                           int(ws_bytes), _stream(stream))
+    if check:
+        _check("mla_fp8_gemm", st)
     return st
 
 

@@ -14,7 +14,8 @@ namespace {
 constexpr int MAX_S_Q = 8;
 constexpr int TARGET_ITEMS = 256;  // (sequence, query, split) work items aimed for per decode: one per CU
 constexpr int MAX_PAGES_PER_SPLIT = 32;  // caps one item's work (2048 tokens) so that ragged batches balance
-constexpr int MAX_OUT_ROWS = 1 << 17;  // rows of one output projection
+constexpr int MAX_OUT_ROWS = 1 << 17;  // rows of one output projection (and of one FP8 GEMM)
+constexpr int MAX_FP8_DIM = 1 << 16;   // N and K of one FP8 GEMM
 constexpr int MAX_PREFILL_TOKENS = 1 << 17;  // keeps every per-head byte offset of the prefill workspace in 32 bits
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -299,6 +300,42 @@ int mla_output_project(const mla_dims* dims, int32_t act_dtype, int32_t rows, co
   if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return MLA_ERR_ALIGN;
   return hip_status(force_generic() ? generic_out_project(a) : out_project(a));
+}
+
+namespace {
+int check_fp8_gemm_dims(int32_t N, int32_t K) {
+  if (N < 1 || K < 1 || N > MAX_FP8_DIM || K > MAX_FP8_DIM) return MLA_ERR_DIMS;
+  if (!fp8_gemm_supported(N, K)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+}  // namespace
+
+int mla_fp8_quantize_weight(const void* W, int32_t N, int32_t K, void* codes, float* scales, void* stream) {
+  if (N < 1 || K < 1 || N > MAX_FP8_DIM || K > MAX_FP8_DIM) return MLA_ERR_DIMS;
+  if (N % 16 || K % 128) return MLA_ERR_UNSUPPORTED;
+  if (!W || !codes || !scales) return MLA_ERR_NULL;
+  if (!aligned16(W) || !aligned16(codes) || ((uintptr_t)scales & 3)) return MLA_ERR_ALIGN;
+  return hip_status(fp8_quantize_weight(N, K, (const bf16_t*)W, (uint8_t*)codes, scales, (hipStream_t)stream));
+}
+
+size_t mla_fp8_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || M > MAX_OUT_ROWS || check_fp8_gemm_dims(N, K)) return 0;
+  return fp8_plan(M, N, K).ws_bytes;
+}
+
+int mla_fp8_gemm(int32_t M, int32_t N, int32_t K, const void* X, const void* W_codes, const float* W_scales, void* Y,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || M > MAX_OUT_ROWS) return MLA_ERR_DIMS;
+  const int st = check_fp8_gemm_dims(N, K);
+  if (st) return st;
+  if (M == 0) return MLA_OK;
+  if (!X || !W_codes || !W_scales || !Y) return MLA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W_codes) || !aligned16(Y) || ((uintptr_t)W_scales & 3)) return MLA_ERR_ALIGN;
+  const size_t need = fp8_plan(M, N, K).ws_bytes;
+  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return MLA_ERR_ALIGN;
+  return hip_status(fp8_gemm(M, N, K, (const bf16_t*)X, (const uint8_t*)W_codes, W_scales, (bf16_t*)Y, (uint8_t*)ws,
+                             (hipStream_t)stream));
 }
 
 double mla_mtp_tokens_per_step(double acceptance, int32_t depth) {

@@ -24,6 +24,7 @@
 // MFMA v_mfma_f32_16x16x32_bf16, C[16][16] += A[16][32] B[32][16]: lane l
 // holds row l%16, k 8(l/16)..+7 of A, the same of B^T, and rows 4(l/16)..+3
 // of column l%16 of C.  With A = W (rows n) and B = X (rows m), C = Y^T.
+#include <algorithm>
 #include <math.h>
 #include "internal.hpp"
 
@@ -81,6 +82,49 @@ struct SkPlan {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
+// One reduction round, after column block nb: every wave has stored its C
+// tiles of the round's NBR column blocks in its slab; all threads sum the
+// waves for their column pairs and hand them to the epilogue (or park them
+// in the final tile when there are several rounds).
+template <int WPB, int NB, class Epi>
+__device__ __forceinline__ void sk_round(float* slab, int nb, int n0, int batch, int kg, int M, const Epi& epi) {
+  using P = SkPlan<WPB, NB>;
+  ring_barrier();  // every wave's slab holds this round (the weight loads stay in flight)
+  constexpr int PAIRS = P::NBR * 8;
+  const int c_base = n0 + 16 * (nb + 1 - P::NBR);
+  for (int p = threadIdx.x; p < PAIRS * 64; p += WPB * 64) {
+    const int m = p / PAIRS, c = 2 * (p % PAIRS);
+    float2 v = *(const float2*)(slab + m * P::LDN + c);
+#pragma unroll
+    for (int w = 1; w < WPB; ++w) {
+      const float2 u = *(const float2*)(slab + w * P::SLAB + m * P::LDN + c);
+      v.x += u.x;
+      v.y += u.y;
+    }
+    if constexpr (P::FINAL == 0) {
+      if (m < M) epi(batch, kg, m, c_base + c, v.x, v.y);
+    } else {
+      *(float2*)(slab + WPB * P::SLAB + m * P::LDF + (c_base - n0) + c) = v;
+    }
+  }
+  ring_barrier();  // the slabs (and final tile) are complete before reuse
+}
+
+// With several rounds: the parked sums go to the epilogue once all are in.
+template <int WPB, int NB, class Epi>
+__device__ __forceinline__ void sk_final(const float* slab, int n0, int batch, int kg, int M, const Epi& epi) {
+  using P = SkPlan<WPB, NB>;
+  if constexpr (P::FINAL != 0) {
+    constexpr int PAIRS = NB * 8;
+    const float* fin = slab + WPB * P::SLAB;
+    for (int p = threadIdx.x; p < PAIRS * 64; p += WPB * 64) {
+      const int m = p / PAIRS, c = 2 * (p % PAIRS);
+      const float2 v = *(const float2*)(fin + m * P::LDF + c);
+      if (m < M) epi(batch, kg, m, n0 + c, v.x, v.y);
+    }
+  }
+}
+
 // Grid (column groups, k-groups, batch); WPB waves of KS k-steps each; NB
 // column blocks of 16 per block, DEPTH of them loading ahead.
 template <int WPB, int KS, int NB, int DEPTH, class XSrc, class Epi>
@@ -125,37 +169,9 @@ __global__ __launch_bounds__(WPB * 64) void k_skinny(SkArgs a, XSrc xs, Epi epi)
     const int nr = nb % P::NBR;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) *(f32x4*)(mine + (16 * mb + i16) * P::LDN + 16 * nr + 4 * g) = acc[mb];
-    if (nr == P::NBR - 1) {
-      ring_barrier();  // every wave's slab holds this round (the weight loads stay in flight)
-      constexpr int PAIRS = P::NBR * 8;
-      const int c_base = n0 + 16 * (nb + 1 - P::NBR);
-      for (int p = threadIdx.x; p < PAIRS * 64; p += WPB * 64) {
-        const int m = p / PAIRS, c = 2 * (p % PAIRS);
-        float2 v = *(const float2*)(slab + m * P::LDN + c);
-#pragma unroll
-        for (int w = 1; w < WPB; ++w) {
-          const float2 u = *(const float2*)(slab + w * P::SLAB + m * P::LDN + c);
-          v.x += u.x;
-          v.y += u.y;
-        }
-        if constexpr (P::FINAL == 0) {
-          if (m < a.M) epi(batch, kg, m, c_base + c, v.x, v.y);
-        } else {
-          *(float2*)(slab + WPB * P::SLAB + m * P::LDF + (c_base - n0) + c) = v;
-        }
-      }
-      ring_barrier();  // the slabs (and final tile) are complete before reuse
-    }
+    if (nr == P::NBR - 1) sk_round<WPB, NB>(slab, nb, n0, batch, kg, a.M, epi);
   }
-  if constexpr (P::FINAL != 0) {
-    constexpr int PAIRS = NB * 8;
-    const float* fin = slab + WPB * P::SLAB;
-    for (int p = threadIdx.x; p < PAIRS * 64; p += WPB * 64) {
-      const int m = p / PAIRS, c = 2 * (p % PAIRS);
-      const float2 v = *(const float2*)(fin + m * P::LDF + c);
-      if (m < a.M) epi(batch, kg, m, n0 + c, v.x, v.y);
-    }
-  }
+  sk_final<WPB, NB>(slab, n0, batch, kg, a.M, epi);
 }
 
 // ------------------------------------------------------------ epilogues
@@ -459,6 +475,201 @@ __global__ __launch_bounds__(UA_WAVES * 64) void k_uq_absorb(UaArgs a) {
   }
 }
 
+// ------------------------------------------------------------ FP8 block-scaled weights
+// E4M3 quantisation of a weight W[N][K] in 128 x 128 blocks (the last
+// row-block may be shorter): scale s = amax / 448 in fp32 (1 for an all-zero
+// block), code = RNE(x / s) saturated.  One 256-thread block per weight
+// block; thread t owns row t/2, columns 64 (t & 1) .. +63.
+__global__ __launch_bounds__(256) void k_quant_w(int N, int K, const bf16_t* __restrict__ W,
+                                                 uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int r0 = blockIdx.x * 128, kb = blockIdx.y;
+  const int r = threadIdx.x >> 1, c0 = kb * 128 + 64 * (threadIdx.x & 1);
+  const bool live = r0 + r < N;
+  float v[64];
+  float am = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    bf16x8 x = live ? *(const bf16x8*)(W + (long)(r0 + r) * K + c0 + 8 * q) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[8 * q + e] = (float)x[e];
+      am = fmaxf(am, fabsf(v[8 * q + e]));
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t u = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u |= (uint32_t)f32_to_e4m3(v[16 * q + 4 * i + e] / sc) << (8 * e);
+        w4[i] = u;
+      }
+      *(uint4*)(codes + (long)(r0 + r) * K + c0 + 16 * q) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
+  if (threadIdx.x == 0) scales[(long)blockIdx.x * (K / 128) + kb] = sc;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 quantisation of activations X[M][K] in 1 x 128 tiles: codes [M][K],
+// scales [M][K / 128].  16 lanes per tile, 8 values a lane; the tile's amax
+// meets by four lane swaps.
+__global__ __launch_bounds__(256) void k_quant_x(int tiles, int K, const bf16_t* __restrict__ X,
+                                                 uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4), j = threadIdx.x & 15;
+  const bool live = t < tiles;
+  const int kt = K / 128, row = live ? t / kt : 0, c0 = live ? (t % kt) * 128 + 8 * j : 0;
+  const bf16x8 x = live ? *(const bf16x8*)(X + (long)row * K + c0) : bf16x8{};
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf((float)x[e]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+  if (!live) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3((float)x[e] / sc) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hi |= (uint32_t)f32_to_e4m3((float)x[4 + e] / sc) << (8 * e);
+  *(uint2*)(codes + (long)row * K + c0) = make_uint2(lo, hi);
+  if (j == 0) scales[t] = sc;
+}
+
+struct F8Args {
+  int M, K;             // activation rows (<= 64), reduction length (multiple of 512)
+  const uint8_t* Xc;    // activation codes [M][K]
+  const float* Xs;      // activation scales [M][K / 128]
+  const uint8_t* Wc;    // weight codes [N][K]
+  const float* Ws;      // weight scales [ceil(N / 128)][K / 128]
+};
+
+// Y[m][n] = sum over 128-wide k-blocks kb of sx[m][kb] sw[n / 128][kb]
+// (Xc[m][kb] . Wc[n][kb]) for at most 64 rows: four waves, wave w of k-group
+// kg owns k-blocks (4 kg + w) KB .. +KB-1; NB column blocks of 16 per block,
+// all of whose weight loads go out at once.  One
+// v_mfma_f32_16x16x128_f8f6f4 per (column block, k-block, row block) gives
+// the integer-grid partial, which the two scales promote into the fp32 sum.
+// A lane's 32 operand bytes of a k-block are k = 16 g .. +15 and
+// 64 + 16 g .. +15 (g = lane / 16), the same order for W and X, so that
+// every 16-byte weight load covers 16 rows x 64 contiguous bytes.
+template <int KB, int NB, class Epi>
+__global__ __launch_bounds__(256) void k_skinny_f8(F8Args a, Epi epi) {
+  constexpr int WPB = 4;
+  using P = SkPlan<WPB, NB>;
+  extern __shared__ __attribute__((aligned(16))) float slab[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int n0 = blockIdx.x * NB * 16, kg = blockIdx.y;
+  const int kb0 = (kg * WPB + wave) * KB;
+  const int kbs = a.K / 128;
+
+  // activation codes and scales of rows 16 mb + i16 (clamped), k-blocks kb0 ..
+  i32x8 xq[4][KB];
+  float xs[4][KB];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int row = min(16 * mb + i16, a.M - 1);
+    const uint8_t* xp = a.Xc + (long)row * a.K + 16 * g;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const uint4 lo = *(const uint4*)(xp + (kb0 + j) * 128);
+      const uint4 hi = *(const uint4*)(xp + (kb0 + j) * 128 + 64);
+      xq[mb][j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      xs[mb][j] = a.Xs[(long)row * kbs + kb0 + j];
+    }
+  }
+  // weight rows n0 + 16 nb + i16: every column block of the block at once
+  i32x8 wf[NB][KB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint8_t* wp = a.Wc + (long)(n0 + 16 * nb + i16) * a.K + 16 * g;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const uint4 lo = *(const uint4*)(wp + (kb0 + j) * 128);
+      const uint4 hi = *(const uint4*)(wp + (kb0 + j) * 128 + 64);
+      wf[nb][j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  }
+
+  float* mine = slab + wave * P::SLAB;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{};
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const float sw = a.Ws[(long)((n0 + 16 * nb) >> 7) * kbs + kb0 + j];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const f32x4 p =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb][j], xq[mb][j], f32x4{}, 0, 0, 0, 0, 0, 0);
+        acc[mb] += (sw * xs[mb][j]) * p;
+      }
+    }
+    // C = Y^T: lane holds n = 16 nb + 4g + r (r = 0..3), m = 16 mb + i16
+    const int nr = nb % P::NBR;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) *(f32x4*)(mine + (16 * mb + i16) * P::LDN + 16 * nr + 4 * g) = acc[mb];
+    if (nr == P::NBR - 1) sk_round<WPB, NB>(slab, nb, n0, 0, kg, a.M, epi);
+  }
+  sk_final<WPB, NB>(slab, n0, 0, kg, a.M, epi);
+}
+
+// Y[m][n] (bf16) directly, when one k-group covers K
+struct EpiRowsBf16 {
+  bf16_t* y;
+  int N;
+  __device__ void operator()(int, int, int m, int n, float v0, float v1) const {
+    bf16x2 v = {(bf16_t)v0, (bf16_t)v1};
+    *(bf16x2*)(y + (long)m * N + n) = v;
+  }
+};
+
+template <int KB, int NB, class Epi>
+hipError_t launch_f8(const F8Args& a, int n_groups, int k_groups, const Epi& epi, hipStream_t st) {
+  constexpr int lds = SkPlan<4, NB>::LDS_BYTES;
+  auto kern = &k_skinny_f8<KB, NB, Epi>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    MLA_TRY(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    attr_set = true;
+  }
+  return launch(kern, dim3(n_groups, k_groups), dim3(256), lds, st, a, epi);
+}
+
+template <int KB, class Epi>
+hipError_t launch_f8_nb(const F8Args& a, int nb, int N, int k_groups, const Epi& epi, hipStream_t st) {
+  switch (nb) {
+    case 4:
+      if constexpr (KB * 4 <= 12) return launch_f8<KB, 4>(a, N / 64, k_groups, epi, st);
+      [[fallthrough]];
+    case 2: return launch_f8<KB, 2>(a, N / 32, k_groups, epi, st);
+    default: return launch_f8<KB, 1>(a, N / 16, k_groups, epi, st);
+  }
+}
+
+template <class Epi>
+hipError_t launch_f8_kb(const F8Args& a, const F8Plan& p, int N, const Epi& epi, hipStream_t st) {
+  switch (p.kb) {
+    case 3: return launch_f8_nb<3>(a, p.nb, N, p.kgroups, epi, st);
+    case 2: return launch_f8_nb<2>(a, p.nb, N, p.kgroups, epi, st);
+    default: return launch_f8_nb<1>(a, p.nb, N, p.kgroups, epi, st);
+  }
+}
+
 template <int WPB, int KS, int NB, int DEPTH, class XSrc, class Epi>
 hipError_t launch_skinny(const SkArgs& a, const XSrc& xs, int n_groups, int k_groups, int batch, const Epi& epi,
                          hipStream_t st) {
@@ -496,6 +707,64 @@ hipError_t skinny_out(const OutProjArgs& a, int kgroups) {
   const int MN = a.rows * a.N;
   return launch(&k_reduce_rows, dim3((MN / 4 + 255) / 256), dim3(256), 0, a.stream, MN, kgroups, (const float*)part,
                 (bf16_t*)a.y);
+}
+
+// ------------------------------------------------------------ FP8 host side
+bool fp8_gemm_supported(int N, int K) { return N >= 16 && N % 16 == 0 && K >= 512 && K % 512 == 0; }
+
+F8Plan fp8_plan(int M, int N, int K) {
+  F8Plan p{};
+  if (!fp8_gemm_supported(N, K) || M < 1) return p;
+  // the most k-blocks per wave, up to 3 (fewest k-groups, so the fewest
+  // fp32 partials; 4 measured slower for W^O), that divide K; then the
+  // widest column group that still gives a block per CU, within the
+  // registers (NB x KB operand tiles of 8 VGPRs)
+  for (int kb : {3, 2, 1})
+    if ((K / 512) % kb == 0) {
+      p.kb = kb;
+      break;
+    }
+  p.kgroups = K / (512 * p.kb);
+  p.nb = 1;
+  for (int nb : {4, 2})
+    if (nb * p.kb <= 12 && (N / 16) % nb == 0 && (long)(N / (16 * nb)) * p.kgroups >= 256) {
+      p.nb = nb;
+      break;
+    }
+  const size_t rows = std::min(M, 64);
+  p.xc_off = 0;
+  p.xs_off = (rows * K + 255) / 256 * 256;
+  p.part_off = p.xs_off + (rows * (K / 128) * 4 + 255) / 256 * 256;
+  p.ws_bytes = p.part_off + (p.kgroups > 1 ? (size_t)p.kgroups * rows * N * 4 : 0);
+  return p;
+}
+
+hipError_t fp8_quantize_weight(int N, int K, const bf16_t* W, uint8_t* codes, float* scales, hipStream_t st) {
+  return launch(&k_quant_w, dim3((N + 127) / 128, K / 128), dim3(256), 0, st, N, K, W, codes, scales);
+}
+
+// Y = Q(X) . Q(W)^T in chunks of 64 rows (each chunk streams the weight).
+hipError_t fp8_gemm(int M, int N, int K, const bf16_t* X, const uint8_t* Wc, const float* Ws, bf16_t* Y, uint8_t* ws,
+                    hipStream_t st) {
+  const F8Plan p = fp8_plan(M, N, K);
+  uint8_t* xc = ws + p.xc_off;
+  float* xs = (float*)(ws + p.xs_off);
+  for (int m0 = 0; m0 < M; m0 += 64) {
+    const int rows = std::min(64, M - m0);
+    const int tiles = rows * (K / 128);
+    MLA_TRY(launch(&k_quant_x, dim3((tiles + 15) / 16), dim3(256), 0, st, tiles, K, X + (long)m0 * K, xc, xs));
+    F8Args a{rows, K, xc, xs, Wc, Ws};
+    bf16_t* y = Y + (long)m0 * N;
+    if (p.kgroups == 1) {
+      MLA_TRY(launch_f8_kb(a, p, N, EpiRowsBf16{y, N}, st));
+      continue;
+    }
+    float* part = (float*)(ws + p.part_off);
+    MLA_TRY(launch_f8_kb(a, p, N, EpiKPart{part, rows, N}, st));
+    const int MN = rows * N;
+    MLA_TRY(launch(&k_reduce_rows, dim3((MN / 4 + 255) / 256), dim3(256), 0, st, MN, p.kgroups, (const float*)part, y));
+  }
+  return hipSuccess;
 }
 
 // c^Q = W^DQ h (k-groups + reduction), then W^UQ with RoPE and the

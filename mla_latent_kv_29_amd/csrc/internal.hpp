@@ -182,6 +182,19 @@ bool prefill_supported(const mla_dims& d, int act);
 hipError_t prefill_projections(const PrefillArgs& a);  // positions, c^KV, k^R, c^Q, q, k^C, v^C
 hipError_t prefill_attention(const PrefillArgs& a);    // causal attention over q, k, v -> out, lse
 hipError_t fast_prefill(const PrefillArgs& a);
+// FP8 (E4M3) block-scaled GEMM Y = Q(X) Q(W)^T: weights in 128 x 128 blocks,
+// activations quantised in 1 x 128 tiles into the workspace.
+struct F8Plan {
+  int kb, kgroups, nb;  // k-blocks per wave, k-groups, column blocks of 16 per block
+  // workspace (one 64-row chunk at a time): activation codes, their scales,
+  // fp32 partials of the k-groups
+  size_t xc_off, xs_off, part_off, ws_bytes;
+};
+bool fp8_gemm_supported(int N, int K);
+F8Plan fp8_plan(int M, int N, int K);
+hipError_t fp8_quantize_weight(int N, int K, const bf16_t* W, uint8_t* codes, float* scales, hipStream_t st);
+hipError_t fp8_gemm(int M, int N, int K, const bf16_t* X, const uint8_t* Wc, const float* Ws, bf16_t* Y, uint8_t* ws,
+                    hipStream_t st);
 bool skinny_out_supported(int rows, int N, int K);
 hipError_t skinny_out(const OutProjArgs& a, int kgroups);  // rows <= 64: k-groups + their sum
 hipError_t generic_out_project(const OutProjArgs& a);

@@ -45,6 +45,14 @@ LAYER_WORKLOADS = {
                                        lengths=("fixed", 4096), table="inorder", sigma=0.006, layers=61),
 }
 
+# FP8 block-scaled projections (mla_fp8_gemm) at decode row counts: every
+# MLA weight of one layer, W^O included, as (name, N, K).
+FP8_PROJECTIONS = (("W_DKV", 512, 7168), ("W_KR", 64, 7168), ("W_DQ", 1536, 7168), ("W_UQ", 24576, 1536),
+                   ("W_UK", 16384, 512), ("W_UV", 16384, 512), ("W_O", 7168, 16384))
+FP8_WORKLOADS = {
+    "fp8_proj_v3_r64": dict(index=10, rows=64, sigma=0.006),
+}
+
 # Prefill of fresh sequences (mla_prefill): batch sequences of the given lengths, packed.
 PREFILL_WORKLOADS = {
     "prefill_v3_bf16_b4_l4096": dict(index=5, dims=V3_DIMS, act="bf16", batch=4, lengths=("fixed", 4096),
@@ -52,7 +60,7 @@ PREFILL_WORKLOADS = {
 }
 
 TENSORS = {"W_DKV": 1, "W_KR": 2, "W_DQ": 3, "W_UQ": 4, "W_UK": 5, "W_UV": 6, "h": 7, "len": 8, "table": 9,
-           "latent": 10, "rope": 11, "W_O": 12, "o": 13}
+           "latent": 10, "rope": 11, "W_O": 12, "o": 13, "gemm_x": 14, "gemm_w": 15}
 
 
 def seed_of(seed, workload_index, tensor, b=0, block=0):
@@ -101,6 +109,14 @@ def head_outputs(dims, rows, std, dtype, device, seed=0, workload_index=0):
     """Per-head attention outputs o ~ N(0, std^2), [rows, n_heads, d_head]."""
     shape = (rows, dims["n_heads"], dims["d_head"])
     return normal(shape, std, seed_of(seed, workload_index, "o"), device, dtype)
+
+
+def gemm_operands(M, N, K, sigma, dtype, device, seed=0, workload_index=0):
+    """A projection's activations X ~ N(0, 1) [M, K] and weight W ~ N(0,
+    sigma^2) [N, K] (stored [out, in])."""
+    X = normal((M, K), 1.0, seed_of(seed, workload_index, "gemm_x", N, K), device, dtype)
+    W = normal((N, K), sigma, seed_of(seed, workload_index, "gemm_w", N, K), device, dtype)
+    return X, W
 
 
 def hidden(dims, b, t0, t1, dtype, device, seed=0, workload_index=0):

@@ -204,3 +204,49 @@ def test_output_project_workspace_and_argument_errors():
     assert call(ws=None) == L.MLA_ERR_WORKSPACE
     assert call(wsb=w - 1) == L.MLA_ERR_WORKSPACE
     assert call(ws=FAKE + 4) == L.MLA_ERR_ALIGN
+
+
+def test_fp8_gemm_workspace_and_argument_errors():
+    # activation codes and scales of one 64-row chunk (256-byte aligned regions), then the
+    # fp32 partials of the k-groups: W^DQ has 7 k-groups of 1024; K = 512 and K = 1536 are
+    # one k-group each (no partials)
+    def x_part(rows, K):
+        return (rows * K + 255) // 256 * 256 + (rows * (K // 128) * 4 + 255) // 256 * 256
+    assert m.mla_fp8_gemm_workspace_bytes(64, 1536, 7168) == x_part(64, 7168) + 7 * 64 * 1536 * 4
+    assert m.mla_fp8_gemm_workspace_bytes(100, 1536, 7168) == x_part(64, 7168) + 7 * 64 * 1536 * 4
+    assert m.mla_fp8_gemm_workspace_bytes(64, 16384, 512) == x_part(64, 512)
+    assert m.mla_fp8_gemm_workspace_bytes(8, 24576, 1536) == x_part(8, 1536)
+    assert m.mla_fp8_gemm_workspace_bytes(64, 7168, 16384) == x_part(64, 16384) + 16 * 64 * 7168 * 4
+    assert m.mla_fp8_gemm_workspace_bytes(8, 24576, 1000) == 0                     # unsupported K
+    assert m.mla_fp8_gemm_workspace_bytes(-1, 64, 512) == 0
+    w = m.mla_fp8_gemm_workspace_bytes(10, 1536, 7168)
+
+    def gemm(**o):
+        a = dict(M=10, N=1536, K=7168, x=FAKE, wc=FAKE, wsc=FAKE, y=FAKE, ws=FAKE, wsb=w)
+        a.update(o)
+        return m.mla_fp8_gemm(a["M"], a["N"], a["K"], a["x"], a["wc"], a["wsc"], a["y"], a["ws"], a["wsb"],
+                              stream=0, check=False)
+
+    assert gemm(M=0) == L.MLA_OK
+    assert gemm(M=-1) == L.MLA_ERR_DIMS
+    assert gemm(N=0) == L.MLA_ERR_DIMS
+    assert gemm(K=1 << 17) == L.MLA_ERR_DIMS
+    assert gemm(N=40) == L.MLA_ERR_UNSUPPORTED
+    assert gemm(K=640) == L.MLA_ERR_UNSUPPORTED
+    assert gemm(x=None) == L.MLA_ERR_NULL
+    assert gemm(wsc=None) == L.MLA_ERR_NULL
+    assert gemm(y=FAKE + 2) == L.MLA_ERR_ALIGN
+    assert gemm(wsc=FAKE + 2) == L.MLA_ERR_ALIGN
+    assert gemm(ws=None) == L.MLA_ERR_WORKSPACE
+    assert gemm(wsb=w - 4) == L.MLA_ERR_WORKSPACE
+
+    def quant(**o):
+        a = dict(w=FAKE, N=1536, K=7168, c=FAKE, s=FAKE)
+        a.update(o)
+        return m.mla_fp8_quantize_weight(a["w"], a["N"], a["K"], a["c"], a["s"], stream=0, check=False)
+
+    assert quant(N=0) == L.MLA_ERR_DIMS
+    assert quant(N=40) == L.MLA_ERR_UNSUPPORTED
+    assert quant(K=100) == L.MLA_ERR_UNSUPPORTED
+    assert quant(c=None) == L.MLA_ERR_NULL
+    assert quant(w=FAKE + 8) == L.MLA_ERR_ALIGN
