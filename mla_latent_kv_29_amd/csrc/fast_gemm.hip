@@ -17,6 +17,7 @@
 // only 64-256 activation rows: they stream the weights, so what matters is
 // keeping enough full cache lines in flight per CU.
 #include <algorithm>
+#include <type_traits>
 #include <math.h>
 #include "internal.hpp"
 
@@ -402,6 +403,29 @@ hipError_t fast_query(const DecodeArgs& a) {
 
 namespace {
 
+// RoPE frequencies theta^(-2m/d_rope), computed on the host in double, into
+// device memory: epilogues index them per lane, which a by-value kernel
+// argument would turn into a private-memory copy in every thread.
+struct FreqTable {
+  double f[32];
+};
+__global__ void k_store_freq(FreqTable t, int half, double* __restrict__ out) {
+  if ((int)threadIdx.x < half) out[threadIdx.x] = t.f[threadIdx.x];
+}
+
+// (cos, sin) of every token's RoPE angles pos_t * theta^(-2m/d_rope): one
+// thread per (token, pair), the same reduction as everywhere else.  The
+// projections' epilogues read them, once per head.
+__global__ void k_rope_table(int n_tok, int half, const int32_t* __restrict__ pos, const double* __restrict__ freq,
+                             float2* __restrict__ tab) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)n_tok * half) return;
+  const int t = (int)(i / half), m = (int)(i % half);
+  float cs, sn;
+  rope_cs_w(pos[t], freq[m], &cs, &sn);
+  tab[i] = make_float2(cs, sn);
+}
+
 // Position of token t in its sequence: t - cu_seqlens[b] for the b with
 // cu_seqlens[b] <= t < cu_seqlens[b + 1] (binary search).
 __global__ void k_positions(const int32_t* __restrict__ cu, int n_seq, int n_tok, int32_t* __restrict__ pos) {
@@ -431,18 +455,17 @@ struct EpiRowStore {
 struct EpiRopeRows {
   bf16_t* y;
   int ld;
-  const int32_t* pos;
-  double freq[32];
+  const float2* cs_tab;  // [n_tok][d_rope / 2] (cos, sin) of the token's angles
   __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
-    const int m = col >> 1;
+    const int m = col >> 1, half = ld >> 1;
     const bool odd = col & 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float other = __shfl_xor(v[r], 1, 64);
       const int rr = row + r;
       if (rr >= M) continue;
-      float cs, sn;
-      rope_cs_w(pos[rr], freq[m], &cs, &sn);
+      const float2 t = cs_tab[(long)rr * half + m];
+      const float cs = t.x, sn = t.y;
       const float x0 = odd ? other : v[r], x1 = odd ? v[r] : other;
       y[(long)rr * ld + col] = (bf16_t)(odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn);
     }
@@ -456,31 +479,18 @@ struct EpiRopeRows {
 struct EpiPrefillQ {
   bf16_t* q;
   int n_tok, d_head, d_rope;
-  const int32_t* pos;
   float scale2;
-  double freq[32];
+  // q[i][row][d] = scale2 * v for column d_head_rope i + d; the RoPE of q^R
+  // is left to the attention kernel, which rotates its query fragments as it
+  // loads them: a table load here would wait (vmcnt counts stores too) for
+  // every store before it.
   __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
     const int w = d_head + d_rope;
     const int i = col / w, d = col % w;
     bf16_t* qi = q + (long)i * n_tok * w;
-    if (d < d_head) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (row + r < M) qi[(long)(row + r) * w + d] = (bf16_t)(scale2 * v[r]);
-      return;
-    }
-    const int m = (d - d_head) >> 1;
-    const bool odd = (d - d_head) & 1;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float other = __shfl_xor(v[r], 1, 64);
-      const int rr = row + r;
-      if (rr >= M) continue;
-      float cs, sn;
-      rope_cs_w(pos[rr], freq[m], &cs, &sn);
-      const float x0 = odd ? other : v[r], x1 = odd ? v[r] : other;
-      qi[(long)rr * w + d] = (bf16_t)(scale2 * (odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn));
-    }
+    for (int r = 0; r < 4; ++r)
+      if (row + r < M) qi[(long)(row + r) * w + d] = (bf16_t)(scale2 * v[r]);
   }
 };
 
@@ -497,6 +507,197 @@ struct EpiHeadMajor {
   }
 };
 
+// ------------------------------------------------------------ 256 x 256 tiles
+// Y = X W^T (W[N][K]) for hundreds of rows and more (the prefill
+// projections).  256 x 256 output tile per 256-thread block, four waves of
+// 128 x 128 (4 x 4 v_mfma_f32_32x32x16_bf16 accumulators, 256 AGPRs), 32-deep
+// k-steps through a ring of four 32 KiB LDS stages (X tile, then W tile:
+// 256 rows x 64 B each) filled by global_load_lds_dwordx4 from asm, three
+// k-steps ahead; one block per CU.  Row r of a tile keeps its 16-byte chunk
+// c at slot c ^ ((r >> 2) & 3), so that the 16 lanes of each phase of a
+// fragment read (rows r .. r+15, one chunk) hit 16 different bank groups.
+// The 8 XCDs take contiguous ranges of tiles, ordered GB_GM row tiles x
+// successive column tiles, so the blocks running together on an XCD share
+// their X and W tiles in its L2.
+constexpr int GB_T = 256;                 // tile rows and columns
+constexpr int GB_BK = 32;                 // k per step
+constexpr int GB_TILE = GB_T * GB_BK * 2; // 16 KiB
+constexpr int GB_STAGE = 2 * GB_TILE;     // 32 KiB
+constexpr int GB_NS = 4;                  // stages
+constexpr int GB_LDS = GB_NS * GB_STAGE;  // 128 KiB
+constexpr int GB_GM = 4;
+
+struct BigArgs {
+  int M, N, K, mt, nt;
+  const bf16_t* X;  // [M][ldx]
+  long ldx;
+  const bf16_t* W;  // [N][ldw]
+  long ldw;
+};
+
+__device__ __forceinline__ void gb_dma(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_addr)
+               : "memory");
+}
+
+// An accumulator element read out of its AGPR where the code stands (the
+// compiler otherwise moves every accumulator of the tile to VGPRs at once).
+__device__ __forceinline__ float agpr_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
+
+template <class Epi>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(BigArgs a, Epi epi) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t gb_raw[];
+  typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hw = lane >> 5;
+  const int T = a.mt * a.nt, per = (T + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (w >= T) return;
+  const int grp = w / (GB_GM * a.nt), gm0 = grp * GB_GM, gsz = min(GB_GM, a.mt - gm0);
+  const int rr = w - grp * GB_GM * a.nt;
+  const int m0 = (gm0 + rr % gsz) * GB_T, n0 = (rr / gsz) * GB_T;
+  const uint32_t lds = (uint32_t)(uintptr_t)gb_raw;
+
+  // copies: wave w issues rows 16 (4w + n) + lane / 4 of each tile
+  // (n = 0..3), chunk slot lane % 4; the k position goes into the scalar base
+  uint32_t xo[4], wo[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int row = 16 * (4 * wave + n) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    xo[n] = (uint32_t)(min(row, a.M - 1 - m0) * a.ldx * 2 + 16 * c);
+    wo[n] = (uint32_t)(row * a.ldw * 2 + 16 * c);
+  }
+  const uint8_t* xb = (const uint8_t*)(a.X + (long)m0 * a.ldx);
+  const uint8_t* wb = (const uint8_t*)(a.W + (long)n0 * a.ldw);
+  auto issue = [&](int ks, int stg) {
+    const uint8_t* xk = xb + ks * 64;
+    const uint8_t* wk = wb + ks * 64;
+    const uint32_t d = lds + stg * GB_STAGE + 4096 * wave;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) gb_dma(xk, xo[n], d + 1024 * n);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) gb_dma(wk, wo[n], d + GB_TILE + 1024 * n);
+  };
+
+  // fragment read addresses of stages 0 and 2 (stages 1 and 3 add GB_STAGE):
+  // row 128 wm + 32 mi + l32 of the X tile, 128 wn + 32 ni + l32 of the W
+  // tile, chunk 2 k16 + hw
+  const int wm = wave >> 1, wn = wave & 1;
+  uint32_t fx[2][2], fw[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k16 = 0; k16 < 2; ++k16) {
+      const uint32_t o = lds + 2 * h * GB_STAGE + l32 * 64 + 16 * ((2 * k16 + hw) ^ ((l32 >> 2) & 3));
+      fx[h][k16] = o + 128 * wm * 64;
+      fw[h][k16] = o + GB_TILE + 128 * wn * 64;
+    }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int nk = a.K / GB_BK;  // a multiple of 4
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  auto step = [&](auto stg_c, int ks) {
+    constexpr int STG = decltype(stg_c)::value;
+    wait_vmcnt<16>();  // this wave's copies of k-step ks landed (two later k-steps may be in flight)
+    ring_barrier();    // every wave's copies of ks landed; every wave is done with ks - 1
+    // k-step ks + 3 into the stage of ks - 1; past the last k-step a repeat of
+    // it (never read), so that the loop body has no branch: a branch there
+    // makes the compiler move the accumulators between AGPRs and VGPRs
+    issue(min(ks + 3, nk - 1), (STG + 3) & 3);
+    constexpr int H = STG >> 1;
+    constexpr uint32_t SO = (STG & 1) * GB_STAGE;
+    bf16x8 xa[2][4], wa[2][4];
+#pragma unroll
+    for (int k16 = 0; k16 < 2; ++k16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[k16][i] = *(const lbf16x8*)(fx[H][k16] + SO + 2048 * i);
+        wa[k16][i] = *(const lbf16x8*)(fw[H][k16] + SO + 2048 * i);
+      }
+#pragma unroll
+    for (int k16 = 0; k16 < 2; ++k16) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[k16][i], wa[k16][j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int ks = 0; ks < nk; ks += 4) {
+    step(std::integral_constant<int, 0>{}, ks);
+    step(std::integral_constant<int, 1>{}, ks + 1);
+    step(std::integral_constant<int, 2>{}, ks + 2);
+    step(std::integral_constant<int, 3>{}, ks + 3);
+  }
+  wait_vmcnt<0>();  // the repeat copies land before the block leaves
+
+  // C lane layout: column l32 of each 32 x 32 block, rows 8 j + 4 hw + 0..3.
+  // The tile origin passes through an empty asm statement so that no output
+  // address is computed before the k-loop and held across it.
+  int row0 = m0 + 128 * wm + 4 * hw, col0 = n0 + 128 * wn + l32;
+  asm volatile("" : "+v"(row0), "+v"(col0));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // one accumulator block at a time leaves the AGPRs (volatile reads,
+      // in program order); a fresh opaque copy of the origin per block keeps
+      // the compiler from holding every block's row addresses at once
+      int rb = row0, cb = col0;
+      asm volatile("" : "+v"(rb), "+v"(cb));
+      f32x16 t;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[e] = agpr_read(acc[i][j][e]);
+      // a block entirely past the last row stores nothing
+      if (__builtin_amdgcn_readfirstlane(m0 + 128 * wm + 32 * i) >= a.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+        epi(0, rb + 32 * i + 8 * q, cb + 32 * j, v, 0, a.M);
+      }
+    }
+}
+
+bool big_gemm_ok(int M, int N, int K) { return M >= GB_T && N % GB_T == 0 && K % 128 == 0; }
+
+template <class Epi>
+hipError_t launch_big(int M, int N, int K, const bf16_t* X, long ldx, const bf16_t* W, long ldw, const Epi& epi,
+                      hipStream_t st) {
+  BigArgs a{M, N, K, (M + GB_T - 1) / GB_T, N / GB_T, X, ldx, W, ldw};
+  static bool attr_set = false;  // one flag per epilogue type
+  if (!attr_set) {
+    MLA_TRY(hipFuncSetAttribute((const void*)&k_gemm_big<Epi>, hipFuncAttributeMaxDynamicSharedMemorySize, GB_LDS));
+    attr_set = true;
+  }
+  const int T = a.mt * a.nt;
+  return launch(&k_gemm_big<Epi>, dim3(8 * ((T + 7) / 8)), dim3(256), GB_LDS, st, a, epi);
+}
+
+// Y = X W^T with the 256 x 256 kernel when the shape fits it, else the
+// 64 x 64 one.
+template <class Epi>
+hipError_t gemm_xwt(int M, int N, int K, const bf16_t* X, long ldx, const bf16_t* W, long ldw, const Epi& epi,
+                    hipStream_t st) {
+  if (big_gemm_ok(M, N, K)) return launch_big(M, N, K, X, ldx, W, ldw, epi, st);
+  GemmArgs g = gemm_args(M, N, K, X, ldx, 0, W, ldw, 0, 1);
+  return launch_gemm<true>(g, 1, 1, epi, st);
+}
+
 }  // namespace
 
 hipError_t prefill_projections(const PrefillArgs& a) {
@@ -510,24 +711,22 @@ hipError_t prefill_projections(const PrefillArgs& a) {
   bf16_t* kc = (bf16_t*)(a.ws + a.L.kc);
   bf16_t* vc = (bf16_t*)(a.ws + a.L.vc);
   MLA_TRY(launch(&k_positions, dim3((n + 255) / 256), dim3(256), 0, a.stream, a.cu_seqlens, a.n_seq, n, pos));
-  double freq[32] = {};
-  for (int m = 0; m < d.d_rope / 2; ++m) freq[m] = pow((double)d.rope_theta, -2.0 * m / d.d_rope);
-  GemmArgs g = gemm_args(n, d.d_c, d.d_model, a.h, d.d_model, 0, a.W_DKV, d.d_model, 0, 1);
-  MLA_TRY(launch_gemm<true>(g, 1, 1, EpiRowStore{ckv, d.d_c}, a.stream));
-  g = gemm_args(n, d.d_rope, d.d_model, a.h, d.d_model, 0, a.W_KR, d.d_model, 0, 1);
-  EpiRopeRows er{kr, d.d_rope, pos, {}};
-  for (int m = 0; m < 32; ++m) er.freq[m] = freq[m];
-  MLA_TRY(launch_gemm<true>(g, 1, 1, er, a.stream));
-  g = gemm_args(n, d.d_cq, d.d_model, a.h, d.d_model, 0, a.W_DQ, d.d_model, 0, 1);
-  MLA_TRY(launch_gemm<true>(g, 1, 1, EpiRowStore{cq, d.d_cq}, a.stream));
-  g = gemm_args(n, H * w, d.d_cq, cq, d.d_cq, 0, a.W_UQ, d.d_cq, 0, 1);
-  EpiPrefillQ eq{q, n, d.d_head, d.d_rope, pos, a.scale * LOG2E, {}};
-  for (int m = 0; m < 32; ++m) eq.freq[m] = freq[m];
-  MLA_TRY(launch_gemm<true>(g, 1, 1, eq, a.stream));
-  g = gemm_args(n, H * d.d_head, d.d_c, ckv, d.d_c, 0, a.W_UK, d.d_c, 0, 1);
-  MLA_TRY(launch_gemm<true>(g, 1, 1, EpiHeadMajor{kc, n, d.d_head}, a.stream));
-  g = gemm_args(n, H * d.d_head, d.d_c, ckv, d.d_c, 0, a.W_UV, d.d_c, 0, 1);
-  return launch_gemm<true>(g, 1, 1, EpiHeadMajor{vc, n, d.d_head}, a.stream);
+  FreqTable ft{};
+  for (int m = 0; m < d.d_rope / 2; ++m) ft.f[m] = pow((double)d.rope_theta, -2.0 * m / d.d_rope);
+  double* freq = (double*)(a.ws + a.L.freq);
+  MLA_TRY(launch(&k_store_freq, dim3(1), dim3(64), 0, a.stream, ft, d.d_rope / 2, freq));
+  float2* cs_tab = (float2*)(a.ws + a.L.rope);
+  const long nrope = (long)n * (d.d_rope / 2);
+  MLA_TRY(launch(&k_rope_table, dim3((unsigned)((nrope + 255) / 256)), dim3(256), 0, a.stream, n, d.d_rope / 2,
+                 (const int32_t*)pos, (const double*)freq, cs_tab));
+  MLA_TRY(gemm_xwt(n, d.d_c, d.d_model, a.h, d.d_model, a.W_DKV, d.d_model, EpiRowStore{ckv, d.d_c}, a.stream));
+  EpiRopeRows er{kr, d.d_rope, cs_tab};
+  MLA_TRY(gemm_xwt(n, d.d_rope, d.d_model, a.h, d.d_model, a.W_KR, d.d_model, er, a.stream));
+  MLA_TRY(gemm_xwt(n, d.d_cq, d.d_model, a.h, d.d_model, a.W_DQ, d.d_model, EpiRowStore{cq, d.d_cq}, a.stream));
+  EpiPrefillQ eq{q, n, d.d_head, d.d_rope, a.scale * LOG2E};
+  MLA_TRY(gemm_xwt(n, H * w, d.d_cq, cq, d.d_cq, a.W_UQ, d.d_cq, eq, a.stream));
+  MLA_TRY(gemm_xwt(n, H * d.d_head, d.d_c, ckv, d.d_c, a.W_UK, d.d_c, EpiHeadMajor{kc, n, d.d_head}, a.stream));
+  return gemm_xwt(n, H * d.d_head, d.d_c, ckv, d.d_c, a.W_UV, d.d_c, EpiHeadMajor{vc, n, d.d_head}, a.stream);
 }
 
 // Combine on MFMA: merge the splits into O_lat, then out_i = W^UV_i O_lat_i

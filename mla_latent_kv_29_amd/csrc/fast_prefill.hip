@@ -7,7 +7,9 @@
 // sequence): for every token j of every packed sequence and every head i,
 //     o_{j,i} = sum_{t<=j} p_t v^C_{t,i},  p = softmax_t(tau q_{j,i} . k_{t,i}),
 // and lse_{j,i} (natural log).  q arrives pre-scaled by tau log2(e), so the
-// softmax runs in the exp2 domain.
+// softmax runs in the exp2 domain, and without its RoPE: each wave rotates
+// the q^R part of its query fragments as it loads them, from a per-token
+// (cos, sin) table.
 //
 // Work item = (sequence, head, tile of 128 query rows); four waves of 32 rows.
 // All query tiles of one (sequence, head) run on one XCD together, so the K
@@ -77,11 +79,12 @@ __device__ __forceinline__ int kr_slot(int r, int c) { return c ^ ((r >> 1) & 7)
 __device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
 
 struct PaArgs {
-  const bf16_t* q;   // [H][n_tok][192], pre-scaled by tau log2(e)
+  const bf16_t* q;   // [H][n_tok][192], pre-scaled by tau log2(e), RoPE not yet applied
   const bf16_t* kc;  // [H][n_tok][128]
   const bf16_t* vc;  // [H][n_tok][128]
   const bf16_t* kr;  // [n_tok][64]
   const int32_t* cu; // [n_seq + 1]
+  const float2* cs_tab;  // [n_tok][32] (cos, sin) of the tokens' RoPE angles
   int n_tok, qtiles, n_seq;
   bf16_t* out;       // [n_tok][H][128]
   float* lse;        // [n_tok][H] or null
@@ -180,9 +183,27 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
   const int qrow = wq0 + l32;
   bf16x8 qf[12];
   {
-    const bf16_t* qp = a.q + ((size_t)h * a.n_tok + start + min(qrow, len - 1)) * PDQK + 8 * hw;
+    const int tok = start + min(qrow, len - 1);
+    const bf16_t* qp = a.q + ((size_t)h * a.n_tok + tok) * PDQK + 8 * hw;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+    // RoPE of q^R (dims 128..191, pairs (2m, 2m+1) within the lane's eight
+    // values) at the token's position, from the (cos, sin) table
+    const float2* cs = a.cs_tab + (size_t)tok * (PDR / 2) + 4 * hw;
+    float2 t[4][4];
+#pragma unroll
+    for (int ks = 8; ks < 12; ++ks)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) t[ks - 8][p] = cs[8 * (ks - 8) + p];
+#pragma unroll
+    for (int ks = 8; ks < 12; ++ks)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = (float)qf[ks][2 * p], x1 = (float)qf[ks][2 * p + 1];
+        const float c = t[ks - 8][p].x, sn = t[ks - 8][p].y;
+        qf[ks][2 * p] = (bf16_t)(x0 * c - x1 * sn);
+        qf[ks][2 * p + 1] = (bf16_t)(x0 * sn + x1 * c);
+      }
   }
   wait_vmcnt<0>();  // the compiler's loads are done before the copies go out
   const TileOffsets to = tile_offsets(wave, lane);
@@ -339,7 +360,8 @@ bool prefill_supported(const mla_dims& d, int act) {
 hipError_t prefill_attention(const PrefillArgs& a) {
   const int qtiles = (a.max_seqlen + BQ - 1) / BQ;
   PaArgs pa{(const bf16_t*)(a.ws + a.L.q), (const bf16_t*)(a.ws + a.L.kc), (const bf16_t*)(a.ws + a.L.vc),
-            (const bf16_t*)(a.ws + a.L.kr), a.cu_seqlens, a.n_tok, qtiles, a.n_seq, a.out, a.lse_out};
+            (const bf16_t*)(a.ws + a.L.kr), a.cu_seqlens, (const float2*)(a.ws + a.L.rope), a.n_tok, qtiles,
+            a.n_seq, a.out, a.lse_out};
   static bool attr_set = false;
   if (!attr_set) {
     MLA_TRY(hipFuncSetAttribute((const void*)&k_prefill_attn, hipFuncAttributeMaxDynamicSharedMemorySize, PA_LDS));

@@ -108,14 +108,16 @@ struct AppendArgs {
 //   kc  : bf16  [H][n][d_head]     k^C = W^UK c^KV (explicit, per head)
 //   vc  : bf16  [H][n][d_head]     v^C = W^UV c^KV
 struct PrefillLayout {
-  size_t pos, ckv, kr, cq, q, kc, vc, total;
+  size_t freq, pos, rope, ckv, kr, cq, q, kc, vc, total;
 };
 
 inline PrefillLayout prefill_layout(const mla_dims& d, int n_tok) {
   const size_t n = (size_t)n_tok, H = d.n_heads;
   PrefillLayout w;
   size_t o = 0;
+  w.freq = o; o = align256(o + 32 * 8);  // RoPE frequencies (double)
   w.pos = o; o = align256(o + n * 4);
+  w.rope = o; o = align256(o + n * (d.d_rope / 2) * 8);  // (cos, sin) per token and RoPE pair
   w.ckv = o; o = align256(o + n * d.d_c * 2);
   w.kr = o;  o = align256(o + n * d.d_rope * 2);
   w.cq = o;  o = align256(o + n * d.d_cq * 2);

@@ -131,9 +131,10 @@ def test_prefill_workspace_and_argument_errors():
     d = _dims()
     w1 = m.mla_prefill_workspace_bytes(d, m.MLA_BF16, 1)
     w100 = m.mla_prefill_workspace_bytes(d, m.MLA_BF16, 100)
-    # per token: position, c^KV, k^R, c^Q, q, k^C and v^C (bf16), 256-byte aligned regions
-    per_tok = 4 + 2 * (512 + 64 + 1536 + 128 * 192 + 2 * 128 * 128)
-    assert w100 >= 100 * per_tok and w100 < 100 * per_tok + 7 * 256
+    # RoPE frequencies (256 B), then per token: position, 32 (cos, sin) pairs, c^KV, k^R, c^Q,
+    # q, k^C and v^C (bf16), 256-byte aligned regions
+    per_tok = 4 + 32 * 8 + 2 * (512 + 64 + 1536 + 128 * 192 + 2 * 128 * 128)
+    assert w100 >= 256 + 100 * per_tok and w100 < 256 + 100 * per_tok + 8 * 256
     assert 0 < w1 < w100
     assert m.mla_prefill_workspace_bytes(d, m.MLA_BF16, -1) == 0
 
