@@ -757,8 +757,13 @@ hipError_t out_project(const OutProjArgs& a) {
   const int s = out_proj_splits(a.act, a.rows, a.N, a.K);
   if (s == 0) return generic_out_project(a);
   if (skinny_out_supported(a.rows, a.N, a.K)) return skinny_out(a, s);
+  // one pass (enough tiles without a K split): the 256 x 256 kernel where it
+  // fits and still gives a block per CU
+  const EpiRowStore ey{(bf16_t*)a.y, a.N};
+  if (s == 1 && big_gemm_ok(a.rows, a.N, a.K) && (long)((a.rows + 255) / 256) * (a.N / 256) >= 256)
+    return launch_big(a.rows, a.N, a.K, (const bf16_t*)a.o, a.K, (const bf16_t*)a.W_O, a.K, ey, a.stream);
   GemmArgs g = gemm_args(a.rows, a.N, a.K, (const bf16_t*)a.o, a.K, 0, (const bf16_t*)a.W_O, a.K, 0, s);
-  if (s == 1) return launch_gemm<true>(g, 1, 1, EpiRowStore{(bf16_t*)a.y, a.N}, a.stream);
+  if (s == 1) return launch_gemm<true>(g, 1, 1, ey, a.stream);
   float* part = (float*)a.ws;
   MLA_TRY(launch_gemm<true>(g, 1, s, EpiPartial{part, a.N, (long)a.rows * a.N}, a.stream));
   return launch(&k_reduce_cq, dim3((a.rows * a.N + 255) / 256), dim3(256), 0, a.stream, a.rows, a.N, s,

@@ -692,9 +692,11 @@ bool skinny_query_supported(const mla_dims& d, int R) {
          d.d_head == AB_DH && d.d_c == 2 * AB_NCOL && d.d_rope == 64 && d.n_heads % 4 == 0;
 }
 
-// W^O: 4 waves x 8 k-steps = 1024 k per k-group, 4 column blocks of 16 per
-// block (64 columns), three of them loading ahead; 70 KiB of LDS, so two
-// blocks share a CU and one's reduction overlaps the other's loads.
+// W^O: 1024 k per k-group.  With N a multiple of 448 (d_model 7168): 8 waves
+// x 4 k-steps and 28 column blocks of 16 per block, four loading ahead, so
+// that each block streams 0.9 MB of the weight without a break (one block
+// per CU); measured 57 us at 64 rows against 84 us for blocks of 64 columns
+// (4 waves x 8 k-steps, three ahead), which serve other N.
 bool skinny_out_supported(int rows, int N, int K) {
   return rows >= 1 && rows <= 64 && N % 64 == 0 && K % 1024 == 0 && K / 1024 <= 64;
 }
@@ -703,7 +705,11 @@ hipError_t skinny_out(const OutProjArgs& a, int kgroups) {
   SkArgs s{a.rows, 1024, (const bf16_t*)a.W_O, a.K, 0};
   XPlain xs{(const bf16_t*)a.o, a.K, 0};
   float* part = (float*)a.ws;
-  MLA_TRY((launch_skinny<4, 8, 4, 3>(s, xs, a.N / 64, kgroups, 1, EpiKPart{part, a.rows, a.N}, a.stream)));
+  const EpiKPart epi{part, a.rows, a.N};
+  if (a.N % 448 == 0)  // 8 waves x 4 k-steps, 28 column blocks streamed four ahead: 256 blocks at V3
+    MLA_TRY((launch_skinny<8, 4, 28, 4>(s, xs, a.N / 448, kgroups, 1, epi, a.stream)));
+  else
+    MLA_TRY((launch_skinny<4, 8, 4, 3>(s, xs, a.N / 64, kgroups, 1, epi, a.stream)));
   const int MN = a.rows * a.N;
   return launch(&k_reduce_rows, dim3((MN / 4 + 255) / 256), dim3(256), 0, a.stream, MN, kgroups, (const float*)part,
                 (bf16_t*)a.y);

@@ -55,6 +55,13 @@ def test_output_project_many_rows_split_k(rows):
     check_rows(o, W, y, list(range(rows)), TOL_BF16)
 
 
+def test_output_project_many_rows_256_tiles():
+    """2600 rows: the 256 x 256-tile kernel (11 row tiles x 28 column tiles),
+    a ragged last row tile; sampled rows against the oracle."""
+    o, W, y = project(V3, m.MLA_BF16, 2600)
+    check_rows(o, W, y, [0, 255, 256, 1300, 2559, 2560, 2599], TOL_BF16)
+
+
 def test_output_project_large_rows_single_pass():
     """1100 rows fill the chip without splitting K; sampled rows (first, last
     of a tile, ragged tail) against the oracle, all rows finite."""
