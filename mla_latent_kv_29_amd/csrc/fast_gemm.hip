@@ -441,8 +441,11 @@ __global__ void k_positions(const int32_t* __restrict__ cu, int n_seq, int n_tok
 
 // Y[row][col] (bf16, row stride ld)
 struct EpiRowStore {
+  static constexpr bool kRows8 = true;  // has mul() and store8() for the staged 256 x 256 epilogue
   bf16_t* y;
   int ld;
+  __device__ float mul() const { return 1.0f; }
+  __device__ void store8(int row, int col, bf16x8 v) const { *(bf16x8*)(y + (long)row * ld + col) = v; }
   __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -477,9 +480,15 @@ struct EpiRopeRows {
 // 16-column block is all content or all RoPE (d_head % 16 == 0), so the
 // branch is wave-uniform.
 struct EpiPrefillQ {
+  static constexpr bool kRows8 = true;
   bf16_t* q;
   int n_tok, d_head, d_rope;
   float scale2;
+  __device__ float mul() const { return scale2; }
+  __device__ void store8(int row, int col, bf16x8 v) const {  // 8 columns never straddle a head (w % 8 == 0)
+    const int w = d_head + d_rope, i = col / w, d = col % w;
+    *(bf16x8*)(q + ((long)i * n_tok + row) * w + d) = v;
+  }
   // q[i][row][d] = scale2 * v for column d_head_rope i + d; the RoPE of q^R
   // is left to the attention kernel, which rotates its query fragments as it
   // loads them: a table load here would wait (vmcnt counts stores too) for
@@ -496,8 +505,14 @@ struct EpiPrefillQ {
 
 // k^C or v^C: column n = d_head i + d -> y[i][row][d]
 struct EpiHeadMajor {
+  static constexpr bool kRows8 = true;
   bf16_t* y;
   int n_tok, d_head;
+  __device__ float mul() const { return 1.0f; }
+  __device__ void store8(int row, int col, bf16x8 v) const {
+    const int i = col / d_head, d = col % d_head;
+    *(bf16x8*)(y + ((long)i * n_tok + row) * d_head + d) = v;
+  }
   __device__ void operator()(int, int row, int col, f32x4 v, int, int M) const {
     const int i = col / d_head, d = col % d_head;
     bf16_t* yi = y + (long)i * n_tok * d_head;
@@ -547,6 +562,12 @@ __device__ __forceinline__ float agpr_read(float x) {
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
   return r;
 }
+
+// Epilogues that can take eight consecutive columns of a row at once
+template <class E, class = void>
+struct has_rows8 : std::false_type {};
+template <class E>
+struct has_rows8<E, std::void_t<decltype(E::kRows8)>> : std::bool_constant<E::kRows8> {};
 
 template <class Epi>
 __global__ __launch_bounds__(256, 1) void k_gemm_big(BigArgs a, Epi epi) {
@@ -646,6 +667,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(BigArgs a, Epi epi) {
   }
   wait_vmcnt<0>();  // the repeat copies land before the block leaves
 
+  if constexpr (has_rows8<Epi>::value) {
+    // Staged epilogue: the wave's 128 x 128 tile goes to LDS (free now) as
+    // bf16, row-major with 256-byte rows (the 64-byte quarter q of row r at
+    // q ^ ((r >> 2) & 1): the two half-waves' rows r and r + 4 use other
+    // banks), then leaves in whole rows: 16 lanes store one row's 256 bytes.
+    ring_barrier();  // every wave is done with the stages
+    const uint32_t tile = lds + 32768 * wave;
+    const float mul = epi.mul();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 32 * i + 8 * (e >> 2) + 4 * hw + (e & 3), c = 32 * j + l32;
+          const uint32_t off = r * 256 + ((2 * c) ^ (((r >> 2) & 1) * 64));
+          *(__attribute__((address_space(3))) bf16_t*)(tile + off) = (bf16_t)(mul * agpr_read(acc[i][j][e]));
+        }
+    const int rbase = m0 + 128 * wm, cbase = n0 + 128 * wn;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int r = 4 * it + (lane >> 4), k = lane & 15;
+      const bf16x8 v = *(const lbf16x8*)(tile + r * 256 + 16 * (k ^ (((r >> 2) & 1) * 4)));
+      if (rbase + r < a.M) epi.store8(rbase + r, cbase + 8 * k, v);
+    }
+    return;
+  }
   // C lane layout: column l32 of each 32 x 32 block, rows 8 j + 4 hw + 0..3.
   // The tile origin passes through an empty asm statement so that no output
   // address is computed before the k-loop and held across it.
