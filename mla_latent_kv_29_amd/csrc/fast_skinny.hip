@@ -564,7 +564,7 @@ struct F8Args {
 // A lane's 32 operand bytes of a k-block are k = 16 g .. +15 and
 // 64 + 16 g .. +15 (g = lane / 16), the same order for W and X, so that
 // every 16-byte weight load covers 16 rows x 64 contiguous bytes.
-template <int KB, int NB, class Epi>
+template <int KB, int NB, int DEPTH, class Epi>
 __global__ __launch_bounds__(256) void k_skinny_f8(F8Args a, Epi epi) {
   constexpr int WPB = 4;
   using P = SkPlan<WPB, NB>;
@@ -590,18 +590,20 @@ __global__ __launch_bounds__(256) void k_skinny_f8(F8Args a, Epi epi) {
       xs[mb][j] = a.Xs[(long)row * kbs + kb0 + j];
     }
   }
-  // weight rows n0 + 16 nb + i16: every column block of the block at once
-  i32x8 wf[NB][KB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  // weight rows n0 + 16 nb + i16, DEPTH column blocks loading ahead (DEPTH =
+  // NB: all of them at once)
+  i32x8 wf[DEPTH][KB];
+  auto load_w = [&](int nb, int slot) {
     const uint8_t* wp = a.Wc + (long)(n0 + 16 * nb + i16) * a.K + 16 * g;
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const uint4 lo = *(const uint4*)(wp + (kb0 + j) * 128);
       const uint4 hi = *(const uint4*)(wp + (kb0 + j) * 128 + 64);
-      wf[nb][j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      wf[slot][j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-  }
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load_w(d, d);
 
   float* mine = slab + wave * P::SLAB;
 #pragma unroll
@@ -614,11 +616,12 @@ __global__ __launch_bounds__(256) void k_skinny_f8(F8Args a, Epi epi) {
       const float sw = a.Ws[(long)((n0 + 16 * nb) >> 7) * kbs + kb0 + j];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const f32x4 p =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb][j], xq[mb][j], f32x4{}, 0, 0, 0, 0, 0, 0);
+        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb % DEPTH][j], xq[mb][j], f32x4{}, 0,
+                                                                        0, 0, 0, 0, 0);
         acc[mb] += (sw * xs[mb][j]) * p;
       }
     }
+    if (nb + DEPTH < NB) load_w(nb + DEPTH, nb % DEPTH);
     // C = Y^T: lane holds n = 16 nb + 4g + r (r = 0..3), m = 16 mb + i16
     const int nr = nb % P::NBR;
 #pragma unroll
@@ -638,10 +641,10 @@ struct EpiRowsBf16 {
   }
 };
 
-template <int KB, int NB, class Epi>
+template <int KB, int NB, class Epi, int DEPTH = NB>
 hipError_t launch_f8(const F8Args& a, int n_groups, int k_groups, const Epi& epi, hipStream_t st) {
   constexpr int lds = SkPlan<4, NB>::LDS_BYTES;
-  auto kern = &k_skinny_f8<KB, NB, Epi>;
+  auto kern = &k_skinny_f8<KB, NB, DEPTH, Epi>;
   static bool attr_set = false;
   if (!attr_set) {
     MLA_TRY(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
@@ -653,6 +656,9 @@ hipError_t launch_f8(const F8Args& a, int n_groups, int k_groups, const Epi& epi
 template <int KB, class Epi>
 hipError_t launch_f8_nb(const F8Args& a, int nb, int N, int k_groups, const Epi& epi, hipStream_t st) {
   switch (nb) {
+    case 28:  // 448 columns a block, streamed four column blocks ahead
+      if constexpr (KB <= 2) return launch_f8<KB, 28, Epi, 4>(a, N / 448, k_groups, epi, st);
+      [[fallthrough]];
     case 4:
       if constexpr (KB * 4 <= 12) return launch_f8<KB, 4>(a, N / 64, k_groups, epi, st);
       [[fallthrough]];
@@ -732,8 +738,8 @@ F8Plan fp8_plan(int M, int N, int K) {
     }
   p.kgroups = K / (512 * p.kb);
   p.nb = 1;
-  for (int nb : {4, 2})
-    if (nb * p.kb <= 12 && (N / 16) % nb == 0 && (long)(N / (16 * nb)) * p.kgroups >= 256) {
+  for (int nb : {28, 4, 2})
+    if ((nb == 28 ? p.kb <= 2 : nb * p.kb <= 12) && (N / 16) % nb == 0 && (long)(N / (16 * nb)) * p.kgroups >= 256) {
       p.nb = nb;
       break;
     }
