@@ -76,3 +76,34 @@ def test_prefill_rows_past_the_end_are_not_written():
     and no output row is left unwritten (no NaN survives the fill)."""
     dims, W, hs, out, lse, tau = run_prefill([5, 70, 1], 1.0)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+def test_prefill_halves_equal_the_whole_call():
+    """mla_prefill_project then mla_prefill_attend (the benchmark's two timed
+    halves) give exactly what mla_prefill gives, on ragged sequences that take
+    the 256 x 256 projections (300 tokens) and the 64 x 64 ones (40)."""
+    for lengths in ([130, 7, 163], [33, 7]):
+        dims = V3
+        W = inputs.weights(dims, 0.006, torch.bfloat16, DEV, 0, 3)
+        h = torch.cat([inputs.hidden(dims, b, 0, int(L), torch.bfloat16, DEV, 0, 3) for b, L in enumerate(lengths)],
+                      0).contiguous()
+        n = h.shape[0]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=DEV)
+        d = m.make_dims(dims)
+        wsb = m.mla_prefill_workspace_bytes(d, m.MLA_BF16, n)
+        outs = []
+        for split in (False, True):
+            ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+            out = torch.full((n, dims["n_heads"], dims["d_head"]), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((n, dims["n_heads"]), float("nan"), dtype=torch.float32, device=DEV)
+            args = (d, m.MLA_BF16, h, n, len(lengths), cu, int(max(lengths)), W["W_DQ"], W["W_UQ"], W["W_UK"],
+                    W["W_UV"], W["W_DKV"], W["W_KR"], tau_of(dims), out, lse, ws, wsb)
+            if split:
+                m.mla_prefill_project(*args)
+                m.mla_prefill_attend(*args)
+            else:
+                m.mla_prefill(*args)
+            torch.cuda.synchronize()
+            outs.append((out.clone(), lse.clone()))
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), lengths
+        assert bool(torch.isfinite(outs[0][0].float()).all())
