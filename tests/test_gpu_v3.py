@@ -172,3 +172,27 @@ def test_v3_bf16_many_rows_two_row_blocks():
     tau = tau_of(V3)
     out, lse, _ = case.run(tau)
     check_all(case, out, lse, tau, TOL_BF16, heads=[0, 77, 127])
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_decode_halves_equal_the_whole_call(cache):
+    """mla_decode_query then mla_decode_attend (the benchmark's timed halves),
+    then mla_combine, give exactly what mla_decode + mla_combine give."""
+    from mla_latent_kv_29_amd import _lib as L
+    case = Case(V3, "bf16", cache, [200, 65, 3], s_q=2, table="shuffled", wl=4, num_splits=2)
+    tau = tau_of(V3) * 20.0
+    hq = case.hq()
+    s = case.sess
+    W = case.W
+    s.decode(hq, W, tau)
+    torch.cuda.synchronize()
+    whole = (s.out.clone(), s.lse.clone())
+    s.out.fill_(float("nan"))
+    s.lse.fill_(float("nan"))
+    args = (s.cdims, s.act, hq, s.batch, s.s_q, W["W_DQ"], W["W_UQ"], W["W_UK"], s.cache, s.block_table,
+            s.max_pages, s.seqlens, tau, s.num_splits, s.ws, s.ws_bytes, None)
+    L.mla_decode_query(*args)
+    L.mla_decode_attend(*args)
+    L.mla_combine(s.cdims, s.act, s.batch, s.s_q, s.ws, s.ws_bytes, W["W_UV"], s.out, s.lse, None)
+    torch.cuda.synchronize()
+    assert torch.equal(whole[0], s.out) and torch.equal(whole[1], s.lse)
