@@ -199,7 +199,7 @@ def run_layers(args, name):
         L.mla_decode_attend(*dargs)
         if e is not None:
             e[1].record(stream)
-        L.mla_combine(c, act, batch, s_q, sess.ws, sess.ws_bytes, W["W_UV"], sess.out, sess.lse, sp)
+        L.mla_combine(c, act, batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes, W["W_UV"], sess.out, sess.lse, sp)
         L.mla_output_project(c, act, R, sess.out, W["W_O"], y, ows, owsb, sp)
 
     def step(ev=None):
@@ -505,8 +505,8 @@ def main():
         L.mla_decode_attend(*dargs(k))
         if e is not None:
             e[2].record(stream)
-        L.mla_combine(c, sess.act, sess.batch, s_q, sess.ws, sess.ws_bytes, sets[k][1]["W_UV"], sess.out, sess.lse,
-                      sp)
+        L.mla_combine(c, sess.act, sess.batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes, sets[k][1]["W_UV"],
+                      sess.out, sess.lse, sp)
         if e is not None:
             e[3].record(stream)
 

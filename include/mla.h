@@ -29,8 +29,10 @@
  *     p_j = seqlens[b] - s_q + j and sees tokens 0..p_j (causal).
  *   - Every pointer argument except `dims`, `cache` (the descriptor itself)
  *     and the returned strings is DEVICE memory, contiguous, row-major, owned
- *     by the caller.  The library never allocates or frees and keeps no
- *     mutable global state; calls on different streams do not interfere.
+ *     by the caller.  The library never allocates or frees.  Its only global
+ *     state is a mutex-guarded record of which kernels have had their LDS
+ *     limit raised on which device, so calls from several threads and on
+ *     different streams do not interfere.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *     enqueued; nothing synchronises.  Arguments are validated on the host
  *     before anything is enqueued: on error a negative mla_status is returned
@@ -194,14 +196,14 @@ MLA_API int mla_fp8_gemm(int32_t M, int32_t N, int32_t K, const void* X, const v
                          const float* W_scales, void* Y, void* ws, size_t ws_bytes, void* stream);
 
 /* Speculative verify with multi-token prediction ("Читаем техотчёт
- * DeepSeek-V3 вместе", §2.2 Multi-Token Prediction, and the tokens_per_step
- * exercise of its practice part): a decode step with s_q = 1 + depth query
- * rows per sequence checks `depth` chained drafts, and the k-th draft counts
- * only if every earlier one was accepted, each with probability
- * `acceptance`.  Returns the expected number of tokens such a step emits,
- * 1 + acceptance + ... + acceptance^depth; NaN if acceptance is outside
- * [0, 1] or depth is outside 0..7 (s_q is at most 8).  Host arithmetic only:
- * no device, no stream.                                                      */
+ * DeepSeek-V3 вместе", §2.2 Multi-Token Prediction; the tokens_per_step
+ * exercise of its practice part): one decode step with s_q = 1 + depth query
+ * rows verifies a chain of `depth` drafted tokens, each drafted token being
+ * kept with probability `acceptance` given that its predecessors were kept.
+ * Returns the mean number of tokens the step yields,
+ * 1 + acceptance + acceptance^2 + ... + acceptance^depth; NaN for an
+ * acceptance outside [0, 1] or a depth outside 0..7 (s_q is at most 8).
+ * Pure host arithmetic: no device, no stream.                                */
 MLA_API double mla_mtp_tokens_per_step(double acceptance, int32_t depth);
 
 /* Workspace bytes needed by mla_decode/mla_combine for these sizes
@@ -252,17 +254,35 @@ MLA_API int mla_decode_attend(const mla_dims* dims, int32_t act_dtype, const voi
                const int32_t* seqlens, float softmax_scale, int32_t num_splits,
                void* ws, size_t ws_bytes, void* stream);
 
+/* Split count that mla_decode uses for these arguments (num_splits 0 = the
+ * default of mla_default_splits; a request is rounded so that every split
+ * spans the same number of pages).  This is the count mla_combine takes.
+ * 0 for invalid arguments.                                                  */
+MLA_API int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                  int32_t max_pages, int32_t num_splits);
+
 /* Decode, second half: merges the splits that the preceding mla_decode on
  * this workspace left (log-sum-exp weighted; empty splits skipped), then
- * applies W^UV per head:
+ * applies W^UV per head (the value path is linear in c^KV, so
+ * sum_t p_t W^UV_i c_t = W^UV_i sum_t p_t c_t; lesson §2.1.1):
  *   out [batch, s_q, n_heads, d_head] (act_dtype) = W^UV_i * O_lat_i;
  *   lse_out [batch, s_q, n_heads] fp32 natural-log log-sum-exp of the scaled
  *   scores, or NULL.  An empty sequence gives out = 0 and lse = -inf.
+ * num_splits: the split count of that mla_decode, i.e.
+ *   mla_decode_splits(dims, batch, s_q, max_pages, its num_splits argument);
+ *   1..4096.  The merge reads exactly num_splits partials per row.
+ * ws, ws_bytes: the decode's workspace; ws_bytes must be at least
+ *   mla_workspace_bytes(dims, act_dtype, batch, s_q, num_splits), else
+ *   MLA_ERR_WORKSPACE and nothing is enqueued.  The combine writes its own
+ *   scratch region of ws (the merged latent rows when it merges before
+ *   W^UV), never the queries or partials, so the halves of mla_decode may be
+ *   re-run on the same ws afterwards.
  * batch, s_q, act_dtype and ws must be those of the preceding mla_decode on
- * the same stream.                                                          */
+ * the same stream; a different num_splits gives wrong results but reads only
+ * inside the validated workspace.                                           */
 MLA_API int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch,
-                int32_t s_q, const void* ws, size_t ws_bytes, const void* W_UV,
-                void* out, float* lse_out, void* stream);
+                int32_t s_q, int32_t num_splits, void* ws, size_t ws_bytes,
+                const void* W_UV, void* out, float* lse_out, void* stream);
 
 /* Prefill (the non-absorbed form of the lesson's §2.1.1 for many new tokens
  * at once): n_seq fresh sequences packed back to back in

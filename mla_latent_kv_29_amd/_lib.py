@@ -15,7 +15,7 @@ MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE = 0, -1, -2, -3
 MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = -4, -5, -6, -7
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 
-EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits",
+EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits", "mla_decode_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
@@ -59,11 +59,12 @@ def _load():
         "mla_cache_append": (ctypes.c_int, [D, I32, P, I32, P, P, P, P, C, P, I32, P]),
         "mla_cache_write": (ctypes.c_int, [D, I32, P, P, I32, P, P, C, P, I32, P]),
         "mla_default_splits": (I32, [D, I32, I32, I32]),
+        "mla_decode_splits": (I32, [D, I32, I32, I32, I32]),
         "mla_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
         "mla_decode": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
         "mla_decode_query": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
         "mla_decode_attend": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
-        "mla_combine": (ctypes.c_int, [D, I32, I32, I32, P, SZ, P, P, P, P]),
+        "mla_combine": (ctypes.c_int, [D, I32, I32, I32, I32, P, SZ, P, P, P, P]),
         "mla_prefill_workspace_bytes": (SZ, [D, I32, I32]),
         "mla_prefill": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
         "mla_prefill_project": (ctypes.c_int, [D, I32, P, I32, I32, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]),
@@ -172,6 +173,10 @@ def mla_default_splits(dims, batch, s_q, max_pages):
     return int(_lib.mla_default_splits(ctypes.byref(dims), int(batch), int(s_q), int(max_pages)))
 
 
+def mla_decode_splits(dims, batch, s_q, max_pages, num_splits):
+    return int(_lib.mla_decode_splits(ctypes.byref(dims), int(batch), int(s_q), int(max_pages), int(num_splits)))
+
+
 def mla_workspace_bytes(dims, act_dtype, batch, s_q, num_splits):
     return int(_lib.mla_workspace_bytes(ctypes.byref(dims), int(act_dtype), int(batch), int(s_q), int(num_splits)))
 
@@ -230,9 +235,10 @@ def mla_decode_attend(*args, **kw):
     return _decode_call("mla_decode_attend", *args, **kw)
 
 
-def mla_combine(dims, act_dtype, batch, s_q, ws, ws_bytes, W_UV, out, lse_out=None, stream=None, check=True):
-    st = _lib.mla_combine(ctypes.byref(dims), int(act_dtype), int(batch), int(s_q), _ptr(ws), int(ws_bytes),
-                          _ptr(W_UV), _ptr(out), _ptr(lse_out), _stream(stream))
+def mla_combine(dims, act_dtype, batch, s_q, num_splits, ws, ws_bytes, W_UV, out, lse_out=None, stream=None,
+                check=True):
+    st = _lib.mla_combine(ctypes.byref(dims), int(act_dtype), int(batch), int(s_q), int(num_splits), _ptr(ws),
+                          int(ws_bytes), _ptr(W_UV), _ptr(out), _ptr(lse_out), _stream(stream))
     if check:
         _check("mla_combine", st)
     return st

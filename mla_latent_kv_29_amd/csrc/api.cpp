@@ -3,11 +3,47 @@
 // allocates device memory or synchronises.
 #include <algorithm>
 #include <math.h>
+#include <mutex>
+#include <set>
 #include <stdlib.h>
 #include <string.h>
+#include <utility>
 #include "internal.hpp"
 
 using namespace mla;
+
+namespace mla {
+
+// The MFMA path's shape: DeepSeek-V3's MLA (d_c 512, d_rope 64, 128 heads of
+// 128, 64-token pages), bf16 activations.
+static bool v3_shape(const mla_dims& d) {
+  return d.d_c == 512 && d.d_rope == 64 && d.n_heads == 128 && d.d_head == 128 && d.page_size == 64 &&
+         d.d_model % 32 == 0 && d.d_cq % 64 == 0;
+}
+
+bool fast_append_supported(const mla_dims& d, int act, int cache_dtype) {
+  return fast_append_shape(d) && act == MLA_BF16 && (cache_dtype == MLA_BF16 || cache_dtype == MLA_FP8_E4M3);
+}
+
+bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q) {
+  return v3_shape(d) && act == MLA_BF16 && (cache_dtype == MLA_BF16 || cache_dtype == MLA_FP8_E4M3) && s_q >= 1 &&
+         s_q <= 8;
+}
+
+hipError_t lds_limit(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
+
+}  // namespace mla
 
 namespace {
 
@@ -196,24 +232,31 @@ int mla_decode_attend(const mla_dims* dims, int32_t act_dtype, const void* hq, i
                      softmax_scale, num_splits, ws, ws_bytes, stream, 2);
 }
 
-int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t s_q, const void* ws, size_t ws_bytes,
-                const void* W_UV, void* out, float* lse_out, void* stream) {
-  (void)ws_bytes;
+int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_pages, int32_t num_splits) {
+  if (check_dims(dims) || batch <= 0 || s_q <= 0 || s_q > MAX_S_Q || max_pages <= 0 || num_splits < 0 ||
+      num_splits > MAX_SPLITS)
+    return 0;
+  int S = 0, pps = 0;
+  resolve_splits(dims, batch, s_q, max_pages, num_splits, &S, &pps);
+  return S;
+}
+
+int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t s_q, int32_t num_splits, void* ws,
+                size_t ws_bytes, const void* W_UV, void* out, float* lse_out, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
-  if (batch < 0 || s_q < 1 || s_q > MAX_S_Q) return MLA_ERR_DIMS;
+  if (batch < 0 || s_q < 1 || s_q > MAX_S_Q || num_splits < 1 || num_splits > MAX_SPLITS) return MLA_ERR_DIMS;
   if (batch == 0) return MLA_OK;
   if (!ws || !W_UV || !out) return MLA_ERR_NULL;
   if (!aligned16(ws) || !aligned16(W_UV) || !aligned16(out) || (lse_out && !aligned16(lse_out))) return MLA_ERR_ALIGN;
-  // The split count is known only to the preceding mla_decode; the kernels read
-  // it from the workspace header.  Host-side, the smallest layout must fit.
-  const size_t need = ws_layout(*dims, act_dtype, batch, s_q, 1).total;
-  if (ws_bytes < need) return MLA_ERR_WORKSPACE;
+  // The workspace must hold the plan of num_splits splits; the kernels read
+  // exactly that many partials, so a too-small workspace is refused here.
+  const WsLayout L = ws_layout(*dims, act_dtype, batch, s_q, num_splits);
+  if (ws_bytes < L.total) return MLA_ERR_WORKSPACE;
   CombineArgs a;
-  a.d = *dims; a.act = act_dtype; a.batch = batch; a.s_q = s_q; a.ws = (const uint8_t*)ws;
-  a.W_UV = W_UV; a.out = out; a.lse_out = lse_out; a.stream = (hipStream_t)stream;
-  a.L = ws_layout(*dims, act_dtype, batch, s_q, 1);
+  a.d = *dims; a.act = act_dtype; a.batch = batch; a.s_q = s_q; a.S = num_splits; a.ws = (uint8_t*)ws;
+  a.W_UV = W_UV; a.out = out; a.lse_out = lse_out; a.stream = (hipStream_t)stream; a.L = L;
   hipError_t e;
   if (!force_generic() && fast_decode_supported(*dims, act_dtype, MLA_BF16, s_q)) e = fast_combine(a);
   else e = generic_combine(a);

@@ -95,7 +95,7 @@ __device__ __forceinline__ void rope_cs(int pos, int m, int d_rope, float theta,
 __device__ __forceinline__ void rope_cs_w(int pos, double w, float* c, float* s) {
   const double x = (double)pos * w;
   const double k = rint(x * 0.15915494309189535);           // 1 / (2 pi)
-  const double r = fma(-k, 1.2246467991473532e-16, fma(-k, 6.283185307179586, x));  // 2 pi = hi + lo
+  const double r = fma(-k, 2.4492935982947064e-16, fma(-k, 6.283185307179586, x));  // 2 pi = hi + lo
   sincosf((float)r, s, c);
 }
 

@@ -178,13 +178,7 @@ __global__ __launch_bounds__(256) void k_append_v3(int n_tok, int d_model, float
 bool fast_append_shape(const mla_dims& d) { return d.d_c == DC && d.d_rope == DR && d.d_model % 32 == 0; }
 
 hipError_t fast_append(const AppendArgs& a) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_append_v3, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       APPEND_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  MLA_TRY(lds_limit((const void*)k_append_v3, APPEND_LDS));
   const int blocks = (a.n_tok + TOK - 1) / TOK;
   MLA_TRY(launch(&k_append_v3, dim3(blocks), dim3(256), APPEND_LDS, a.stream, a.n_tok, a.d.d_model,
                      a.d.rope_theta, (const bf16_t*)a.h, a.seq_id, a.pos, (const bf16_t*)a.W_DKV,

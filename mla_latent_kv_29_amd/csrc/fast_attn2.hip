@@ -136,10 +136,12 @@ struct Ctx {
   int wave, lane;
   uint32_t dma_ofs;           // lane part of a stage copy
   uint32_t dma_ofs_w;         // bf16: the same plus this wave's first copy (4096 * wave)
-  uint32_t koff;              // K fragment of the scores MFMA
-  uint32_t qr_ofs0, qr_ofs1;  // RoPE query fragments (k-steps 16, 17)
+  uint32_t koff_e, koff_o;    // K fragment of the scores MFMA (even / odd k-step), inside its stage
+  int kst;                    // 1 if this lane's score rows are tokens of the step's second stage
+  uint32_t qr_base;           // RoPE query fragments: row of the lane's head, its k-half
+  int qr_key;                 // ... and the chunk-pair permutation of that row
   uint32_t vofs1, vofs2;      // V^T transposing reads (wave's first channel block)
-  uint32_t pw_ofs, pr_ofs;    // P write (scores layout) / read (P.V layout)
+  uint32_t pw_ofs, pr_ofs;    // P write (this wave's head block) / read (P.V layout)
 };
 
 template <bool F8>
@@ -239,91 +241,52 @@ __device__ __forceinline__ void wait_step(const Ctx& c, int m) {
   }
 }
 
-// Score MFMA with a VGPR accumulator (see the file comment).
-__device__ __forceinline__ f32x4 mfma_s0(bf16x8 a, bf16x8 b) {
-  f32x4 c;
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+// Score MFMA with a VGPR accumulator (see the file comment).  One
+// v_mfma_f32_32x32x16_bf16 chain per step: dependent MFMAs that accumulate
+// into exactly the same registers issue back to back (the hardware forwards
+// the accumulator), and on gfx950 this shape runs at the full matrix rate,
+// which the 16x16x32 shape does not reach from one wave.
+__device__ __forceinline__ f32x16 mfma_s0(bf16x8 a, bf16x8 b) {
+  f32x16 c;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
   return c;
 }
-__device__ __forceinline__ f32x4 mfma_s(bf16x8 a, bf16x8 b, f32x4 c) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+__device__ __forceinline__ f32x16 mfma_s(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
   return c;
 }
-// Last MFMA of a chain: 12 wait states before anything may read the result.
-__device__ __forceinline__ f32x4 mfma_s_last(bf16x8 a, bf16x8 b, f32x4 c) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(c) : "v"(a), "v"(b));
+// Last MFMA of the chain: 12 wait states before a VALU instruction may read
+// the result (what the compiler itself inserts for this shape).
+__device__ __forceinline__ f32x16 mfma_s_last(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(c) : "v"(a), "v"(b));
   return c;
 }
 
-// S^T[16 tokens][16 heads] for stages A, B x head blocks 0, 1: 72 MFMAs in
-// four chains; every K fragment feeds two.  The K fragments of k-step ks+KD
-// are read while k-step ks multiplies; sched_barrier keeps that order (the
-// scheduler would otherwise sink each read to its use).
+// S^T[32 tokens][32 heads] of the step's two stages (rows 0-15: the first
+// stage, 16-31: the second) = K . Q^T over the 576 channels: 36 k-steps of
+// 16.  Lane l reads token l%32 of its stage, channels 16 ks + 8 (l/32) .. +7:
+// one 16-byte chunk, 2 ks + l/32, at the chunk-major offset of its token.
+// The K fragments of k-step ks+KD are read while k-step ks multiplies;
+// sched_barrier keeps that order (the scheduler would otherwise sink each
+// read to its use).  The RoPE query fragments (k-steps 32-35) come from LDS.
 constexpr int KD = 4;
+constexpr int KSTEPS = DKV / 16;  // 36
 template <bool F8>
-__device__ __forceinline__ bf16x8 rope_q(const Ctx& c, int ks, int hb) {
-  return *(lbf16x8*)(c.lds + Lay<F8>::QR_OFF + (ks == 16 ? c.qr_ofs0 : c.qr_ofs1) + 16 * 128 * hb);
+__device__ __forceinline__ bf16x8 rope_q(const Ctx& c, int r) {
+  return *(lbf16x8*)(c.lds + c.qr_base + 32 * (r ^ c.qr_key));
 }
-template <bool F8>
-__device__ __forceinline__ void step_scores(const Ctx& c, const lu8* stA, const lu8* stB, const bf16x8 (&qf)[16][2],
-                                            f32x4 (&sc)[2][2], const StageCopy& cx, const StageCopy& cy) {
-  const lu8* ka = stA + c.koff;
-  const lu8* kb = stB + c.koff;
-  bf16x8 fa[KD], fb[KD];
-#pragma unroll
-  for (int d = 0; d < KD; ++d) {
-    fa[d] = *(lbf16x8*)(ka + 1024 * d);
-    fb[d] = *(lbf16x8*)(kb + 1024 * d);
-  }
-  bf16x8 r0[2], r1[2];
-#pragma unroll
-  for (int ks = 0; ks < 18; ++ks) {
-    if (ks == 12) {  // RoPE query fragments for k-steps 16, 17
-      r0[0] = rope_q<F8>(c, 16, 0); r0[1] = rope_q<F8>(c, 16, 1);
-      r1[0] = rope_q<F8>(c, 17, 0); r1[1] = rope_q<F8>(c, 17, 1);
-    }
-    const bf16x8 a = fa[ks % KD], b = fb[ks % KD];
-    const bf16x8 q0 = ks < 16 ? qf[ks][0] : (ks == 16 ? r0[0] : r1[0]);
-    const bf16x8 q1 = ks < 16 ? qf[ks][1] : (ks == 16 ? r0[1] : r1[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (ks == 0) {
-      sc[0][0] = mfma_s0(a, q0);
-      sc[0][1] = mfma_s0(a, q1);
-      sc[1][0] = mfma_s0(b, q0);
-      sc[1][1] = mfma_s0(b, q1);
-    } else if (ks < 17) {
-      sc[0][0] = mfma_s(a, q0, sc[0][0]);
-      sc[0][1] = mfma_s(a, q1, sc[0][1]);
-      sc[1][0] = mfma_s(b, q0, sc[1][0]);
-      sc[1][1] = mfma_s(b, q1, sc[1][1]);
-    } else {
-      sc[0][0] = mfma_s_last(a, q0, sc[0][0]);
-      sc[0][1] = mfma_s_last(a, q1, sc[0][1]);
-      sc[1][0] = mfma_s_last(b, q0, sc[1][0]);
-      sc[1][1] = mfma_s_last(b, q1, sc[1][1]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (ks + KD < 18) {
-      fa[ks % KD] = *(lbf16x8*)(ka + 1024 * (ks + KD));
-      fb[ks % KD] = *(lbf16x8*)(kb + 1024 * (ks + KD));
-    }
-    // the next two stages' copies go out between these MFMAs, early in the
-    // step: the first at k-steps 1..5, the second at 6..10
-    if constexpr (!F8) {  // (the fp8 copies go out in the widening phase)
-      if (ks >= 1 && ks <= 5) copy_at(c, cx, ks - 1);
-      if (ks >= 6 && ks <= 10) copy_at(c, cy, ks - 6);
-    }
-  }
+__device__ __forceinline__ bf16x8 kfrag(const lu8* kb, const Ctx& c, int ks) {
+  return *(lbf16x8*)(kb + (ks & 1 ? c.koff_o : c.koff_e) + 512 * ks);
 }
-
-// Lane layout of S^T: head 16w + lane%16, tokens 4*(lane/16) + r.  Masks
-// tokens past the end of the split (nvalid may be <= 0: a padding stage).
-__device__ __forceinline__ void mask(const Ctx& c, f32x4& s, int nvalid) {
-  if (nvalid < T) {
-    const int tb = 4 * (c.lane >> 4);
+// Lane layout of S^T: head 32w + lane%32, value i is row (token of the step)
+// 8 (i/4) + 4 (lane/32) + i%4.  Masks tokens past the end of the split (nv
+// may be <= 0: a padding step).
+__device__ __forceinline__ void mask(const Ctx& c, f32x16& s, int nv) {
+  if (nv < 2 * T) {
+    const int hi = 4 * (c.lane >> 5);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (tb + r >= nvalid) s[r] = -INFINITY;
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + hi + (i & 3) >= nv) s[i] = -INFINITY;
   }
 }
 
@@ -343,114 +306,156 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return r;
 }
 
-// Maximum over the lanes l, l^16 (permlane16 swap leaves the two values of
-// each pair in the two results) and over l, l^32.
-__device__ __forceinline__ float max_x16(float m) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// Maximum over the lanes l and l^32 (the permlane32 swap leaves the two
+// values of each pair in its two results).
 __device__ __forceinline__ float max_x32(float m) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// P.V MFMAs of stages 2m-2, 2m-1 interleaved with the softmax of this
-// step's (masked) scores: the VALU instructions issue while each MFMA
-// occupies the matrix unit.  A wave issues about one instruction per four
-// cycles and a 32x32x16 MFMA keeps the unit busy for 32, so the softmax is
-// cut into 12 items of a few instructions, spread over the 32 slots
-// (generated at compile time; sched_barrier pins their order); head blocks
-// 0 and 1 alternate, which also spaces each item from the one it needs.  Weights go to P buffer m&1 as bf16; lane
-// heads 32w + 16hb + lane%16 (hb = 0, 1).
-struct PvwState {
+// One step of the pass, as one compile-time schedule of 68 MFMAs:
+//   part 1: the 36-MFMA score chain of stages 2m, 2m+1, with the 16 P.V
+//           MFMAs of stage 2m-2 (the previous step's first stage) slotted
+//           after every second score MFMA from k-step 3 on;
+//   part 2: the 16 P.V MFMAs of stage 2m-1 with the softmax of this step's
+//           scores cut into 9 items between them (the VALU work issues
+//           while each MFMA occupies the matrix unit).
+// So the matrix unit always has independent work queued: the fill of one
+// product's operand reads is covered by the other's MFMAs.  The weights go
+// to P buffer m&1 (see the softmax items) for the next step's P.V.
+//
+// P.V: O^T[128 ch][128 heads] of this wave's channel blocks += V^T . P^T;
+// MFMA t of a stage is channel block t%4 of head block t/4 (V^T fragment t%4
+// of the stage, P^T fragment t/4).  The stage's four V^T fragments are read
+// once per stage; the P^T fragments stream two ahead.
+//
+// The lane's 16 scores belong to head 32w + lane%32: values 0-7 are tokens
+// of the first stage in exactly the order the P.V operand takes them (tokens
+// 0-3, 8-11 on lanes 0-31; 4-7, 12-15 on lanes 32-63), values 8-15 those of
+// the second stage.  So the weights leave as two 16-byte stores, at the
+// place where the P.V read of head block w expects them.
+struct Fused {
   const Ctx& c;
   int m;
-  const f32x4 (&sc)[2][2];
-  const bf16x8 (&v)[2][4];
-  const bf16x8 (&p)[2][4];
+  const lu8* kb;                 // K fragments: the lane's stage
+  const bf16x8 (&qf)[32];
+  bf16x8 f[KD];                  // K fragments in flight
+  bf16x8 r[4];                   // RoPE query fragments (k-steps 32-35)
+  f32x16 sc;
+  const lu8 *va, *vb, *prd;      // previous step's two stages and P buffer
+  bf16x8 v[4], p[4];             // V^T of the current P.V stage; P^T ring
   f32x16 (&o)[4][4];
-  float (&m_ref)[2];
-  float (&m_all)[2];
-  float (&l_run)[2];
+  float& m_ref;
+  float& m_all;
+  float& l_run;
   bool& ovf;
   lu8* pw;
-  float ml[2];
-  f32x4 xa[2], xb[2];
+  const StageCopy &cx, &cy;
+  float ml;
+  float x[16];
 };
 
-template <int K>
-__device__ __forceinline__ void pvw_slot(PvwState& st) {
-  {
-    constexpr int j = K >> 4, hb = (K >> 2) & 3, i = K & 3;
-    st.o[i][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.v[j][i], st.p[j][hb], st.o[i][hb], 0, 0, 0);
+__device__ __forceinline__ void read_v(Fused& F, const lu8* st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(st + F.c.vofs1 + 1024 * i));
+    const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(st + F.c.vofs2 + 1024 * i));
+    const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+    F.v[i] = __builtin_bit_cast(bf16x8, s8);
   }
-  // item i (0..11) sits in slot 8i/3: part i/2 of head block i%2
-  constexpr int item = (3 * K + 7) / 8;
-  if constexpr (item < 12 && (8 * item) / 3 == K) {
-    constexpr int h = item & 1, part = item >> 1;
-    const f32x4 sA = st.sc[0][h], sB = st.sc[1][h];
-    if constexpr (part == 0) {
-      st.ml[h] = vmax(vmax3(sA[0], sA[1], sA[2]), vmax3(sA[3], sB[0], vmax3(sB[1], sB[2], sB[3])));
-    } else if constexpr (part == 1) {
-      st.ml[h] = max_x16(st.ml[h]);
-    } else if constexpr (part == 2) {
-      st.ml[h] = max_x32(st.ml[h]);
-      st.m_all[h] = vmax(st.m_all[h], st.ml[h]);
+}
+__device__ __forceinline__ void read_p(Fused& F, int j, int hb) {
+  F.p[hb] = *(lbf16x8*)(F.prd + j * P_STAGE + 1024 * hb);
+}
+// P.V MFMA t (0..15) of the current stage
+template <int T_>
+__device__ __forceinline__ void pv_mfma(Fused& F) {
+  constexpr int hb = T_ >> 2, i = T_ & 3;
+  F.o[i][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.v[i], F.p[hb], F.o[i][hb], 0, 0, 0);
+}
+
+// Part 1, k-step KS: score MFMA, K read KD ahead, and the P.V MFMA of stage
+// 2m-2 that follows it (after k-steps 3, 5, .., 33); the P^T fragment of
+// head block hb is read two P.V MFMAs before its first use.
+template <bool F8, int KS>
+__device__ __forceinline__ void part1(Fused& F) {
+  const Ctx& c = F.c;
+  if constexpr (KS == 26) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) F.r[q] = rope_q<F8>(c, q);
+  }
+  {
+    const bf16x8 a = F.f[KS % KD];
+    const bf16x8 q = KS < 32 ? F.qf[KS] : F.r[KS - 32];
+    if constexpr (KS == 0) F.sc = mfma_s0(a, q);
+    else if constexpr (KS < KSTEPS - 1) F.sc = mfma_s(a, q, F.sc);
+    else F.sc = mfma_s_last(a, q, F.sc);
+  }
+  if constexpr (KS + KD < KSTEPS) F.f[KS % KD] = kfrag(F.kb, c, KS + KD);
+  constexpr int t = (KS - 3) / 2;
+  if constexpr (KS >= 3 && (KS - 3) % 2 == 0 && t < 16) {
+    pv_mfma<t>(F);
+    // P^T of head block hb+2, one MFMA into head block hb
+    if constexpr ((t & 3) == 1 && t < 9) read_p(F, 0, (t >> 2) + 2);
+    if constexpr (t == 15) read_v(F, F.vb);  // the second stage's V^T, for part 2
+    if constexpr (t == 15) { read_p(F, 1, 0); read_p(F, 1, 1); }
+  }
+  // stage copies: the first at k-steps 1, 8, 15, 22, 29
+  if constexpr (!F8) {
+    if constexpr (KS % 7 == 1) copy_at(c, F.cx, KS / 7);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <bool F8, int... K>
+__device__ __forceinline__ void part1_all(Fused& F, std::integer_sequence<int, K...>) {
+  (part1<F8, K>(F), ...);
+}
+
+// Part 2, P.V MFMA T of stage 2m-1 and the softmax item that follows it.
+template <bool F8, int T_>
+__device__ __forceinline__ void part2(Fused& F) {
+  pv_mfma<T_>(F);
+  if constexpr ((T_ & 3) == 1 && T_ < 9) read_p(F, 1, (T_ >> 2) + 2);
+  // items at slots 0, 1, 2, 4, 6, 8, 10, 12, 14
+  constexpr int item = T_ < 3 ? T_ : (T_ % 2 == 0 ? T_ / 2 + 1 : -1);
+  if constexpr (item >= 0 && item < 9) {
+    const f32x16& s = F.sc;
+    if constexpr (item == 0) {
+      F.ml = vmax(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], vmax3(s[5], s[6], s[7])));
+    } else if constexpr (item == 1) {
+      F.ml = vmax3(F.ml, vmax3(s[8], s[9], s[10]), vmax3(s[11], s[12], vmax3(s[13], s[14], s[15])));
+    } else if constexpr (item == 2) {
+      F.ml = max_x32(F.ml);
+      F.m_all = vmax(F.m_all, F.ml);
       // the reference: the first step's maximum, or the exact maximum
       // already in m_ref when the pass is redone (it is never smaller)
-      if (st.m == 0) st.m_ref[h] = vmax(st.m_ref[h], st.ml[h]);
-      st.ovf |= st.ml[h] > st.m_ref[h] + HEADROOM;
-    } else if constexpr (part == 3) {
+      if (F.m == 0) F.m_ref = vmax(F.m_ref, F.ml);
+      F.ovf |= F.ml > F.m_ref + HEADROOM;
+    } else if constexpr (item <= 6) {
       // raw v_exp_f32: results below 2^-126 flush to zero, harmless here; a
       // score above the headroom only occurs in a pass that is redone
+      constexpr int q = item - 3;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st.xa[h][r] = __builtin_amdgcn_exp2f(sA[r] - st.m_ref[h]);
-    } else if constexpr (part == 4) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.xb[h][r] = __builtin_amdgcn_exp2f(sB[r] - st.m_ref[h]);
+      for (int rr = 0; rr < 4; ++rr) F.x[4 * q + rr] = __builtin_amdgcn_exp2f(s[4 * q + rr] - F.m_ref);
     } else {
-      const f32x4 xa = st.xa[h], xb = st.xb[h];
-      st.l_run[h] += (xa[0] + xa[1]) + (xa[2] + xa[3]) + (xb[0] + xb[1]) + (xb[2] + xb[3]);
-      bf16x4 pa, pb;
+      constexpr int h = item - 7;  // stage
+      const float* x = F.x + 8 * h;
+      F.l_run += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+      bf16x8 pk;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pa[r] = (bf16_t)xa[r];
-        pb[r] = (bf16_t)xb[r];
-      }
-      *(__attribute__((address_space(3))) bf16x4*)(st.pw + 512 * h) = pa;
-      *(__attribute__((address_space(3))) bf16x4*)(st.pw + 512 * h + P_STAGE) = pb;
+      for (int rr = 0; rr < 8; ++rr) pk[rr] = (bf16_t)x[rr];
+      *(__attribute__((address_space(3))) bf16x8*)(F.pw + h * P_STAGE) = pk;
     }
+  }
+  // the second stage copy: at P.V MFMAs 3, 6, 9, 12, 15
+  if constexpr (!F8) {
+    if constexpr (T_ % 3 == 0 && T_ > 0) copy_at(F.c, F.cy, T_ / 3 - 1);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
-
-template <int... K>
-__device__ __forceinline__ void pvw_slots(PvwState& st, std::integer_sequence<int, K...>) {
-  (pvw_slot<K>(st), ...);
-}
-
-template <bool F8>
-__device__ __forceinline__ void pv_weights_step(const Ctx& c, int m, const f32x4 (&sc)[2][2], const lu8* stA,
-                                                const lu8* stB, const lu8* prd, f32x16 (&o)[4][4],
-                                                float (&m_ref)[2], float (&m_all)[2], float (&l_run)[2], bool& ovf) {
-  bf16x8 v[2][4], p[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const lu8* st = j ? stB : stA;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(st + c.vofs1 + 1024 * i));
-      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(st + c.vofs2 + 1024 * i));
-      const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
-      v[j][i] = __builtin_bit_cast(bf16x8, s8);
-    }
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) p[j][hb] = *(lbf16x8*)(prd + j * P_STAGE + 1024 * hb);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  PvwState st{c, m, sc, v, p, o, m_ref, m_all, l_run, ovf, c.lds + Lay<F8>::P_OFF + (m & 1) * P_BYTES + c.pw_ofs,
-              {0.0f, 0.0f}, {}, {}};
-  pvw_slots(st, std::make_integer_sequence<int, 32>{});
+template <bool F8, int... K>
+__device__ __forceinline__ void part2_all(Fused& F, std::integer_sequence<int, K...>) {
+  (part2<F8, K>(F), ...);
 }
 
 // Zeroes the latent part of the tokens past the end of the split in its last
@@ -521,8 +526,8 @@ __device__ __forceinline__ void widen_stage(const Ctx& c, int fs, int bs) {
   if (tid < 128) *(__attribute__((address_space(3))) bf16x8*)(dst + 256 * 64) = *(lbf16x8*)(f8 + F8_ROPE + dofs);
 }
 template <bool F8>
-__device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2], float (&m_ref)[2],
-                                         float (&m_all)[2], float (&l_run)[2], f32x16 (&o)[4][4]) {
+__device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], float& m_ref, float& m_all,
+                                         float& l_run, f32x16 (&o)[4][4]) {
   using Ly = Lay<F8>;
   zero_p1<F8>(c);
   bool ovf = false;
@@ -552,22 +557,23 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2]
       cx = plan_stage<F8>(c, 2 * m + 3, wrap<F8>(sa + 3));
       cy = plan_stage<F8>(c, 2 * m + 4, wrap<F8>(sa + 4));
     }
-    f32x4 sc[2][2];
-    if (m < c.nsteps) {
-      const int sb = 2 * m + 1 < c.nst ? wrap<F8>(sa + 1) : sa;
-      if ((c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
-      step_scores<F8>(c, c.lds + sa * ST_BYTES, c.lds + sb * ST_BYTES, qf, sc, cx, cy);
-      const int nv = c.ntok - 2 * m * T;
+    // The step after the last one only completes the P.V of the last stages:
+    // its scores run on a stale slot and are all masked.
+    const int sb = 2 * m + 1 < c.nst ? wrap<F8>(sa + 1) : sa;
+    if ((c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
+    const lu8* stA = c.lds + sa * ST_BYTES;
+    const lu8* stB = c.lds + sb * ST_BYTES;
+    Fused F{c, m, c.kst ? stB : stA, qf, {}, {}, {}, va, vb, prd, {}, {}, o, m_ref, m_all, l_run, ovf,
+            c.lds + Ly::P_OFF + (m & 1) * P_BYTES + c.pw_ofs, cx, cy, 0.0f, {}};
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        mask(c, sc[0][hb], nv);
-        mask(c, sc[1][hb], nv - T);
-      }
-    } else {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) sc[0][hb] = sc[1][hb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    }
-    pv_weights_step<F8>(c, m, sc, va, vb, prd, o, m_ref, m_all, l_run, ovf);
+    for (int d = 0; d < KD; ++d) F.f[d] = kfrag(F.kb, c, d);
+    read_v(F, va);
+    read_p(F, 0, 0);
+    read_p(F, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    part1_all<F8>(F, std::make_integer_sequence<int, KSTEPS>{});
+    mask(c, F.sc, m < c.nsteps ? c.ntok - 2 * m * T : 0);
+    part2_all<F8>(F, std::make_integer_sequence<int, 16>{});
     sa = wrap<F8>(sa + 2);
     if constexpr (F8) fa = wrap5(fa + 2);
   }
@@ -577,20 +583,16 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[16][2]
 // Normalised partial output of the item: O / l per head (bf16) and the
 // per-head log2-sum-exp2 m_ref + log2(l).
 template <bool F8>
-__device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4], const float (&m_ref)[2],
-                                          const float (&l_run)[2], bf16_t* opart, float* lpart, size_t prow0) {
+__device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4], float m_ref, float l_run,
+                                          bf16_t* opart, float* lpart, size_t prow0) {
   const int lane = c.lane, wave = c.wave;
-  const int g = lane >> 4, hq = 32 * wave + (lane & 15);
-  // per-head sums of the weights: the 4 token groups of a head are lanes i16 + 16g
+  const int hq = 32 * wave + (lane & 31);
+  // per-head sums of the weights: the two token halves of a head are lanes l, l^32
   float* lsum = (float*)(c.lds + Lay<F8>::L_OFF);
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    float l_tot = l_run[hb] + __shfl_xor(l_run[hb], 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    if (g == 0) {
-      lsum[hq + 16 * hb] = l_tot;
-      lpart[prow0 + hq + 16 * hb] = m_ref[hb] + log2f(l_tot);
-    }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (lane < 32) {
+    lsum[hq] = l_tot;
+    lpart[prow0 + hq] = m_ref + log2f(l_tot);
   }
   __syncthreads();
 
@@ -650,8 +652,8 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   if (u / RB >= n_per || p >= P_items) return;
   const int b = p / S, s = p % S;
 
-  const int g = lane >> 4, i16 = lane & 15;
-  const int hq = 32 * wave + i16;  // head of this lane in head block 0 of the scores layout
+  const int g = lane >> 4, i16 = lane & 15, hi = lane >> 5;
+  const int hq = 32 * wave + (lane & 31);  // head of this lane in the scores layout
   const bf16_t* qblk = qt + (size_t)(b * s_q + j) * H * DKV;
   const int32_t* bt_row = bt + (size_t)b * max_pages;
   const int p0 = s * pps;
@@ -669,12 +671,11 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
     const int pos = 64 * i + lane, h = pos >> 3, lc = (pos & 7) ^ ((h >> 1) & 7);
     dma_1k((const uint8_t*)qblk, (uint32_t)((h * DKV + DC + 8 * lc) * 2), lds_addr + Lay<F8>::QR_OFF + i * 1024);
   }
-  // Absorbed query rows as B operands: lane holds qt[hq + 16 hb][32 ks + 8 g .. +8].
-  bf16x8 qf[16][2];
+  // Absorbed query rows as B operands of the score MFMAs: lane holds
+  // qt[hq][16 ks + 8 (lane/32) .. +8] for the 32 k-steps of the latent part.
+  bf16x8 qf[32];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) qf[ks][hb] = *(const bf16x8*)(qblk + (size_t)(hq + 16 * hb) * DKV + 32 * ks + 8 * g);
+  for (int ks = 0; ks < 32; ++ks) qf[ks] = *(const bf16x8*)(qblk + (size_t)hq * DKV + 16 * ks + 8 * hi);
 
   int vis = L > 0 ? L - s_q + j + 1 : 0;
   vis = vis < 0 ? 0 : vis;
@@ -710,11 +711,19 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   issue_stage<F8>(c, 2, 2);
   wait_vmcnt<0>();  // the compiler's own loads are then known complete (and stages 0-2 have landed)
 
-  // K fragment: token i16, chunk 4 ks + g (chunk % 4 = g)
-  c.koff = (uint32_t)(256 * g + 16 * (i16 ^ slot_x(g)));
-  // (head block 1, heads hq + 16, sits 16 rows further with the same permutation)
-  c.qr_ofs0 = (uint32_t)(hq * 128 + 16 * ((0 + g) ^ ((hq >> 1) & 7)));
-  c.qr_ofs1 = (uint32_t)(hq * 128 + 16 * ((4 + g) ^ ((hq >> 1) & 7)));
+  // K fragment of k-step ks: token i16 of the stage chosen by lane bit 4,
+  // chunk 2 ks + lane/32, i.e. chunk % 4 = lane/32 (even ks) or 2 + lane/32
+  // (odd ks); the k-step adds 512 ks.
+  c.kst = (lane >> 4) & 1;
+  c.koff_e = (uint32_t)(256 * hi + 16 * (i16 ^ slot_x(hi)));
+  c.koff_o = (uint32_t)(256 * hi + 16 * (i16 ^ slot_x(2 + hi)));
+  // RoPE query fragment r (k-step 32 + r): chunk 2r + lane/32 of row hq,
+  // stored at 16 (chunk ^ key), key = (hq/2) % 8
+  {
+    const int key = (hq >> 1) & 7;
+    c.qr_base = (uint32_t)(Lay<F8>::QR_OFF + hq * 128 + 16 * (hi ^ (key & 1)));
+    c.qr_key = key >> 1;
+  }
   {
     // V^T[32 ch][16 tokens] of channel block 4w (+1, +2, +3): chunk 4cb + cl,
     // lane group layout of the transposing read
@@ -726,16 +735,15 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   {
     // P row of head h (one per stage): 16 bf16 weights in token order 0-3,
     // 8-11, 4-7, 12-15 (the k order of the transposed V^T fragment), 16-byte
-    // halves swapped when bit 3 of h is set.  Writer: tokens 4g..4g+3 of head
-    // hq (head hq + 16 is 512 bytes further, same swap).
-    const int pos = ((g & 1) << 1) | (g >> 1);
-    c.pw_ofs = (uint32_t)(hq * 32 + 16 * ((pos >> 1) ^ ((hq >> 3) & 1)) + 8 * (pos & 1));
-    const int n = lane & 31;  // reader: head 32 hb + n, half lane/32
+    // halves swapped when bit 3 of h is set.  Reader: head 32 hb + n, half
+    // lane/32.  Writer: the same lane pattern in this wave's head block.
+    const int n = lane & 31;
     c.pr_ofs = (uint32_t)(n * 32 + 16 * ((lane >> 5) ^ ((n >> 3) & 1)));
+    c.pw_ofs = c.pr_ofs + 1024u * (uint32_t)wave;
   }
 
   f32x16 o[4][4];
-  float m_ref[2] = {-INFINITY, -INFINITY}, m_all[2], l_run[2];
+  float m_ref = -INFINITY, m_all, l_run;
   // A second pass, against the exact maximum, only if a score outgrew the
   // first step's reference.  Both passes run the same code (a runtime loop,
   // nothing to specialise on), so the step code exists once.
@@ -745,13 +753,12 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
-    m_all[0] = m_all[1] = -INFINITY;
-    l_run[0] = l_run[1] = 0.0f;
+    m_all = -INFINITY;
+    l_run = 0.0f;
     const bool ovf = run_pass<F8>(c, qf, m_ref, m_all, l_run, o);
     const bool again = __syncthreads_or(ovf);  // also: every wave is done with the ring
     if (pass > 0 || !again) break;
-    m_ref[0] = m_all[0];
-    m_ref[1] = m_all[1];
+    m_ref = m_all;
     issue_stage<F8>(c, 0, 0);
     issue_stage<F8>(c, 1, 1);
     issue_stage<F8>(c, 2, 2);
@@ -764,11 +771,7 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
 template <bool F8>
 static hipError_t launch_attn(const DecodeArgs& a) {
   constexpr int lds = Lay<F8>::LDS_BYTES;
-  static bool attr_set = false;  // one flag per instantiation
-  if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)&k_attn_v3b<F8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    attr_set = true;
-  }
+  MLA_TRY(lds_limit((const void*)&k_attn_v3b<F8>, lds));
   const int P_items = a.batch * a.S;
   const int grid = ((P_items + 7) / 8) * 8 * a.s_q;
   return launch(&k_attn_v3b<F8>, dim3(grid), dim3(256), lds, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
@@ -776,7 +779,7 @@ static hipError_t launch_attn(const DecodeArgs& a) {
                 (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch);
 }
 
-hipError_t fast_attention_b(const DecodeArgs& a) {
+hipError_t fast_attention(const DecodeArgs& a) {
   if (a.cache_dtype == MLA_FP8_E4M3) {
     // the page geometry the fp8 stage copies are compiled for
     if (a.g.fp8_scale_off != (size_t)F8_PG_SCALES || a.g.fp8_rope_off != (size_t)F8_PG_ROPE) return hipErrorInvalidValue;

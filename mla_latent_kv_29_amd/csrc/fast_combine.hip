@@ -1,8 +1,11 @@
 // Combine for at most 64 query rows (gfx950): the merge of the attention's
 // per-split partials and the W^UV projection in one kernel.
 //
-// What it computes (DeepSeek-V3 reading lesson, §2.1.1 Question 2, and the
-// split-KV merge of its decode discussion): for query row r and head i,
+// What it computes: the softmax over all visible tokens from the softmaxes
+// the attention took over disjoint token ranges (split s: normalised
+// latent output O_s and log2-sum-exp2 lse_s of its scores), and then W^UV
+// after the weighted latent sum, which the linearity of v^C = W^UV c^KV
+// permits (DeepSeek-V3 reading lesson, §2.1.1).  For query row r and head i,
 //     O_lat = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),  M = max_s lse_s
 // over the splits s that saw at least one token (lse_s = -inf marks an empty
 // split, whose rows are never read), rounded to bf16, and then
@@ -57,6 +60,7 @@ __device__ __forceinline__ float wsum(float v) {
 
 struct CbArgs {
   int batch, s_q, H, R;
+  int S;              // splits (the host's count, checked against the workspace size)
   const uint8_t* ws;
   size_t lpart_off;
   const bf16_t* Wuv;  // [H][d_head][d_c]
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
 
   // 1. merge: wave w, rows w + 8i of the block; lane l, channels 8l .. +7
   const int32_t* hdr = (const int32_t*)a.ws;
-  const int S = hdr[HDR_S];
+  const int S = a.S;
   const bool pbf16 = hdr[HDR_PDT] == MLA_BF16;
   const float* lpart = (const float*)(a.ws + a.lpart_off);
   const uint8_t* opart = a.ws + opart_offset(a.lpart_off, a.batch, S, a.s_q, a.H);
@@ -282,12 +286,8 @@ hipError_t merge_uv(const CombineArgs& a) {
   const int R = a.batch * a.s_q, H = a.d.n_heads;
   const int nrb = (R + CB_ROWS - 1) / CB_ROWS;
   if ((H * nrb) % 8 != 0) return hipErrorInvalidValue;
-  CbArgs cb{a.batch, a.s_q, H, R, a.ws, a.L.lpart, (const bf16_t*)a.W_UV, (bf16_t*)a.out, a.lse_out};
-  static bool attr_set = false;
-  if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)&k_merge_uv, hipFuncAttributeMaxDynamicSharedMemorySize, CB_LDS));
-    attr_set = true;
-  }
+  CbArgs cb{a.batch, a.s_q, H, R, a.S, a.ws, a.L.lpart, (const bf16_t*)a.W_UV, (bf16_t*)a.out, a.lse_out};
+  MLA_TRY(lds_limit((const void*)&k_merge_uv, CB_LDS));
   return launch(&k_merge_uv, dim3(H * nrb), dim3(CB_WAVES * 64), CB_LDS, a.stream, cb);
 }
 

@@ -264,10 +264,10 @@ __global__ void k_reduce_cq(int R, int N, int splits, const float* part, bf16_t*
 // Merge of the per-split attention partials into O_lat (bf16 [R][H][d_c]) and
 // the row's log-sum-exp: weights exp2(lse_s - max_s lse), empty splits
 // (lse = -inf) skipped.  One wave per (row, head); each lane owns 8 channels
-// per pass (16-byte partial reads).  Partials are fp32 or bf16 (header).
-__global__ __launch_bounds__(256) void k_merge(int batch, int H, int s_q, int d_c, const uint8_t* ws,
+// per pass (16-byte partial reads).  S splits (the host's, already checked
+// against the workspace size); partials are fp32 or bf16 (header).
+__global__ __launch_bounds__(256) void k_merge(int batch, int H, int s_q, int S, int d_c, const uint8_t* ws,
                                                size_t lpart_off, bf16_t* olat, float* lse_out) {
-  const int S = ((const int32_t*)ws)[HDR_S];
   const bool pbf16 = ((const int32_t*)ws)[HDR_PDT] == MLA_BF16;
   const float* lpart = (const float*)(ws + lpart_off);
   const uint8_t* opart = ws + opart_offset(lpart_off, batch, S, s_q, H);
@@ -727,11 +727,7 @@ template <class Epi>
 hipError_t launch_big(int M, int N, int K, const bf16_t* X, long ldx, const bf16_t* W, long ldw, const Epi& epi,
                       hipStream_t st) {
   BigArgs a{M, N, K, (M + GB_T - 1) / GB_T, N / GB_T, X, ldx, W, ldw};
-  static bool attr_set = false;  // one flag per epilogue type
-  if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)&k_gemm_big<Epi>, hipFuncAttributeMaxDynamicSharedMemorySize, GB_LDS));
-    attr_set = true;
-  }
+  MLA_TRY(lds_limit((const void*)&k_gemm_big<Epi>, GB_LDS));
   const int T = a.mt * a.nt;
   return launch(&k_gemm_big<Epi>, dim3(8 * ((T + 7) / 8)), dim3(256), GB_LDS, st, a, epi);
 }
@@ -818,13 +814,13 @@ hipError_t out_project(const OutProjArgs& a) {
                 (const float*)part, (bf16_t*)a.y);
 }
 
-hipError_t fast_combine_mfma(const CombineArgs& a) {
+hipError_t fast_combine(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
   if (merge_uv_supported(d, R)) return merge_uv(a);
-  bf16_t* olat = (bf16_t*)(a.ws + a.L.qt);  // the query buffer is free after the attention
-  MLA_TRY(launch(&k_merge, dim3((R * H + 3) / 4), dim3(256), 0, a.stream, a.batch, H, a.s_q, d.d_c, a.ws, a.L.lpart,
-                 olat, a.lse_out));
+  bf16_t* olat = (bf16_t*)(a.ws + a.L.olat);  // the combine's own region: the queries stay intact
+  MLA_TRY(launch(&k_merge, dim3((R * H + 3) / 4), dim3(256), 0, a.stream, a.batch, H, a.s_q, a.S, d.d_c,
+                 (const uint8_t*)a.ws, a.L.lpart, olat, a.lse_out));
   hipError_t e;
   GemmArgs g = gemm_args(R, d.d_head, d.d_c, olat, (long)H * d.d_c, d.d_c, (const bf16_t*)a.W_UV, d.d_c,
                          (long)d.d_head * d.d_c, 1);

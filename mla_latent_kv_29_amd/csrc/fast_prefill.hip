@@ -362,11 +362,7 @@ hipError_t prefill_attention(const PrefillArgs& a) {
   PaArgs pa{(const bf16_t*)(a.ws + a.L.q), (const bf16_t*)(a.ws + a.L.kc), (const bf16_t*)(a.ws + a.L.vc),
             (const bf16_t*)(a.ws + a.L.kr), a.cu_seqlens, (const float2*)(a.ws + a.L.rope), a.n_tok, qtiles,
             a.n_seq, a.out, a.lse_out};
-  static bool attr_set = false;
-  if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)&k_prefill_attn, hipFuncAttributeMaxDynamicSharedMemorySize, PA_LDS));
-    attr_set = true;
-  }
+  MLA_TRY(lds_limit((const void*)&k_prefill_attn, PA_LDS));
   // at most 2^30 workgroups a launch: sequences in chunks
   const int chunk = std::max(1, (1 << 30) / (qtiles * PH));
   for (int s0 = 0; s0 < a.n_seq; s0 += chunk) {

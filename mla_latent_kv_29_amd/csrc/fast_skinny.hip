@@ -645,11 +645,7 @@ template <int KB, int NB, class Epi, int DEPTH = NB>
 hipError_t launch_f8(const F8Args& a, int n_groups, int k_groups, const Epi& epi, hipStream_t st) {
   constexpr int lds = SkPlan<4, NB>::LDS_BYTES;
   auto kern = &k_skinny_f8<KB, NB, DEPTH, Epi>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    attr_set = true;
-  }
+  MLA_TRY(lds_limit((const void*)kern, lds));
   return launch(kern, dim3(n_groups, k_groups), dim3(256), lds, st, a, epi);
 }
 
@@ -681,11 +677,7 @@ hipError_t launch_skinny(const SkArgs& a, const XSrc& xs, int n_groups, int k_gr
                          hipStream_t st) {
   constexpr int lds = SkPlan<WPB, NB>::LDS_BYTES;
   auto kern = &k_skinny<WPB, KS, NB, DEPTH, XSrc, Epi>;
-  static bool attr_set = false;  // one flag per instantiation
-  if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    attr_set = true;
-  }
+  MLA_TRY(lds_limit((const void*)kern, lds));
   return launch(kern, dim3(n_groups, k_groups, batch), dim3(WPB * 64), lds, st, a, xs, epi);
 }
 
@@ -802,11 +794,7 @@ hipError_t skinny_query(const DecodeArgs& a) {
   }
   UaArgs ua{R, H, d.d_c, d.d_rope, a.s_q, cq, (const bf16_t*)a.W_UQ, (const bf16_t*)a.W_UK, qt, a.seqlens, scale2, {}};
   for (int m = 0; m < d.d_rope / 2; ++m) ua.freq[m] = pow((double)d.rope_theta, -2.0 * m / d.d_rope);
-  static bool attr_set = false;
-  if (!attr_set) {
-    MLA_TRY(hipFuncSetAttribute((const void*)&k_uq_absorb, hipFuncAttributeMaxDynamicSharedMemorySize, UA_LDS));
-    attr_set = true;
-  }
+  MLA_TRY(lds_limit((const void*)&k_uq_absorb, UA_LDS));
   return launch(&k_uq_absorb, dim3(2 * H), dim3(UA_WAVES * 64), UA_LDS, a.stream, ua);
 }
 

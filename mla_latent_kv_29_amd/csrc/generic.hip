@@ -224,12 +224,11 @@ __global__ __launch_bounds__(256) void k_attn_generic(int H, int s_q, CacheGeom 
 // Merge the splits (log-sum-exp weights, empty splits skipped) and apply
 // W^UV of the row's head: out = W^UV_i O_lat.
 template <typename OT>
-__global__ __launch_bounds__(256) void k_combine_generic(int batch, int H, int s_q, int d_head, int d_c,
+__global__ __launch_bounds__(256) void k_combine_generic(int batch, int H, int s_q, int S, int d_head, int d_c,
                                                           const uint8_t* ws, size_t lpart_off,
                                                           const OT* W_UV, OT* out, float* lse_out) {
   extern __shared__ float olat[];
   float* wsm = olat + d_c;  // S weights
-  const int S = ((const int32_t*)ws)[HDR_S];
   const bool pbf16 = ((const int32_t*)ws)[HDR_PDT] == MLA_BF16;
   const float* lpart = (const float*)(ws + lpart_off);
   const uint8_t* opart = ws + opart_offset(lpart_off, batch, S, s_q, H);
@@ -356,11 +355,6 @@ hipError_t generic_attention(const DecodeArgs& a) {
   return a.act == MLA_F32 ? generic_attention_t<float>(a) : generic_attention_t<bf16_t>(a);
 }
 
-hipError_t generic_decode(const DecodeArgs& a) {
-  hipError_t e = generic_query(a);
-  if (e != hipSuccess) return e;
-  return generic_attention(a);
-}
 
 // fp32 -> bf16 (round to nearest even), elementwise.
 __global__ __launch_bounds__(256) void k_f32_to_bf16(long n, const float* __restrict__ x, bf16_t* __restrict__ y) {
@@ -386,14 +380,14 @@ hipError_t generic_out_project(const OutProjArgs& a) {
 hipError_t generic_combine(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q;
-  const size_t lds = (size_t)(d.d_c + MAX_SPLITS) * 4;
+  const size_t lds = (size_t)(d.d_c + a.S) * 4;
   if (a.act == MLA_F32)
     MLA_TRY(launch(&k_combine_generic<float>, dim3(R * d.n_heads), dim3(256), lds, a.stream, a.batch,
-                       d.n_heads, a.s_q, d.d_head, d.d_c, a.ws, a.L.lpart, (const float*)a.W_UV, (float*)a.out,
-                       a.lse_out));
+                       d.n_heads, a.s_q, a.S, d.d_head, d.d_c, (const uint8_t*)a.ws, a.L.lpart, (const float*)a.W_UV,
+                       (float*)a.out, a.lse_out));
   else
     MLA_TRY(launch(&k_combine_generic<bf16_t>, dim3(R * d.n_heads), dim3(256), lds, a.stream, a.batch,
-                       d.n_heads, a.s_q, d.d_head, d.d_c, a.ws, a.L.lpart, (const bf16_t*)a.W_UV,
+                       d.n_heads, a.s_q, a.S, d.d_head, d.d_c, (const uint8_t*)a.ws, a.L.lpart, (const bf16_t*)a.W_UV,
                        (bf16_t*)a.out, a.lse_out));
   return hipSuccess;
 }

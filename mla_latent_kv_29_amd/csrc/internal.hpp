@@ -13,6 +13,8 @@ namespace mla {
 //   cq       : act [R][d_cq]               c^Q
 //   u        : f32 [R][H][d_head+d_rope]   W^UQ c^Q (bf16 q^C for the MFMA path)
 //   qt       : act [R][H][d_c+d_rope]      absorbed, scaled query [q_abs | q^R]
+//   olat     : act [R][H][d_c]             merged latent rows (the combine's own
+//                                          scratch when it merges before W^UV)
 //   lpart    : f32 [B][S][s_q][H]          per-split log2-sum-exp2 of scores
 //   opart    : f32 or bf16 [B][S][s_q][H][d_c]  per-split normalised latent outputs
 //                                        (sized for f32; element type in the header)
@@ -25,7 +27,7 @@ constexpr int WS_HEADER_INTS = 64;
 constexpr int32_t WS_MAGIC = 0x4d4c4144;  // "MLAD"
 
 struct WsLayout {
-  size_t header, cq_part, cq, u, qt, opart, lpart, total;
+  size_t header, cq_part, cq, u, qt, olat, opart, lpart, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -44,6 +46,7 @@ inline WsLayout ws_layout(const mla_dims& d, int act, int batch, int s_q, int S)
   w.cq = o;      o = align256(o + R * d.d_cq * es);
   w.u = o;       o = align256(o + R * H * (d.d_head + d.d_rope) * 4);
   w.qt = o;      o = align256(o + R * H * (d.d_c + d.d_rope) * es);
+  w.olat = o;    o = align256(o + R * H * d.d_c * es);
   w.lpart = o;   o = align256(o + (size_t)batch * S * s_q * H * 4);
   w.opart = o;   o = align256(o + (size_t)batch * S * s_q * H * d.d_c * 4);
   w.total = o;
@@ -76,7 +79,8 @@ struct CombineArgs {
   mla_dims d;
   int act;
   int batch, s_q;
-  const uint8_t* ws;
+  int S;  // split count of the decode that filled ws (validated against ws_bytes on the host)
+  uint8_t* ws;
   WsLayout L;
   const void* W_UV;
   void* out;
@@ -157,10 +161,13 @@ struct OutProjArgs {
 int out_proj_splits(int act, int rows, int N, int K);
 size_t out_proj_ws_bytes(int act, int rows, int N, int K);
 
+// Raises the dynamic LDS limit of `kernel` to `bytes` on the current device,
+// once per (kernel, device); safe to call from several threads.
+hipError_t lds_limit(const void* kernel, int bytes);
+
 // Launchers (return the first HIP error of the enqueue, hipSuccess otherwise).
 hipError_t generic_append(const AppendArgs& a);
 hipError_t generic_write(const AppendArgs& a);
-hipError_t generic_decode(const DecodeArgs& a);
 hipError_t generic_query(const DecodeArgs& a);       // header, c^Q, W^UQ, RoPE, absorption -> qt
 hipError_t generic_attention(const DecodeArgs& a);   // qt + cache -> per-split partials
 hipError_t generic_combine(const CombineArgs& a);
@@ -170,12 +177,9 @@ bool fast_append_supported(const mla_dims& d, int act, int cache_dtype);
 bool fast_append_shape(const mla_dims& d);
 bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q);
 hipError_t fast_append(const AppendArgs& a);
-hipError_t fast_decode(const DecodeArgs& a);
 hipError_t fast_combine(const CombineArgs& a);
 hipError_t fast_attention(const DecodeArgs& a);
-hipError_t fast_attention_b(const DecodeArgs& a);
 hipError_t fast_query(const DecodeArgs& a);
-hipError_t fast_combine_mfma(const CombineArgs& a);
 bool skinny_query_supported(const mla_dims& d, int R);
 hipError_t skinny_query(const DecodeArgs& a);
 bool merge_uv_supported(const mla_dims& d, int R);

@@ -43,7 +43,11 @@ class DecodeSession:
         self.lse = torch.empty((self.batch, s_q, H), dtype=torch.float32, device=device)
 
     def set_splits(self, num_splits):
-        s = num_splits if num_splits > 0 else L.mla_default_splits(self.cdims, self.batch, self.s_q, self.max_pages)
+        """Split plan: num_splits per sequence (0 = the library default), as
+        mla_decode resolves it; the combine takes the same count."""
+        s = L.mla_decode_splits(self.cdims, self.batch, self.s_q, self.max_pages, num_splits)
+        if s <= 0:
+            raise ValueError("invalid split request")
         self.num_splits = s
         self.ws_bytes = L.mla_workspace_bytes(self.cdims, self.act, self.batch, self.s_q, s)
         if self.ws_bytes == 0:
@@ -84,8 +88,8 @@ class DecodeSession:
         L.mla_decode(self.cdims, self.act, hq, self.batch, self.s_q, W["W_DQ"] if use_dq else None, W["W_UQ"],
                      W["W_UK"], self.cache, self.block_table, self.max_pages, self.seqlens, softmax_scale,
                      self.num_splits, self.ws, self.ws_bytes, stream)
-        L.mla_combine(self.cdims, self.act, self.batch, self.s_q, self.ws, self.ws_bytes, W["W_UV"], self.out,
-                      self.lse, stream)
+        L.mla_combine(self.cdims, self.act, self.batch, self.s_q, self.num_splits, self.ws, self.ws_bytes, W["W_UV"],
+                      self.out, self.lse, stream)
         return self.out, self.lse
 
     # ---------------------------------------------------------------- inspection

@@ -2,13 +2,15 @@
 INFRASTRUCTURE ONLY.
 
 Source: "Читаем техотчёт DeepSeek-V3 вместе" (ai.flicky.cc course lesson),
-section 2.2 "Multi-Token Prediction" (the second token is accepted 85-90% of
-the time, about 1.8x generation speed), the `tokens_per_step` docstring of
-"Практика: перепроверяем числа статьи" (the main model always yields one
-token; `depth` drafts are proposed in a chain; the k-th counts only if all
-earlier ones were accepted, each accepted with probability `acceptance`),
-quiz item 5 of "Проверь себя" and the lesson summary (about 1.85 tokens per
-step at depth 1 and acceptance 0.85).
+section 2.2 "Multi-Token Prediction" (second-token acceptance of 85-90%,
+about 1.8x generation speed), the `tokens_per_step` exercise of its practice
+part, quiz item 5 and the lesson summary (about 1.85 tokens per step at depth
+1 and acceptance 0.85).
+
+Model, as read here: a verify step always keeps the main model's token; the
+drafts form a chain, and a drafted token is kept only while every draft
+before it was kept, each draft being kept independently with probability
+`acceptance`.
 
 The function below is the expectation written out over every accept/reject
 outcome of the drafts (2^depth of them), not a closed form.  Pins in the test

@@ -56,6 +56,10 @@ def test_default_splits_and_workspace():
     w1 = m.mla_workspace_bytes(d, m.MLA_BF16, 64, 1, 1)
     w4 = m.mla_workspace_bytes(d, m.MLA_BF16, 64, 1, 4)
     assert w4 - w1 >= 3 * 64 * 128 * 512 * 4
+    # the combine's merged-latent region is part of every workspace: queries
+    # (576 bf16 a head and row) and merged latents (512) both fit beside the
+    # partials of one split (lse and 512 fp32 a head and row)
+    assert w1 >= 64 * 128 * (2 * 576 + 2 * 512 + 4 + 4 * 512)
 
 
 FAKE = 1 << 40  # aligned non-null value; never dereferenced on the paths below
@@ -120,11 +124,51 @@ def test_append_and_combine_argument_errors():
                               check=False) == L.MLA_ERR_ALIGN
     assert m.mla_cache_write(d, m.MLA_BF16, FAKE, None, 3, FAKE, FAKE, cache, FAKE, 4, stream=0,
                              check=False) == L.MLA_ERR_NULL
-    assert m.mla_combine(d, m.MLA_BF16, 2, 1, FAKE, 10, FAKE, FAKE, None, stream=0, check=False) == \
+    assert m.mla_combine(d, m.MLA_BF16, 2, 1, 1, FAKE, 10, FAKE, FAKE, None, stream=0, check=False) == \
         L.MLA_ERR_WORKSPACE
-    assert m.mla_combine(d, m.MLA_BF16, 2, 1, FAKE, 1 << 34, None, FAKE, None, stream=0, check=False) == \
+    assert m.mla_combine(d, m.MLA_BF16, 2, 1, 1, FAKE, 1 << 34, None, FAKE, None, stream=0, check=False) == \
         L.MLA_ERR_NULL
-    assert m.mla_combine(d, m.MLA_BF16, 0, 1, None, 0, None, None, None, stream=0, check=False) == L.MLA_OK
+    assert m.mla_combine(d, m.MLA_BF16, 0, 1, 1, None, 0, None, None, None, stream=0, check=False) == L.MLA_OK
+    for bad in (0, -1, 4097):
+        assert m.mla_combine(d, m.MLA_BF16, 2, 1, bad, FAKE, 1 << 34, FAKE, FAKE, None, stream=0,
+                             check=False) == L.MLA_ERR_DIMS
+
+
+def test_combine_refuses_a_workspace_smaller_than_its_split_plan():
+    """A 64-split plan (128K-token sequences) against a workspace sized for one
+    split is refused on the host: the merge would read 64 partials per row."""
+    d = _dims()
+    batch, s_q, mp = 4, 1, 2048
+    S = m.mla_decode_splits(d, batch, s_q, mp, 0)
+    assert S == m.mla_default_splits(d, batch, s_q, mp) == 64
+    w1 = m.mla_workspace_bytes(d, m.MLA_BF16, batch, s_q, 1)
+    wS = m.mla_workspace_bytes(d, m.MLA_BF16, batch, s_q, S)
+    assert wS > w1
+    assert m.mla_combine(d, m.MLA_BF16, batch, s_q, S, FAKE, w1, FAKE, FAKE, None, stream=0, check=False) == \
+        L.MLA_ERR_WORKSPACE
+    assert m.mla_combine(d, m.MLA_BF16, batch, s_q, S, FAKE, wS - 1, FAKE, FAKE, None, stream=0, check=False) == \
+        L.MLA_ERR_WORKSPACE
+
+
+def test_decode_splits_resolution():
+    """mla_decode_splits: the default for 0, and a request rounded so that all
+    splits span the same whole number of pages (ceil(max_pages / pages per
+    split)); resolving a resolved count gives it back."""
+    d = _dims()
+    assert m.mla_decode_splits(d, 64, 1, 64, 0) == m.mla_default_splits(d, 64, 1, 64)
+    assert m.mla_decode_splits(d, 64, 1, 64, 7) == 7       # 10 pages a split, the last one 4
+    assert m.mla_decode_splits(d, 2, 1, 9, 4) == 3         # 3 pages a split
+    assert m.mla_decode_splits(d, 2, 1, 5, 9) == 5         # at most one page a split
+    for mp in (1, 5, 9, 64, 100, 2048):
+        for req in (1, 2, 3, 7, 16, 63, 64):
+            S = m.mla_decode_splits(d, 3, 1, mp, req)
+            pps = -(-mp // min(req, mp))
+            assert S == -(-mp // pps)
+            assert m.mla_decode_splits(d, 3, 1, mp, S) == S
+    assert m.mla_decode_splits(d, 0, 1, 64, 0) == 0
+    assert m.mla_decode_splits(d, 2, 9, 64, 0) == 0
+    assert m.mla_decode_splits(d, 2, 1, 0, 0) == 0
+    assert m.mla_decode_splits(d, 2, 1, 64, 4097) == 0
 
 
 def test_prefill_workspace_and_argument_errors():

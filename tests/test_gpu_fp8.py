@@ -114,3 +114,56 @@ def test_fp8_bytes_past_the_end_are_ignored(splits):
     for b in range(3):
         o_q, _ = case.oracle(b, tau, fp8=True)
         assert max_abs(out[b], o_q) <= 2e-2 * float(np.abs(o_q).max()), b
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_mfma_append_epilogue_bit_exact(cache):
+    """The MFMA append (the path that builds every benchmarked cache), pinned
+    bit for bit: with W^DKV = [I_512 | 0] and a W^KR that picks columns
+    512..575, every fp32 accumulation holds one exact product, so c^KV equals
+    the first 512 channels of h exactly.  Its E4M3 codes and fp32 scales must
+    then be the oracle's tile quantisation of those values bit for bit (fp8),
+    or the values themselves (bf16); k^R, rotated in fp32 and rounded to bf16,
+    within one bf16 step of the oracle's float64 rotation.  Tiles are scaled
+    by powers of two from 2^-20 to 2^12 and one tile is all zero, so the
+    scale, the saturation edge and the zero-tile rule all occur."""
+    from mla_latent_kv_29_amd.session import DecodeSession
+    dims = V3
+    d_model, dc, dr = dims["d_model"], dims["d_c"], dims["d_rope"]
+    W_DKV = torch.zeros((dc, d_model), dtype=torch.bfloat16, device=DEV)
+    W_DKV[torch.arange(dc), torch.arange(dc)] = 1.0
+    W_KR = torch.zeros((dr, d_model), dtype=torch.bfloat16, device=DEV)
+    W_KR[torch.arange(dr), dc + torch.arange(dr)] = 1.0
+    W = {"W_DKV": W_DKV, "W_KR": W_KR}
+    lengths = np.array([200, 131])
+    bt, pool = inputs.block_table(lengths, dims["page_size"], "shuffled", 0, 9)
+    sess = DecodeSession(dims, "bf16", cache, lengths, bt, pool, 1, 0, DEV)
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    hs = []
+    for b, Lb in enumerate(lengths):
+        h = torch.randn((int(Lb), d_model), generator=g)
+        tile_pow = torch.randint(-20, 13, (int(Lb), dc // 128), generator=g).to(torch.float32)
+        h[:, :dc] *= torch.repeat_interleave(2.0 ** tile_pow, 128, dim=1)
+        h[3, 128:256] = 0.0                      # an all-zero tile: scale 1, codes 0
+        hs.append(h.to(torch.bfloat16).to(DEV))
+        sess.append(hs[-1], b, 0, W)
+    torch.cuda.synchronize()
+    for b, Lb in enumerate(lengths):
+        Lb = int(Lb)
+        hb = to_np(hs[b])
+        npg = (Lb + 63) // 64
+        kr_ref = oracle.rope(hb[:, dc:dc + dr], np.arange(Lb), dims["rope_theta"])
+        if cache == "fp8":
+            codes, scales, rope = read_fp8_rows(sess.pages, bt[b, :npg], dims)
+            ref_codes, ref_scales = oracle.quantize_tiles(hb[:, :dc])
+            np.testing.assert_array_equal(codes[:Lb], ref_codes)
+            np.testing.assert_array_equal(scales[:Lb], ref_scales)
+            assert np.all(ref_scales[3, 1] == 1.0) and np.all(ref_codes[3, 128:256] == 0)
+            kr = rope[:Lb]
+        else:
+            rows = read_bf16_rows(sess.pages, bt[b, :npg], dims)[:Lb]
+            np.testing.assert_array_equal(rows[:, :dc], hb[:, :dc])
+            kr = rows[:, dc:]
+        # one bf16 step: 2^-7 relative to the value's binade
+        step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(kr_ref), 1e-30))) - 7)
+        assert np.all(np.abs(kr - kr_ref) <= step)

@@ -52,7 +52,9 @@ def bf16_round(x):
     return to_np(torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16))
 
 
-def check(name, samples, kappas):
+def check(name, samples, kappas, all_heads=()):
+    """Decode the workload at full size; compare the sampled sequences (HEADS
+    of them, and every head for the sequences in all_heads) with the oracle."""
     spec, dims, lengths, W, sess, gen_h, hq = full_session(name)
     s_q = spec["s_q"]
     fp8 = spec["cache"] == "fp8"
@@ -76,9 +78,10 @@ def check(name, samples, kappas):
             Lb = int(lengths[b])
             c, r, cq, rq = lat[b]
             hqb = hqn[b * s_q:(b + 1) * s_q]
-            args = (Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], dims, Lb, s_q, tau, HEADS)
+            heads = list(range(dims["n_heads"])) if b in all_heads else HEADS
+            args = (Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], dims, Lb, s_q, tau, heads)
             o_ref, l_ref = oracle.decode_from_latents(c, r, hqb, *args)
-            got, got_l = out[b][:, HEADS], lse[b][:, HEADS]
+            got, got_l = out[b][:, heads], lse[b][:, heads]
             tol = (5e-2 if fp8 else 2e-2) * float(np.max(np.abs(o_ref)))
             err = max_abs(got, o_ref)
             assert err <= tol, (name, b, Lb, kappa, err, tol)
@@ -88,19 +91,44 @@ def check(name, samples, kappas):
                 assert max_abs(got, o_q) <= 2e-2 * float(np.max(np.abs(o_q))), (name, b, kappa, "emulated")
 
 
+EIGHT = [0, 9, 18, 27, 37, 46, 55, 63]   # 8 of 64 sequences, both ends included
+
+
 def test_full_v3_bf16_b64_l4096():
-    check("v3_bf16_b64_l4096", [0, 37, 63], [1.0, 56.0])
+    """8 of the 64 sequences, every head of sequence 37."""
+    check("v3_bf16_b64_l4096", EIGHT, [1.0, 56.0], all_heads=(37,))
 
 
 def test_full_v3_bf16_b128_var32k_paged():
+    """8 of the 128 sequences: the shortest and the longest among them."""
     lengths = inputs.seqlens(inputs.WORKLOADS["v3_bf16_b128_var32k_paged"]["lengths"], 128, 0, 2)
-    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 5})
+    order = np.argsort(lengths)
+    picks = sorted({int(order[0]), int(order[-1]), 5, 31, 64, 90, 101, 127})
+    assert len(picks) == 8
     check("v3_bf16_b128_var32k_paged", picks, [1.0, 56.0])
 
 
 def test_full_v3_bf16_b4_l128k():
-    check("v3_bf16_b4_l128k", [3], [1.0, 56.0])
+    """All four 131072-token sequences (64 splits each)."""
+    check("v3_bf16_b4_l128k", [0, 1, 2, 3], [1.0, 56.0])
 
 
 def test_full_v3_fp8_b128_l8192_sq2():
-    check("v3_fp8_b128_l8192_sq2", [0, 127], [1.0, 56.0])
+    """8 of the 128 sequences, both query rows, every head of sequence 64."""
+    check("v3_fp8_b128_l8192_sq2", [0, 17, 36, 64, 80, 99, 113, 127], [1.0, 56.0], all_heads=(64,))
+
+
+def test_full_v3_bf16_b64_l4096_sq4():
+    """The depth-3 verify workload (four causal query rows a sequence)."""
+    check("v3_bf16_b64_l4096_sq4", [0, 21, 42, 63], [1.0, 56.0])
+
+
+def test_full_v3_repeated_decode_is_bitwise_deterministic():
+    """Two decodes of the benchmark workload on the same inputs give the same
+    bits: the split merge adds the splits in a fixed order (no atomics)."""
+    spec, dims, lengths, W, sess, gen_h, hq = full_session("v3_bf16_b64_l4096")
+    tau = tau_of(dims)
+    o1, l1 = (t.clone() for t in sess.decode(hq, W, tau))
+    o2, l2 = sess.decode(hq, W, tau)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

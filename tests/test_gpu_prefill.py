@@ -107,3 +107,48 @@ def test_prefill_halves_equal_the_whole_call():
             outs.append((out.clone(), lse.clone()))
         assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), lengths
         assert bool(torch.isfinite(outs[0][0].float()).all())
+
+
+@pytest.mark.parametrize("kappa", [1.0, 56.0])
+def test_prefill_benchmark_shape_sampled_rows(kappa):
+    """The benchmarked prefill: 4 sequences x 4096 tokens packed (the bench's
+    seeds and launch), so every query tile, the XCD placement of all 16384
+    work items and the 256 x 256 projection epilogues run at full size.  Row
+    j of a sequence is the oracle's decode with one query row and seqlen
+    j + 1; rows 0, 127, 128, 2047 and 4095 of the first and the last
+    sequence, three heads."""
+    spec = inputs.PREFILL_WORKLOADS["prefill_v3_bf16_b4_l4096"]
+    dims, wl = spec["dims"], spec["index"]
+    lengths = inputs.seqlens(spec["lengths"], spec["batch"], 0, wl)
+    W = inputs.weights(dims, spec["sigma"], torch.bfloat16, DEV, 0, wl)
+    hs = [inputs.hidden(dims, b, 0, int(L), torch.bfloat16, DEV, 0, wl) for b, L in enumerate(lengths)]
+    h = torch.cat(hs, 0).contiguous()
+    n = h.shape[0]
+    cu_np = np.concatenate([[0], np.cumsum(lengths)])
+    cu = torch.tensor(cu_np, dtype=torch.int32, device=DEV)
+    d = m.make_dims(dims)
+    wsb = m.mla_prefill_workspace_bytes(d, m.MLA_BF16, n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    out = torch.full((n, dims["n_heads"], dims["d_head"]), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((n, dims["n_heads"]), float("nan"), dtype=torch.float32, device=DEV)
+    tau = kappa * tau_of(dims)
+    args = (d, m.MLA_BF16, h, n, len(lengths), cu, int(max(lengths)), W["W_DQ"], W["W_UQ"], W["W_UK"], W["W_UV"],
+            W["W_DKV"], W["W_KR"], tau, out, lse, ws, wsb)
+    m.mla_prefill_project(*args)
+    m.mla_prefill_attend(*args)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+    Wn = {k: to_np(v) for k, v in W.items()}
+    rows = [0, 127, 128, 2047, 4095]
+    for b in (0, len(lengths) - 1):
+        hb = to_np(hs[b])
+        c, kr = oracle.kv_latents(hb, Wn["W_DKV"], Wn["W_KR"], np.arange(hb.shape[0]), dims["rope_theta"])
+        for j in rows:
+            o_ref, l_ref = oracle.decode_from_latents(c[:j + 1], kr[:j + 1], hb[j:j + 1], Wn["W_DQ"], Wn["W_UQ"],
+                                                      Wn["W_UK"], Wn["W_UV"], dims, j + 1, 1, tau, HEADS)
+            g = int(cu_np[b]) + j
+            got = to_np(out[g, HEADS])
+            got_l = to_np(lse[g, HEADS])
+            ref = float(np.max(np.abs(o_ref)))
+            assert max_abs(got, o_ref[0]) <= TOL_BF16 * ref, (b, j, kappa)
+            assert max_abs(got_l, l_ref[0]) <= TOL_BF16 * max(1.0, float(np.max(np.abs(l_ref)))), (b, j, kappa)

@@ -193,6 +193,44 @@ def test_decode_halves_equal_the_whole_call(cache):
             s.max_pages, s.seqlens, tau, s.num_splits, s.ws, s.ws_bytes, None)
     L.mla_decode_query(*args)
     L.mla_decode_attend(*args)
-    L.mla_combine(s.cdims, s.act, s.batch, s.s_q, s.ws, s.ws_bytes, W["W_UV"], s.out, s.lse, None)
+    L.mla_combine(s.cdims, s.act, s.batch, s.s_q, s.num_splits, s.ws, s.ws_bytes, W["W_UV"], s.out, s.lse, None)
     torch.cuda.synchronize()
     assert torch.equal(whole[0], s.out) and torch.equal(whole[1], s.lse)
+
+
+def test_v3_sequence_is_independent_of_its_batch_mates():
+    """Sequence 0 (same seed, same length) decoded beside different batch-mates
+    and at a different place in the page pool gives the same bits: no row of
+    the query projections, attention items or merge reads another sequence."""
+    tau = tau_of(V3) * 20.0
+    outs = []
+    for lengths, table in (([300, 129, 64], "inorder"), ([300, 7], "shuffled"), ([300], "inorder")):
+        case = Case(V3, "bf16", "bf16", lengths, s_q=2, table=table, wl=1, num_splits=3)
+        out, lse, _ = case.run(tau)
+        outs.append((out[0], lse[0]))
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+
+
+def test_v3_split_counts_agree_with_each_other():
+    """The same batch with 1, 2, 3 and 7 splits per sequence: each split count
+    is an exact rewrite of the softmax, so the outputs agree far more closely
+    than either agrees with the float64 oracle (1e-2 max|o|, against 2e-2)."""
+    case = Case(V3, "bf16", "bf16", [300, 129, 448, 64], s_q=1, table="shuffled", wl=1, num_splits=1)
+    tau = tau_of(V3) * 30.0
+    ref, lref, _ = case.run(tau, num_splits=1)
+    for splits in (2, 3, 7):
+        out, lse, _ = case.run(tau, num_splits=splits)
+        assert case.sess.num_splits == splits
+        assert max_abs(out, ref) <= 1e-2 * float(np.abs(ref).max()), splits
+        assert max_abs(lse, lref) <= 1e-4 * float(np.abs(lref).max()), splits
+
+
+def test_v3_empty_sequence_in_a_batch():
+    """A sequence of length 0 beside others, through the MFMA query, attention
+    and merge kernels: its output is 0 and its lse -inf; the others match the
+    oracle."""
+    case = Case(V3, "bf16", "bf16", [200, 0, 65], s_q=1, table="shuffled", wl=1, num_splits=2)
+    tau = tau_of(V3) * 10.0
+    out, lse, _ = case.run(tau)
+    check_all(case, out, lse, tau, TOL_BF16)

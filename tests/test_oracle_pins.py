@@ -309,15 +309,18 @@ def test_head_subset_matches_all_heads():
     np.testing.assert_allclose(l_sub[:, 1], l_all[:, 0], rtol=1e-13)
 
 
-def test_brute_force_loops_tiny():
-    """Scalar-loop evaluation of one (query, head) on a 4-token cache, with the
-    key assembled element by element as [k^C; k^R]."""
+@pytest.mark.parametrize("L,chunk", [(4, 4096), (7, 3)])
+def test_brute_force_loops_tiny(L, chunk):
+    """Scalar-loop evaluation of one (query, head) on a short cache, with the
+    key assembled element by element as [k^C; k^R] and every token rotated at
+    its absolute position.  With chunk=3 the oracle builds the latents of
+    tokens 3.. in later chunks, so a position offset slipped at a chunk
+    boundary would fail here."""
     rng = np.random.default_rng(13)
     d = TINY
-    L = 4
     W, h = _setup(rng, T=L)
     tau = 0.45
-    o, lse = oracle.decode_from_h(h, W, d, seqlen=L, s_q=1, tau=tau)
+    o, lse = oracle.decode_from_h(h, W, d, seqlen=L, s_q=1, tau=tau, chunk=chunk)
     i = 1
     dh, dr, dc, dm = d["d_head"], d["d_rope"], d["d_c"], d["d_model"]
     import math
@@ -346,6 +349,18 @@ def test_brute_force_loops_tiny():
                for t in range(L)) for a in range(dh)]
     np.testing.assert_allclose(o[0, i], out, rtol=1e-11, atol=1e-13)
     assert abs(lse[0, i] - (mx + math.log(z))) < 1e-12
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 4, 9])
+def test_chunked_latents_equal_one_chunk(chunk):
+    """The chunk loop of decode_from_h only bounds memory: any chunk length
+    gives the single-chunk result (10 tokens, three causal query rows)."""
+    rng = np.random.default_rng(21)
+    W, h = _setup(rng, T=10)
+    o1, l1 = oracle.decode_from_h(h, W, TINY, seqlen=10, s_q=3, tau=0.8)
+    o2, l2 = oracle.decode_from_h(h, W, TINY, seqlen=10, s_q=3, tau=0.8, chunk=chunk)
+    assert float(np.max(np.abs(o1 - o2))) <= 1e-12
+    assert float(np.max(np.abs(l1 - l2))) <= 1e-12
 
 
 # ---------------------------------------------------------------- MTP verify model
