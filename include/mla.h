@@ -284,6 +284,30 @@ MLA_API int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch,
                 int32_t s_q, int32_t num_splits, void* ws, size_t ws_bytes,
                 const void* W_UV, void* out, float* lse_out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * step, mla_decode followed by mla_combine, with its workspace in a static
+ * array of MLA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends, instead of a caller's ws.  Arguments are
+ * those of mla_decode without ws/ws_bytes, plus W_UV, out and lse_out of
+ * mla_combine, with the same meaning, layout and validation; out and lse_out
+ * receive what mla_decode + mla_combine give on the same inputs.
+ * The MFMA path only (the DeepSeek-V3 head shape, BF16 activations, BF16 or
+ * FP8 cache, s_q 1..8): anything else returns MLA_ERR_UNSUPPORTED.  A split
+ * plan whose workspace exceeds the array returns MLA_ERR_WORKSPACE (the
+ * 64 x 4096-token batch with 4 splits takes about 58 MB).  Nothing is
+ * allocated and nothing is enqueued on an error.  Every call on one GPU uses
+ * that GPU's one array, and nothing in it needs to start at zero (a call
+ * writes every byte it reads): calls that overlap on one GPU, on different
+ * streams or threads, race.                                                */
+#define MLA_NOALLOC_SCRATCH_BYTES (64 << 20)
+MLA_API int mla_decode_step_noalloc(const mla_dims* dims, int32_t act_dtype, const void* hq,
+               int32_t batch, int32_t s_q, const void* W_DQ, const void* W_UQ,
+               const void* W_UK, const void* W_UV, const mla_cache* cache,
+               const int32_t* block_table, int32_t max_pages,
+               const int32_t* seqlens, float softmax_scale, int32_t num_splits,
+               void* out, float* lse_out, void* stream);
+
 /* Prefill (the non-absorbed form of the lesson's §2.1.1 for many new tokens
  * at once): n_seq fresh sequences packed back to back in
  *   h [n_tok, d_model] (BF16): sequence b is rows cu_seqlens[b] ..

@@ -20,7 +20,7 @@ EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
            "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
-           "mla_status_str", "mla_last_hip_error", "mla_version")
+           "mla_decode_step_noalloc", "mla_status_str", "mla_last_hip_error", "mla_version")
 
 
 class mla_dims(ctypes.Structure):
@@ -75,6 +75,7 @@ def _load():
         "mla_fp8_gemm_workspace_bytes": (SZ, [I32, I32, I32]),
         "mla_fp8_gemm": (ctypes.c_int, [I32, I32, I32, P, P, P, P, P, SZ, P]),
         "mla_mtp_tokens_per_step": (ctypes.c_double, [ctypes.c_double, I32]),
+        "mla_decode_step_noalloc": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, P, C, P, I32, P, F, I32, P, P, P]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
         "mla_last_hip_error": (ctypes.c_char_p, []),
@@ -241,6 +242,20 @@ def mla_combine(dims, act_dtype, batch, s_q, num_splits, ws, ws_bytes, W_UV, out
                           int(ws_bytes), _ptr(W_UV), _ptr(out), _ptr(lse_out), _stream(stream))
     if check:
         _check("mla_combine", st)
+    return st
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES of include/mla.h
+
+
+def mla_decode_step_noalloc(dims, act_dtype, hq, batch, s_q, W_DQ, W_UQ, W_UK, W_UV, cache, block_table, max_pages,
+                            seqlens, softmax_scale, num_splits, out, lse_out=None, stream=None, check=True):
+    st = _lib.mla_decode_step_noalloc(ctypes.byref(dims), int(act_dtype), _ptr(hq), int(batch), int(s_q), _ptr(W_DQ),
+                                      _ptr(W_UQ), _ptr(W_UK), _ptr(W_UV), ctypes.byref(cache), _ptr(block_table),
+                                      int(max_pages), _ptr(seqlens), float(softmax_scale), int(num_splits),
+                                      _ptr(out), _ptr(lse_out), _stream(stream))
+    if check:
+        _check("mla_decode_step_noalloc", st)
     return st
 
 

@@ -263,6 +263,39 @@ int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t 
   return hip_status(e);
 }
 
+int mla_decode_step_noalloc(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q,
+                            const void* W_DQ, const void* W_UQ, const void* W_UK, const void* W_UV,
+                            const mla_cache* cache, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seqlens, float softmax_scale, int32_t num_splits, void* out,
+                            float* lse_out, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_act(act_dtype)) return MLA_ERR_DTYPE;
+  if (batch < 0 || s_q < 1 || s_q > MAX_S_Q || num_splits < 0 || num_splits > MAX_SPLITS) return MLA_ERR_DIMS;
+  if ((st = check_cache(dims, cache, block_table, max_pages))) return st;
+  if (act_dtype == MLA_BF16 && cache->dtype == MLA_F32) return MLA_ERR_DTYPE;
+  if (!(softmax_scale == softmax_scale)) return MLA_ERR_DIMS;
+  if (force_generic() || !fast_decode_supported(*dims, act_dtype, cache->dtype, s_q)) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!hq || !W_UQ || !W_UK || !W_UV || !seqlens || !out) return MLA_ERR_NULL;
+  if (!aligned16(hq) || !aligned16(W_UQ) || !aligned16(W_UK) || !aligned16(W_UV) || !aligned16(seqlens) ||
+      !aligned16(out) || (W_DQ && !aligned16(W_DQ)) || (lse_out && !aligned16(lse_out)))
+    return MLA_ERR_ALIGN;
+  DecodeArgs a;
+  a.d = *dims; a.act = act_dtype; a.cache_dtype = cache->dtype; a.hq = hq; a.batch = batch; a.s_q = s_q;
+  a.W_DQ = W_DQ; a.W_UQ = W_UQ; a.W_UK = W_UK; a.pages = (const uint8_t*)cache->pages;
+  a.g = make_geom(*dims, cache->dtype); a.block_table = block_table; a.max_pages = max_pages; a.seqlens = seqlens;
+  a.scale = softmax_scale;
+  resolve_splits(dims, batch, s_q, max_pages, num_splits, &a.S, &a.pages_per_split);
+  a.L = noalloc_layout(*dims, batch, s_q, a.S);
+  if (a.L.total > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  a.stream = (hipStream_t)stream;
+  CombineArgs c;
+  c.d = *dims; c.act = act_dtype; c.batch = batch; c.s_q = s_q; c.S = a.S; c.L = a.L;
+  c.W_UV = W_UV; c.out = out; c.lse_out = lse_out; c.stream = a.stream;
+  return hip_status(noalloc_decode_step(a, c));
+}
+
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t n_tok) {
   if (check_dims(dims) || !valid_act(act_dtype) || n_tok < 0 || n_tok > MAX_PREFILL_TOKENS) return 0;
   return prefill_layout(*dims, n_tok).total;

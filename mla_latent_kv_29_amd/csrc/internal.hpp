@@ -161,6 +161,11 @@ struct OutProjArgs {
 int out_proj_splits(int act, int rows, int N, int K);
 size_t out_proj_ws_bytes(int act, int rows, int N, int K);
 
+// The decode step without a caller workspace (noalloc.hip): the workspace of
+// the MFMA path inside the library's static per-device array.
+WsLayout noalloc_layout(const mla_dims& d, int batch, int s_q, int S);
+hipError_t noalloc_decode_step(DecodeArgs& a, CombineArgs& c);
+
 // Raises the dynamic LDS limit of `kernel` to `bytes` on the current device,
 // once per (kernel, device); safe to call from several threads.
 hipError_t lds_limit(const void* kernel, int bytes);

@@ -295,3 +295,25 @@ def test_fp8_gemm_workspace_and_argument_errors():
     assert quant(K=100) == L.MLA_ERR_UNSUPPORTED
     assert quant(c=None) == L.MLA_ERR_NULL
     assert quant(w=FAKE + 8) == L.MLA_ERR_ALIGN
+
+
+def test_decode_step_noalloc_argument_errors():
+    """The allocation-free decode step refuses, on the host and before it
+    touches the device: shapes off the MFMA path, a split plan larger than
+    its static array, and missing pointers."""
+    d = _dims()
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 100)
+
+    def call(dims=d, act=m.MLA_BF16, batch=2, s_q=1, mp=64, splits=0, out=FAKE, c=cache):
+        return L.mla_decode_step_noalloc(dims, act, FAKE, batch, s_q, FAKE, FAKE, FAKE, FAKE, c, FAKE, mp, FAKE, 0.1,
+                                         splits, out, None, stream=0, check=False)
+
+    t = m.make_dims(inputs.TINY_DIMS)
+    assert call(dims=t, act=m.MLA_F32, c=L.cache_struct(FAKE, m.MLA_F32, 100)) == L.MLA_ERR_UNSUPPORTED
+    assert call(act=m.MLA_F32) == L.MLA_ERR_UNSUPPORTED                    # f32 activations: generic path only
+    assert call(batch=0) == L.MLA_OK
+    assert call(out=None) == L.MLA_ERR_NULL
+    assert call(s_q=9) == L.MLA_ERR_DIMS
+    # 128 sequences x 2 rows x 4 splits of 8192 tokens: about 134 MB of bf16 partials alone
+    assert call(batch=128, s_q=2, mp=128) == L.MLA_ERR_WORKSPACE
+    assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
