@@ -458,6 +458,28 @@ __device__ __forceinline__ void part2_all(Fused& F, std::integer_sequence<int, K
   (part2<F8, K>(F), ...);
 }
 
+// After the last step: the P.V of its two stages alone (32 MFMAs, no scores).
+template <bool F8>
+__device__ __forceinline__ void pv_tail(Fused& F) {
+  read_v(F, F.va);
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) read_p(F, 0, hb);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_mfma<0>(F); pv_mfma<1>(F); pv_mfma<2>(F); pv_mfma<3>(F);
+  pv_mfma<4>(F); pv_mfma<5>(F); pv_mfma<6>(F); pv_mfma<7>(F);
+  pv_mfma<8>(F); pv_mfma<9>(F); pv_mfma<10>(F); pv_mfma<11>(F);
+  pv_mfma<12>(F); pv_mfma<13>(F); pv_mfma<14>(F); pv_mfma<15>(F);
+  __builtin_amdgcn_sched_barrier(0);
+  read_v(F, F.vb);
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) read_p(F, 1, hb);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_mfma<0>(F); pv_mfma<1>(F); pv_mfma<2>(F); pv_mfma<3>(F);
+  pv_mfma<4>(F); pv_mfma<5>(F); pv_mfma<6>(F); pv_mfma<7>(F);
+  pv_mfma<8>(F); pv_mfma<9>(F); pv_mfma<10>(F); pv_mfma<11>(F);
+  pv_mfma<12>(F); pv_mfma<13>(F); pv_mfma<14>(F); pv_mfma<15>(F);
+}
+
 // Zeroes the latent part of the tokens past the end of the split in its last
 // stage, so that whatever bytes the page holds there cannot turn a zero
 // weight into NaN in P.V.  Runs after the barrier that publishes the stage
@@ -533,15 +555,13 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
   bool ovf = false;
   int sa = 0;  // slot of stage 2m
   int fa = 0;  // fp8: fp8-ring slot of stage 2m
-  for (int m = 0; m <= c.nsteps; ++m) {
-    if (m < c.nsteps) wait_step<F8>(c, m);
+  for (int m = 0; m < c.nsteps; ++m) {
+    wait_step<F8>(c, m);
     ring_barrier();
     if constexpr (F8) {
       // this step's two stages into the bf16 slots freed by the last P.V
-      if (m < c.nsteps) {
-        widen_stage(c, fa, sa);
-        if (2 * m + 1 < c.nst) widen_stage(c, wrap5(fa + 1), wrap<F8>(sa + 1));
-      }
+      widen_stage(c, fa, sa);
+      if (2 * m + 1 < c.nst) widen_stage(c, wrap5(fa + 1), wrap<F8>(sa + 1));
       // copies of stages 2m+3, 2m+4 into the fp8 slots widened last step
       issue_stage<F8>(c, 2 * m + 3, wrap5(fa + 3));
       issue_stage<F8>(c, 2 * m + 4, wrap5(fa + 4));
@@ -557,8 +577,6 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
       cx = plan_stage<F8>(c, 2 * m + 3, wrap<F8>(sa + 3));
       cy = plan_stage<F8>(c, 2 * m + 4, wrap<F8>(sa + 4));
     }
-    // The step after the last one only completes the P.V of the last stages:
-    // its scores run on a stale slot and are all masked.
     const int sb = 2 * m + 1 < c.nst ? wrap<F8>(sa + 1) : sa;
     if ((c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
     const lu8* stA = c.lds + sa * ST_BYTES;
@@ -572,10 +590,21 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
     read_p(F, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
     part1_all<F8>(F, std::make_integer_sequence<int, KSTEPS>{});
-    mask(c, F.sc, m < c.nsteps ? c.ntok - 2 * m * T : 0);
+    mask(c, F.sc, c.ntok - 2 * m * T);
     part2_all<F8>(F, std::make_integer_sequence<int, 16>{});
     sa = wrap<F8>(sa + 2);
     if constexpr (F8) fa = wrap5(fa + 2);
+  }
+  // the P.V of the last step's stages, once every wave has written its weights
+  ring_barrier();
+  {
+    const int m = c.nsteps;
+    const int pa = wrap<F8>(sa + Ly::NST - 2), pb = 2 * m - 1 < c.nst ? wrap<F8>(sa + Ly::NST - 1) : pa;
+    const StageCopy none{nullptr, 0};
+    Fused F{c, m, c.lds, qf, {}, {}, {}, c.lds + pa * ST_BYTES, c.lds + pb * ST_BYTES,
+            c.lds + Ly::P_OFF + ((m - 1) & 1) * P_BYTES + c.pr_ofs, {}, {}, o, m_ref, m_all, l_run, ovf,
+            c.lds, none, none, 0.0f, {}};
+    pv_tail<F8>(F);
   }
   return ovf;
 }
