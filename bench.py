@@ -146,6 +146,50 @@ def copy_calibration(mib, dev):
     del src, dst
 
 
+def run_hbm_probe(args):
+    """Achievable HBM bandwidth on this GPU: a plain streaming read
+    (mla_hbm_read_probe: 16-byte loads over the whole GPU) and a copy
+    (torch's copy kernel), each over several buffers in turn so that no pass
+    finds its data in the 256 MB last-level cache; 75 MB and 302 MB (one
+    attention launch's query rows and cache).  Reports the median over the
+    passes."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_29_amd import _lib as L
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    props = torch.cuda.get_device_properties(0)
+    res = {"probe": "hbm", "device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+           "compute_units": props.multi_processor_count, "results": []}
+    for mb in (75, 302):
+        n = mb * 1000 * 1000 // 4
+        nbuf = max(2, (1024 // mb) + 1)
+        srcs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(nbuf)]
+        dsts = [torch.empty_like(srcs[0]) for _ in range(nbuf)]
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        for kind in ("read", "copy"):
+            ts = []
+            for rep in range(3 * nbuf + 20):
+                i = rep % nbuf
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if kind == "read":
+                    L.mla_hbm_read_probe(srcs[i], 4 * n, sink)
+                else:
+                    dsts[i].copy_(srcs[i])
+                e1.record()
+                e1.synchronize()
+                if rep >= nbuf:
+                    ts.append(e0.elapsed_time(e1) * 1e-3)
+            t = float(np.median(ts))
+            moved = 4 * n * (1 if kind == "read" else 2)
+            res["results"].append({"kind": kind, "mb": mb, "us": t * 1e6, "GB_per_s": moved / t / 1e9,
+                                   "bytes": moved})
+        del srcs, dsts
+        torch.cuda.empty_cache()
+    print(json.dumps(res))
+
+
 def run_layers(args, name):
     """Layer-stack workload: one step = for every layer, mla_decode_query +
     mla_decode_attend + mla_combine + mla_output_project, each layer with its
@@ -432,6 +476,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="copies of cache+weights rotated across steps")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="measure achievable HBM read and copy bandwidth (75 MB, 302 MB) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB three times (untimed), as the "
                          "reference for hardware byte counters")
@@ -442,6 +488,9 @@ def main():
               f"share at its real shape and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
+    if args.hbm_probe:
+        run_hbm_probe(args)
+        return
     from mla_latent_kv_29_amd import inputs
     if args.workload in inputs.PREFILL_WORKLOADS:
         run_prefill(args, args.workload)
@@ -523,6 +572,7 @@ def main():
     q_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sampled]
     a_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in sampled]
     c_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in sampled]
+    s_ms = [ev[i][0].elapsed_time(ev[i][3]) for i in sampled]
     ms_per_step = wall / args.steps * 1e3
     tokens = float(np.sum(lengths))
     alg = algorithmic(spec, dims, lengths)
@@ -552,7 +602,9 @@ def main():
                    if spec["lengths"][0] == "fixed" else f"U[{spec['lengths'][1]},{spec['lengths'][2]}]",
                    "s_q": s_q, "cache": spec["cache"], "splits": sess.num_splits,
                    "cached_tokens": int(tokens), "rotation_sets": len(sets)},
-        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+        "roofline": {"scope": "dominant kernel (the split-KV attention launch) only; the whole step is in "
+                              "step_roofline",
+                     "bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": measured_traffic(args.workload, spec["cache"]),
                      "kernel": ("k_attn_v3b<false>" if spec["cache"] == "bf16" else "k_attn_v3b<true>") + " (mla_decode_attend)",
                      "attn_ms_mean": float(np.mean(a_ms))},
@@ -560,6 +612,10 @@ def main():
                           "step_bytes": alg["step_bytes"], "step_flops": alg["step_flops"]},
         "phases_ms": {"query": float(np.median(q_ms)), "attend": float(np.median(a_ms)),
                       "combine": float(np.median(c_ms))},
+        # per-step times of the sampled steps (events at both ends of each, so
+        # each includes one event's wait): p10 / p50 / p90, and the mean
+        "step_ms_sampled": {"p10": float(np.percentile(s_ms, 10)), "p50": float(np.percentile(s_ms, 50)),
+                            "p90": float(np.percentile(s_ms, 90)), "mean": float(np.mean(s_ms)), "n": len(s_ms)},
         "cache_build_s": build_s,
     }
     if s_q > 1:

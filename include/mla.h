@@ -350,6 +350,14 @@ MLA_API int mla_prefill_attend(const mla_dims* dims, int32_t act_dtype, const vo
                 const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
                 float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement helper (no part of the decode maths): streams `bytes` (a
+ * multiple of 16) of device memory at src with 16-byte loads over the whole
+ * GPU and writes nothing (sink: one device int32 that is practically never
+ * written).  Timing it gives the achievable HBM read bandwidth that the
+ * decode kernels' byte roofline is read against next to the data-sheet
+ * figure.  Errors: MLA_ERR_NULL, MLA_ERR_DIMS (bytes % 16), MLA_ERR_ALIGN.  */
+MLA_API int mla_hbm_read_probe(const void* src, size_t bytes, int32_t* sink, void* stream);
+
 /* Static description of a status code.                                      */
 MLA_API const char* mla_status_str(int status);
 

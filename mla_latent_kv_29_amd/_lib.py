@@ -20,7 +20,8 @@ EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
            "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
-           "mla_decode_step_noalloc", "mla_status_str", "mla_last_hip_error", "mla_version")
+           "mla_decode_step_noalloc", "mla_hbm_read_probe", "mla_status_str", "mla_last_hip_error",
+           "mla_version")
 
 
 class mla_dims(ctypes.Structure):
@@ -76,6 +77,7 @@ def _load():
         "mla_fp8_gemm": (ctypes.c_int, [I32, I32, I32, P, P, P, P, P, SZ, P]),
         "mla_mtp_tokens_per_step": (ctypes.c_double, [ctypes.c_double, I32]),
         "mla_decode_step_noalloc": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, P, C, P, I32, P, F, I32, P, P, P]),
+        "mla_hbm_read_probe": (ctypes.c_int, [P, SZ, P, P]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
         "mla_last_hip_error": (ctypes.c_char_p, []),
@@ -256,6 +258,13 @@ def mla_decode_step_noalloc(dims, act_dtype, hq, batch, s_q, W_DQ, W_UQ, W_UK, W
                                       _ptr(out), _ptr(lse_out), _stream(stream))
     if check:
         _check("mla_decode_step_noalloc", st)
+    return st
+
+
+def mla_hbm_read_probe(src, nbytes, sink, stream=None, check=True):
+    st = _lib.mla_hbm_read_probe(_ptr(src), int(nbytes), _ptr(sink), _stream(stream))
+    if check:
+        _check("mla_hbm_read_probe", st)
     return st
 
 

@@ -414,6 +414,14 @@ int mla_fp8_gemm(int32_t M, int32_t N, int32_t K, const void* X, const void* W_c
                              (hipStream_t)stream));
 }
 
+int mla_hbm_read_probe(const void* src, size_t bytes, int32_t* sink, void* stream) {
+  if (bytes == 0) return MLA_OK;
+  if (!src || !sink) return MLA_ERR_NULL;
+  if (bytes % 16) return MLA_ERR_DIMS;
+  if (!aligned16(src) || ((uintptr_t)sink & 3)) return MLA_ERR_ALIGN;
+  return hip_status(read_probe(src, bytes, sink, (hipStream_t)stream));
+}
+
 double mla_mtp_tokens_per_step(double acceptance, int32_t depth) {
   if (!(acceptance >= 0.0 && acceptance <= 1.0) || depth < 0 || depth > MAX_S_Q - 1) return NAN;
   // Horner form of 1 + a + ... + a^depth: the draft chain's survival probabilities

@@ -166,6 +166,9 @@ size_t out_proj_ws_bytes(int act, int rows, int N, int K);
 WsLayout noalloc_layout(const mla_dims& d, int batch, int s_q, int S);
 hipError_t noalloc_decode_step(DecodeArgs& a, CombineArgs& c);
 
+// Streaming read of `bytes` (a multiple of 16) from src (probe.hip).
+hipError_t read_probe(const void* src, size_t bytes, int* sink, hipStream_t st);
+
 // Raises the dynamic LDS limit of `kernel` to `bytes` on the current device,
 // once per (kernel, device); safe to call from several threads.
 hipError_t lds_limit(const void* kernel, int bytes);

@@ -317,3 +317,10 @@ def test_decode_step_noalloc_argument_errors():
     # 128 sequences x 2 rows x 4 splits of 8192 tokens: about 134 MB of bf16 partials alone
     assert call(batch=128, s_q=2, mp=128) == L.MLA_ERR_WORKSPACE
     assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_hbm_read_probe_argument_errors():
+    assert L.mla_hbm_read_probe(FAKE, 0, FAKE, stream=0, check=False) == L.MLA_OK
+    assert L.mla_hbm_read_probe(None, 64, FAKE, stream=0, check=False) == L.MLA_ERR_NULL
+    assert L.mla_hbm_read_probe(FAKE, 65, FAKE, stream=0, check=False) == L.MLA_ERR_DIMS
+    assert L.mla_hbm_read_probe(FAKE + 8, 64, FAKE, stream=0, check=False) == L.MLA_ERR_ALIGN
