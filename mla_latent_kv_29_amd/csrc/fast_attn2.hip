@@ -10,21 +10,23 @@
 //
 // Work item = (sequence b, split s, query j): all 128 heads over the split's
 // tokens.  Four waves, one per SIMD, split the two products differently:
-//   * scores: wave w owns heads 32w..32w+31.  S^T[16 tokens][16 heads]
-//     blocks = K . Q^T with v_mfma_f32_16x16x32_bf16 (each K fragment read
-//     from LDS feeds two of them); the wave's 512-wide absorbed query rows
-//     sit in 128 VGPRs, the 64-wide RoPE rows of all heads in LDS.
+//   * scores: wave w owns heads 32w..32w+31.  A step's S^T[32 tokens][32
+//     heads] = K . Q^T is one chain of 36 v_mfma_f32_32x32x16_bf16 over the
+//     576 channels (k-steps of 16): the K fragments (tokens of the step's
+//     two 16-token stages) come from LDS, the wave's 512-wide absorbed query
+//     rows sit in 128 VGPRs, the 64-wide RoPE rows of all heads in LDS.
 //   * P.V: wave w owns latent channels 128w..128w+127 of all 128 heads.
 //     O^T[128 ch][128 heads] += V^T . P^T with v_mfma_f32_32x32x16_bf16 into
 //     all 256 AGPRs; V^T comes from the staged tokens with the transposing
 //     ds_read_b64_tr_b16, P^T from an LDS buffer that every wave writes its
 //     heads' weights to.
-// Splitting P.V by channel means each wave reads only a quarter of V.  A
-// step covers two 16-token stages: the scores of stages 2m, 2m+1 and the P.V
-// of stages 2m-2, 2m-1 run between the same two barriers, so one barrier per
-// 32 tokens publishes both the new stages and the previous weights.  The
-// softmax VALU work is interleaved one slot at a time with the P.V MFMAs, so
-// it issues while the matrix unit is busy.
+// Splitting P.V by channel means each wave reads only a quarter of V.  Step
+// m scores stages 2m, 2m+1 and multiplies the weights of stages 2m-2, 2m-1
+// by V between the same two barriers, so one barrier per 32 tokens
+// publishes both the new stages and the previous weights; the last step's
+// P.V runs on its own afterwards.  The P.V MFMAs are interleaved with the
+// score chain and the softmax VALU work with the P.V MFMAs, so that the
+// vector work issues while the matrix unit is busy.
 //
 // The score MFMAs are written as inline asm with VGPR accumulators: with O
 // holding every AGPR, compiler-selected MFMAs would put the scores in AGPRs
