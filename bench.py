@@ -42,7 +42,11 @@ def algorithmic(spec, dims, lengths):
     cache = sum(L) * tok_bytes
     attn_flops = vis * H * 2 * ((dc + dr) + dc)
     R = len(L) * s_q
-    w_bytes = es * (dq * d + H * (dh + dr) * dq + 2 * H * dh * dc)
+    if spec.get("weights") == "fp8":  # E4M3 codes and one fp32 scale per 128 x 128 block
+        w_el = dq * d + H * (dh + dr) * dq + 2 * H * dh * dc
+        w_bytes = w_el + 4 * w_el // (128 * 128)
+    else:
+        w_bytes = es * (dq * d + H * (dh + dr) * dq + 2 * H * dh * dc)
     io_bytes = es * (R * d + R * H * dh)
     q_flops = 2 * R * (dq * d + H * (dh + dr) * dq + H * dh * dc)
     o_flops = 2 * R * H * dh * dc
@@ -96,6 +100,9 @@ def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=64):
         threads = None
     Wn = {k: v.to("cpu", torch.float64).numpy() for k, v in W.items()}
     s_q = spec["s_q"]
+    fp8w = spec.get("weights") == "fp8"
+    if fp8w:  # the weights' block quantisation is preparation, not part of a step: untimed
+        Wq = {k: oracle.quantize_blocks(Wn[k]) for k in ("W_DQ", "W_UQ", "W_UK", "W_UV")}
     order = np.argsort(lengths)[::-1] if spec["lengths"][0] != "fixed" else range(len(lengths))
     t_used, toks, n = 0.0, 0, 0
     for b in list(order)[:max_seqs]:
@@ -105,7 +112,10 @@ def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=64):
         hq = h[Lb - s_q:Lb]
         tau = 1.0 / math.sqrt(dims["d_head"] + dims["d_rope"])
         t0 = time.perf_counter()
-        oracle.decode_from_latents(c, kr, hq, Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], dims, Lb, s_q, tau)
+        if fp8w:
+            oracle.decode_fp8w_from_latents(c, kr, hq, Wq, dims, Lb, s_q, tau)
+        else:
+            oracle.decode_from_latents(c, kr, hq, Wn["W_DQ"], Wn["W_UQ"], Wn["W_UK"], Wn["W_UV"], dims, Lb, s_q, tau)
         t_used += time.perf_counter() - t0
         toks += Lb
         n += 1
@@ -113,7 +123,8 @@ def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=64):
             break
     return {"value": toks / t_used, "unit": "cached-tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} sequence(s), {toks} cached tokens, float64 numpy, decode from cached latents "
-                      f"(explicit k^C/v^C per head), {t_used:.1f} s",
+                      + ("(FP8 block-scaled projections, absorbed form)" if fp8w else
+                         "(explicit k^C/v^C per head)") + f", {t_used:.1f} s",
             "host_cpus": os.cpu_count(), "cpu_model": platform.processor() or platform.machine()}
 
 
@@ -544,18 +555,34 @@ def main():
     sampled = list(range(0, args.steps, every))
     ev = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for i in sampled}
 
+    fp8w = spec.get("weights") == "fp8"
+    if fp8w:
+        # E4M3 weights with 128 x 128-block scales, quantised by the library once per rotation set
+        qsets = [sess.quantize_fp8w(Wk) for _, Wk in sets]
+        sess.fp8w_workspace()
+        fargs = lambda i: (c, hq, sess.batch, s_q, qsets[i]["W_DQ"], qsets[i]["W_UQ"], qsets[i]["W_UKT"], caches[i],
+                           sess.block_table, sess.max_pages, sess.seqlens, tau, sess.num_splits, sess.ws,
+                           sess.ws_bytes, sp)
+
     def step(i, e=None):
         k = i % len(sets)
         if e is not None:
             e[0].record(stream)
-        L.mla_decode_query(*dargs(k))
+        if fp8w:
+            L.mla_decode_fp8w_query(*fargs(k))
+        else:
+            L.mla_decode_query(*dargs(k))
         if e is not None:
             e[1].record(stream)
         L.mla_decode_attend(*dargs(k))
         if e is not None:
             e[2].record(stream)
-        L.mla_combine(c, sess.act, sess.batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes, sets[k][1]["W_UV"],
-                      sess.out, sess.lse, sp)
+        if fp8w:
+            L.mla_combine_fp8w(c, sess.batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes, qsets[k]["W_UV"],
+                               sess.out, sess.lse, sp)
+        else:
+            L.mla_combine(c, sess.act, sess.batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes,
+                          sets[k][1]["W_UV"], sess.out, sess.lse, sp)
         if e is not None:
             e[3].record(stream)
 
@@ -596,11 +623,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": spec["act"] if spec["cache"] != "fp8" else "bf16+fp8cache",
+        "dtype": (spec["act"] if spec["cache"] != "fp8" else "bf16+fp8cache") + ("+fp8weights" if fp8w else ""),
         "data": "synthetic (seeded N(0,1) hidden states, N(0,sigma^2) weights at DeepSeek-V3 MLA shapes)",
         "config": {"workload": args.workload, "batch": int(spec["batch"]), "seq_len": spec["lengths"][1]
                    if spec["lengths"][0] == "fixed" else f"U[{spec['lengths'][1]},{spec['lengths'][2]}]",
-                   "s_q": s_q, "cache": spec["cache"], "splits": sess.num_splits,
+                   "s_q": s_q, "cache": spec["cache"], "weights": spec.get("weights", spec["act"]),
+                   "splits": sess.num_splits,
                    "cached_tokens": int(tokens), "rotation_sets": len(sets)},
         "roofline": {"scope": "dominant kernel (the split-KV attention launch) only; the whole step is in "
                               "step_roofline",

@@ -191,6 +191,15 @@ MLA_API int mla_output_project(const mla_dims* dims, int32_t act_dtype, int32_t 
  * MLA_ERR_HIP.  Device pointers, caller-owned, no allocation.               */
 MLA_API int mla_fp8_quantize_weight(const void* W, int32_t N, int32_t K, void* codes,
                                     float* scales, void* stream);
+/* mla_fp8_quantize_weight of the transposes of `batch` matrices: W [batch,
+ * R, C] bf16 -> codes [batch, C, R] (row b*C + c holds column c of W[b])
+ * and scales [batch, C/128, R/128]; each 128 x 128 block of W[b]^T is the
+ * transpose of a block of W[b] and gets that block's scale.  R and C
+ * multiples of 128 (else MLA_ERR_UNSUPPORTED), at most 65536, batch 1..65536.
+ * For W^UK [n_heads, d_head, d_c], which mla_decode_fp8w takes transposed
+ * per head.                                                                 */
+MLA_API int mla_fp8_quantize_weight_t(const void* W, int32_t batch, int32_t R, int32_t C,
+                                      void* codes, float* scales, void* stream);
 MLA_API size_t mla_fp8_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 MLA_API int mla_fp8_gemm(int32_t M, int32_t N, int32_t K, const void* X, const void* W_codes,
                          const float* W_scales, void* Y, void* ws, size_t ws_bytes, void* stream);
@@ -239,8 +248,10 @@ MLA_API int mla_decode(const mla_dims* dims, int32_t act_dtype, const void* hq,
  * them separately (same arguments and validation as mla_decode):
  * mla_decode_query runs the query projection and absorption into ws;
  * mla_decode_attend then runs the split-KV attention over the cache using
- * the queries in ws and records the split plan there for mla_combine.
- * mla_decode == query then attend.                                          */
+ * the queries in ws and records the split plan there for mla_combine.  The
+ * attention reads neither hq nor the weights, so mla_decode_attend accepts
+ * NULL for hq, W_DQ, W_UQ and W_UK (it also serves the queries that
+ * mla_decode_fp8w_query leaves in ws).  mla_decode == query then attend.    */
 MLA_API int mla_decode_query(const mla_dims* dims, int32_t act_dtype, const void* hq,
                int32_t batch, int32_t s_q, const void* W_DQ, const void* W_UQ,
                const void* W_UK, const mla_cache* cache,
@@ -283,6 +294,57 @@ MLA_API int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t s
 MLA_API int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch,
                 int32_t s_q, int32_t num_splits, void* ws, size_t ws_bytes,
                 const void* W_UV, void* out, float* lse_out, void* stream);
+
+/* Decode step with FP8 block-scaled projection weights: the query phase
+ * and the combine of mla_decode / mla_combine with W^DQ, W^UQ, W^UK and
+ * W^UV in E4M3 ("Читаем техотчёт DeepSeek-V3 вместе", §3.3 "Обучение в
+ * FP8", items 2-4: weights in 128 x 128 blocks, activations in 1 x 128
+ * tiles, scale s = amax / 448 per group, every 128-wide partial product
+ * promoted into an fp32 sum with its two scales).  Each projection is
+ * Y = Q(X) . Q(W)^T with W quantised once by mla_fp8_quantize_weight and X
+ * quantised in the step:
+ *   c^Q = W^DQ hq;  u = W^UQ c^Q;  qt_i = tau*log2(e) [W^UK_i^T q^C_i ;
+ *   RoPE(q^R_i)];  out_i = W^UV_i O_lat_i
+ * (bf16 rounding of c^Q, u and O_lat between the GEMMs, as the bf16 step
+ * does).  The attention between them is that of the bf16 step, on a BF16 or
+ * FP8 cache.
+ *   hq [batch*s_q, d_model] BF16 hidden states (W^DQ is required).
+ *   W_DQ: codes [d_cq, d_model], scales [d_cq/128, d_model/128].
+ *   W_UQ: codes [n_heads*(d_head+d_rope), d_cq], scales [rows/128, d_cq/128]
+ *     (the rows of mla_decode's W_UQ).
+ *   W_UKT: W^UK transposed per head, codes [n_heads*d_c, d_head] (row
+ *     i*d_c + n, column k holds W^UK[i][k][n]), scales [n_heads*d_c/128,
+ *     d_head/128]: mla_fp8_quantize_weight_t(W_UK, n_heads, d_head, d_c).
+ *   W_UV: codes [n_heads*d_head, d_c], scales [n_heads*d_head/128, d_c/128].
+ * Codes 16-byte aligned, scales 4-byte aligned, all device, caller-owned.
+ * The other arguments are mla_decode's (act_dtype is BF16).  ws holds
+ * mla_decode_fp8w_workspace_bytes(...) bytes: the bf16 step's workspace
+ * (so mla_decode_attend and the split plan work on it unchanged) followed
+ * by the FP8 GEMMs' activation codes, scales and partial sums.
+ * mla_decode_fp8w = mla_decode_fp8w_query, then the attention;
+ * mla_combine_fp8w merges the splits as mla_combine does and applies W_UV.
+ * Supported: the DeepSeek-V3 head shape of the MFMA path (d_head 128, d_c
+ * 512, d_rope 64, 128 heads, 64-token pages), d_cq and d_model multiples of
+ * 512, s_q 1..8; anything else returns MLA_ERR_UNSUPPORTED (and the
+ * workspace size 0).  Errors as for mla_decode; nothing is enqueued on an
+ * error other than MLA_ERR_HIP.                                             */
+MLA_API size_t mla_decode_fp8w_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                               int32_t num_splits);
+MLA_API int mla_decode_fp8w(const mla_dims* dims, const void* hq, int32_t batch, int32_t s_q,
+               const void* W_DQ_codes, const float* W_DQ_scales, const void* W_UQ_codes,
+               const float* W_UQ_scales, const void* W_UKT_codes, const float* W_UKT_scales,
+               const mla_cache* cache, const int32_t* block_table, int32_t max_pages,
+               const int32_t* seqlens, float softmax_scale, int32_t num_splits,
+               void* ws, size_t ws_bytes, void* stream);
+MLA_API int mla_decode_fp8w_query(const mla_dims* dims, const void* hq, int32_t batch, int32_t s_q,
+               const void* W_DQ_codes, const float* W_DQ_scales, const void* W_UQ_codes,
+               const float* W_UQ_scales, const void* W_UKT_codes, const float* W_UKT_scales,
+               const mla_cache* cache, const int32_t* block_table, int32_t max_pages,
+               const int32_t* seqlens, float softmax_scale, int32_t num_splits,
+               void* ws, size_t ws_bytes, void* stream);
+MLA_API int mla_combine_fp8w(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t num_splits,
+               void* ws, size_t ws_bytes, const void* W_UV_codes, const float* W_UV_scales,
+               void* out, float* lse_out, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the decode

@@ -12,7 +12,8 @@ from ._lib import (mla_page_bytes, mla_cache_append, mla_cache_write, mla_defaul
                    mla_workspace_bytes, mla_decode, mla_decode_query, mla_decode_attend, mla_combine,
                    mla_prefill_workspace_bytes, mla_prefill, mla_prefill_project, mla_prefill_attend,
                    mla_output_project_workspace_bytes, mla_output_project, mla_fp8_quantize_weight,
-                   mla_fp8_gemm_workspace_bytes, mla_fp8_gemm, mla_mtp_tokens_per_step,
+                   mla_fp8_quantize_weight_t, mla_fp8_gemm_workspace_bytes, mla_fp8_gemm, mla_mtp_tokens_per_step,
+                   mla_decode_fp8w_workspace_bytes, mla_decode_fp8w, mla_decode_fp8w_query, mla_combine_fp8w,
                    status_str, version, make_dims,
                    MLAError, MLA_F32, MLA_BF16, MLA_FP8_E4M3)
 
@@ -20,6 +21,7 @@ __all__ = ["mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
-           "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
+           "mla_fp8_quantize_weight_t", "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
+           "mla_decode_fp8w_workspace_bytes", "mla_decode_fp8w", "mla_decode_fp8w_query", "mla_combine_fp8w",
            "status_str", "version", "make_dims",
            "MLAError", "MLA_F32", "MLA_BF16", "MLA_FP8_E4M3"]

@@ -19,9 +19,10 @@ EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
-           "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
-           "mla_decode_step_noalloc", "mla_hbm_read_probe", "mla_status_str", "mla_last_hip_error",
-           "mla_version")
+           "mla_fp8_quantize_weight_t", "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
+           "mla_decode_step_noalloc", "mla_decode_fp8w_workspace_bytes", "mla_decode_fp8w",
+           "mla_decode_fp8w_query", "mla_combine_fp8w", "mla_hbm_read_probe", "mla_status_str",
+           "mla_last_hip_error", "mla_version")
 
 
 class mla_dims(ctypes.Structure):
@@ -73,10 +74,15 @@ def _load():
         "mla_output_project_workspace_bytes": (SZ, [D, I32, I32]),
         "mla_output_project": (ctypes.c_int, [D, I32, I32, P, P, P, P, SZ, P]),
         "mla_fp8_quantize_weight": (ctypes.c_int, [P, I32, I32, P, P, P]),
+        "mla_fp8_quantize_weight_t": (ctypes.c_int, [P, I32, I32, I32, P, P, P]),
         "mla_fp8_gemm_workspace_bytes": (SZ, [I32, I32, I32]),
         "mla_fp8_gemm": (ctypes.c_int, [I32, I32, I32, P, P, P, P, P, SZ, P]),
         "mla_mtp_tokens_per_step": (ctypes.c_double, [ctypes.c_double, I32]),
         "mla_decode_step_noalloc": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, P, C, P, I32, P, F, I32, P, P, P]),
+        "mla_decode_fp8w_workspace_bytes": (SZ, [D, I32, I32, I32]),
+        "mla_decode_fp8w": (ctypes.c_int, [D, P, I32, I32, P, P, P, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
+        "mla_decode_fp8w_query": (ctypes.c_int, [D, P, I32, I32, P, P, P, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
+        "mla_combine_fp8w": (ctypes.c_int, [D, I32, I32, I32, P, SZ, P, P, P, P, P]),
         "mla_hbm_read_probe": (ctypes.c_int, [P, SZ, P, P]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
@@ -153,6 +159,14 @@ def mla_fp8_quantize_weight(W, N, K, codes, scales, stream=None, check=True):
     st = _lib.mla_fp8_quantize_weight(_ptr(W), int(N), int(K), _ptr(codes), _ptr(scales), _stream(stream))
     if check:
         _check("mla_fp8_quantize_weight", st)
+    return st
+
+
+def mla_fp8_quantize_weight_t(W, batch, R, C, codes, scales, stream=None, check=True):
+    st = _lib.mla_fp8_quantize_weight_t(_ptr(W), int(batch), int(R), int(C), _ptr(codes), _ptr(scales),
+                                        _stream(stream))
+    if check:
+        _check("mla_fp8_quantize_weight_t", st)
     return st
 
 
@@ -244,6 +258,39 @@ def mla_combine(dims, act_dtype, batch, s_q, num_splits, ws, ws_bytes, W_UV, out
                           int(ws_bytes), _ptr(W_UV), _ptr(out), _ptr(lse_out), _stream(stream))
     if check:
         _check("mla_combine", st)
+    return st
+
+
+def mla_decode_fp8w_workspace_bytes(dims, batch, s_q, num_splits):
+    return int(_lib.mla_decode_fp8w_workspace_bytes(ctypes.byref(dims), int(batch), int(s_q), int(num_splits)))
+
+
+def _fp8w_call(name, dims, hq, batch, s_q, W_DQ, W_UQ, W_UKT, cache, block_table, max_pages, seqlens,
+               softmax_scale, num_splits, ws, ws_bytes, stream=None, check=True):
+    """W_DQ, W_UQ, W_UKT: (codes, scales) pairs of mla_fp8_quantize_weight."""
+    st = getattr(_lib, name)(ctypes.byref(dims), _ptr(hq), int(batch), int(s_q), _ptr(W_DQ[0]), _ptr(W_DQ[1]),
+                             _ptr(W_UQ[0]), _ptr(W_UQ[1]), _ptr(W_UKT[0]), _ptr(W_UKT[1]), ctypes.byref(cache),
+                             _ptr(block_table), int(max_pages), _ptr(seqlens), float(softmax_scale),
+                             int(num_splits), _ptr(ws), int(ws_bytes), _stream(stream))
+    if check:
+        _check(name, st)
+    return st
+
+
+def mla_decode_fp8w(*args, **kw):
+    return _fp8w_call("mla_decode_fp8w", *args, **kw)
+
+
+def mla_decode_fp8w_query(*args, **kw):
+    return _fp8w_call("mla_decode_fp8w_query", *args, **kw)
+
+
+def mla_combine_fp8w(dims, batch, s_q, num_splits, ws, ws_bytes, W_UV, out, lse_out=None, stream=None, check=True):
+    """W_UV: (codes, scales) of mla_fp8_quantize_weight."""
+    st = _lib.mla_combine_fp8w(ctypes.byref(dims), int(batch), int(s_q), int(num_splits), _ptr(ws), int(ws_bytes),
+                               _ptr(W_UV[0]), _ptr(W_UV[1]), _ptr(out), _ptr(lse_out), _stream(stream))
+    if check:
+        _check("mla_combine_fp8w", st)
     return st
 
 

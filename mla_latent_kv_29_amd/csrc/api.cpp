@@ -188,10 +188,12 @@ static int decode_impl(const mla_dims* dims, int32_t act_dtype, const void* hq, 
   if (act_dtype == MLA_BF16 && cache->dtype == MLA_F32) return MLA_ERR_DTYPE;
   if (!(softmax_scale == softmax_scale)) return MLA_ERR_DIMS;
   if (batch == 0) return MLA_OK;
-  if (!hq || !W_UQ || !W_UK || !seqlens || !ws) return MLA_ERR_NULL;
-  if (!aligned16(hq) || !aligned16(W_UQ) || !aligned16(W_UK) || !aligned16(seqlens) || !aligned16(ws) ||
-      (W_DQ && !aligned16(W_DQ)))
-    return MLA_ERR_ALIGN;
+  if (!seqlens || !ws) return MLA_ERR_NULL;
+  if (!aligned16(seqlens) || !aligned16(ws)) return MLA_ERR_ALIGN;
+  if (parts & 1) {  // the attention alone reads only the workspace's queries, the cache and seqlens
+    if (!hq || !W_UQ || !W_UK) return MLA_ERR_NULL;
+    if (!aligned16(hq) || !aligned16(W_UQ) || !aligned16(W_UK) || (W_DQ && !aligned16(W_DQ))) return MLA_ERR_ALIGN;
+  }
   DecodeArgs a;
   a.d = *dims; a.act = act_dtype; a.cache_dtype = cache->dtype; a.hq = hq; a.batch = batch; a.s_q = s_q;
   a.W_DQ = W_DQ; a.W_UQ = W_UQ; a.W_UK = W_UK; a.pages = (const uint8_t*)cache->pages;
@@ -261,6 +263,98 @@ int mla_combine(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t 
   if (!force_generic() && fast_decode_supported(*dims, act_dtype, MLA_BF16, s_q)) e = fast_combine(a);
   else e = generic_combine(a);
   return hip_status(e);
+}
+
+size_t mla_decode_fp8w_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t num_splits) {
+  if (check_dims(dims) || batch <= 0 || s_q <= 0 || s_q > MAX_S_Q || num_splits <= 0 || num_splits > MAX_SPLITS ||
+      !fp8w_supported(*dims))
+    return 0;
+  const WsLayout L = ws_layout(*dims, MLA_BF16, batch, s_q, num_splits);
+  return fp8w_scratch_offset(L) + fp8w_scratch_bytes(*dims, batch * s_q);
+}
+
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+
+static int fp8w_decode_impl(const mla_dims* dims, const void* hq, int32_t batch, int32_t s_q, const void* W_DQ_codes,
+                            const float* W_DQ_scales, const void* W_UQ_codes, const float* W_UQ_scales,
+                            const void* W_UKT_codes, const float* W_UKT_scales, const mla_cache* cache,
+                            const int32_t* block_table, int32_t max_pages, const int32_t* seqlens,
+                            float softmax_scale, int32_t num_splits, void* ws, size_t ws_bytes, void* stream,
+                            int parts) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (batch < 0 || s_q < 1 || s_q > MAX_S_Q || num_splits < 0 || num_splits > MAX_SPLITS) return MLA_ERR_DIMS;
+  if ((st = check_cache(dims, cache, block_table, max_pages))) return st;
+  if (cache->dtype == MLA_F32) return MLA_ERR_DTYPE;
+  if (!(softmax_scale == softmax_scale)) return MLA_ERR_DIMS;
+  if (force_generic() || !fp8w_supported(*dims) || !fast_decode_supported(*dims, MLA_BF16, cache->dtype, s_q))
+    return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!seqlens || !ws) return MLA_ERR_NULL;
+  if (!aligned16(seqlens) || !aligned16(ws)) return MLA_ERR_ALIGN;
+  if (parts & 1) {
+    if (!hq || !W_DQ_codes || !W_DQ_scales || !W_UQ_codes || !W_UQ_scales || !W_UKT_codes || !W_UKT_scales)
+      return MLA_ERR_NULL;
+    if (!aligned16(hq) || !aligned16(W_DQ_codes) || !aligned16(W_UQ_codes) || !aligned16(W_UKT_codes) ||
+        !aligned4(W_DQ_scales) || !aligned4(W_UQ_scales) || !aligned4(W_UKT_scales))
+      return MLA_ERR_ALIGN;
+  }
+  DecodeArgs a;
+  a.d = *dims; a.act = MLA_BF16; a.cache_dtype = cache->dtype; a.hq = hq; a.batch = batch; a.s_q = s_q;
+  a.W_DQ = nullptr; a.W_UQ = nullptr; a.W_UK = nullptr; a.pages = (const uint8_t*)cache->pages;
+  a.g = make_geom(*dims, cache->dtype); a.block_table = block_table; a.max_pages = max_pages; a.seqlens = seqlens;
+  a.scale = softmax_scale;
+  resolve_splits(dims, batch, s_q, max_pages, num_splits, &a.S, &a.pages_per_split);
+  a.L = ws_layout(*dims, MLA_BF16, batch, s_q, a.S);
+  if (ws_bytes < fp8w_scratch_offset(a.L) + fp8w_scratch_bytes(*dims, batch * s_q)) return MLA_ERR_WORKSPACE;
+  a.ws = (uint8_t*)ws; a.stream = (hipStream_t)stream;
+  const Fp8Weights w{(const uint8_t*)W_DQ_codes, (const uint8_t*)W_UQ_codes, (const uint8_t*)W_UKT_codes,
+                     W_DQ_scales, W_UQ_scales, W_UKT_scales};
+  hipError_t e = hipSuccess;
+  if (parts & 1) e = fp8w_query(a, w);
+  if (e == hipSuccess && (parts & 2)) e = fast_attention(a);
+  return hip_status(e);
+}
+
+int mla_decode_fp8w(const mla_dims* dims, const void* hq, int32_t batch, int32_t s_q, const void* W_DQ_codes,
+                    const float* W_DQ_scales, const void* W_UQ_codes, const float* W_UQ_scales,
+                    const void* W_UKT_codes, const float* W_UKT_scales, const mla_cache* cache,
+                    const int32_t* block_table, int32_t max_pages, const int32_t* seqlens, float softmax_scale,
+                    int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+  return fp8w_decode_impl(dims, hq, batch, s_q, W_DQ_codes, W_DQ_scales, W_UQ_codes, W_UQ_scales, W_UKT_codes,
+                          W_UKT_scales, cache, block_table, max_pages, seqlens, softmax_scale, num_splits, ws,
+                          ws_bytes, stream, 3);
+}
+
+int mla_decode_fp8w_query(const mla_dims* dims, const void* hq, int32_t batch, int32_t s_q, const void* W_DQ_codes,
+                          const float* W_DQ_scales, const void* W_UQ_codes, const float* W_UQ_scales,
+                          const void* W_UKT_codes, const float* W_UKT_scales, const mla_cache* cache,
+                          const int32_t* block_table, int32_t max_pages, const int32_t* seqlens,
+                          float softmax_scale, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+  return fp8w_decode_impl(dims, hq, batch, s_q, W_DQ_codes, W_DQ_scales, W_UQ_codes, W_UQ_scales, W_UKT_codes,
+                          W_UKT_scales, cache, block_table, max_pages, seqlens, softmax_scale, num_splits, ws,
+                          ws_bytes, stream, 1);
+}
+
+int mla_combine_fp8w(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t num_splits, void* ws,
+                     size_t ws_bytes, const void* W_UV_codes, const float* W_UV_scales, void* out, float* lse_out,
+                     void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (batch < 0 || s_q < 1 || s_q > MAX_S_Q || num_splits < 1 || num_splits > MAX_SPLITS) return MLA_ERR_DIMS;
+  if (force_generic() || !fp8w_supported(*dims) || !fast_decode_supported(*dims, MLA_BF16, MLA_BF16, s_q))
+    return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!ws || !W_UV_codes || !W_UV_scales || !out) return MLA_ERR_NULL;
+  if (!aligned16(ws) || !aligned16(W_UV_codes) || !aligned4(W_UV_scales) || !aligned16(out) ||
+      (lse_out && !aligned16(lse_out)))
+    return MLA_ERR_ALIGN;
+  const WsLayout L = ws_layout(*dims, MLA_BF16, batch, s_q, num_splits);
+  if (ws_bytes < L.total) return MLA_ERR_WORKSPACE;
+  CombineArgs a;
+  a.d = *dims; a.act = MLA_BF16; a.batch = batch; a.s_q = s_q; a.S = num_splits; a.ws = (uint8_t*)ws;
+  a.W_UV = nullptr; a.out = out; a.lse_out = lse_out; a.stream = (hipStream_t)stream; a.L = L;
+  return hip_status(fp8w_combine(a, (const uint8_t*)W_UV_codes, W_UV_scales));
 }
 
 int mla_decode_step_noalloc(const mla_dims* dims, int32_t act_dtype, const void* hq, int32_t batch, int32_t s_q,
@@ -392,6 +486,16 @@ int mla_fp8_quantize_weight(const void* W, int32_t N, int32_t K, void* codes, fl
   if (!W || !codes || !scales) return MLA_ERR_NULL;
   if (!aligned16(W) || !aligned16(codes) || ((uintptr_t)scales & 3)) return MLA_ERR_ALIGN;
   return hip_status(fp8_quantize_weight(N, K, (const bf16_t*)W, (uint8_t*)codes, scales, (hipStream_t)stream));
+}
+
+int mla_fp8_quantize_weight_t(const void* W, int32_t batch, int32_t R, int32_t C, void* codes, float* scales,
+                              void* stream) {
+  if (batch < 1 || R < 1 || C < 1 || R > MAX_FP8_DIM || C > MAX_FP8_DIM || batch > MAX_FP8_DIM) return MLA_ERR_DIMS;
+  if (R % 128 || C % 128) return MLA_ERR_UNSUPPORTED;
+  if (!W || !codes || !scales) return MLA_ERR_NULL;
+  if (!aligned16(W) || !aligned16(codes) || ((uintptr_t)scales & 3)) return MLA_ERR_ALIGN;
+  return hip_status(
+      fp8_quantize_weight_t(batch, R, C, (const bf16_t*)W, (uint8_t*)codes, scales, (hipStream_t)stream));
 }
 
 size_t mla_fp8_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {

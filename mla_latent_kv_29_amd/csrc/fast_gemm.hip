@@ -814,13 +814,20 @@ hipError_t out_project(const OutProjArgs& a) {
                 (const float*)part, (bf16_t*)a.y);
 }
 
+// O_lat (bf16, the combine's own region: the queries stay intact) and the
+// rows' lse from the split partials.
+hipError_t merge_partials(const CombineArgs& a) {
+  const int R = a.batch * a.s_q, H = a.d.n_heads;
+  return launch(&k_merge, dim3((R * H + 3) / 4), dim3(256), 0, a.stream, a.batch, H, a.s_q, a.S, a.d.d_c,
+                (const uint8_t*)a.ws, a.L.lpart, (bf16_t*)(a.ws + a.L.olat), a.lse_out);
+}
+
 hipError_t fast_combine(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
   if (merge_uv_supported(d, R)) return merge_uv(a);
-  bf16_t* olat = (bf16_t*)(a.ws + a.L.olat);  // the combine's own region: the queries stay intact
-  MLA_TRY(launch(&k_merge, dim3((R * H + 3) / 4), dim3(256), 0, a.stream, a.batch, H, a.s_q, a.S, d.d_c,
-                 (const uint8_t*)a.ws, a.L.lpart, olat, a.lse_out));
+  MLA_TRY(merge_partials(a));
+  const bf16_t* olat = (const bf16_t*)(a.ws + a.L.olat);
   hipError_t e;
   GemmArgs g = gemm_args(R, d.d_head, d.d_c, olat, (long)H * d.d_c, d.d_c, (const bf16_t*)a.W_UV, d.d_c,
                          (long)d.d_head * d.d_c, 1);

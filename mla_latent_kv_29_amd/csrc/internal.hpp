@@ -209,6 +209,22 @@ F8Plan fp8_plan(int M, int N, int K);
 hipError_t fp8_quantize_weight(int N, int K, const bf16_t* W, uint8_t* codes, float* scales, hipStream_t st);
 hipError_t fp8_gemm(int M, int N, int K, const bf16_t* X, const uint8_t* Wc, const float* Ws, bf16_t* Y, uint8_t* ws,
                     hipStream_t st);
+// Decode with FP8 block-scaled projection weights: the step's query phase
+// and combine on E4M3 weights (the attention is the bf16 step's).  W^UK is
+// given per head transposed, [H][d_c][d_head], so that every projection is
+// Y = X . W^T with W stored [out][in].
+struct Fp8Weights {
+  const uint8_t *dq_c, *uq_c, *ukt_c;
+  const float *dq_s, *uq_s, *ukt_s;
+};
+bool fp8w_supported(const mla_dims& d);
+hipError_t fp8_quantize_weight_t(int batch, int R, int C, const bf16_t* W, uint8_t* codes, float* scales,
+                                 hipStream_t st);
+size_t fp8w_scratch_offset(const WsLayout& L);
+size_t fp8w_scratch_bytes(const mla_dims& d, int R);
+hipError_t fp8w_query(const DecodeArgs& a, const Fp8Weights& w);
+hipError_t fp8w_combine(const CombineArgs& a, const uint8_t* uv_c, const float* uv_s);
+hipError_t merge_partials(const CombineArgs& a);  // split partials -> O_lat (ws olat) and lse
 bool skinny_out_supported(int rows, int N, int K);
 hipError_t skinny_out(const OutProjArgs& a, int kgroups);  // rows <= 64: k-groups + their sum
 hipError_t generic_out_project(const OutProjArgs& a);

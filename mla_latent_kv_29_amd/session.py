@@ -92,6 +92,45 @@ class DecodeSession:
                       self.out, self.lse, stream)
         return self.out, self.lse
 
+    # ---------------------------------------------------------------- FP8 projection weights
+    def quantize_fp8w(self, W, stream=None):
+        """E4M3 codes and 128 x 128-block scales of W^DQ, W^UQ, W^UK (transposed
+        per head, the layout mla_decode_fp8w takes) and W^UV, made by the
+        library: {name: (codes, scales)}."""
+        d = self.dims
+        H, dh, dr, dc = d["n_heads"], d["d_head"], d["d_rope"], d["d_c"]
+
+        def q(w, N, K):
+            codes = torch.empty((N, K), dtype=torch.uint8, device=self.device)
+            scales = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=self.device)
+            L.mla_fp8_quantize_weight(w, N, K, codes, scales, stream)
+            return codes, scales
+
+        ukt = (torch.empty((H * dc, dh), dtype=torch.uint8, device=self.device),
+               torch.empty((H * dc // 128, dh // 128), dtype=torch.float32, device=self.device))
+        L.mla_fp8_quantize_weight_t(W["W_UK"], H, dh, dc, ukt[0], ukt[1], stream)
+        return {"W_DQ": q(W["W_DQ"], d["d_cq"], d["d_model"]), "W_UQ": q(W["W_UQ"], H * (dh + dr), d["d_cq"]),
+                "W_UKT": ukt, "W_UV": q(W["W_UV"], H * dh, dc)}
+
+    def fp8w_workspace(self):
+        """Grow the workspace to what mla_decode_fp8w needs for the current split plan."""
+        need = L.mla_decode_fp8w_workspace_bytes(self.cdims, self.batch, self.s_q, self.num_splits)
+        if need == 0:
+            raise ValueError("the FP8-weight decode does not support these dims")
+        if self.ws_bytes < need:
+            self.ws_bytes = need
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def decode_fp8w(self, hq, Wq, softmax_scale, stream=None):
+        """The decode step on FP8 weights (Wq from quantize_fp8w): mla_decode_fp8w + mla_combine_fp8w."""
+        self.fp8w_workspace()
+        L.mla_decode_fp8w(self.cdims, hq, self.batch, self.s_q, Wq["W_DQ"], Wq["W_UQ"], Wq["W_UKT"], self.cache,
+                          self.block_table, self.max_pages, self.seqlens, softmax_scale, self.num_splits, self.ws,
+                          self.ws_bytes, stream)
+        L.mla_combine_fp8w(self.cdims, self.batch, self.s_q, self.num_splits, self.ws, self.ws_bytes, Wq["W_UV"],
+                           self.out, self.lse, stream)
+        return self.out, self.lse
+
     # ---------------------------------------------------------------- inspection
     def page_view(self):
         """Raw pages as uint8 [num_pages, page_bytes] (for layout tests)."""

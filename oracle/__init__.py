@@ -26,6 +26,7 @@ from .mla import (rope, kv_latents, queries, attend_nonabsorbed, attend_absorbed
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_values, e5m2_decode,
                   quantize_tiles, dequantize_tiles, quantize_blocks, dequantize_blocks,
                   gemm_block_scaled)
+from .fp8w import decode_absorbed_exact, decode_fp8w_from_latents, bf16_round
 from .sizes import (cache_values_per_token, mha_values_per_token, cache_bytes,
                     mla_params_per_layer)
 from .mtp import tokens_per_step
@@ -35,6 +36,7 @@ __all__ = [
     "decode_from_latents", "decode_from_h", "softmax_lse", "output_projection",
     "e4m3_decode", "e4m3_encode", "e4m3_values", "e5m2_decode",
     "quantize_tiles", "dequantize_tiles", "quantize_blocks", "dequantize_blocks", "gemm_block_scaled",
+    "decode_absorbed_exact", "decode_fp8w_from_latents", "bf16_round",
     "cache_values_per_token", "mha_values_per_token", "cache_bytes",
     "mla_params_per_layer", "tokens_per_step",
 ]

@@ -324,3 +324,77 @@ def test_hbm_read_probe_argument_errors():
     assert L.mla_hbm_read_probe(None, 64, FAKE, stream=0, check=False) == L.MLA_ERR_NULL
     assert L.mla_hbm_read_probe(FAKE, 65, FAKE, stream=0, check=False) == L.MLA_ERR_DIMS
     assert L.mla_hbm_read_probe(FAKE + 8, 64, FAKE, stream=0, check=False) == L.MLA_ERR_ALIGN
+
+
+def test_attend_alone_needs_no_query_inputs():
+    """mla_decode_attend reads only the queries already in the workspace: NULL
+    hq and weights pass its checks (here it stops at the workspace size),
+    while mla_decode and mla_decode_query still require them."""
+    d = _dims()
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 10)
+    for fn, expect in ((L.mla_decode_attend, L.MLA_ERR_WORKSPACE), (L.mla_decode_query, L.MLA_ERR_NULL),
+                       (L.mla_decode, L.MLA_ERR_NULL)):
+        assert fn(d, m.MLA_BF16, None, 2, 1, None, None, None, cache, FAKE, 4, FAKE, 0.1, 1, FAKE, 1000, stream=0,
+                  check=False) == expect
+
+
+def test_fp8w_workspace_and_argument_errors():
+    """The FP8-weight decode: its workspace is the bf16 step's plus the FP8
+    GEMMs' scratch; shapes off the MFMA path, missing or misaligned codes and
+    scales, an f32 cache and a short workspace are refused on the host."""
+    d = _dims()
+    t = m.make_dims(inputs.TINY_DIMS)
+    S = m.mla_decode_splits(d, 2, 1, 64, 0)
+    wb = m.mla_workspace_bytes(d, m.MLA_BF16, 2, 1, S)
+    w8 = m.mla_decode_fp8w_workspace_bytes(d, 2, 1, S)
+    # the W^DQ GEMM's scratch: 2 rows of activation codes and scales, 7 k-groups of fp32 partials
+    assert w8 >= wb + 2 * 7168 + 7 * 2 * 1536 * 4
+    assert w8 == (wb + 255) // 256 * 256 + m.mla_fp8_gemm_workspace_bytes(2, 1536, 7168)
+    assert m.mla_decode_fp8w_workspace_bytes(t, 2, 1, 1) == 0
+    assert m.mla_decode_fp8w_workspace_bytes(d, 2, 9, 1) == 0
+    assert m.mla_decode_fp8w_workspace_bytes(d, 2, 1, 0) == 0
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 100)
+    pair = (FAKE, FAKE)
+
+    def call(fn=L.mla_decode_fp8w, **o):
+        a = dict(dims=d, hq=FAKE, batch=2, s_q=1, dq=pair, uq=pair, ukt=pair, c=cache, mp=64, ns=0, ws=FAKE,
+                 wsb=1 << 34)
+        a.update(o)
+        return fn(a["dims"], a["hq"], a["batch"], a["s_q"], a["dq"], a["uq"], a["ukt"], a["c"], FAKE, a["mp"], FAKE,
+                  0.1, a["ns"], a["ws"], a["wsb"], stream=0, check=False)
+
+    assert call(dims=t) == L.MLA_ERR_UNSUPPORTED
+    assert call(batch=0) == L.MLA_OK
+    assert call(s_q=9) == L.MLA_ERR_DIMS
+    assert call(hq=None) == L.MLA_ERR_NULL
+    assert call(fn=L.mla_decode_fp8w_query, dq=(FAKE, None)) == L.MLA_ERR_NULL
+    assert call(ukt=(FAKE + 4, FAKE)) == L.MLA_ERR_ALIGN
+    assert call(uq=(FAKE, FAKE + 2)) == L.MLA_ERR_ALIGN
+    assert call(c=L.cache_struct(FAKE, m.MLA_F32, 100)) == L.MLA_ERR_DTYPE
+    assert call(wsb=wb) == L.MLA_ERR_WORKSPACE
+    assert call(wsb=w8 - 1) == L.MLA_ERR_WORKSPACE
+
+    def comb(**o):
+        a = dict(dims=d, batch=2, s_q=1, ns=S, ws=FAKE, wsb=wb, uv=pair, out=FAKE)
+        a.update(o)
+        return L.mla_combine_fp8w(a["dims"], a["batch"], a["s_q"], a["ns"], a["ws"], a["wsb"], a["uv"], a["out"],
+                                  None, stream=0, check=False)
+
+    assert comb(wsb=wb - 1) == L.MLA_ERR_WORKSPACE
+    assert comb(uv=(None, FAKE)) == L.MLA_ERR_NULL
+    assert comb(uv=(FAKE, FAKE + 1)) == L.MLA_ERR_ALIGN
+    assert comb(batch=0) == L.MLA_OK
+    assert comb(ns=0) == L.MLA_ERR_DIMS
+    assert comb(dims=t) == L.MLA_ERR_UNSUPPORTED
+
+    def quant_t(**o):
+        a = dict(w=FAKE, batch=128, R=128, C=512, c=FAKE, s=FAKE)
+        a.update(o)
+        return L.mla_fp8_quantize_weight_t(a["w"], a["batch"], a["R"], a["C"], a["c"], a["s"], stream=0,
+                                           check=False)
+
+    assert quant_t(batch=0) == L.MLA_ERR_DIMS
+    assert quant_t(R=100) == L.MLA_ERR_UNSUPPORTED
+    assert quant_t(C=640 + 64) == L.MLA_ERR_UNSUPPORTED
+    assert quant_t(c=None) == L.MLA_ERR_NULL
+    assert quant_t(w=FAKE + 8) == L.MLA_ERR_ALIGN

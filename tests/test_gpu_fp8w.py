@@ -1,0 +1,165 @@
+"""Parity of the decode step with FP8 block-scaled projection weights
+(mla_decode_fp8w + mla_combine_fp8w) with the float64 oracle.
+
+Two references on the same seeded inputs: the oracle's FP8-weight decode
+(oracle.decode_fp8w_from_latents: every projection the block-scaled GEMM of
+§3.3 items 2-3 on weights the oracle quantises itself), and the exact
+absorbed decode with the bf16 weights, which the device may miss by no more
+than the oracle's own FP8 error on the same inputs plus the bar below (the
+quantisation error is the method's, not the device's).  The weights' codes
+and scales come from the library and are checked bit for bit against the
+oracle's.
+
+The bar against the FP8-weight oracle is derived, not the bf16 one: the
+activation codes are decided from stored bf16 intermediates (c^Q, u, O_lat),
+and the device's differ from the oracle's by bf16 roundings (fp32 sums,
+bf16 split partials), which flip some codes by a whole E4M3 step.
+Perturbing the oracle's own stored intermediates by 2^-9 relative noise
+moves its output by up to 2.3% of the largest output (1.5% rms) at this
+shape, so the bar is 4e-2 of the largest output, and 2e-2 in rms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_29_amd import inputs
+from mla_latent_kv_29_amd.session import DecodeSession
+from gpu_common import DEV, tau_of, to_np, max_abs
+
+pytestmark = pytest.mark.gpu
+
+V3 = inputs.V3_DIMS
+TOL = 4e-2      # largest |device - FP8 oracle| / largest |oracle output|
+TOL_RMS = 2e-2  # rms(device - FP8 oracle) / rms(oracle output)
+HEADS = [0, 77, 127]
+
+
+def oracle_quantised(Wn):
+    return {k: oracle.quantize_blocks(Wn[k]) for k in ("W_DQ", "W_UQ", "W_UK", "W_UV")}
+
+
+def latents(dims, Wn, h):
+    """The sequence's c^KV and k^R as its bf16 cache holds them."""
+    c, kr = oracle.kv_latents(h, Wn["W_DKV"], Wn["W_KR"], np.arange(h.shape[0]), dims["rope_theta"])
+    return oracle.bf16_round(c), oracle.bf16_round(kr)
+
+
+def compare(out, lse, b, s_q, c, kr, hqb, Wn, Wq, dims, Lb, tau, heads):
+    """Device rows of sequence b against both references."""
+    o_q, l_q = oracle.decode_fp8w_from_latents(c, kr, hqb, Wq, dims, Lb, s_q, tau, heads)
+    o_e, l_e = oracle.decode_absorbed_exact(c, kr, hqb, Wn, dims, Lb, s_q, tau, heads)
+    got = out[b][:, heads]
+    gl = lse[b][:, heads]
+    ref = max(float(np.max(np.abs(o_q))), 1e-30)
+    if Lb == 0:
+        assert np.all(got == 0) and np.all(np.isneginf(gl)), b
+        return
+    err_q = max_abs(got, o_q)
+    assert err_q <= TOL * ref, (b, err_q / ref)
+    rms = float(np.sqrt(np.mean((got - o_q) ** 2)) / np.sqrt(np.mean(o_q ** 2)))
+    assert rms <= TOL_RMS, (b, rms)
+    assert max_abs(gl, l_q) <= TOL * max(1.0, float(np.max(np.abs(l_q)))), b
+    # the device is no further from the exact decode than the method itself, plus the bar
+    method = max_abs(o_q, o_e)
+    assert max_abs(got, o_e) <= method + TOL * ref, (b, max_abs(got, o_e) / ref, method / ref)
+
+
+def test_quantised_weights_match_the_oracle_bit_for_bit():
+    """Codes and scales of W^DQ, W^UQ, W^UV (mla_fp8_quantize_weight) and of
+    W^UK transposed per head (mla_fp8_quantize_weight_t) equal the oracle's
+    block quantisation of the same bf16 values."""
+    W = inputs.weights(V3, 0.006, torch.bfloat16, DEV, 0, 11)
+    sess = DecodeSession(V3, "bf16", "bf16", np.array([64]), np.zeros((1, 1), np.int32), 1, 1, 0, DEV)
+    Wq = sess.quantize_fp8w(W)
+    torch.cuda.synchronize()
+    H, dh, dc = V3["n_heads"], V3["d_head"], V3["d_c"]
+    for name, src in (("W_DQ", "W_DQ"), ("W_UQ", "W_UQ"), ("W_UV", "W_UV")):
+        rc, rs = oracle.quantize_blocks(to_np(W[src]))
+        np.testing.assert_array_equal(Wq[name][0].cpu().numpy(), rc, err_msg=name)
+        np.testing.assert_array_equal(Wq[name][1].cpu().numpy(), rs, err_msg=name)
+    ukt = to_np(W["W_UK"]).reshape(H, dh, dc).transpose(0, 2, 1).reshape(H * dc, dh)
+    rc, rs = oracle.quantize_blocks(ukt)
+    np.testing.assert_array_equal(Wq["W_UKT"][0].cpu().numpy(), rc)
+    np.testing.assert_array_equal(Wq["W_UKT"][1].cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("lengths,s_q,splits", [([300, 65, 1, 129], 1, 0), ([200, 0, 50], 2, 3), ([640], 4, 2)])
+def test_fp8w_decode_ragged_batches(lengths, s_q, splits):
+    """Ragged sequences (one token, a page plus one, an empty sequence) at
+    1, 2 and 4 query rows, default and forced split counts; every head of
+    the first sequence, three heads of the others."""
+    dims = V3
+    lengths = np.asarray(lengths, dtype=np.int64)
+    W = inputs.weights(dims, 0.006, torch.bfloat16, DEV, 3, 11)
+    bt, pool = inputs.block_table(lengths, dims["page_size"], "shuffled", 3, 11)
+    sess = DecodeSession(dims, "bf16", "bf16", lengths, bt, pool, s_q, splits, DEV)
+    gen_h = lambda b, t0, t1: inputs.hidden(dims, b, t0, t1, torch.bfloat16, DEV, 3, 11)
+    sess.build_from_h(gen_h, W)
+    rows = [gen_h(b, int(L) - s_q, int(L)) if L >= s_q else
+            torch.zeros((s_q, dims["d_model"]), dtype=torch.bfloat16, device=DEV) for b, L in enumerate(lengths)]
+    hq = torch.cat(rows, 0).contiguous()
+    tau = tau_of(dims)
+    Wq_dev = sess.quantize_fp8w(W)
+    out, lse = sess.decode_fp8w(hq, Wq_dev, tau)
+    torch.cuda.synchronize()
+    out, lse = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(out))
+    Wn = {k: to_np(v) for k, v in W.items()}
+    Wq = oracle_quantised(Wn)
+    for b, Lb in enumerate(lengths):
+        Lb = int(Lb)
+        h = to_np(gen_h(b, 0, Lb)) if Lb else np.zeros((0, dims["d_model"]))
+        c, kr = latents(dims, Wn, h)
+        hqb = to_np(hq[b * s_q:(b + 1) * s_q])
+        heads = list(range(dims["n_heads"])) if b == 0 else HEADS
+        compare(out, lse, b, s_q, c, kr, hqb, Wn, Wq, dims, Lb, tau, heads)
+
+
+def test_fp8w_benchmark_workload_sampled_sequences():
+    """The benchmarked v3_fp8w_b64_l4096 step at full size (its seeds, lengths,
+    block table and default split plan): sequences 0, 21, 42 and 63, three
+    heads each, against both references."""
+    spec = inputs.WORKLOADS["v3_fp8w_b64_l4096"]
+    dims, wl = spec["dims"], spec["index"]
+    lengths = inputs.seqlens(spec["lengths"], spec["batch"], 0, wl)
+    table, pool = inputs.block_table(lengths, dims["page_size"], spec["table"], 0, wl)
+    W = inputs.weights(dims, spec["sigma"], torch.bfloat16, DEV, 0, wl)
+    sess = DecodeSession(dims, "bf16", "bf16", lengths, table, pool, 1, 0, DEV)
+    gen_h = lambda b, t0, t1: inputs.hidden(dims, b, t0, t1, torch.bfloat16, DEV, 0, wl)
+    sess.build_from_h(gen_h, W, chunk=32768)
+    hq = torch.cat([gen_h(b, int(L) - 1, int(L)) for b, L in enumerate(lengths)], 0).contiguous()
+    tau = tau_of(dims)
+    Wq_dev = sess.quantize_fp8w(W)
+    out, lse = sess.decode_fp8w(hq, Wq_dev, tau)
+    torch.cuda.synchronize()
+    out, lse = to_np(out), to_np(lse)
+    Wn = {k: to_np(v) for k, v in W.items()}
+    Wq = oracle_quantised(Wn)
+    for b in (0, 21, 42, 63):
+        Lb = int(lengths[b])
+        c, kr = latents(dims, Wn, to_np(gen_h(b, 0, Lb)))
+        compare(out, lse, b, 1, c, kr, to_np(hq[b:b + 1]), Wn, Wq, dims, Lb, tau, HEADS)
+
+
+def test_fp8w_step_is_deterministic_and_leaves_the_bf16_step_intact():
+    """Two FP8-weight steps give identical bytes; the bf16 step on the same
+    session afterwards equals a bf16 step run before them."""
+    dims = V3
+    lengths = np.array([260, 70], dtype=np.int64)
+    W = inputs.weights(dims, 0.006, torch.bfloat16, DEV, 5, 11)
+    bt, pool = inputs.block_table(lengths, dims["page_size"], "inorder", 5, 11)
+    sess = DecodeSession(dims, "bf16", "bf16", lengths, bt, pool, 1, 0, DEV)
+    gen_h = lambda b, t0, t1: inputs.hidden(dims, b, t0, t1, torch.bfloat16, DEV, 5, 11)
+    sess.build_from_h(gen_h, W)
+    hq = torch.cat([gen_h(b, int(L) - 1, int(L)) for b, L in enumerate(lengths)], 0).contiguous()
+    tau = tau_of(dims)
+    o_bf, l_bf = (t.clone() for t in sess.decode(hq, W, tau))
+    Wq = sess.quantize_fp8w(W)
+    o1, l1 = (t.clone() for t in sess.decode_fp8w(hq, Wq, tau))
+    o2, l2 = (t.clone() for t in sess.decode_fp8w(hq, Wq, tau))
+    o3, l3 = (t.clone() for t in sess.decode(hq, W, tau))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o_bf) and torch.equal(l3, l_bf)
+    assert not torch.equal(o1, o_bf)

@@ -496,3 +496,103 @@ def test_block_scaled_gemm_by_promoted_partial_sums():
     exact = x @ w.T
     bound = (np.abs(x) @ np.abs(w).T) * (2 * 2.0 ** -4 + 2.0 ** -8) + 1e-6
     assert np.all(np.abs(y - exact) <= bound)
+
+
+# ---------------------------------------------------------------- decode with FP8 projection weights
+
+FP8W_DIMS = dict(d_model=256, n_heads=2, d_head=128, d_rope=64, d_c=256, d_cq=128, page_size=64, rope_theta=10000.0)
+
+
+def _fp8w_case(rng, T):
+    d = FP8W_DIMS
+    H, dh, dr, dc, dq, dm = d["n_heads"], d["d_head"], d["d_rope"], d["d_c"], d["d_cq"], d["d_model"]
+    W = {"W_DQ": rng.normal(0, 0.06, (dq, dm)), "W_UQ": rng.normal(0, 0.09, (H * (dh + dr), dq)),
+         "W_UK": rng.normal(0, 0.06, (H * dh, dc)), "W_UV": rng.normal(0, 0.06, (H * dh, dc)),
+         "W_DKV": rng.normal(0, 0.06, (dc, dm)), "W_KR": rng.normal(0, 0.06, (dr, dm))}
+    h = rng.normal(0, 1.0, (T, dm))
+    c, kr = oracle.kv_latents(h, W["W_DKV"], W["W_KR"], np.arange(T), d["rope_theta"])
+    return d, W, h, c, kr
+
+
+@pytest.mark.parametrize("T,s_q", [(40, 1), (40, 3), (3, 3)])
+def test_fp8w_steps_with_exact_projections_equal_nonabsorbed_decode(T, s_q):
+    """The absorbed step sequence of the FP8-weight decode, with exact
+    projections, is the non-absorbed decode of §2.1.1 (keys and values built
+    per head): every head slice, transpose, RoPE position and scale of its
+    plumbing.  T = 3, s_q = 3: the first query row sees one token."""
+    d, W, h, c, kr = _fp8w_case(np.random.default_rng(20 + T + s_q), T)
+    tau = 1.0 / np.sqrt(d["d_head"] + d["d_rope"])
+    hq = h[T - s_q:T]
+    o_ref, l_ref = oracle.decode_from_latents(c, kr, hq, W["W_DQ"], W["W_UQ"], W["W_UK"], W["W_UV"], d, T, s_q, tau)
+    o, lse = oracle.decode_absorbed_exact(c, kr, hq, W, d, T, s_q, tau)
+    assert np.max(np.abs(o - o_ref)) <= 1e-10 * max(1.0, np.max(np.abs(o_ref)))
+    fin = np.isfinite(l_ref)
+    np.testing.assert_array_equal(np.isfinite(lse), fin)
+    assert np.all(np.abs(lse[fin] - l_ref[fin]) <= 1e-10)
+
+
+def test_fp8w_quantised_steps_stay_within_the_fp8_error():
+    """With every projection the block-scaled FP8 GEMM (§3.3 items 2-3), the
+    output differs from the exact step sequence (the quantisation is applied)
+    by no more than the error of four chained E4M3 GEMMs: each rounds a
+    typical operand by 2-4% (3 mantissa bits; a Gaussian block's amax maps to
+    448, its typical values to about 100, where the step is 8), and these
+    inputs measure 5.8% of the largest output (4-10% over other seeds)."""
+    d, W, h, c, kr = _fp8w_case(np.random.default_rng(31), 48)
+    tau = 1.0 / np.sqrt(d["d_head"] + d["d_rope"])
+    s_q = 2
+    hq = h[48 - s_q:48]
+    Wq = {k: oracle.quantize_blocks(W[k]) for k in ("W_DQ", "W_UQ", "W_UK", "W_UV")}
+    o_q, l_q = oracle.decode_fp8w_from_latents(c, kr, hq, Wq, d, 48, s_q, tau)
+    o_e, l_e = oracle.decode_absorbed_exact(c, kr, hq, W, d, 48, s_q, tau)
+    err = np.max(np.abs(o_q - o_e)) / np.max(np.abs(o_e))
+    assert 1e-3 < err < 0.1, err
+    assert np.max(np.abs(l_q - l_e)) < 5e-2
+
+
+def test_fp8w_uses_each_heads_own_weight_blocks():
+    """Scaling head 1's W^UK and W^UV blocks by powers of two (which the
+    block quantisation absorbs into the scales exactly) changes only head 1:
+    its scores scale by the W^UK factor and its output by the W^UV factor,
+    head 0 stays bit-identical.  A wrong head slice or scale row fails."""
+    d, W, h, c, kr = _fp8w_case(np.random.default_rng(32), 24)
+    tau = 1.0 / np.sqrt(d["d_head"] + d["d_rope"])
+    hq = h[23:24]
+    dh = d["d_head"]
+    Wq = {k: oracle.quantize_blocks(W[k]) for k in ("W_DQ", "W_UQ", "W_UK", "W_UV")}
+    o1, l1 = oracle.decode_fp8w_from_latents(c, kr, hq, Wq, d, 24, 1, tau)
+    W2 = dict(W)
+    W2["W_UK"] = W["W_UK"].copy()
+    W2["W_UV"] = W["W_UV"].copy()
+    W2["W_UV"][dh:2 * dh] *= 8.0
+    Wq2 = dict(Wq)
+    Wq2["W_UV"] = oracle.quantize_blocks(W2["W_UV"])
+    o2, l2 = oracle.decode_fp8w_from_latents(c, kr, hq, Wq2, d, 24, 1, tau)
+    np.testing.assert_array_equal(o2[:, 0], o1[:, 0])
+    np.testing.assert_array_equal(l2, l1)
+    assert np.max(np.abs(o2[:, 1] - 8.0 * o1[:, 1])) <= 1e-12 * np.max(np.abs(o1[:, 1])) * 8
+    # W^UK of head 1 doubled: the content scores of head 1 double, head 0 is unchanged
+    W2["W_UK"][dh:2 * dh] *= 2.0
+    Wq3 = dict(Wq)
+    Wq3["W_UK"] = oracle.quantize_blocks(W2["W_UK"])
+    o3, l3 = oracle.decode_fp8w_from_latents(c, kr, hq, Wq3, d, 24, 1, tau)
+    np.testing.assert_array_equal(o3[:, 0], o1[:, 0])
+    assert np.max(np.abs(o3[:, 1] - o1[:, 1])) > 1e-6
+
+
+def test_bf16_round_ties_and_independent_conversion():
+    """Round to nearest bf16, ties to an even mantissa: 1 + 2^-8 lies halfway
+    between 1 and 1 + 2^-7 and goes to 1; 1 + 3 2^-8 lies halfway between
+    1 + 2^-7 (odd) and 1 + 2^-6 (even) and goes up; anything above a tie
+    rounds up; the sign is kept; and on random values it agrees with torch's
+    own float32 -> bfloat16 conversion."""
+    import torch
+    r = oracle.bf16_round
+    assert r(1.0 + 2.0 ** -8) == 1.0
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert r(-(1.0 + 3 * 2.0 ** -8)) == -(1.0 + 2.0 ** -6)
+    assert r(0.0) == 0.0 and r(2.0 ** -130) == r(2.0 ** -130)
+    x = np.random.default_rng(7).normal(0, 3.0, 10000)
+    t = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(r(x), t)
