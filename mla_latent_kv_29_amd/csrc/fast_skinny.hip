@@ -641,6 +641,35 @@ struct EpiRowsBf16 {
   }
 };
 
+// u = Q(c^Q) . Q(W^UQ)^T of the FP8-weight decode with its RoPE epilogue:
+// the content part q^C_i goes to qc [R][H][d_head] (bf16), the RoPE pairs
+// (adjacent columns 2p, 2p + 1 of the head's d_rope) are rotated at the
+// row's position, scaled by tau log2 e and written to the tail of qt.
+struct EpiUQF8 {
+  bf16_t* qc;
+  bf16_t* qt;
+  const int32_t* seqlens;
+  int H, d_head, d_rope, d_c, s_q, m0;  // m0: first row of this 64-row chunk
+  float scale2;
+  double freq[32];  // theta^(-2p/d_rope) of RoPE pair p
+  __device__ void operator()(int, int, int m, int n, float v0, float v1) const {
+    const int w = d_head + d_rope, i = n / w, d = n % w;
+    const int rr = m0 + m;
+    if (d < d_head) {
+      bf16x2 o = {(bf16_t)v0, (bf16_t)v1};
+      *(bf16x2*)(qc + ((long)rr * H + i) * d_head + d) = o;
+      return;
+    }
+    const int b = rr / s_q, j = rr % s_q;
+    int pos = seqlens[b] - s_q + j;
+    pos = pos < 0 ? 0 : pos;
+    float cs, sn;
+    rope_cs_w(pos, freq[(d - d_head) >> 1], &cs, &sn);
+    bf16x2 o = {(bf16_t)(scale2 * (v0 * cs - v1 * sn)), (bf16_t)(scale2 * (v0 * sn + v1 * cs))};
+    *(bf16x2*)(qt + ((long)rr * H + i) * (d_c + d_rope) + d_c + (d - d_head)) = o;
+  }
+};
+
 template <int KB, int NB, class Epi, int DEPTH = NB>
 hipError_t launch_f8(const F8Args& a, int n_groups, int k_groups, const Epi& epi, hipStream_t st) {
   constexpr int lds = SkPlan<4, NB>::LDS_BYTES;
@@ -767,6 +796,36 @@ hipError_t fp8_gemm(int M, int N, int K, const bf16_t* X, const uint8_t* Wc, con
     MLA_TRY(launch_f8_kb(a, p, N, EpiKPart{part, rows, N}, st));
     const int MN = rows * N;
     MLA_TRY(launch(&k_reduce_rows, dim3((MN / 4 + 255) / 256), dim3(256), 0, st, MN, p.kgroups, (const float*)part, y));
+  }
+  return hipSuccess;
+}
+
+// W^UQ of the FP8-weight decode (one k-group: K = d_cq = 1536 is three
+// k-blocks a wave): the activations quantised per 64-row chunk, then one
+// GEMM launch whose epilogue splits q^C from the rotated RoPE pairs.  Six
+// column blocks of 96 columns a block give 256 blocks at V3 (one per CU),
+// streamed three ahead.
+hipError_t fp8w_uq(const DecodeArgs& a, const uint8_t* Wc, const float* Ws, const bf16_t* cq, bf16_t* qc,
+                   uint8_t* ws) {
+  const mla_dims& d = a.d;
+  const int R = a.batch * a.s_q, H = d.n_heads, N = H * (d.d_head + d.d_rope), K = d.d_cq;
+  const F8Plan p = fp8_plan(R, N, K);
+  if (p.kgroups != 1 || d.d_rope / 2 > 32) return hipErrorInvalidValue;
+  EpiUQF8 epi{qc, (bf16_t*)(a.ws + a.L.qt), a.seqlens, H, d.d_head, d.d_rope, d.d_c, a.s_q, 0,
+              a.scale * 1.4426950408889634f, {}};
+  for (int m = 0; m < d.d_rope / 2; ++m) epi.freq[m] = pow((double)d.rope_theta, -2.0 * m / d.d_rope);
+  uint8_t* xc = ws + p.xc_off;
+  float* xs = (float*)(ws + p.xs_off);
+  for (int m0 = 0; m0 < R; m0 += 64) {
+    const int rows = std::min(64, R - m0);
+    const int tiles = rows * (K / 128);
+    MLA_TRY(launch(&k_quant_x, dim3((tiles + 15) / 16), dim3(256), 0, a.stream, tiles, K, cq + (long)m0 * K, xc, xs));
+    F8Args f{rows, K, xc, xs, Wc, Ws};
+    epi.m0 = m0;
+    if (p.kb == 3 && (N / 16) % 6 == 0)
+      MLA_TRY((launch_f8<3, 6, EpiUQF8, 3>(f, N / 96, 1, epi, a.stream)));
+    else
+      MLA_TRY(launch_f8_kb(f, p, N, epi, a.stream));
   }
   return hipSuccess;
 }

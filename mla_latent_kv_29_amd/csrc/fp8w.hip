@@ -9,8 +9,8 @@
 // the absorbed decode step (lesson §2.1.1 and its Question 2):
 //
 //   c^Q = W^DQ h                    fp8_gemm (one GEMM over all rows)
-//   u   = W^UQ c^Q                  fp8_gemm; u = [q^C_i ; q^R_i] per head
-//   qt_i[d_c:]  = tau log2(e) RoPE(q^R_i)            k_rope_tail
+//   u   = W^UQ c^Q = [q^C_i ; q^R_i]                 k_skinny_f8 (fp8w_uq), whose
+//   qt_i[d_c:]  = tau log2(e) RoPE(q^R_i)            epilogue rotates the RoPE pairs
 //   qt_i[:d_c]  = tau log2(e) W^UK_i^T q^C_i         k_f8_heads (per head)
 //   ... the attention of the bf16 step, unchanged, on qt and the cache ...
 //   out_i = W^UV_i O_lat_i                           k_merge, then k_f8_heads
@@ -76,13 +76,22 @@ __global__ __launch_bounds__(256) void k_f8_heads(F8HeadsArgs a) {
   }
 
   // quantise rows m0 .. m0 + 63 (clamped to M - 1: rows past M are computed
-  // and never stored) of this head, tile (row r, k-block j) by 16 lanes
+  // and never stored) of this head, tile (row r, k-block j) by 16 lanes;
+  // a thread's 4 KB tiles t = tid/16 + 16 n, all loads issued before the first use
   {
+    constexpr int NT = 4 * KB;
     const int q = threadIdx.x & 15;
-    for (int t = threadIdx.x >> 4; t < 64 * KB; t += 16) {  // the same trip count on every lane
-      const int r = t / KB, j = t % KB;
+    bf16x8 xv[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int t = (threadIdx.x >> 4) + 16 * n, r = t / KB, j = t % KB;
       const int m = min(m0 + r, a.M - 1);
-      const bf16x8 x = *(const bf16x8*)(a.X + (long)m * a.ldx + (long)head * a.hx + 128 * j + 8 * q);
+      xv[n] = *(const bf16x8*)(a.X + (long)m * a.ldx + (long)head * a.hx + 128 * j + 8 * q);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int t = (threadIdx.x >> 4) + 16 * n, r = t / KB, j = t % KB;
+      const bf16x8 x = xv[n];
       float am = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf((float)x[e]));
@@ -140,37 +149,6 @@ __global__ __launch_bounds__(256) void k_f8_heads(F8HeadsArgs a) {
       }
     }
   }
-}
-
-constexpr int RT_PAIRS = 32;  // d_rope / 2
-struct RopeTailArgs {
-  int M, H, s_q;
-  const bf16_t* u;         // [M][H][d_head + d_rope]
-  int d_head;
-  bf16_t* qt;              // [M][H][d_c + d_rope]
-  int d_c;
-  const int32_t* seqlens;  // row m = b s_q + j sits at position seqlens[b] - s_q + j
-  float scale2;            // tau log2 e
-  double freq[RT_PAIRS];   // theta^(-2p / d_rope) of RoPE pair p
-};
-
-// qt_i[d_c + 2p, +1] = scale2 R(pos) (u_i[d_head + 2p], u_i[d_head + 2p + 1]):
-// one thread per (row, head, pair), the rotation of the bf16 path.
-__global__ __launch_bounds__(256) void k_rope_tail(RopeTailArgs a) {
-  const long t = (long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (long)a.M * a.H * RT_PAIRS) return;
-  const int p = (int)(t % RT_PAIRS);
-  const long mi = t / RT_PAIRS;
-  const int i = (int)(mi % a.H), m = (int)(mi / a.H);
-  int pos = a.seqlens[m / a.s_q] - a.s_q + m % a.s_q;
-  pos = pos < 0 ? 0 : pos;
-  const bf16_t* src = a.u + mi * (a.d_head + 2 * RT_PAIRS) + a.d_head + 2 * p;
-  const float v0 = (float)src[0], v1 = (float)src[1];
-  float cs, sn;
-  rope_cs_w(pos, a.freq[p], &cs, &sn);
-  bf16_t* dst = a.qt + mi * (a.d_c + 2 * RT_PAIRS) + a.d_c + 2 * p;
-  dst[0] = (bf16_t)(a.scale2 * (v0 * cs - v1 * sn));
-  dst[1] = (bf16_t)(a.scale2 * (v0 * sn + v1 * cs));
 }
 
 // E4M3 quantisation of the transposes of `batch` matrices W[b][R][C] (bf16)
@@ -232,7 +210,7 @@ hipError_t fp8_quantize_weight_t(int batch, int R, int C, const bf16_t* W, uint8
 }
 
 bool fp8w_supported(const mla_dims& d) {
-  return d.d_head == 128 && d.d_c == 512 && d.d_rope == 2 * RT_PAIRS && fp8_gemm_supported(d.d_cq, d.d_model) &&
+  return d.d_head == 128 && d.d_c == 512 && d.d_rope == 64 && fp8_gemm_supported(d.d_cq, d.d_model) &&
          fp8_gemm_supported(d.n_heads * (d.d_head + d.d_rope), d.d_cq);
 }
 
@@ -244,25 +222,19 @@ size_t fp8w_scratch_bytes(const mla_dims& d, int R) {
   return align256(a.ws_bytes > b.ws_bytes ? a.ws_bytes : b.ws_bytes);
 }
 
-// c^Q, u, the RoPE tail and the absorption: qt of the bf16 step.  The u
-// region of the bf16 workspace (fp32-sized) holds u in bf16.
+// c^Q, u with its RoPE tail, and the absorption: qt of the bf16 step.
 hipError_t fp8w_query(const DecodeArgs& a, const Fp8Weights& w) {
   const mla_dims& d = a.d;
-  const int R = a.batch * a.s_q, H = d.n_heads, dq = d.d_head + d.d_rope;
+  const int R = a.batch * a.s_q, H = d.n_heads;
   uint8_t* f8ws = a.ws + fp8w_scratch_offset(a.L);
   bf16_t* cq = (bf16_t*)(a.ws + a.L.cq);
-  bf16_t* u = (bf16_t*)(a.ws + a.L.u);
+  bf16_t* qc = (bf16_t*)(a.ws + a.L.u);  // q^C [R][H][d_head] in the (fp32-sized) u region
   bf16_t* qt = (bf16_t*)(a.ws + a.L.qt);
-  const float scale2 = a.scale * 1.4426950408889634f;
   MLA_TRY(fp8_gemm(R, d.d_cq, d.d_model, (const bf16_t*)a.hq, w.dq_c, w.dq_s, cq, f8ws, a.stream));
-  MLA_TRY(fp8_gemm(R, H * dq, d.d_cq, cq, w.uq_c, w.uq_s, u, f8ws, a.stream));
-  RopeTailArgs rt{R, H, a.s_q, u, d.d_head, qt, d.d_c, a.seqlens, scale2, {}};
-  for (int p = 0; p < RT_PAIRS; ++p) rt.freq[p] = pow((double)d.rope_theta, -2.0 * p / d.d_rope);
-  const long n = (long)R * H * RT_PAIRS;
-  MLA_TRY(launch(&k_rope_tail, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, rt));
-  // absorption: X = q^C_i (the first d_head of u_i), W = (W^UK_i)^T [d_c][d_head]
-  const F8HeadsArgs f{R, u, (long)H * dq, dq, w.ukt_c, w.ukt_s, qt, (long)H * (d.d_c + d.d_rope), d.d_c + d.d_rope,
-                      scale2};
+  MLA_TRY(fp8w_uq(a, w.uq_c, w.uq_s, cq, qc, f8ws));
+  // absorption: X = q^C_i, W = (W^UK_i)^T [d_c][d_head]
+  const F8HeadsArgs f{R, qc, (long)H * d.d_head, d.d_head, w.ukt_c, w.ukt_s, qt, (long)H * (d.d_c + d.d_rope),
+                      d.d_c + d.d_rope, a.scale * 1.4426950408889634f};
   return launch_heads<1, 4>(f, H, a.stream);
 }
 

@@ -223,6 +223,9 @@ hipError_t fp8_quantize_weight_t(int batch, int R, int C, const bf16_t* W, uint8
 size_t fp8w_scratch_offset(const WsLayout& L);
 size_t fp8w_scratch_bytes(const mla_dims& d, int R);
 hipError_t fp8w_query(const DecodeArgs& a, const Fp8Weights& w);
+// u = W^UQ c^Q on FP8 weights: q^C into qc [R][H][d_head], RoPE pairs into qt
+hipError_t fp8w_uq(const DecodeArgs& a, const uint8_t* Wc, const float* Ws, const bf16_t* cq, bf16_t* qc,
+                   uint8_t* ws);
 hipError_t fp8w_combine(const CombineArgs& a, const uint8_t* uv_c, const float* uv_s);
 hipError_t merge_partials(const CombineArgs& a);  // split partials -> O_lat (ws olat) and lse
 bool skinny_out_supported(int rows, int N, int K);
