@@ -412,6 +412,23 @@ MLA_API int mla_prefill_attend(const mla_dims* dims, int32_t act_dtype, const vo
                 const void* W_DKV, const void* W_KR, float softmax_scale, void* out,
                 float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Metadata check before a decode step (what the host validation of the
+ * other calls cannot see, since it lives in device memory): counts
+ *   bad[0]: sequences whose seqlens[b] is negative or exceeds
+ *           max_pages * page_size;
+ *   bad[1]: block-table entries block_table[b][p] of pages the sequence uses
+ *           (p * page_size < seqlens[b]) outside 0 .. cache->num_pages - 1,
+ * and writes both to bad (device int32[2], 4-byte aligned) on `stream`; the
+ * caller reads them after the stream.  An entry counted in bad[1] would make
+ * mla_decode read outside the page pool, which the decode itself does not
+ * check.  Arguments as for mla_decode; batch 0 writes zeros (seqlens may
+ * then be NULL).  Errors:
+ * MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE, MLA_ERR_ALIGN; nothing is
+ * enqueued on an error other than MLA_ERR_HIP.                              */
+MLA_API int mla_check_metadata(const mla_dims* dims, const mla_cache* cache, const int32_t* block_table,
+                               int32_t max_pages, const int32_t* seqlens, int32_t batch, int32_t* bad,
+                               void* stream);
+
 /* Measurement helper (no part of the decode maths): streams `bytes` (a
  * multiple of 16) of device memory at src with 16-byte loads over the whole
  * GPU and writes nothing (sink: one device int32 that is practically never

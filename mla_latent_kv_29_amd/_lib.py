@@ -21,7 +21,7 @@ EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
            "mla_fp8_quantize_weight_t", "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
            "mla_decode_step_noalloc", "mla_decode_fp8w_workspace_bytes", "mla_decode_fp8w",
-           "mla_decode_fp8w_query", "mla_combine_fp8w", "mla_hbm_read_probe", "mla_status_str",
+           "mla_decode_fp8w_query", "mla_combine_fp8w", "mla_check_metadata", "mla_hbm_read_probe", "mla_status_str",
            "mla_last_hip_error", "mla_version")
 
 
@@ -83,6 +83,7 @@ def _load():
         "mla_decode_fp8w": (ctypes.c_int, [D, P, I32, I32, P, P, P, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
         "mla_decode_fp8w_query": (ctypes.c_int, [D, P, I32, I32, P, P, P, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
         "mla_combine_fp8w": (ctypes.c_int, [D, I32, I32, I32, P, SZ, P, P, P, P, P]),
+        "mla_check_metadata": (ctypes.c_int, [D, C, P, I32, P, I32, P, P]),
         "mla_hbm_read_probe": (ctypes.c_int, [P, SZ, P, P]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
@@ -291,6 +292,15 @@ def mla_combine_fp8w(dims, batch, s_q, num_splits, ws, ws_bytes, W_UV, out, lse_
                                _ptr(W_UV[0]), _ptr(W_UV[1]), _ptr(out), _ptr(lse_out), _stream(stream))
     if check:
         _check("mla_combine_fp8w", st)
+    return st
+
+
+def mla_check_metadata(dims, cache, block_table, max_pages, seqlens, batch, bad, stream=None, check=True):
+    """Enqueues the metadata check; bad (device int32[2]) holds the counts once the stream has run."""
+    st = _lib.mla_check_metadata(ctypes.byref(dims), ctypes.byref(cache), _ptr(block_table), int(max_pages),
+                                 _ptr(seqlens), int(batch), _ptr(bad), _stream(stream))
+    if check:
+        _check("mla_check_metadata", st)
     return st
 
 

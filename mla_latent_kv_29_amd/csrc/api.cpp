@@ -518,6 +518,18 @@ int mla_fp8_gemm(int32_t M, int32_t N, int32_t K, const void* X, const void* W_c
                              (hipStream_t)stream));
 }
 
+int mla_check_metadata(const mla_dims* dims, const mla_cache* cache, const int32_t* block_table, int32_t max_pages,
+                       const int32_t* seqlens, int32_t batch, int32_t* bad, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  if ((st = check_cache(dims, cache, block_table, max_pages))) return st;
+  if (!bad || (batch > 0 && !seqlens)) return MLA_ERR_NULL;
+  if ((seqlens && !aligned16(seqlens)) || ((uintptr_t)bad & 3)) return MLA_ERR_ALIGN;
+  return hip_status(check_metadata(batch, max_pages, dims->page_size, cache->num_pages, block_table, seqlens, bad,
+                                   (hipStream_t)stream));
+}
+
 int mla_hbm_read_probe(const void* src, size_t bytes, int32_t* sink, void* stream) {
   if (bytes == 0) return MLA_OK;
   if (!src || !sink) return MLA_ERR_NULL;

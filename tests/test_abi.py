@@ -398,3 +398,22 @@ def test_fp8w_workspace_and_argument_errors():
     assert quant_t(C=640 + 64) == L.MLA_ERR_UNSUPPORTED
     assert quant_t(c=None) == L.MLA_ERR_NULL
     assert quant_t(w=FAKE + 8) == L.MLA_ERR_ALIGN
+
+
+def test_check_metadata_argument_errors():
+    d = _dims()
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 10)
+
+    def call(**o):
+        a = dict(c=cache, bt=FAKE, mp=4, sl=FAKE, batch=2, bad=FAKE)
+        a.update(o)
+        return L.mla_check_metadata(d, a["c"], a["bt"], a["mp"], a["sl"], a["batch"], a["bad"], stream=0, check=False)
+
+    assert call(bt=None) == L.MLA_ERR_NULL
+    assert call(sl=None) == L.MLA_ERR_NULL
+    assert call(bad=None) == L.MLA_ERR_NULL
+    assert call(bad=FAKE + 2) == L.MLA_ERR_ALIGN
+    assert call(sl=FAKE + 4) == L.MLA_ERR_ALIGN
+    assert call(batch=-1) == L.MLA_ERR_DIMS
+    assert call(mp=0) == L.MLA_ERR_DIMS
+    assert call(c=L.cache_struct(FAKE, 9, 10)) == L.MLA_ERR_DTYPE
