@@ -1,5 +1,6 @@
-// Combine for at most 64 query rows (gfx950): the merge of the attention's
-// per-split partials and the W^UV projection in one kernel.
+// Combine for up to 64 query rows, or up to 512 rows of at most 4 splits
+// (gfx950): the merge of the attention's per-split partials and the W^UV
+// projection in one kernel.
 //
 // What it computes: the softmax over all visible tokens from the softmaxes
 // the attention took over disjoint token ranges (split s: normalised
@@ -277,11 +278,17 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
 
 }  // namespace
 
-bool merge_uv_supported(const mla_dims& d, int R) {
-  return R >= 1 && R <= 2 * CB_ROWS && d.d_c == CB_DC && d.d_head == CB_DV;
+// Up to 64 rows always; up to 512 rows while there are at most 4 splits to
+// merge (each wave merges four rows, four splits at a time: with more splits
+// the one-wave-per-row merge of the general path keeps more loads in flight).
+// Measured at 256 rows: 2 splits 60 -> 49 us of combine, 4 splits 65.7 ->
+// 64.9 us; at 128 rows of 16 splits 47.2 -> 48.4 us, so that case stays on
+// the general path.
+bool merge_uv_supported(const mla_dims& d, int R, int S) {
+  return R >= 1 && (R <= 2 * CB_ROWS || (R <= 16 * CB_ROWS && S <= 4)) && d.d_c == CB_DC && d.d_head == CB_DV;
 }
 
-// Merge + W^UV for R <= 64 rows: grid H x ceil(R / 32).
+// Merge + W^UV: grid H x ceil(R / 32).
 hipError_t merge_uv(const CombineArgs& a) {
   const int R = a.batch * a.s_q, H = a.d.n_heads;
   const int nrb = (R + CB_ROWS - 1) / CB_ROWS;

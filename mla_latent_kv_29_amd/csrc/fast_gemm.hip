@@ -825,7 +825,7 @@ hipError_t merge_partials(const CombineArgs& a) {
 hipError_t fast_combine(const CombineArgs& a) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
-  if (merge_uv_supported(d, R)) return merge_uv(a);
+  if (merge_uv_supported(d, R, a.S)) return merge_uv(a);
   MLA_TRY(merge_partials(a));
   const bf16_t* olat = (const bf16_t*)(a.ws + a.L.olat);
   hipError_t e;

@@ -192,7 +192,7 @@ hipError_t fast_attention(const DecodeArgs& a);
 hipError_t fast_query(const DecodeArgs& a);
 bool skinny_query_supported(const mla_dims& d, int R);
 hipError_t skinny_query(const DecodeArgs& a);
-bool merge_uv_supported(const mla_dims& d, int R);
+bool merge_uv_supported(const mla_dims& d, int R, int S);
 hipError_t merge_uv(const CombineArgs& a);
 bool prefill_supported(const mla_dims& d, int act);
 hipError_t prefill_projections(const PrefillArgs& a);  // positions, c^KV, k^R, c^Q, q, k^C, v^C
