@@ -50,8 +50,7 @@ def _load():
     # the torch tensors it is handed live in one HIP context.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
-                          f"python -m mla_latent_kv_29_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python mla_latent_kv_29_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     D = ctypes.POINTER(mla_dims)

@@ -234,3 +234,29 @@ def test_v3_empty_sequence_in_a_batch():
     tau = tau_of(V3) * 10.0
     out, lse, _ = case.run(tau)
     check_all(case, out, lse, tau, TOL_BF16)
+
+
+@pytest.mark.parametrize("lengths,s_q", [([70 + 37 * i for i in range(9)], 8), ([300, 65, 9], 1)])
+def test_attend_and_combine_rerun_on_the_same_workspace(lengths, s_q):
+    """query, attend, combine, then attend and combine again on the same
+    workspace give identical bytes: the combine writes only its own region
+    (the merged latent rows), never the queries the attention reads.  72 rows
+    (the many-row combine) and 3 rows (the fused one)."""
+    from mla_latent_kv_29_amd import _lib as L
+    case = Case(V3, "bf16", "bf16", lengths, s_q=s_q, table="shuffled", wl=6)
+    sess = case.sess
+    hq = case.hq()
+    tau = tau_of(V3)
+    W = case.W
+    args = (sess.cdims, sess.act, hq, sess.batch, s_q, W["W_DQ"], W["W_UQ"], W["W_UK"], sess.cache,
+            sess.block_table, sess.max_pages, sess.seqlens, tau, sess.num_splits, sess.ws, sess.ws_bytes)
+    comb = lambda: L.mla_combine(sess.cdims, sess.act, sess.batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes,
+                                 W["W_UV"], sess.out, sess.lse)
+    L.mla_decode_query(*args)
+    L.mla_decode_attend(*args)
+    comb()
+    o1, l1 = sess.out.clone(), sess.lse.clone()
+    L.mla_decode_attend(*args)
+    comb()
+    torch.cuda.synchronize()
+    assert torch.equal(sess.out, o1) and torch.equal(sess.lse, l1)
