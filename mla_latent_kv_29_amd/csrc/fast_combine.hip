@@ -35,6 +35,11 @@ constexpr int CB_DC = 512, CB_DV = 128, CB_ROWS = 32, CB_WAVES = 8;
 constexpr int CB_W_OFF = CB_ROWS * CB_DC * 2;          // 32 KiB
 constexpr int CB_LDS = CB_W_OFF + CB_DV * CB_DC * 2;   // 160 KiB
 static_assert(CB_LDS <= 160 * 1024, "LDS");
+// E4M3 weights: O_lat codes [32 rows][512], W^UV_i codes [128 n][512 k], the
+// O_lat tile scales [32][4]; rows of 512 bytes, chunk q at slot q ^ (row & 15)
+constexpr int CB8_W_OFF = CB_ROWS * CB_DC;                // 16 KiB
+constexpr int CB8_S_OFF = CB8_W_OFF + CB_DV * CB_DC;      // 80 KiB
+constexpr int CB8_LDS = CB8_S_OFF + CB_ROWS * (CB_DC / 128) * 4;
 
 typedef __attribute__((address_space(3))) uint8_t lu8;
 typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
@@ -46,6 +51,18 @@ typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
 __device__ __forceinline__ void cb_dma(const void* gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_addr)
                : "memory");
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x4 li32x4;
+
+// 32 E4M3 bytes of an MFMA operand: 16-byte slots s0 and s1 of an LDS row
+__device__ __forceinline__ i32x8 frag8(const lu8* row, int s0, int s1) {
+  const i32x4 lo = *(const li32x4*)(row + 16 * s0);
+  const i32x4 hi = *(const li32x4*)(row + 16 * s1);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 __device__ __forceinline__ float wmax(float v) {
@@ -67,8 +84,11 @@ struct CbArgs {
   const bf16_t* Wuv;  // [H][d_head][d_c]
   bf16_t* out;        // [R][H][d_head]
   float* lse_out;     // [R][H] or null
+  const uint8_t* Wc;  // E4M3 form: codes [H][d_head][d_c], scales [H][d_c / 128]
+  const float* Ws;
 };
 
+template <bool F8>
 __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lu8* lds = (lu8*)lds_raw;
@@ -86,7 +106,17 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
   // compiler's wait for those loads covers the copy too, as loads complete
   // in order).  Row n = instruction n (16 per wave), chunk q of the row at
   // slot q ^ (n & 15), i.e. lane l reads chunk l ^ (n & 15).
-  {
+  // E4M3: rows n = 2t (lanes 0..31) and 2t + 1 (lanes 32..63) in instruction
+  // t (8 per wave), chunk q of row n at slot q ^ (n & 15).
+  if constexpr (F8) {
+    const uint8_t* W = a.Wc + (size_t)head * CB_DV * CB_DC;
+    const uint32_t wt = (uint32_t)(uintptr_t)(lds + CB8_W_OFF);
+#pragma unroll
+    for (int jj = 0; jj < CB_DV / 2 / CB_WAVES; ++jj) {
+      const int t = wave + CB_WAVES * jj, n = 2 * t + (lane >> 5);
+      cb_dma(W, (uint32_t)(n * CB_DC + 16 * ((lane & 31) ^ (n & 15))), wt + 1024 * t);
+    }
+  } else {
     const bf16_t* W = a.Wuv + (size_t)head * CB_DV * CB_DC;
     const uint32_t wt = (uint32_t)(uintptr_t)(lds + CB_W_OFF);
 #pragma unroll
@@ -224,13 +254,39 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
     }
   }
   // merged rows (bf16) to the O_lat tile; rows past R are zero
+  if constexpr (F8) {
+    // the bf16 rows quantised in 1 x 128 tiles (16 lanes a tile): scale
+    // s = amax / 448 (1 for an all-zero tile), code = E4M3 of x / s
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = wave + CB_WAVES * i;
-    bf16x8 o;
+    for (int i = 0; i < 4; ++i) {
+      const int m = wave + CB_WAVES * i;
+      float x[8], am = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16_t)(acc[i][e] * invW[i]);
-    *(lbf16x8*)(lds + 1024 * m + 16 * (lane ^ (m & 15))) = o;
+      for (int e = 0; e < 8; ++e) {
+        x[e] = (float)(bf16_t)(acc[i][e] * invW[i]);
+        am = fmaxf(am, fabsf(x[e]));
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+      const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3(x[e] / sc) << (8 * e);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hi |= (uint32_t)f32_to_e4m3(x[4 + e] / sc) << (8 * e);
+      *(__attribute__((address_space(3))) i32x2*)(lds + 512 * m + 16 * ((lane >> 1) ^ (m & 15)) + 8 * (lane & 1)) =
+          i32x2{(int)lo, (int)hi};
+      if ((lane & 15) == 0) *(__attribute__((address_space(3))) float*)(lds + CB8_S_OFF + 4 * (4 * m + (lane >> 4))) = sc;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wave + CB_WAVES * i;
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16_t)(acc[i][e] * invW[i]);
+      *(lbf16x8*)(lds + 1024 * m + 16 * (lane ^ (m & 15))) = o;
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W^UV copies
   __syncthreads();
@@ -239,7 +295,25 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
   // column blocks 2(w>>1), 2(w>>1)+1; K = d_c in 16 k-steps.
   const int mb = wave & 1, nb0 = 2 * (wave >> 1);
   f32x4 c[2] = {f32x4{}, f32x4{}};
-  {
+  if constexpr (F8) {
+    // per k-block j: the integer-grid partial of one 16 x 16 x 128 product,
+    // promoted by the weight block's scale times the row tile's scale
+    const int ma = 16 * mb + i16;
+    const lu8* arow = lds + 512 * ma;
+    const lu8* brow0 = lds + CB8_W_OFF + 512 * (16 * nb0 + i16);
+    const lu8* brow1 = brow0 + 512 * 16;
+    const float* sw = a.Ws + (size_t)head * (CB_DC / 128);
+#pragma unroll
+    for (int j = 0; j < CB_DC / 128; ++j) {
+      const int s0 = (8 * j + g) ^ i16, s1 = (8 * j + 4 + g) ^ i16;  // k = 128 j + 16 g .., 128 j + 64 + 16 g ..
+      const i32x8 xq = frag8(arow, s0, s1), w0 = frag8(brow0, s0, s1), w1 = frag8(brow1, s0, s1);
+      const float xs = *(const __attribute__((address_space(3))) float*)(lds + CB8_S_OFF + 4 * (4 * ma + j));
+      const f32x4 p0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w0, xq, f32x4{}, 0, 0, 0, 0, 0, 0);
+      const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w1, xq, f32x4{}, 0, 0, 0, 0, 0, 0);
+      c[0] += (sw[j] * xs) * p0;
+      c[1] += (sw[j] * xs) * p1;
+    }
+  } else {
     const int ma = 16 * mb + i16;
     const lu8* arow = lds + 1024 * ma;
     const lu8* brow0 = lds + CB_W_OFF + 1024 * (16 * nb0 + i16);
@@ -293,9 +367,22 @@ hipError_t merge_uv(const CombineArgs& a) {
   const int R = a.batch * a.s_q, H = a.d.n_heads;
   const int nrb = (R + CB_ROWS - 1) / CB_ROWS;
   if ((H * nrb) % 8 != 0) return hipErrorInvalidValue;
-  CbArgs cb{a.batch, a.s_q, H, R, a.S, a.ws, a.L.lpart, (const bf16_t*)a.W_UV, (bf16_t*)a.out, a.lse_out};
-  MLA_TRY(lds_limit((const void*)&k_merge_uv, CB_LDS));
-  return launch(&k_merge_uv, dim3(H * nrb), dim3(CB_WAVES * 64), CB_LDS, a.stream, cb);
+  CbArgs cb{a.batch, a.s_q, H, R, a.S, a.ws, a.L.lpart, (const bf16_t*)a.W_UV, (bf16_t*)a.out, a.lse_out,
+            nullptr, nullptr};
+  MLA_TRY(lds_limit((const void*)&k_merge_uv<false>, CB_LDS));
+  return launch(&k_merge_uv<false>, dim3(H * nrb), dim3(CB_WAVES * 64), CB_LDS, a.stream, cb);
+}
+
+// The same on E4M3 W^UV (codes [H][d_head][d_c], one scale per 128 x 128
+// block, so [H][d_c / 128]): the merged rows are quantised in 1 x 128 tiles
+// in LDS and each k-block's product is promoted by its two scales.
+hipError_t merge_uv_f8(const CombineArgs& a, const uint8_t* uv_c, const float* uv_s) {
+  const int R = a.batch * a.s_q, H = a.d.n_heads;
+  const int nrb = (R + CB_ROWS - 1) / CB_ROWS;
+  if ((H * nrb) % 8 != 0) return hipErrorInvalidValue;
+  CbArgs cb{a.batch, a.s_q, H, R, a.S, a.ws, a.L.lpart, nullptr, (bf16_t*)a.out, a.lse_out, uv_c, uv_s};
+  MLA_TRY(lds_limit((const void*)&k_merge_uv<true>, CB8_LDS));
+  return launch(&k_merge_uv<true>, dim3(H * nrb), dim3(CB_WAVES * 64), CB8_LDS, a.stream, cb);
 }
 
 }  // namespace mla

@@ -13,7 +13,8 @@
 //   qt_i[d_c:]  = tau log2(e) RoPE(q^R_i)            epilogue rotates the RoPE pairs
 //   qt_i[:d_c]  = tau log2(e) W^UK_i^T q^C_i         k_f8_heads (per head)
 //   ... the attention of the bf16 step, unchanged, on qt and the cache ...
-//   out_i = W^UV_i O_lat_i                           k_merge, then k_f8_heads
+//   out_i = W^UV_i O_lat_i                           k_merge_uv<true> (merge +
+//                                                    W^UV), or k_merge, k_f8_heads
 //
 // k_f8_heads is the per-head form of the block-scaled GEMM for at most 64
 // rows a block: Y[m][i][n] = alpha sum_kb sx[m][i][kb] sw[i][n/128][kb]
@@ -239,10 +240,12 @@ hipError_t fp8w_query(const DecodeArgs& a, const Fp8Weights& w) {
 }
 
 // The merge of the split partials (O_lat and the lse) as in the bf16 step,
-// then out_i = W^UV_i O_lat_i on the FP8 weight.
+// then out_i = W^UV_i O_lat_i on the FP8 weight: in one kernel where the
+// bf16 step fuses the two, else k_merge into O_lat and k_f8_heads.
 hipError_t fp8w_combine(const CombineArgs& a, const uint8_t* uv_c, const float* uv_s) {
   const mla_dims& d = a.d;
   const int R = a.batch * a.s_q, H = d.n_heads;
+  if (merge_uv_supported(d, R, a.S)) return merge_uv_f8(a, uv_c, uv_s);
   MLA_TRY(merge_partials(a));
   const F8HeadsArgs f{R, (const bf16_t*)(a.ws + a.L.olat), (long)H * d.d_c, d.d_c, uv_c, uv_s, (bf16_t*)a.out,
                       (long)H * d.d_head, d.d_head, 1.0f};

@@ -116,6 +116,40 @@ def test_fp8w_decode_ragged_batches(lengths, s_q, splits):
         compare(out, lse, b, s_q, c, kr, hqb, Wn, Wq, dims, Lb, tau, heads)
 
 
+@pytest.mark.parametrize("splits", [2, 6])
+def test_fp8w_decode_72_rows(splits):
+    """72 one-row sequences (1 .. 340 tokens, three empty): with 2 splits the
+    merge and the W^UV projection run as one kernel (rows 64 .. 71 in a
+    second row block), with 6 splits as the merge kernel and the per-head
+    GEMM; sequences 0, 5, 40, 71 against both references."""
+    dims = V3
+    rng = np.random.default_rng(72)
+    lengths = rng.integers(1, 341, size=72).astype(np.int64)
+    lengths[[3, 17, 64]] = 0
+    W = inputs.weights(dims, 0.006, torch.bfloat16, DEV, 7, 11)
+    bt, pool = inputs.block_table(lengths, dims["page_size"], "shuffled", 7, 11)
+    sess = DecodeSession(dims, "bf16", "bf16", lengths, bt, pool, 1, splits, DEV)
+    gen_h = lambda b, t0, t1: inputs.hidden(dims, b, t0, t1, torch.bfloat16, DEV, 7, 11)
+    sess.build_from_h(gen_h, W)
+    rows = [gen_h(b, int(L) - 1, int(L)) if L >= 1 else
+            torch.zeros((1, dims["d_model"]), dtype=torch.bfloat16, device=DEV) for b, L in enumerate(lengths)]
+    hq = torch.cat(rows, 0).contiguous()
+    tau = tau_of(dims)
+    Wq_dev = sess.quantize_fp8w(W)
+    out, lse = sess.decode_fp8w(hq, Wq_dev, tau)
+    torch.cuda.synchronize()
+    out, lse = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(out))
+    for b in (3, 17, 64):
+        assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b]))
+    Wn = {k: to_np(v) for k, v in W.items()}
+    Wq = oracle_quantised(Wn)
+    for b in (0, 5, 40, 71):
+        Lb = int(lengths[b])
+        c, kr = latents(dims, Wn, to_np(gen_h(b, 0, Lb)))
+        compare(out, lse, b, 1, c, kr, to_np(hq[b:b + 1]), Wn, Wq, dims, Lb, tau, HEADS)
+
+
 def test_fp8w_benchmark_workload_sampled_sequences():
     """The benchmarked v3_fp8w_b64_l4096 step at full size (its seeds, lengths,
     block table and default split plan): sequences 0, 21, 42 and 63, three
