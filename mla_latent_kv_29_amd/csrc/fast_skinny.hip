@@ -547,6 +547,48 @@ __global__ __launch_bounds__(256) void k_quant_x(int tiles, int K, const bf16_t*
   if (j == 0) scales[t] = sc;
 }
 
+// The k-group sums of k_reduce_rows for Y[M][N] (N a multiple of 128), also
+// quantised in 1 x 128 tiles from the bf16 sums, exactly as k_quant_x would
+// quantise Y: codes [M][N], scales [M][N / 128].  16 lanes per tile.
+__global__ __launch_bounds__(256) void k_reduce_quant(int M, int N, int KG, const float* __restrict__ part,
+                                                      bf16_t* __restrict__ y, uint8_t* __restrict__ codes,
+                                                      float* __restrict__ scales) {
+  const int nt = N / 128, t = blockIdx.x * 16 + (threadIdx.x >> 4), j = threadIdx.x & 15;
+  const bool live = t < M * nt;
+  const long i = live ? (long)(t / nt) * N + (t % nt) * 128 + 8 * j : 0;
+  const long MN = (long)M * N;
+  f32x4 s0 = f32x4{}, s1 = f32x4{};
+  if (live) {
+    s0 = *(const f32x4*)(part + i);
+    s1 = *(const f32x4*)(part + i + 4);
+    for (int k = 1; k < KG; ++k) {
+      s0 += *(const f32x4*)(part + k * MN + i);
+      s1 += *(const f32x4*)(part + k * MN + i + 4);
+    }
+  }
+  bf16x8 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = (bf16_t)s0[e];
+    x[4 + e] = (bf16_t)s1[e];
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf((float)x[e]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+  if (!live) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3((float)x[e] / sc) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hi |= (uint32_t)f32_to_e4m3((float)x[4 + e] / sc) << (8 * e);
+  *(bf16x8*)(y + i) = x;
+  *(uint2*)(codes + i) = make_uint2(lo, hi);
+  if (j == 0) scales[t] = sc;
+}
+
 struct F8Args {
   int M, K;             // activation rows (<= 64), reduction length (multiple of 512)
   const uint8_t* Xc;    // activation codes [M][K]
@@ -777,8 +819,11 @@ hipError_t fp8_quantize_weight(int N, int K, const bf16_t* W, uint8_t* codes, fl
 }
 
 // Y = Q(X) . Q(W)^T in chunks of 64 rows (each chunk streams the weight).
+// With yc (at most 64 rows, N a multiple of 128), Y is also quantised in
+// 1 x 128 tiles into yc [M][N] and ys [M][N / 128].
 hipError_t fp8_gemm(int M, int N, int K, const bf16_t* X, const uint8_t* Wc, const float* Ws, bf16_t* Y, uint8_t* ws,
-                    hipStream_t st) {
+                    hipStream_t st, uint8_t* yc, float* ys) {
+  if (yc && (M > 64 || N % 128 != 0)) return hipErrorInvalidValue;
   const F8Plan p = fp8_plan(M, N, K);
   uint8_t* xc = ws + p.xc_off;
   float* xs = (float*)(ws + p.xs_off);
@@ -790,11 +835,21 @@ hipError_t fp8_gemm(int M, int N, int K, const bf16_t* X, const uint8_t* Wc, con
     bf16_t* y = Y + (long)m0 * N;
     if (p.kgroups == 1) {
       MLA_TRY(launch_f8_kb(a, p, N, EpiRowsBf16{y, N}, st));
+      if (yc) {
+        const int yt = rows * (N / 128);
+        MLA_TRY(launch(&k_quant_x, dim3((yt + 15) / 16), dim3(256), 0, st, yt, N, (const bf16_t*)y, yc, ys));
+      }
       continue;
     }
     float* part = (float*)(ws + p.part_off);
     MLA_TRY(launch_f8_kb(a, p, N, EpiKPart{part, rows, N}, st));
     const int MN = rows * N;
+    if (yc) {
+      const int yt = rows * (N / 128);
+      MLA_TRY(launch(&k_reduce_quant, dim3((yt + 15) / 16), dim3(256), 0, st, rows, N, p.kgroups, (const float*)part,
+                     y, yc, ys));
+      continue;
+    }
     MLA_TRY(launch(&k_reduce_rows, dim3((MN / 4 + 255) / 256), dim3(256), 0, st, MN, p.kgroups, (const float*)part, y));
   }
   return hipSuccess;

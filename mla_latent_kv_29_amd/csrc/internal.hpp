@@ -210,8 +210,10 @@ struct F8Plan {
 bool fp8_gemm_supported(int N, int K);
 F8Plan fp8_plan(int M, int N, int K);
 hipError_t fp8_quantize_weight(int N, int K, const bf16_t* W, uint8_t* codes, float* scales, hipStream_t st);
+// With yc: Y also quantised in 1 x 128 tiles (codes yc [M][N], scales ys
+// [M][N / 128]); at most 64 rows, N a multiple of 128.
 hipError_t fp8_gemm(int M, int N, int K, const bf16_t* X, const uint8_t* Wc, const float* Ws, bf16_t* Y, uint8_t* ws,
-                    hipStream_t st);
+                    hipStream_t st, uint8_t* yc = nullptr, float* ys = nullptr);
 // Decode with FP8 block-scaled projection weights: the step's query phase
 // and combine on E4M3 weights (the attention is the bf16 step's).  W^UK is
 // given per head transposed, [H][d_c][d_head], so that every projection is
