@@ -380,6 +380,7 @@ hipError_t fast_query(const DecodeArgs& a) {
                        (const float*)part, cqb));
     cq = cqb;
   }
+  if (rows_query_supported(d, R)) return rows_query(a, cq);
   {
     GemmArgs g = gemm_args(R, H * (d.d_head + d.d_rope), d.d_cq, cq, d.d_cq, 0, (const bf16_t*)a.W_UQ, d.d_cq, 0, 1);
     EpiUQ epi{qc, qt, a.seqlens, H, d.d_head, d.d_rope, d.d_c, a.s_q, scale2, {}};

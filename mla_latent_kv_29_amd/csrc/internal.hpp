@@ -194,6 +194,9 @@ bool skinny_query_supported(const mla_dims& d, int R);
 hipError_t skinny_query(const DecodeArgs& a);
 bool merge_uv_supported(const mla_dims& d, int R, int S);
 hipError_t merge_uv(const CombineArgs& a);
+// W^UQ + RoPE + W^UK absorption for more than 64 rows (V3 shape), from c^Q
+bool rows_query_supported(const mla_dims& d, int R);
+hipError_t rows_query(const DecodeArgs& a, const bf16_t* cq);
 hipError_t merge_uv_f8(const CombineArgs& a, const uint8_t* uv_c, const float* uv_s);  // E4M3 W^UV
 bool prefill_supported(const mla_dims& d, int act);
 hipError_t prefill_projections(const PrefillArgs& a);  // positions, c^KV, k^R, c^Q, q, k^C, v^C
