@@ -83,6 +83,19 @@ def test_v3_bf16_verify_more_than_64_rows():
     check_all(case, out, lse, tau, TOL_BF16, heads=[0, 63, 127])
 
 
+@pytest.mark.parametrize("lengths,s_q", [([65] + [40 + i for i in range(64)], 1),
+                                         ([5 + 3 * i for i in range(43)], 3),
+                                         ([4 + i for i in range(100)], 3)])
+def test_v3_bf16_many_row_query_block_edges(lengths, s_q):
+    """The many-row query kernel (128 rows a block) at 65 rows (one block,
+    63 clamped rows), 129 rows (a second block with one row) and 300 rows
+    (three blocks, the last partly filled); ragged lengths, default plan."""
+    case = Case(V3, "bf16", "bf16", lengths, s_q=s_q, table="shuffled", wl=8)
+    tau = tau_of(V3) * 20.0
+    out, lse, _ = case.run(tau)
+    check_all(case, out, lse, tau, TOL_BF16, heads=[0, 63, 127])
+
+
 def test_v3_planted_latents_sharp():
     """Cache written directly (std 0.5, the scale of W^DKV h at these
     weights), queries from h; sharpened softmax."""
