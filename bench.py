@@ -201,6 +201,85 @@ def run_hbm_probe(args):
     print(json.dumps(res))
 
 
+class PowerSampler:
+    """Board power and mean shader clock from `amd-smi metric -p -c`, sampled
+    in a background thread: [(time, watts, MHz)]."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.stop, self.ok = [], False, True
+        self.th = threading.Thread(target=self.run, daemon=True)
+        self.th.start()
+
+    def run(self):
+        import re
+        import subprocess
+        while not self.stop:
+            t = time.time()
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], capture_output=True, text=True,
+                                     timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                self.ok = False
+                return
+            pw = re.search(r"SOCKET_POWER:\s*(\d+)\s*W", out)
+            clks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
+            if pw:
+                self.samples.append((t, int(pw.group(1)), sum(clks) / len(clks) if clks else None))
+            time.sleep(0.05)
+
+    def mean(self, t0, t1):
+        s = [x for x in self.samples if t0 <= x[0] <= t1]
+        if not s:
+            return None, None, 0
+        c = [x[2] for x in s if x[2] is not None]
+        return sum(x[1] for x in s) / len(s), (sum(c) / len(c) if c else None), len(s)
+
+
+def run_phase_power(workload, secs, phases, stream):
+    """Each phase launched back to back for `secs` seconds (in batches of 100
+    launches, then a synchronisation), idle before and after; power and clock
+    averaged over the samples inside each window (the first 0.3 s skipped)."""
+    import torch
+    ps = PowerSampler()
+    time.sleep(1.0)
+    res = {"probe": "phase_power", "workload": workload, "seconds": secs, "phases": []}
+
+    def window(name, t0, t1, launch_us=None, gpu_us=None):
+        p, clk, n = ps.mean(t0 + 0.3, t1)
+        r = {"phase": name, "power_w": p, "gfx_mhz": clk, "samples": n}
+        if launch_us is not None:
+            r.update({"launch_us": launch_us, "gpu_us": gpu_us,
+                      "energy_mj": p * launch_us * 1e-3 if p is not None else None})
+        res["phases"].append(r)
+
+    t0 = time.time()
+    time.sleep(secs)
+    window("idle", t0, time.time())
+    for name in ("step", "attend", "query", "combine"):
+        f = phases[name]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(20):
+            f(i)
+        e0.record(stream)
+        for i in range(200):
+            f(i)
+        e1.record(stream)
+        e1.synchronize()
+        gpu_us = e0.elapsed_time(e1) * 1e3 / 200
+        n, t0 = 0, time.time()
+        while time.time() - t0 < secs:
+            for i in range(100):
+                f(n + i)
+            n += 100
+            torch.cuda.synchronize()
+        t1 = time.time()
+        window(name, t0, t1, (t1 - t0) * 1e6 / n, gpu_us)
+    ps.stop = True
+    res["amd_smi"] = ps.ok
+    print(json.dumps(res))
+
+
 def run_layers(args, name):
     """Layer-stack workload: one step = for every layer, mla_decode_query +
     mla_decode_attend + mla_combine + mla_output_project, each layer with its
@@ -489,6 +568,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="measure achievable HBM read and copy bandwidth (75 MB, 302 MB) and exit")
+    ap.add_argument("--phase-power", type=float, default=0.0, metavar="SECS",
+                    help="run idle, the whole step, and each phase (attention, query, combine) back to back "
+                         "for SECS seconds each while amd-smi samples board power and clocks; print one "
+                         "JSON line of per-phase launch time, power, clock and energy per launch, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB three times (untimed), as the "
                          "reference for hardware byte counters")
@@ -564,27 +647,44 @@ def main():
                            sess.block_table, sess.max_pages, sess.seqlens, tau, sess.num_splits, sess.ws,
                            sess.ws_bytes, sp)
 
-    def step(i, e=None):
-        k = i % len(sets)
-        if e is not None:
-            e[0].record(stream)
+    def query(k):
         if fp8w:
             L.mla_decode_fp8w_query(*fargs(k))
         else:
             L.mla_decode_query(*dargs(k))
-        if e is not None:
-            e[1].record(stream)
+
+    def attend(k):
         L.mla_decode_attend(*dargs(k))
-        if e is not None:
-            e[2].record(stream)
+
+    def combine(k):
         if fp8w:
             L.mla_combine_fp8w(c, sess.batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes, qsets[k]["W_UV"],
                                sess.out, sess.lse, sp)
         else:
             L.mla_combine(c, sess.act, sess.batch, s_q, sess.num_splits, sess.ws, sess.ws_bytes,
                           sets[k][1]["W_UV"], sess.out, sess.lse, sp)
+
+    def step(i, e=None):
+        k = i % len(sets)
+        if e is not None:
+            e[0].record(stream)
+        query(k)
+        if e is not None:
+            e[1].record(stream)
+        attend(k)
+        if e is not None:
+            e[2].record(stream)
+        combine(k)
         if e is not None:
             e[3].record(stream)
+
+    if args.phase_power > 0:
+        step(0)
+        torch.cuda.synchronize()
+        phases = {"step": lambda i: step(i), "attend": lambda i: attend(i % len(sets)),
+                  "query": lambda i: query(i % len(sets)), "combine": lambda i: combine(i % len(sets))}
+        run_phase_power(args.workload, args.phase_power, phases, stream)
+        return
 
     copy_calibration(args.copy_calibration, dev)
 
