@@ -138,6 +138,29 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
   const uint8_t* opart = a.ws + opart_offset(a.lpart_off, a.batch, S, a.s_q, a.H);
   const size_t pstep = (size_t)a.s_q * a.H;  // partial row stride between splits
 
+  // With several row blocks and at most 4 splits, the next block's lse values
+  // and partial rows are loaded as soon as this block's are consumed, so that
+  // they arrive while this block's projection runs (rows of empty splits
+  // are loaded too and selected away, the sums stay as without prefetch).
+  const bool pf = pbf16 && a.passes > 1 && S <= 4;
+  float pre_lt[4];
+  bf16x8 pre_v[4][4];
+  bool have_pre = false;
+  auto prefetch = [&](int rbn) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = CB_ROWS * rbn + wave + CB_WAVES * i;
+      const bool lv = row < a.R;
+      const int b = lv ? row / a.s_q : 0, j = lv ? row % a.s_q : 0;
+      const size_t q0 = (((size_t)b * S) * a.s_q + j) * a.H + head;
+      pre_lt[i] = lv && lane < S ? lpart[q0 + (size_t)lane * pstep] : -INFINITY;
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu)
+        pre_v[i][uu] = lv && uu < S ? *(const bf16x8*)((const bf16_t*)opart + (q0 + (size_t)uu * pstep) * CB_DC + 8 * lane)
+                                    : bf16x8{};
+    }
+  };
+
   // Row blocks rg * passes + p, one after the other: W^UV_i stays in LDS.
   for (int pass = 0; pass < a.passes; ++pass) {
     const int rb = rg * a.passes + pass;
@@ -155,7 +178,10 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
       live[i] = row < a.R;
       const int b = live[i] ? row / a.s_q : 0, j = live[i] ? row % a.s_q : 0;
       p0[i] = (((size_t)b * S) * a.s_q + j) * a.H + head;
-      lt[i] = live[i] && lane < S ? lpart[p0[i] + (size_t)lane * pstep] : -INFINITY;
+      if (have_pre)
+        lt[i] = pre_lt[i];
+      else
+        lt[i] = live[i] && lane < S ? lpart[p0[i] + (size_t)lane * pstep] : -INFINITY;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -183,7 +209,18 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
-    if (pbf16 && !live[1]) {
+    if (have_pre) {
+      // the prefetched rows: the sums of the four-row path below, in its order
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          const float w = __shfl(wt0[i], uu, 64);  // 0 past the splits (lanes >= S hold 0)
+          const bf16x8 v = w != 0.0f ? pre_v[i][uu] : bf16x8{};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[i][e] += w * (float)v[e];
+        }
+    } else if (pbf16 && !live[1]) {
       // One row on this wave (at most 8 rows per block): sixteen splits in
       // flight at a time instead of four, so that a long split list costs a
       // quarter of the memory round trips.
@@ -298,7 +335,14 @@ __global__ __launch_bounds__(CB_WAVES * 64) void k_merge_uv(CbArgs a) {
         *(lbf16x8*)(lds + 1024 * m + 16 * (lane ^ (m & 15))) = o;
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W^UV copies
+    // this wave's W^UV copies (issued first; the merge's loads, already
+    // consumed, waited for them in practice), before any prefetch goes out
+    if (pass == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    have_pre = false;
+    if (pf && pass + 1 < a.passes && rb + 1 < nrb) {
+      prefetch(rb + 1);
+      have_pre = true;
+    }
     __syncthreads();
 
     // 2. out tile [32 m][128 n] = O_lat W^UV_i^T: wave w, row block w&1,
