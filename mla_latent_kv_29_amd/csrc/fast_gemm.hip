@@ -363,9 +363,11 @@ hipError_t fast_query(const DecodeArgs& a) {
   hipError_t e = hipSuccess;
   const bf16_t* cq = (const bf16_t*)a.hq;
   if (a.W_DQ) {
-    // c^Q = W^DQ h: split K so that the grid covers the GPU
+    // c^Q = W^DQ h: split K so that the grid fills the GPU's 512 block slots
+    // (two 64 KiB blocks a CU) in one round: rounding up left a second round
+    // of a few blocks (576 blocks at 256 rows, 528 at 128)
     const int ntile = d.d_cq / 64 * ((R + 63) / 64);
-    int splits = (512 + ntile - 1) / ntile;
+    int splits = std::max(1, 512 / ntile);
     splits = splits > KSPLIT_MAX ? KSPLIT_MAX : splits;
     while (splits > 1 && d.d_model / splits < 2 * BK) --splits;
     GemmArgs g = gemm_args(R, d.d_cq, d.d_model, (const bf16_t*)a.hq, d.d_model, 0, (const bf16_t*)a.W_DQ,
