@@ -256,8 +256,7 @@ def run_phase_power(workload, secs, phases, stream):
     t0 = time.time()
     time.sleep(secs)
     window("idle", t0, time.time())
-    for name in ("step", "attend", "query", "combine"):
-        f = phases[name]
+    for name, f in phases.items():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(20):
             f(i)
@@ -514,6 +513,14 @@ def run_prefill(args, name):
         if e is not None:
             e[2].record(stream)
 
+    if args.phase_power > 0:
+        step()
+        torch.cuda.synchronize()
+        phases = {"step": lambda i: step(), "project": lambda i: L.mla_prefill_project(*pargs),
+                  "attend": lambda i: L.mla_prefill_attend(*pargs)}
+        run_phase_power(name, args.phase_power, phases, stream)
+        return
+
     copy_calibration(args.copy_calibration, dev)
     for _ in range(args.warmup):
         step()
@@ -569,7 +576,8 @@ def main():
     ap.add_argument("--hbm-probe", action="store_true",
                     help="measure achievable HBM read and copy bandwidth (75 MB, 302 MB) and exit")
     ap.add_argument("--phase-power", type=float, default=0.0, metavar="SECS",
-                    help="run idle, the whole step, and each phase (attention, query, combine) back to back "
+                    help="run idle, the whole step, and each phase (decode: attention, query, combine; "
+                         "prefill: projections, attention) back to back "
                          "for SECS seconds each while amd-smi samples board power and clocks; print one "
                          "JSON line of per-phase launch time, power, clock and energy per launch, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

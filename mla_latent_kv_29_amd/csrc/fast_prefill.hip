@@ -28,11 +28,17 @@
 //     itself (keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key step make the eight
 //     k-slots of half-wave h), and two transposing LDS reads deliver V^T in
 //     the same key order, so P never leaves the registers.
-// K and V tiles stream HBM/L2 -> LDS with global_load_lds into two 40 KiB
-// buffers (one tile in flight while the other is multiplied); at 80 KiB a
-// block, two blocks share a CU, i.e. two waves per SIMD.  The LDS layouts
-// (16-byte chunk q of row r at slot q ^ f(r)) spread the K fragment reads and
-// the transposing V reads over the banks.
+// The tiles are software-pipelined within each wave: step i computes the
+// scores of tile i+1 with the exponentials of tile i slotted between those
+// MFMAs, then tile i's P.V with tile i+1's row maximum between those.  The
+// vector work of the softmax thus issues while the matrix unit runs the
+// other product, instead of after it.
+// K and V tiles stream HBM/L2 -> LDS with global_load_lds into two K slots
+// (24 KiB) and two V slots (16 KiB): step i reads K tile i+1 and V tile i
+// while K tile i+2 and V tile i+1 are in flight.  At 80 KiB a block, two
+// blocks share a CU, i.e. two waves per SIMD.  The LDS layouts (16-byte chunk
+// q of row r at slot q ^ f(r)) spread the K fragment reads and the
+// transposing V reads over the banks.
 #include <algorithm>
 #include <type_traits>
 
@@ -45,11 +51,11 @@ constexpr int PH = 128, PDH = 128, PDR = 64, PDQK = PDH + PDR;  // heads, d_head
 constexpr int BQ = 128, BKT = 64;                                // query rows per block, keys per tile
 constexpr int KC_BYTES = BKT * PDH * 2;                          // 16 KiB
 constexpr int KR_BYTES = BKT * PDR * 2;                          // 8 KiB
+constexpr int K_BYTES = KC_BYTES + KR_BYTES;                     // 24 KiB: a K slot (k^C rows, then k^R rows)
 constexpr int V_BYTES = BKT * PDH * 2;                           // 16 KiB
-constexpr int STAGE = KC_BYTES + KR_BYTES + V_BYTES;             // 40 KiB
-constexpr int PA_LDS = 2 * STAGE;                                // 80 KiB
-constexpr int COPIES = STAGE / 1024;                             // 40 wave-instructions per tile
-static_assert(COPIES == 40, "ten copies per wave");
+constexpr int V_OFF = 2 * K_BYTES;                               // the two V slots follow the two K slots
+constexpr int PA_LDS = 2 * K_BYTES + 2 * V_BYTES;                // 80 KiB
+static_assert(K_BYTES == 24 * 1024 && V_BYTES == 16 * 1024, "six K and four V copies per wave and tile");
 
 typedef __attribute__((address_space(3))) uint8_t lu8;
 typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
@@ -105,29 +111,26 @@ __device__ __forceinline__ TileOffsets tile_offsets(int wave, int lane) {
   return t;
 }
 
-// Tile kt (keys 64 kt .. +63 of the sequence, clamped to its last token) into
-// stage buffer `buf`.  Of the 40 copies (0-15 k^C rows, 16-23 k^R rows, 24-39
-// V rows) wave w issues w, w+4, ..., w+36: copies n = 0-3 of the wave are
-// k^C, 4-5 k^R, 6-9 V, whatever w is.  A tile inside the sequence needs no
-// clamping: its copies take the per-lane offsets above and the tile's
-// position in the scalar base; the sequence's last tile clamps rows.
-__device__ __forceinline__ void issue_tile(const bf16_t* kc_h, const bf16_t* vc_h, const bf16_t* kr, int start,
-                                           int len, int kt, uint32_t buf, int wave, int lane, const TileOffsets& to) {
+// Key tile kt (keys 64 kt .. +63 of the sequence, clamped to its last token):
+// its k^C and k^R rows into the K slot at kbuf, its V rows into the V slot at
+// vbuf.  Of a K tile's 24 copies (0-15 k^C rows, 16-23 k^R rows) wave w issues
+// w, w+4, ..., w+20: copies n = 0-3 of the wave are k^C, 4-5 k^R; of a V
+// tile's 16, w, w+4, w+8, w+12.  A tile inside the sequence needs no clamping:
+// its copies take the per-lane offsets above and the tile's position in the
+// scalar base; the sequence's last tile clamps rows.
+__device__ __forceinline__ void issue_k(const bf16_t* kc_h, const bf16_t* kr, int start, int len, int kt,
+                                        uint32_t kbuf, int wave, int lane, const TileOffsets& to) {
   const int k0 = kt * BKT;
+  const uint32_t lb = kbuf + 1024 * wave;
   if (k0 + BKT <= len) {
     const uint8_t* kcb = (const uint8_t*)kc_h + (size_t)(start + k0 + 4 * wave) * PDH * 2;
     const uint8_t* krb = (const uint8_t*)kr + (size_t)(start + k0 + 8 * wave) * PDR * 2;
-    const uint8_t* vb = (const uint8_t*)vc_h + (size_t)(start + k0 + 4 * wave) * PDH * 2;
-    const uint32_t lb = buf + 1024 * wave;
 #pragma unroll
     for (int n = 0; n < 4; ++n) pa_dma(kcb + 16 * n * PDH * 2, to.kc, lb + 4096 * n);
 #pragma unroll
     for (int n = 0; n < 2; ++n) pa_dma(krb + 32 * n * PDR * 2, to.kr, lb + KC_BYTES + 4096 * n);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) pa_dma(vb + 16 * n * PDH * 2, to.v, lb + KC_BYTES + KR_BYTES + 4096 * n);
     return;
   }
-  const uint32_t lb = buf + 1024 * wave;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int r = 4 * (wave + 4 * n) + (lane >> 4), c = kc_slot(r, lane & 15);
@@ -140,11 +143,22 @@ __device__ __forceinline__ void issue_tile(const bf16_t* kc_h, const bf16_t* vc_
     const int key = min(k0 + r, len - 1);
     pa_dma(kr, (uint32_t)(((start + key) * PDR + 8 * c) * 2), lb + KC_BYTES + 4096 * n);
   }
+}
+__device__ __forceinline__ void issue_v(const bf16_t* vc_h, int start, int len, int kt, uint32_t vbuf, int wave,
+                                        int lane, const TileOffsets& to) {
+  const int k0 = kt * BKT;
+  const uint32_t lb = vbuf + 1024 * wave;
+  if (k0 + BKT <= len) {
+    const uint8_t* vb = (const uint8_t*)vc_h + (size_t)(start + k0 + 4 * wave) * PDH * 2;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) pa_dma(vb + 16 * n * PDH * 2, to.v, lb + 4096 * n);
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int r = 4 * (wave + 4 * n) + (lane >> 4), c = (lane & 15) ^ v_swz(r);
     const int key = min(k0 + r, len - 1);
-    pa_dma(vc_h, (uint32_t)(((start + key) * PDH + 8 * c) * 2), lb + KC_BYTES + KR_BYTES + 4096 * n);
+    pa_dma(vc_h, (uint32_t)(((start + key) * PDH + 8 * c) * 2), lb + 4096 * n);
   }
 }
 
@@ -153,6 +167,14 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+// maximum over the lanes l and l ^ 32
+__device__ __forceinline__ float max_x32(float m) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
@@ -207,15 +229,17 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
   }
   wait_vmcnt<0>();  // the compiler's loads are done before the copies go out
   const TileOffsets to = tile_offsets(wave, lane);
-  issue_tile(kc_h, vc_h, a.kr, start, len, 0, ring, wave, lane, to);
-  if (ntiles > 1) issue_tile(kc_h, vc_h, a.kr, start, len, 1, ring + STAGE, wave, lane, to);
+  // K tile t lives in K slot t & 1, V tile t in V slot t & 1
+  issue_k(kc_h, a.kr, start, len, 0, ring, wave, lane, to);
+  if (ntiles > 1) issue_k(kc_h, a.kr, start, len, 1, ring + K_BYTES, wave, lane, to);
+  issue_v(vc_h, start, len, 0, ring + V_OFF, wave, lane, to);
 
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.0f;  // row maximum in use (log2 domain) and this lane's partial sum
 
-  // LDS byte addresses of the lane's reads in stage 0 (the stage, the key
+  // LDS byte addresses of the lane's reads in slot 0 (the slot, the key
   // block and the key step become instruction offsets):
   //  K: k-step ks (16-wide slice 16 ks .. of the 192-wide key row, this
   //     lane's half 8 hw ..) of key row l32;
@@ -232,60 +256,50 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
     const int e = (lane & 15) >> 2, qq = lane & 3, gsub = (lane >> 4) & 1;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-      va[db] = base + KC_BYTES + KR_BYTES + (4 * hw + e) * 256 + 16 * ((4 * db + 2 * gsub + (qq >> 1)) ^ v_swz(e)) +
-               8 * (qq & 1);
+      va[db] = base + V_OFF + (4 * hw + e) * 256 + 16 * ((4 * db + 2 * gsub + (qq >> 1)) ^ v_swz(e)) + 8 * (qq & 1);
   }
 
-  // One key tile kt in stage buffer STG (compile-time, so every LDS offset is
-  // an immediate).
-  auto tile = [&](auto stg, int kt) {
-    constexpr int STG = decltype(stg)::value;
-    if (kt == 0 && ntiles > 1) wait_vmcnt<10>();  // tile 1 may stay in flight
-    else wait_vmcnt<0>();
-    ring_barrier();  // tile kt is in; every wave is done with tile kt-1, whose buffer takes tile kt+1
-    if (kt >= 1 && kt + 1 < ntiles)
-      issue_tile(kc_h, vc_h, a.kr, start, len, kt + 1, ring + (1 - STG) * STAGE, wave, lane, to);
+  // K fragment t of the score chain (k-step t/2, key block t&1) in K slot KSL
+  auto kread = [&](auto ksl, int t) -> bf16x8 {
+    constexpr int KSL = decltype(ksl)::value;
+    const int ks = t >> 1, kb = t & 1;
+    return *(const lbf16x8*)(ka[ks] + KSL * K_BYTES + (ks < 8 ? kb * 8192 : kb * 4096));
+  };
+  // V^T fragment of P.V MFMA u (key step u/4, channel block u%4) in V slot VSL
+  auto vread = [&](auto vsl, int u) -> bf16x8 {
+    constexpr int VSL = decltype(vsl)::value;
+    const uint32_t adr = va[u & 3] + VSL * V_BYTES + (u >> 2) * 4096;
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)adr);
+    const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(adr + 2048));
+    const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+    return __builtin_bit_cast(bf16x8, s8);
+  };
+  // Scores S^T of a key tile: lane holds keys 32 kb + 8 j + 4 hw + i (VGPR
+  // 4j + i of sc[kb]) of query l32.  The two key blocks alternate (two
+  // independent chains); K fragments are read D MFMAs ahead.
+  constexpr int D = 3;
+  // keys after the lane's query get -inf (only tiles that reach past the
+  // wave's first query have any)
+  auto mask = [&](int kt, f32x16(&sc)[2]) {
     const int k0 = kt * BKT;
-    if (k0 > wq0 + 31) return;  // every key of the tile is after every query of this wave
-
-    // S^T blocks: lane holds keys 32 kb + 8 j + 4 hw + i (VGPR 4j + i) of
-    // query l32.  The two key blocks alternate (two independent chains) and
-    // the K fragments are read four MFMAs ahead.
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    {
-      constexpr int D = 4;
-      auto rd = [&](int t) -> bf16x8 {
-        const int ks = t >> 1, kb = t & 1;
-        const uint32_t off = STG * STAGE + (ks < 8 ? kb * 8192 : kb * 4096);
-        return *(const lbf16x8*)(ka[ks] + off);
-      };
-      bf16x8 kf[D];
-#pragma unroll
-      for (int t = 0; t < D; ++t) kf[t] = rd(t);
-#pragma unroll
-      for (int t = 0; t < 24; ++t) {
-        s[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % D], qf[t >> 1], s[t & 1], 0, 0, 0);
-        if (t + D < 24) kf[t % D] = rd(t + D);
-        __builtin_amdgcn_sched_barrier(0);  // keep the reads D steps ahead
-      }
-    }
-    if (k0 + BKT - 1 > wq0) {  // some key of the tile is after some query of the wave
+    if (k0 + BKT - 1 > wq0) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (k0 + 32 * kb + 8 * (v >> 2) + 4 * hw + (v & 3) > qrow) s[kb][v] = -INFINITY;
+          if (k0 + 32 * kb + 8 * (v >> 2) + 4 * hw + (v & 3) > qrow) sc[kb][v] = -INFINITY;
     }
-    // Online softmax with a lazily raised maximum: p = 2^(s - m) with the m
-    // in use, which moves (and O and the sum are rescaled) only when some
-    // score exceeds it by more than 2^8; every p stays below 256, and the
-    // result o / l is the same for any m.
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; v += 4) mt = vmax3(mt, vmax3(s[kb][v], s[kb][v + 1], s[kb][v + 2]), s[kb][v + 3]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  };
+  // part j (0..7) of the row maximum: keys 4 (j & 3) .. +3 of key block j/2
+  auto max_part = [&](const f32x16(&sc)[2], int j, float mx) -> float {
+    const int kb = j >> 2, v = 4 * (j & 3);
+    return vmax3(mx, vmax3(sc[kb][v], sc[kb][v + 1], sc[kb][v + 2]), sc[kb][v + 3]);
+  };
+  // Online softmax with a lazily raised maximum: p = 2^(s - m) with the m in
+  // use, which moves (and O and the sum are rescaled) only when some score
+  // exceeds it by more than 2^8; every p stays below 256, and the result
+  // o / l is the same for any m.
+  auto rescale = [&](float mt) {
     if (__any(mt > m + 8.0f)) {  // tile 0 always: m is -inf and every query sees key 0
       const float mn = mt > m + 8.0f ? mt : m;
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
@@ -294,40 +308,122 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
       m = mn;
     }
+  };
+  // Weights of scores v, v+1 (v even): p = 2^(s - m), summed into ls.  The
+  // empty asm statements pin each result where it is computed: without them
+  // the compiler sinks these pure instructions past the score MFMAs they are
+  // meant to overlap, to the block after the mask's branch.
+  auto exp2v = [&](f32x16(&sc)[2], int v, float& ls) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float p = __builtin_amdgcn_exp2f(sc[(v + e) >> 4][(v + e) & 15] - m);
+      asm volatile("" : "+v"(p));
+      sc[(v + e) >> 4][(v + e) & 15] = p;
+      ls += p;
+    }
+    asm volatile("" : "+v"(ls));
+  };
+  // P^T fragment of key step g: keys 16g + 4hw + 0..3 and 16g + 8 + 4hw + 0..3,
+  // which are values 8 (g & 1) .. +7 of sc[g / 2]: the S^T layout itself
+  auto pack = [&](const f32x16(&sc)[2], int g) -> bf16x8 {
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = (bf16_t)sc[g >> 1][8 * (g & 1) + i];
+    return pb;
+  };
+
+  f32x16 s[2][2];  // scores of the tiles in the two K slots
+  float mt;        // row maximum of the scores that the next step turns into weights
+
+  // Tile 0's scores on their own.
+  if (ntiles > 1) wait_vmcnt<10>();  // K tile 1 and V tile 0 may stay in flight
+  else wait_vmcnt<4>();
+  ring_barrier();
+  {
+    s[0][0] = f32x16{};
+    s[0][1] = f32x16{};
+    bf16x8 kf[D];
+#pragma unroll
+    for (int t = 0; t < D; ++t) kf[t] = kread(IC<0>{}, t);
+#pragma unroll
+    for (int t = 0; t < 24; ++t) {
+      s[0][t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % D], qf[t >> 1], s[0][t & 1], 0, 0, 0);
+      if (t + D < 24) kf[t % D] = kread(IC<0>{}, t + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mask(0, s[0]);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = max_part(s[0], j, mx);
+    mt = max_x32(mx);
+  }
+
+  // Step i (P = i & 1): the weights of tile i and its P.V, overlapped with
+  // the scores of tile i+1.  Part (a): the 24 score MFMAs of tile i+1 (K slot
+  // 1-P), the exponentials and bf16 packing of tile i's weights slotted
+  // between them; part (b): tile i's 16 P.V MFMAs (V slot P), the mask and
+  // row maximum of tile i+1 between them.  So the matrix unit has
+  // independent work queued while the vector unit computes the softmax.
+  // After the barrier every wave is done with step i-1, i.e. with K tile i
+  // and V tile i-1, whose slots take K tile i+2 and V tile i+1.
+  auto step = [&](auto par, int i) {
+    constexpr int P = decltype(par)::value;
+    wait_vmcnt<0>();  // K tile i+1 and V tile i (issued one step earlier)
+    ring_barrier();
+    if (i + 2 < ntiles) issue_k(kc_h, a.kr, start, len, i + 2, ring + P * K_BYTES, wave, lane, to);
+    if (i + 1 < ntiles) issue_v(vc_h, start, len, i + 1, ring + V_OFF + (1 - P) * V_BYTES, wave, lane, to);
+    if (i * BKT > wq0 + 31) return;  // every key of tile i is after every query of this wave
+    // One code path for every step: when the wave has no tile i+1 (its keys
+    // are all after the wave's queries, or past the block's last tile), the
+    // score MFMAs still run on whatever K slot 1-P holds and their results
+    // are never used.
+    f32x16(&sc)[2] = s[P];
+    f32x16(&sn)[2] = s[1 - P];
+    rescale(mt);
     float ls = 0.0f;
+    bf16x8 pb[4];
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    {
+      bf16x8 kf[D];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int t = 0; t < D; ++t) kf[t] = kread(IC<1 - P>{}, t);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][v] - m);
-        s[kb][v] = p;
-        ls += p;
+      for (int t = 0; t < 24; ++t) {
+        sn[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % D], qf[t >> 1], sn[t & 1], 0, 0, 0);
+        if (t + D < 24) kf[t % D] = kread(IC<1 - P>{}, t + D);
+        const int g = t / 6, r = t % 6;
+        if (r < 4) exp2v(sc, 8 * g + 2 * r, ls);
+        else if (r == 4) {
+          pb[g] = pack(sc, g);
+          asm volatile("" : "+v"(pb[g]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    mask(i + 1, sn);
     l += ls;
-    // O^T += V^T P^T, k-step kk = keys 16 kk .. +15 of the tile: half-wave hw
-    // holds keys 16kk + 4hw + 0..3 (VGPRs 4j0..) and 16kk + 8 + 4hw + 0..3
+    // (b) O^T += V^T P^T; V^T fragments read two MFMAs ahead
+    constexpr int DV = 2;
+    bf16x8 vf[DV + 1];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int kb = kk >> 1, j0 = 2 * (kk & 1);
-      bf16x8 pb;
+    for (int u = 0; u < DV; ++u) vf[u] = vread(IC<P>{}, u);
+    float mx = -INFINITY;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (bf16_t)s[kb][4 * j0 + i];
-        pb[4 + i] = (bf16_t)s[kb][4 * j0 + 4 + i];
-      }
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint32_t off = STG * STAGE + kk * 4096;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(va[db] + off));
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4*)(va[db] + off + 2048));
-        const short s8 __attribute__((ext_vector_type(8))) = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s8), pb, o[db], 0, 0, 0);
-      }
+    for (int u = 0; u < 16; ++u) {
+      o[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u % (DV + 1)], pb[u >> 2], o[u & 3], 0, 0, 0);
+      if (u + DV < 16) vf[(u + DV) % (DV + 1)] = vread(IC<P>{}, u + DV);
+      // tile i+1's row maximum (unused when this wave has no tile i+1)
+      if (u >= 2 && u < 10) mx = max_part(sn, u - 2, mx);
+      if (u == 10) mt = max_x32(mx);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int kt = 0; kt < ntiles; kt += 2) {
-    tile(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < ntiles) tile(std::integral_constant<int, 1>{}, kt + 1);
+    step(IC<0>{}, kt);
+    if (kt + 1 < ntiles) step(IC<1>{}, kt + 1);
   }
   wait_vmcnt<0>();  // nothing in flight into LDS when the block leaves
 
