@@ -236,6 +236,47 @@ class PowerSampler:
         return sum(x[1] for x in s) / len(s), (sum(c) / len(c) if c else None), len(s)
 
 
+def run_mfma_probe(secs):
+    """Achievable bf16 MFMA rate under the board's power limit: the register-
+    only MFMA probe (mla_mfma_probe, 4096 waves of v_mfma_f32_32x32x16_bf16
+    chains) launched back to back for `secs` seconds while amd-smi samples
+    power and clocks; the rate is taken over the whole window (launch time
+    from the wall clock), after 2 s of warm-up launches."""
+    import torch
+    from mla_latent_kv_29_amd import _lib as L
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    g = torch.Generator(device="cpu").manual_seed(7)
+    ops = torch.randn(12 * 64 * 8, generator=g).to(torch.bfloat16).to(dev)
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    iters = 2000
+    ps = PowerSampler()
+    time.sleep(1.0)
+    t0 = time.time()
+    time.sleep(2.0)
+    idle = ps.mean(t0 + 0.3, time.time())
+    _, flops = L.mla_mfma_probe(ops, iters, sink)
+    t0 = time.time()
+    while time.time() - t0 < 2.0:
+        for _ in range(20):
+            L.mla_mfma_probe(ops, iters, sink)
+        torch.cuda.synchronize()
+    n, t0 = 0, time.time()
+    while time.time() - t0 < secs:
+        for _ in range(20):
+            L.mla_mfma_probe(ops, iters, sink)
+        n += 20
+        torch.cuda.synchronize()
+    t1 = time.time()
+    ps.stop = True
+    p, clk, ns = ps.mean(t0 + 0.3, t1)
+    launch_s = (t1 - t0) / n
+    print(json.dumps({"probe": "mfma", "flops_per_launch": flops, "launches": n, "launch_us": launch_s * 1e6,
+                      "tflops": flops / launch_s / 1e12, "frac_of_peak": flops / launch_s / MFMA_BF16_PEAK,
+                      "power_w": p, "gfx_mhz": clk, "samples": ns, "idle_power_w": idle[0],
+                      "idle_gfx_mhz": idle[1], "amd_smi": ps.ok}))
+
+
 def run_phase_power(workload, secs, phases, stream):
     """Each phase launched back to back for `secs` seconds (in batches of 100
     launches, then a synchronisation), idle before and after; power and clock
@@ -580,6 +621,9 @@ def main():
                          "prefill: projections, attention) back to back "
                          "for SECS seconds each while amd-smi samples board power and clocks; print one "
                          "JSON line of per-phase launch time, power, clock and energy per launch, and exit")
+    ap.add_argument("--mfma-probe", type=float, default=0.0, metavar="SECS",
+                    help="run the register-only bf16 MFMA probe back to back for SECS seconds while amd-smi "
+                         "samples power and clocks; print one JSON line of the achieved MFMA rate and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB three times (untimed), as the "
                          "reference for hardware byte counters")
@@ -590,6 +634,9 @@ def main():
               f"share at its real shape and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
+    if args.mfma_probe > 0:
+        run_mfma_probe(args.mfma_probe)
+        return
     if args.hbm_probe:
         run_hbm_probe(args)
         return

@@ -437,6 +437,19 @@ MLA_API int mla_check_metadata(const mla_dims* dims, const mla_cache* cache, con
  * figure.  Errors: MLA_ERR_NULL, MLA_ERR_DIMS (bytes % 16), MLA_ERR_ALIGN.  */
 MLA_API int mla_hbm_read_probe(const void* src, size_t bytes, int32_t* sink, void* stream);
 
+/* Measurement helper (no part of the decode maths): 4096 waves, each
+ * running iters x 32 v_mfma_f32_32x32x16_bf16 in four independent chains on
+ * operands held in registers, loaded once from ops (12 x 64 bf16x8 = 12 KiB
+ * of device memory, 16-byte aligned; finite values such as N(0,1) samples).
+ * No other memory traffic; sink (one device float) is practically never
+ * written.  *flops (host, may be NULL) receives the launch's floating-point
+ * operations (2 per multiply-add).  Run back to back, it gives the bf16 MFMA
+ * rate that the board's power limit allows, the ceiling that the MFMA-bound
+ * kernels are read against next to the data-sheet peak.  iters == 0 only
+ * sets *flops.  Errors: MLA_ERR_DIMS (iters < 0), MLA_ERR_NULL,
+ * MLA_ERR_ALIGN.                                                             */
+MLA_API int mla_mfma_probe(const void* ops, int32_t iters, float* sink, double* flops, void* stream);
+
 /* Static description of a status code.                                      */
 MLA_API const char* mla_status_str(int status);
 

@@ -21,7 +21,7 @@ EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
            "mla_fp8_quantize_weight_t", "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
            "mla_decode_step_noalloc", "mla_decode_fp8w_workspace_bytes", "mla_decode_fp8w",
-           "mla_decode_fp8w_query", "mla_combine_fp8w", "mla_check_metadata", "mla_hbm_read_probe", "mla_status_str",
+           "mla_decode_fp8w_query", "mla_combine_fp8w", "mla_check_metadata", "mla_hbm_read_probe", "mla_mfma_probe", "mla_status_str",
            "mla_last_hip_error", "mla_version")
 
 
@@ -84,6 +84,7 @@ def _load():
         "mla_combine_fp8w": (ctypes.c_int, [D, I32, I32, I32, P, SZ, P, P, P, P, P]),
         "mla_check_metadata": (ctypes.c_int, [D, C, P, I32, P, I32, P, P]),
         "mla_hbm_read_probe": (ctypes.c_int, [P, SZ, P, P]),
+        "mla_mfma_probe": (ctypes.c_int, [P, ctypes.c_int32, P, ctypes.POINTER(ctypes.c_double), P]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mla_version": (ctypes.c_char_p, []),
         "mla_last_hip_error": (ctypes.c_char_p, []),
@@ -315,6 +316,15 @@ def mla_decode_step_noalloc(dims, act_dtype, hq, batch, s_q, W_DQ, W_UQ, W_UK, W
     if check:
         _check("mla_decode_step_noalloc", st)
     return st
+
+
+def mla_mfma_probe(ops, iters, sink, stream=None, check=True):
+    """Returns (status, flops of the launch)."""
+    fl = ctypes.c_double(0.0)
+    st = _lib.mla_mfma_probe(_ptr(ops), int(iters), _ptr(sink), ctypes.byref(fl), _stream(stream))
+    if check:
+        _check("mla_mfma_probe", st)
+    return st, fl.value
 
 
 def mla_hbm_read_probe(src, nbytes, sink, stream=None, check=True):

@@ -538,6 +538,15 @@ int mla_hbm_read_probe(const void* src, size_t bytes, int32_t* sink, void* strea
   return hip_status(read_probe(src, bytes, sink, (hipStream_t)stream));
 }
 
+int mla_mfma_probe(const void* ops, int32_t iters, float* sink, double* flops, void* stream) {
+  if (iters < 0) return MLA_ERR_DIMS;
+  if (flops) *flops = mfma_probe_flops(iters);
+  if (iters == 0) return MLA_OK;
+  if (!ops || !sink) return MLA_ERR_NULL;
+  if (!aligned16(ops) || ((uintptr_t)sink & 3)) return MLA_ERR_ALIGN;
+  return hip_status(mfma_probe(ops, iters, sink, (hipStream_t)stream));
+}
+
 double mla_mtp_tokens_per_step(double acceptance, int32_t depth) {
   if (!(acceptance >= 0.0 && acceptance <= 1.0) || depth < 0 || depth > MAX_S_Q - 1) return NAN;
   // Horner form of 1 + a + ... + a^depth: the draft chain's survival probabilities

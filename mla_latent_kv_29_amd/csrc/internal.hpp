@@ -168,6 +168,8 @@ hipError_t noalloc_decode_step(DecodeArgs& a, CombineArgs& c);
 
 // Streaming read of `bytes` (a multiple of 16) from src (probe.hip).
 hipError_t read_probe(const void* src, size_t bytes, int* sink, hipStream_t st);
+hipError_t mfma_probe(const void* ops, int iters, float* sink, hipStream_t st);  // ops: 12 x 64 bf16x8
+double mfma_probe_flops(int iters);
 hipError_t check_metadata(int batch, int max_pages, int page_size, int num_pages, const int32_t* bt,
                           const int32_t* seqlens, int32_t* bad, hipStream_t st);
 

@@ -319,6 +319,19 @@ def test_decode_step_noalloc_argument_errors():
     assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
+def test_mfma_probe_argument_errors_and_flop_count():
+    # iters == 0 only reports the flop count; checks come before any launch
+    st, fl = L.mla_mfma_probe(None, 0, None, stream=0, check=False)
+    assert st == L.MLA_OK and fl == 0.0
+    assert L.mla_mfma_probe(FAKE, -1, FAKE, stream=0, check=False)[0] == L.MLA_ERR_DIMS
+    assert L.mla_mfma_probe(None, 5, FAKE, stream=0, check=False)[0] == L.MLA_ERR_NULL
+    assert L.mla_mfma_probe(FAKE, 5, None, stream=0, check=False)[0] == L.MLA_ERR_NULL
+    st, fl = L.mla_mfma_probe(FAKE + 8, 5, FAKE, stream=0, check=False)
+    assert st == L.MLA_ERR_ALIGN
+    # 4096 waves x iters x 32 MFMAs of 32 x 32 x 16 multiply-adds
+    assert fl == 4096 * 5 * 32 * (32 * 32 * 16 * 2)
+
+
 def test_hbm_read_probe_argument_errors():
     assert L.mla_hbm_read_probe(FAKE, 0, FAKE, stream=0, check=False) == L.MLA_OK
     assert L.mla_hbm_read_probe(None, 64, FAKE, stream=0, check=False) == L.MLA_ERR_NULL
