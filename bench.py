@@ -237,7 +237,7 @@ class PowerSampler:
 
 
 def run_mfma_probe(secs):
-    """Achievable bf16 MFMA rate under the board's power limit: the register-
+    """Achievable bf16 MFMA rate: the register-
     only MFMA probe (mla_mfma_probe, 4096 waves of v_mfma_f32_32x32x16_bf16
     chains) launched back to back for `secs` seconds while amd-smi samples
     power and clocks; the rate is taken over the whole window (launch time

@@ -438,7 +438,7 @@ MLA_API int mla_check_metadata(const mla_dims* dims, const mla_cache* cache, con
 MLA_API int mla_hbm_read_probe(const void* src, size_t bytes, int32_t* sink, void* stream);
 
 /* Measurement helper (no part of the decode maths): 4096 waves, each
- * running iters x 32 v_mfma_f32_32x32x16_bf16 in four independent chains on
+ * running iters x 32 v_mfma_f32_32x32x16_bf16 in eight independent chains on
  * operands held in registers, loaded once from ops (12 x 64 bf16x8 = 12 KiB
  * of device memory, 16-byte aligned; finite values such as N(0,1) samples).
  * No other memory traffic; sink (one device float) is practically never

@@ -531,7 +531,8 @@ struct EpiHeadMajor {
 // 128 x 128 (4 x 4 v_mfma_f32_32x32x16_bf16 accumulators, 256 AGPRs), 32-deep
 // k-steps through a ring of four 32 KiB LDS stages (X tile, then W tile:
 // 256 rows x 64 B each) filled by global_load_lds_dwordx4 from asm, three
-// k-steps ahead; one block per CU.  Row r of a tile keeps its 16-byte chunk
+// k-steps ahead; one block per CU.  The fragments of the next k-step are read
+// from LDS between the current step's MFMAs (two register sets).  Row r of a tile keeps its 16-byte chunk
 // c at slot c ^ ((r >> 2) & 3), so that the 16 lanes of each phase of a
 // fragment read (rows r .. r+15, one chunk) hit 16 different bank groups.
 // The 8 XCDs take contiguous ranges of tiles, ordered GB_GM row tiles x
@@ -630,35 +631,50 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(BigArgs a, Epi epi) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   const int nk = a.K / GB_BK;  // a multiple of 4
+  // Fragments of a k-step: X rows 32 i (+ 128 wm), W rows 32 j (+ 128 wn), the
+  // two 16-deep halves k16.  Step ks multiplies the fragments read during
+  // step ks-1 and reads those of ks+1 between its MFMAs, so no MFMA waits for
+  // an LDS read issued after the barrier.
+  bf16x8 fa[2][2][4], fb[2][2][4];  // [register set][k16][i or j]
+  auto read_frags = [&](auto stg_c, auto set_c, int k16, int i) {
+    constexpr int STG = decltype(stg_c)::value, SET = decltype(set_c)::value;
+    constexpr int H = STG >> 1;
+    constexpr uint32_t SO = (STG & 1) * GB_STAGE;
+    fa[SET][k16][i] = *(const lbf16x8*)(fx[H][k16] + SO + 2048 * i);
+    fb[SET][k16][i] = *(const lbf16x8*)(fw[H][k16] + SO + 2048 * i);
+  };
   issue(0, 0);
   issue(1, 1);
   issue(2, 2);
+  issue(3, 3);
+  wait_vmcnt<24>();  // this wave's copies of k-step 0 landed
+  ring_barrier();
+#pragma unroll
+  for (int k16 = 0; k16 < 2; ++k16)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, k16, i);
+  // Step ks (stage ks & 3, register set ks & 1): after the barrier, every
+  // wave's copies of k-step ks+1 have landed and every wave has read k-step
+  // ks's fragments, so the stage of ks takes k-step ks+4; past the last
+  // k-step a repeat of it (never used), so that the loop body has no branch:
+  // a branch there makes the compiler move the accumulators between AGPRs
+  // and VGPRs.  The fragments read for ks+1 at the last step are never used.
   auto step = [&](auto stg_c, int ks) {
     constexpr int STG = decltype(stg_c)::value;
-    wait_vmcnt<16>();  // this wave's copies of k-step ks landed (two later k-steps may be in flight)
-    ring_barrier();    // every wave's copies of ks landed; every wave is done with ks - 1
-    // k-step ks + 3 into the stage of ks - 1; past the last k-step a repeat of
-    // it (never read), so that the loop body has no branch: a branch there
-    // makes the compiler move the accumulators between AGPRs and VGPRs
-    issue(min(ks + 3, nk - 1), (STG + 3) & 3);
-    constexpr int H = STG >> 1;
-    constexpr uint32_t SO = (STG & 1) * GB_STAGE;
-    bf16x8 xa[2][4], wa[2][4];
-#pragma unroll
-    for (int k16 = 0; k16 < 2; ++k16)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[k16][i] = *(const lbf16x8*)(fx[H][k16] + SO + 2048 * i);
-        wa[k16][i] = *(const lbf16x8*)(fw[H][k16] + SO + 2048 * i);
-      }
+    constexpr int SET = STG & 1;
+    wait_vmcnt<16>();  // this wave's copies of ks+1 landed (ks+2, ks+3 may be in flight)
+    ring_barrier();
+    issue(min(ks + 4, nk - 1), STG);
 #pragma unroll
     for (int k16 = 0; k16 < 2; ++k16) {
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[k16][i], wa[k16][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET][k16][i], fb[SET][k16][j], acc[i][j], 0, 0, 0);
+        read_frags(std::integral_constant<int, (STG + 1) & 3>{}, std::integral_constant<int, 1 - SET>{}, k16, i);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };

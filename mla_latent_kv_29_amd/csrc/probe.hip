@@ -3,12 +3,14 @@
 //    kernels' byte roofline is read against beside the 8 TB/s of the data
 //    sheet: a plain stream of 16-byte loads over a buffer, 2048 blocks of 256
 //    threads in a grid-stride loop, nothing written.
-//  * Achievable bf16 MFMA rate under the board's power limit: every wave
-//    runs four independent chains of v_mfma_f32_32x32x16_bf16 on operands
-//    held in registers (eight A and four B fragments of random values, so
-//    that the inputs change from one MFMA to the next as in a real kernel),
-//    with no memory traffic at all.  It is the ceiling that an MFMA-bound
-//    kernel can reach once the clock drops to hold the power limit.
+//  * Achievable bf16 MFMA rate: every wave runs eight independent chains of
+//    v_mfma_f32_32x32x16_bf16 on operands held in registers (eight A and
+//    four B fragments of random values, so that the inputs change from one
+//    MFMA to the next as in a real kernel), with no memory traffic at all.
+//    It is the ceiling that an MFMA-bound kernel can reach at the clock the
+//    part holds under dense MFMA work.  (Four chains at four waves a SIMD
+//    ran about 15% slower than this form; eight chains, or one wave a SIMD,
+//    reach the same rate.)
 #include "internal.hpp"
 
 namespace mla {
@@ -25,7 +27,7 @@ __global__ __launch_bounds__(256) void k_read_probe(const i32x4* __restrict__ p,
   if (r == 0x5bd1e995) sink[0] = r;  // keeps the loads; practically never stores
 }
 
-constexpr int MP_BLOCKS = 1024, MP_A = 8, MP_B = 4;  // 4096 waves: four on each SIMD
+constexpr int MP_BLOCKS = 1024, MP_A = 8, MP_B = 4, MP_C = 8;  // 4096 waves, eight accumulator chains
 
 __global__ __launch_bounds__(256) void k_mfma_probe(const bf16x8* __restrict__ ops, int iters, float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
@@ -34,18 +36,20 @@ __global__ __launch_bounds__(256) void k_mfma_probe(const bf16x8* __restrict__ o
   for (int k = 0; k < MP_A; ++k) a[k] = ops[64 * k + lane];
 #pragma unroll
   for (int j = 0; j < MP_B; ++j) b[j] = ops[64 * (MP_A + j) + lane];
-  f32x16 c[MP_B];
+  f32x16 c[MP_C];
 #pragma unroll
-  for (int j = 0; j < MP_B; ++j) c[j] = f32x16{};
+  for (int j = 0; j < MP_C; ++j) c[j] = f32x16{};
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
     for (int k = 0; k < MP_A; ++k)
 #pragma unroll
-      for (int j = 0; j < MP_B; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[j], c[j], 0, 0, 0);
+      for (int j = 0; j < MP_B; ++j) {
+        c[(MP_B * k + j) % MP_C] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[j], c[(MP_B * k + j) % MP_C], 0, 0, 0);
+      }
   }
   float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < MP_B; ++j) s += c[j][lane & 15];
+  for (int j = 0; j < MP_C; ++j) s += c[j][lane & 15];
   if (s == 1234.5f) sink[0] = s;  // keeps the products; practically never stores
 }
 
