@@ -659,12 +659,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(BigArgs a, Epi epi) {
   // k-step a repeat of it (never used), so that the loop body has no branch:
   // a branch there makes the compiler move the accumulators between AGPRs
   // and VGPRs.  The fragments read for ks+1 at the last step are never used.
+  // The step's eight copies are spread over its MFMA groups, one after each
+  // group of four: a wave whose copy waits for the address unit issues
+  // nothing else meanwhile, so copies issued back to back after the barrier
+  // left the matrix unit idle.
   auto step = [&](auto stg_c, int ks) {
     constexpr int STG = decltype(stg_c)::value;
     constexpr int SET = STG & 1;
     wait_vmcnt<16>();  // this wave's copies of ks+1 landed (ks+2, ks+3 may be in flight)
     ring_barrier();
-    issue(min(ks + 4, nk - 1), STG);
+    const int kc = min(ks + 4, nk - 1);
+    const uint8_t* xk = xb + kc * 64;
+    const uint8_t* wk = wb + kc * 64;
+    const uint32_t d = lds + STG * GB_STAGE + 4096 * wave;
 #pragma unroll
     for (int k16 = 0; k16 < 2; ++k16) {
 #pragma unroll
@@ -674,6 +681,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(BigArgs a, Epi epi) {
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET][k16][i], fb[SET][k16][j], acc[i][j], 0, 0, 0);
         read_frags(std::integral_constant<int, (STG + 1) & 3>{}, std::integral_constant<int, 1 - SET>{}, k16, i);
+        // copy n = i of the X tile (k16 = 0) or of the W tile (k16 = 1)
+        if (k16 == 0) gb_dma(xk, xo[i], d + 1024 * i);
+        else gb_dma(wk, wo[i], d + GB_TILE + 1024 * i);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
