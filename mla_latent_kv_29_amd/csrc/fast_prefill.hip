@@ -370,9 +370,31 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
     constexpr int P = decltype(par)::value;
     wait_vmcnt<0>();  // K tile i+1 and V tile i (issued one step earlier)
     ring_barrier();
-    if (i + 2 < ntiles) issue_k(kc_h, a.kr, start, len, i + 2, ring + P * K_BYTES, wave, lane, to);
-    if (i + 1 < ntiles) issue_v(vc_h, start, len, i + 1, ring + V_OFF + (1 - P) * V_BYTES, wave, lane, to);
-    if (i * BKT > wq0 + 31) return;  // every key of tile i is after every query of this wave
+    const uint32_t kbuf = ring + P * K_BYTES, vbuf = ring + V_OFF + (1 - P) * V_BYTES;
+    const bool act = i * BKT <= wq0 + 31;  // some key of tile i is visible to some query of this wave
+    // K tile i+2 and V tile i+1: a tile inside the sequence is copied between
+    // the score MFMAs below (a wave whose copy waits for the address unit
+    // issues nothing else, so copies issued back to back here would leave the
+    // matrix unit idle); a clamped last tile, or a wave with no tile i, copies
+    // here.
+    const bool kin = i + 2 < ntiles && (i + 3) * BKT <= len, vin = i + 1 < ntiles && (i + 2) * BKT <= len;
+    if (i + 2 < ntiles && (!kin || !act)) issue_k(kc_h, a.kr, start, len, i + 2, kbuf, wave, lane, to);
+    if (i + 1 < ntiles && (!vin || !act)) issue_v(vc_h, start, len, i + 1, vbuf, wave, lane, to);
+    if (!act) return;  // every key of tile i is after every query of this wave
+    const uint8_t* kcb = (const uint8_t*)kc_h + (size_t)(start + (i + 2) * BKT + 4 * wave) * PDH * 2;
+    const uint8_t* krb = (const uint8_t*)a.kr + (size_t)(start + (i + 2) * BKT + 8 * wave) * PDR * 2;
+    const uint8_t* vcb = (const uint8_t*)vc_h + (size_t)(start + (i + 1) * BKT + 4 * wave) * PDH * 2;
+    // copy c (0-5: K tile, 6-9: V tile) of this wave, the offsets of issue_k / issue_v's
+    // in-sequence case
+    auto copy = [&](int c) {
+      if (c < 4) {
+        if (kin) pa_dma(kcb + 16 * c * PDH * 2, to.kc, kbuf + 1024 * wave + 4096 * c);
+      } else if (c < 6) {
+        if (kin) pa_dma(krb + 32 * (c - 4) * PDR * 2, to.kr, kbuf + KC_BYTES + 1024 * wave + 4096 * (c - 4));
+      } else {
+        if (vin) pa_dma(vcb + 16 * (c - 6) * PDH * 2, to.v, vbuf + 1024 * wave + 4096 * (c - 6));
+      }
+    };
     // One code path for every step: when the wave has no tile i+1 (its keys
     // are all after the wave's queries, or past the block's last tile), the
     // score MFMAs still run on whatever K slot 1-P holds and their results
@@ -399,6 +421,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(PaArgs a) {
           pb[g] = pack(sc, g);
           asm volatile("" : "+v"(pb[g]));
         }
+        if ((t & 1) && t < 20) copy(t >> 1);  // copies 0-9 after MFMAs 1, 3, .., 19
         __builtin_amdgcn_sched_barrier(0);
       }
     }
