@@ -277,6 +277,52 @@ def run_mfma_probe(secs):
                       "idle_gfx_mhz": idle[1], "amd_smi": ps.ok}))
 
 
+def measure_decode_append(sess, W, hq, lengths, s_q, dims, n_cached, build_s, reps=50):
+    """The append of a decode step (mla_cache_append of the batch's B * s_q
+    newest tokens, one call; here the last s_q tokens of every sequence are
+    written again from their own hidden states), timed with HIP events on
+    the launch stream, median of `reps`, against its HBM bound (the 576 x
+    d_model weight rows, the h rows and the written rows at 8 TB/s); and the
+    cache build's rate (whole-sequence calls, wall clock) against its MFMA
+    bound (2 x 576 x d_model flops a token at 2.5 PF/s).  Each timed append
+    is queued behind a 512 MiB fill, so that the start event fires only when
+    the append's launch is already in the queue (on an idle stream the
+    interval would hold the host's launch overhead); the fill also leaves
+    the weights out of the caches, as a decode step finds them."""
+    import numpy as np
+    import torch
+    dev = hq.device
+    n = hq.shape[0]
+    seq_id = torch.repeat_interleave(torch.arange(len(lengths), dtype=torch.int32), s_q).to(dev)
+    pos = torch.cat([torch.arange(int(Lb) - s_q, int(Lb), dtype=torch.int32) for Lb in lengths]).to(dev)
+    stream = torch.cuda.current_stream()
+    pad = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    for _ in range(5):
+        sess.append_rows(hq, seq_id, pos, W)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pad.zero_()
+        e0.record(stream)
+        sess.append_rows(hq, seq_id, pos, W)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del pad
+    t = float(np.median(ts))
+    d = dims["d_c"] + dims["d_rope"]
+    row_bytes = sess.page_bytes // dims["page_size"]
+    byts = d * dims["d_model"] * 2 + n * dims["d_model"] * 2 + n * row_bytes
+    t_bound = byts / HBM_PEAK
+    flops_tok = 2.0 * d * dims["d_model"]
+    return {"decode_tokens": n, "decode_us": t * 1e6, "decode_bound_us": t_bound * 1e6,
+            "decode_frac": t_bound / t, "decode_bytes": byts,
+            "kernel": ("k_append_rows" if (dims["d_c"], dims["d_rope"]) == (512, 64) and hq.dtype == torch.bfloat16
+                       and dims["d_model"] % 256 == 0 and n <= 2048 else "other") + " (mla_cache_append)",
+            "build_tokens_per_s": n_cached / build_s,
+            "build_bound_tokens_per_s": MFMA_BF16_PEAK / flops_tok}
+
+
 def run_phase_power(workload, secs, phases, stream):
     """Each phase launched back to back for `secs` seconds (in batches of 100
     launches, then a synchronisation), idle before and after; power and clock
@@ -677,6 +723,7 @@ def main():
     s_q = spec["s_q"]
     hq = torch.cat([gen_h(b, int(Lb) - s_q, int(Lb)) for b, Lb in enumerate(lengths)], 0).contiguous()
     tau = 1.0 / math.sqrt(dims["d_head"] + dims["d_rope"])
+    append = measure_decode_append(sess, W, hq, lengths, s_q, dims, int(sum(int(x) for x in lengths)), build_s)
 
     # ---- rotation sets: same values in distinct buffers
     sets = [(sess.pages, W)]
@@ -800,6 +847,7 @@ def main():
         "step_ms_sampled": {"p10": float(np.percentile(s_ms, 10)), "p50": float(np.percentile(s_ms, 50)),
                             "p90": float(np.percentile(s_ms, 90)), "mean": float(np.mean(s_ms)), "n": len(s_ms)},
         "cache_build_s": build_s,
+        "append": append,
     }
     if s_q > 1:
         # the verify step checks s_q - 1 drafts; expected emitted tokens at the

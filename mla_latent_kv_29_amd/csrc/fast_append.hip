@@ -173,11 +173,175 @@ __global__ __launch_bounds__(256) void k_append_v3(int n_tok, int d_model, float
   }
 }
 
+// ------------------------------------------------------------ few tokens
+// The append of a decode step (one or a few new tokens per sequence): a block
+// of k_append_v3 covers 64 tokens and streams the whole 8.26 MB of
+// [W^DKV; W^KR], so a batch of 64 new tokens would be one block on one CU
+// (372 us for 64 tokens, against 70 us here with 20 blocks; a CU streams
+// these weight rows at about 30 GB/s, so the time is the bytes per block).
+// Here a block takes one 128-channel tile of the outputs (four latent tiles,
+// then the 64 RoPE channels) for 16 tokens, and its eight waves split
+// d_model, each streaming its share of the tile's weight rows straight into
+// MFMA operands (v_mfma_f32_16x16x32_bf16, A = h rows, B^T = weight rows,
+// several k-steps of loads in flight); the eight partial tiles meet in LDS
+// (summed in a fixed order) and the same epilogue arithmetic as above
+// finishes each token row: RoPE on the RoPE tile, bf16 or E4M3 with the
+// tile's scale, the scatter into the token's page slot.
+constexpr int AR_TOK = 16, AR_COLS = 128, AR_NW = 8, AR_PD = 4;
+constexpr int AR_TILES = DC / AR_COLS + 1;                    // 4 latent tiles + the RoPE tile
+constexpr int AR_LDS = AR_NW * AR_TOK * AR_COLS * 4;          // 64 KiB of partial tiles
+constexpr int APPEND_ROWS_MAX = 2048;                         // tokens a call up to which this path is taken
+
+template <int NSUB>  // 16-column sub-tiles: 8 (latent tile) or 4 (RoPE tile)
+__device__ __forceinline__ void ar_tile(int n_tok, int d_model, int tg, const bf16_t* __restrict__ h,
+                                        const bf16_t* __restrict__ W, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int tok = min(tg * AR_TOK + r16, n_tok - 1);  // rows past the last token: computed, never stored
+  const int kw = d_model / AR_NW, nks = kw / 32;
+  const bf16_t* hp = h + (size_t)tok * d_model + wave * kw + 8 * kq;
+  const bf16_t* wp = W + (size_t)r16 * d_model + wave * kw + 8 * kq;
+  f32x4 acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{};
+  bf16x8 fa[AR_PD], fb[AR_PD][NSUB];
+  // nks is a multiple of AR_PD (the launcher checks d_model).  The loads of a
+  // k-step go out in one fixed order (its weight rows s = 0.., then its h
+  // rows), in the prologue as in the loop, each pinned by a scheduling
+  // barrier: the compiler's wait counts then see the same order on both
+  // edges into the loop and wait, before each MFMA, only for the loads of
+  // its own k-step (mismatched orders made it wait for nearly every load in
+  // flight).  The steady state has no branch, for the same reason.
+#pragma unroll
+  for (int i = 0; i < AR_PD; ++i) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      fb[i][s] = *(const bf16x8*)(wp + (size_t)16 * s * d_model + 32 * i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fa[i] = *(const bf16x8*)(hp + 32 * i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int ks = 0; ks < nks - AR_PD; ks += AR_PD) {
+#pragma unroll
+    for (int i = 0; i < AR_PD; ++i) {
+      const int kn = ks + i + AR_PD;  // the k-step that takes this slot next
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[i][s], acc[s], 0, 0, 0);
+        fb[i][s] = *(const bf16x8*)(wp + (size_t)16 * s * d_model + 32 * kn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      fa[i] = *(const bf16x8*)(hp + 32 * kn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < AR_PD; ++i)
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[i][s], acc[s], 0, 0, 0);
+  // C lane layout: tokens 4 kq + r of column 16 s + r16
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * AR_TOK + 4 * kq + r) * AR_COLS + 16 * s + r16] = acc[s][r];
+}
+
+__global__ __launch_bounds__(AR_NW * 64) void k_append_rows(int n_tok, int d_model, float theta,
+                                                           const bf16_t* __restrict__ h,
+                                                           const int32_t* __restrict__ seq_id,
+                                                           const int32_t* __restrict__ pos,
+                                                           const bf16_t* __restrict__ W_DKV,
+                                                           const bf16_t* __restrict__ W_KR, uint8_t* __restrict__ pages,
+                                                           CacheGeom g, const int32_t* __restrict__ bt, int max_pages) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  float* red = (float*)lds;  // [AR_NW][AR_TOK][AR_COLS]
+  const int ct = blockIdx.x % AR_TILES, tg = blockIdx.x / AR_TILES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncols = ct < AR_TILES - 1 ? AR_COLS : DR;
+  if (ct < AR_TILES - 1) ar_tile<AR_COLS / 16>(n_tok, d_model, tg, h, W_DKV + (size_t)AR_COLS * ct * d_model, red);
+  else ar_tile<DR / 16>(n_tok, d_model, tg, h, W_KR, red);
+  __syncthreads();
+  // the tile: the eight partials summed in wave order into red[0]
+  for (int i = tid; i < AR_TOK * ncols; i += AR_NW * 64) {
+    const int t = i / ncols, c = i % ncols;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < AR_NW; ++w) v += red[(w * AR_TOK + t) * AR_COLS + c];
+    red[t * AR_COLS + c] = v;
+  }
+  __syncthreads();
+  // lane: token 4 wave + lane / 16 (waves 0-3), eight channels 8 (lane % 16)
+  if (wave >= 4) return;
+  const int tl = 4 * wave + (lane >> 4), c8 = lane & 15;
+  const int t = tg * AR_TOK + tl;
+  const bool live = t < n_tok && 8 * c8 < ncols;
+  int p = 0;
+  uint8_t* pg = pages;
+  int slot = 0;
+  if (t < n_tok) {
+    p = pos[t];
+    pg = pages + (size_t)bt[(long)seq_id[t] * max_pages + p / g.page_size] * g.page_bytes;
+    slot = p % g.page_size;
+  }
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = red[tl * AR_COLS + 8 * c8 + e];
+  if (ct == AR_TILES - 1) {
+    if (!live) return;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float cs, sn;
+      rope_cs(p, (8 * c8 + e) >> 1, DR, theta, &cs, &sn);
+      const float x0 = v[e], x1 = v[e + 1];
+      v[e] = x0 * cs - x1 * sn;
+      v[e + 1] = x0 * sn + x1 * cs;
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16_t)v[e];
+    if (g.dtype == MLA_BF16) *(bf16x8*)(pg + bf16_page_off(slot, DC + 8 * c8, g.page_size)) = o;
+    else *(bf16x8*)(pg + g.fp8_rope_off + fp8_rope_elem_off(slot, 8 * c8, g.page_size)) = o;
+    return;
+  }
+  const int ch = AR_COLS * ct + 8 * c8;
+  if (g.dtype == MLA_BF16) {
+    if (!live) return;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16_t)v[e];
+    *(bf16x8*)(pg + bf16_page_off(slot, ch, g.page_size)) = o;
+    return;
+  }
+  // E4M3: the 16 lanes of a token hold its 1 x 128 tile
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  if (!live) return;
+  const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3(v[e] / sc) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hi |= (uint32_t)f32_to_e4m3(v[4 + e] / sc) << (8 * e);
+  *(uint2*)(pg + fp8_code_off(slot, ch, g.page_size)) = make_uint2(lo, hi);
+  if (c8 == 0) ((float*)(pg + g.fp8_scale_off))[slot * (DC / 128) + ct] = sc;
+}
+
 }  // namespace
 
 bool fast_append_shape(const mla_dims& d) { return d.d_c == DC && d.d_rope == DR && d.d_model % 32 == 0; }
 
 hipError_t fast_append(const AppendArgs& a) {
+  if (a.n_tok <= APPEND_ROWS_MAX && a.d.d_model % (32 * AR_NW * AR_PD) == 0) {
+    MLA_TRY(lds_limit((const void*)k_append_rows, AR_LDS));
+    const int blocks = AR_TILES * ((a.n_tok + AR_TOK - 1) / AR_TOK);
+    return launch(&k_append_rows, dim3(blocks), dim3(AR_NW * 64), AR_LDS, a.stream, a.n_tok, a.d.d_model,
+                  a.d.rope_theta, (const bf16_t*)a.h, a.seq_id, a.pos, (const bf16_t*)a.W_DKV,
+                  (const bf16_t*)a.W_KR, a.pages, a.g, a.block_table, a.max_pages);
+  }
   MLA_TRY(lds_limit((const void*)k_append_v3, APPEND_LDS));
   const int blocks = (a.n_tok + TOK - 1) / TOK;
   MLA_TRY(launch(&k_append_v3, dim3(blocks), dim3(256), APPEND_LDS, a.stream, a.n_tok, a.d.d_model,

@@ -118,15 +118,17 @@ def test_fp8_bytes_past_the_end_are_ignored(splits):
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
 def test_mfma_append_epilogue_bit_exact(cache):
-    """The MFMA append (the path that builds every benchmarked cache), pinned
-    bit for bit: with W^DKV = [I_512 | 0] and a W^KR that picks columns
-    512..575, every fp32 accumulation holds one exact product, so c^KV equals
-    the first 512 channels of h exactly.  Its E4M3 codes and fp32 scales must
-    then be the oracle's tile quantisation of those values bit for bit (fp8),
-    or the values themselves (bf16); k^R, rotated in fp32 and rounded to bf16,
-    within one bf16 step of the oracle's float64 rotation.  Tiles are scaled
-    by powers of two from 2^-20 to 2^12 and one tile is all zero, so the
-    scale, the saturation edge and the zero-tile rule all occur."""
+    """Both MFMA appends pinned bit for bit: the 64-token blocks that build
+    long sequences (the 2100-token call) and the few-token path (calls of at
+    most 2048 tokens: the 131-token call).  With W^DKV = [I_512 | 0] and a
+    W^KR that picks columns 512..575, every fp32 accumulation holds one exact
+    product (in any summation order), so c^KV equals the first 512 channels
+    of h exactly.  Its E4M3 codes and fp32 scales must then be the oracle's
+    tile quantisation of those values bit for bit (fp8), or the values
+    themselves (bf16); k^R, rotated in fp32 and rounded to bf16, within one
+    bf16 step of the oracle's float64 rotation.  Tiles are scaled by powers
+    of two from 2^-20 to 2^12 and one tile is all zero, so the scale, the
+    saturation edge and the zero-tile rule all occur."""
     from mla_latent_kv_29_amd.session import DecodeSession
     dims = V3
     d_model, dc, dr = dims["d_model"], dims["d_c"], dims["d_rope"]
@@ -135,7 +137,7 @@ def test_mfma_append_epilogue_bit_exact(cache):
     W_KR = torch.zeros((dr, d_model), dtype=torch.bfloat16, device=DEV)
     W_KR[torch.arange(dr), dc + torch.arange(dr)] = 1.0
     W = {"W_DKV": W_DKV, "W_KR": W_KR}
-    lengths = np.array([200, 131])
+    lengths = np.array([2100, 131])
     bt, pool = inputs.block_table(lengths, dims["page_size"], "shuffled", 0, 9)
     sess = DecodeSession(dims, "bf16", cache, lengths, bt, pool, 1, 0, DEV)
     g = torch.Generator(device="cpu").manual_seed(1234)
@@ -167,3 +169,45 @@ def test_mfma_append_epilogue_bit_exact(cache):
         # one bf16 step: 2^-7 relative to the value's binade
         step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(kr_ref), 1e-30))) - 7)
         assert np.all(np.abs(kr - kr_ref) <= step)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_decode_step_append_one_token_per_sequence(cache):
+    """The append of a decode step: one call that writes the newest token of
+    each of 37 sequences (ragged lengths, shuffled pages; 37 is not a multiple
+    of the 16-token groups), after the earlier tokens went in whole-sequence
+    calls.  Every row must match the oracle's latents as a whole-sequence
+    append does: bf16 rows within 1e-2 of the largest value, E4M3 codes within
+    one E4M3 step of the exact latent, k^R within 2e-2."""
+    from mla_latent_kv_29_amd.session import DecodeSession
+    dims = V3
+    rng = np.random.default_rng(17)
+    lengths = rng.integers(1, 300, size=37)
+    bt, pool = inputs.block_table(lengths, dims["page_size"], "shuffled", 0, 11)
+    W = inputs.weights(dims, 0.006, torch.bfloat16, DEV, 0, 11)
+    sess = DecodeSession(dims, "bf16", cache, lengths, bt, pool, 1, 0, DEV)
+    hs = [inputs.hidden(dims, b, 0, int(Lb), torch.bfloat16, DEV, 0, 11) for b, Lb in enumerate(lengths)]
+    for b, Lb in enumerate(lengths):
+        if Lb > 1:
+            sess.append(hs[b][:Lb - 1], b, 0, W)
+    last = torch.stack([hs[b][int(Lb) - 1] for b, Lb in enumerate(lengths)]).contiguous()
+    seq_id = torch.arange(len(lengths), dtype=torch.int32, device=DEV)
+    pos = torch.tensor(lengths - 1, dtype=torch.int32, device=DEV)
+    sess.append_rows(last, seq_id, pos, W)
+    torch.cuda.synchronize()
+    Wn = {k: to_np(v) for k, v in W.items()}
+    for b, Lb in enumerate(lengths):
+        Lb = int(Lb)
+        c, kr = oracle.kv_latents(to_np(hs[b]), Wn["W_DKV"], Wn["W_KR"], np.arange(Lb), V3["rope_theta"])
+        npg = (Lb + 63) // 64
+        if cache == "bf16":
+            rows = read_bf16_rows(sess.pages, bt[b, :npg], V3)[:Lb]
+            ref = np.concatenate([c, kr], 1)
+            assert max_abs(rows, ref) <= 1e-2 * np.abs(ref).max(), b
+        else:
+            codes, scales, rope = read_fp8_rows(sess.pages, bt[b, :npg], V3)
+            deq = oracle.dequantize_tiles(codes[:Lb], scales[:Lb])
+            g = np.abs(c).reshape(Lb, 4, 128)
+            step = np.maximum(g * 2.0 ** -3, 2.0 ** -9 * scales[:Lb, :, None])
+            assert np.all(np.abs(deq - c).reshape(Lb, 4, 128) <= step), b
+            assert max_abs(rope[:Lb], kr) <= 2e-2 * np.abs(kr).max(), b
