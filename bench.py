@@ -278,7 +278,8 @@ def run_mfma_probe(secs):
 
 
 def measure_decode_append(sess, W, hq, lengths, s_q, dims, n_cached, build_s, reps=50):
-    """The append of a decode step (mla_cache_append of the batch's B * s_q
+    """The append of a decode step (mla_cache_append, and mla_cache_append_ws
+    where it applies, of the batch's B * s_q
     newest tokens, one call; here the last s_q tokens of every sequence are
     written again from their own hidden states), timed with HIP events on
     the launch stream, median of `reps`, against its HBM bound (the 576 x
@@ -297,19 +298,26 @@ def measure_decode_append(sess, W, hq, lengths, s_q, dims, n_cached, build_s, re
     pos = torch.cat([torch.arange(int(Lb) - s_q, int(Lb), dtype=torch.int32) for Lb in lengths]).to(dev)
     stream = torch.cuda.current_stream()
     pad = torch.empty(1 << 27, dtype=torch.float32, device=dev)
-    for _ in range(5):
-        sess.append_rows(hq, seq_id, pos, W)
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        pad.zero_()
-        e0.record(stream)
-        sess.append_rows(hq, seq_id, pos, W)
-        e1.record(stream)
-        e1.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3)
+
+    def timed(ws):
+        for _ in range(5):
+            sess.append_rows(hq, seq_id, pos, W, ws=ws)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            pad.zero_()
+            e0.record(stream)
+            sess.append_rows(hq, seq_id, pos, W, ws=ws)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    t = timed(False)
+    from mla_latent_kv_29_amd import _lib as L
+    ws_bytes = L.mla_append_workspace_bytes(sess.cdims, sess.act, n)
+    t_ws = timed(True) if ws_bytes else None
     del pad
-    t = float(np.median(ts))
     d = dims["d_c"] + dims["d_rope"]
     row_bytes = sess.page_bytes // dims["page_size"]
     byts = d * dims["d_model"] * 2 + n * dims["d_model"] * 2 + n * row_bytes
@@ -317,8 +325,10 @@ def measure_decode_append(sess, W, hq, lengths, s_q, dims, n_cached, build_s, re
     flops_tok = 2.0 * d * dims["d_model"]
     return {"decode_tokens": n, "decode_us": t * 1e6, "decode_bound_us": t_bound * 1e6,
             "decode_frac": t_bound / t, "decode_bytes": byts,
+            "decode_ws_us": t_ws * 1e6 if t_ws else None, "decode_ws_frac": t_bound / t_ws if t_ws else None,
+            "ws_kernels": "k_skinny (k-group partials) + k_append_reduce (mla_cache_append_ws)" if t_ws else None,
             "kernel": ("k_append_rows" if (dims["d_c"], dims["d_rope"]) == (512, 64) and hq.dtype == torch.bfloat16
-                       and dims["d_model"] % 256 == 0 and n <= 2048 else "other") + " (mla_cache_append)",
+                       and dims["d_model"] % 256 == 0 and n <= 4096 else "other") + " (mla_cache_append)",
             "build_tokens_per_s": n_cached / build_s,
             "build_bound_tokens_per_s": MFMA_BF16_PEAK / flops_tok}
 

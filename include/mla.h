@@ -130,6 +130,28 @@ MLA_API int mla_cache_append(const mla_dims* dims, int32_t act_dtype, const void
                      const int32_t* block_table, int32_t max_pages,
                      void* stream);
 
+/* The append of a decode step with a workspace: the same tokens, the same
+ * rows and the same error behaviour as mla_cache_append (same citation), the
+ * latent rows' matrix product split over d_model into fp32 partial sums in
+ * ws, so that a few tokens spread over the whole GPU; the rows then equal
+ * mla_cache_append's up to the fp32 summation order.
+ *   ws  device workspace of at least mla_append_workspace_bytes(dims,
+ *       act_dtype, n_tok) bytes, 16-byte aligned, caller-owned; its contents
+ *       are overwritten.  May be NULL when that size is 0: then this is
+ *       mla_cache_append.
+ * mla_append_workspace_bytes is non-zero for BF16 activations at the
+ * DeepSeek-V3 latent shape (d_c 512, d_rope 64, d_model a multiple of 896)
+ * and 1..64 tokens with a BF16 or FP8 cache; 0 otherwise (and for invalid
+ * dims).  Extra errors: MLA_ERR_NULL / MLA_ERR_ALIGN for ws, and
+ * MLA_ERR_WORKSPACE when ws_bytes is below the required size; nothing is
+ * enqueued on an error other than MLA_ERR_HIP.                              */
+MLA_API size_t mla_append_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t n_tok);
+MLA_API int mla_cache_append_ws(const mla_dims* dims, int32_t act_dtype, const void* h,
+                        int32_t n_tok, const int32_t* seq_id, const int32_t* pos,
+                        const void* W_DKV, const void* W_KR, const mla_cache* cache,
+                        const int32_t* block_table, int32_t max_pages, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* Direct cache write: stores given latent rows c_kv [n_tok, d_c] and already
  * rotated k_rope [n_tok, d_rope] (dtype act_dtype, F32 or BF16) at
  * (seq_id[r], pos[r]), converting or quantising exactly as mla_cache_append

@@ -15,7 +15,7 @@ MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE = 0, -1, -2, -3
 MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = -4, -5, -6, -7
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 
-EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits", "mla_decode_splits",
+EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_append_workspace_bytes", "mla_cache_append_ws", "mla_cache_write", "mla_default_splits", "mla_decode_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
@@ -58,6 +58,8 @@ def _load():
     sig = {
         "mla_page_bytes": (SZ, [D, I32]),
         "mla_cache_append": (ctypes.c_int, [D, I32, P, I32, P, P, P, P, C, P, I32, P]),
+        "mla_append_workspace_bytes": (SZ, [D, I32, I32]),
+        "mla_cache_append_ws": (ctypes.c_int, [D, I32, P, I32, P, P, P, P, C, P, I32, P, SZ, P]),
         "mla_cache_write": (ctypes.c_int, [D, I32, P, P, I32, P, P, C, P, I32, P]),
         "mla_default_splits": (I32, [D, I32, I32, I32]),
         "mla_decode_splits": (I32, [D, I32, I32, I32, I32]),
@@ -142,6 +144,20 @@ def _check(fn, st):
 
 def mla_page_bytes(dims, cache_dtype):
     return int(_lib.mla_page_bytes(ctypes.byref(dims), int(cache_dtype)))
+
+
+def mla_append_workspace_bytes(dims, act, n_tok):
+    return int(_lib.mla_append_workspace_bytes(ctypes.byref(dims), int(act), int(n_tok)))
+
+
+def mla_cache_append_ws(dims, act_dtype, h, n_tok, seq_id, pos, W_DKV, W_KR, cache, block_table, max_pages, ws,
+                        ws_bytes, stream=None, check=True):
+    st = _lib.mla_cache_append_ws(ctypes.byref(dims), int(act_dtype), _ptr(h), int(n_tok), _ptr(seq_id), _ptr(pos),
+                                  _ptr(W_DKV), _ptr(W_KR), ctypes.byref(cache), _ptr(block_table), int(max_pages),
+                                  _ptr(ws), int(ws_bytes), _stream(stream))
+    if check:
+        _check("mla_cache_append_ws", st)
+    return st
 
 
 def mla_output_project_workspace_bytes(dims, act, rows):

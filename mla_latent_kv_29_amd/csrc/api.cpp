@@ -107,9 +107,16 @@ int resolve_splits(const mla_dims* d, int32_t batch, int32_t s_q, int32_t max_pa
   return MLA_OK;
 }
 
+// fp32 partial bytes of the workspace append, or 0 where it does not apply
+size_t append_ws_bytes(const mla_dims& d, int act, int n_tok) {
+  if (force_generic() || act != MLA_BF16 || !fast_append_shape(d) || !skinny_append_supported(d, n_tok)) return 0;
+  return (size_t)skinny_append_kgroups(d) * n_tok * (d.d_c + d.d_rope) * 4;
+}
+
 int append_common(const mla_dims* dims, int32_t act, const void* a0, const void* a1, int32_t n_tok,
                   const int32_t* seq_id, const int32_t* pos, const void* W_DKV, const void* W_KR,
-                  const mla_cache* cache, const int32_t* bt, int32_t max_pages, void* stream, bool write) {
+                  const mla_cache* cache, const int32_t* bt, int32_t max_pages, void* stream, bool write,
+                  void* ws = nullptr, size_t ws_bytes = 0, bool with_ws = false) {
   int st = check_dims(dims);
   if (st) return st;
   if (!valid_act(act)) return MLA_ERR_DTYPE;
@@ -120,12 +127,22 @@ int append_common(const mla_dims* dims, int32_t act, const void* a0, const void*
   if (write ? !a1 : (!W_DKV || !W_KR)) return MLA_ERR_NULL;
   if (!aligned16(a0) || !aligned16(seq_id) || !aligned16(pos)) return MLA_ERR_ALIGN;
   if (write ? !aligned16(a1) : (!aligned16(W_DKV) || !aligned16(W_KR))) return MLA_ERR_ALIGN;
+  const bool fast = !write && !force_generic() && fast_append_supported(*dims, act, cache->dtype);
+  const size_t need = with_ws && fast ? append_ws_bytes(*dims, act, n_tok) : 0;
+  if (need) {
+    if (!ws) return MLA_ERR_NULL;
+    if (!aligned16(ws)) return MLA_ERR_ALIGN;
+    if (ws_bytes < need) return MLA_ERR_WORKSPACE;
+  }
   AppendArgs a;
   a.d = *dims; a.act = act; a.h = a0; a.k_rope = a1; a.n_tok = n_tok; a.seq_id = seq_id; a.pos = pos;
   a.W_DKV = W_DKV; a.W_KR = W_KR; a.pages = (uint8_t*)cache->pages; a.g = make_geom(*dims, cache->dtype);
   a.block_table = bt; a.max_pages = max_pages; a.stream = (hipStream_t)stream;
   hipError_t e;
-  if (write) e = generic_write(a);
+  if (need) {
+    e = skinny_append_partials(a, (float*)ws);
+    if (e == hipSuccess) e = append_reduce(a, (const float*)ws, skinny_append_kgroups(*dims));
+  } else if (write) e = generic_write(a);
   else if (!force_generic() && fast_append_supported(*dims, act, cache->dtype)) e = fast_append(a);
   else e = generic_append(a);
   return hip_status(e);
@@ -147,6 +164,18 @@ int mla_cache_append(const mla_dims* dims, int32_t act_dtype, const void* h, int
                      const int32_t* block_table, int32_t max_pages, void* stream) {
   return append_common(dims, act_dtype, h, nullptr, n_tok, seq_id, pos, W_DKV, W_KR, cache, block_table, max_pages,
                        stream, false);
+}
+
+size_t mla_append_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t n_tok) {
+  if (check_dims(dims) || !valid_act(act_dtype) || n_tok < 0) return 0;
+  return append_ws_bytes(*dims, act_dtype, n_tok);
+}
+
+int mla_cache_append_ws(const mla_dims* dims, int32_t act_dtype, const void* h, int32_t n_tok, const int32_t* seq_id,
+                        const int32_t* pos, const void* W_DKV, const void* W_KR, const mla_cache* cache,
+                        const int32_t* block_table, int32_t max_pages, void* ws, size_t ws_bytes, void* stream) {
+  return append_common(dims, act_dtype, h, nullptr, n_tok, seq_id, pos, W_DKV, W_KR, cache, block_table, max_pages,
+                       stream, false, ws, ws_bytes, true);
 }
 
 int mla_cache_write(const mla_dims* dims, int32_t act_dtype, const void* c_kv, const void* k_rope, int32_t n_tok,

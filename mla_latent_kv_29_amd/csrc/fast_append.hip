@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void k_append_v3(int n_tok, int d_model, float
 constexpr int AR_TOK = 16, AR_COLS = 128, AR_NW = 8, AR_PD = 4;
 constexpr int AR_TILES = DC / AR_COLS + 1;                    // 4 latent tiles + the RoPE tile
 constexpr int AR_LDS = AR_NW * AR_TOK * AR_COLS * 4;          // 64 KiB of partial tiles
-constexpr int APPEND_ROWS_MAX = 2048;                         // tokens a call up to which this path is taken
+constexpr int APPEND_ROWS_MAX = 4096;                         // tokens a call up to which this path is taken
 
 template <int NSUB>  // 16-column sub-tiles: 8 (latent tile) or 4 (RoPE tile)
 __device__ __forceinline__ void ar_tile(int n_tok, int d_model, int tg, const bf16_t* __restrict__ h,
@@ -330,7 +330,73 @@ __global__ __launch_bounds__(AR_NW * 64) void k_append_rows(int n_tok, int d_mod
   if (c8 == 0) ((float*)(pg + g.fp8_scale_off))[slot * (DC / 128) + ct] = sc;
 }
 
+// The second half of the workspace append: token blockIdx.x's row is the sum
+// of the k-group partials (in k-group order), then the same epilogue as
+// above.  Threads 0-63: latent channels 8 t .. +7 (a 1 x 128 tile is 16
+// threads); threads 64-71: the RoPE channels 8 (t - 64) .. +7.
+__global__ __launch_bounds__(128) void k_append_reduce(int n_tok, int kgroups, const float* __restrict__ part,
+                                                       float theta, const int32_t* __restrict__ seq_id,
+                                                       const int32_t* __restrict__ pos, uint8_t* __restrict__ pages,
+                                                       CacheGeom g, const int32_t* __restrict__ bt, int max_pages) {
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const bool rope = tid >= DC / 8;
+  const int c8 = rope ? tid - DC / 8 : tid;
+  if (rope && c8 >= DR / 8) return;
+  const int ch = rope ? DC + 8 * c8 : 8 * c8;
+  float v[8] = {};
+  for (int k = 0; k < kgroups; ++k) {
+    const float* src = part + ((long)k * n_tok + t) * D + ch;
+    const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
+    v[0] += a0.x; v[1] += a0.y; v[2] += a0.z; v[3] += a0.w;
+    v[4] += a1.x; v[5] += a1.y; v[6] += a1.z; v[7] += a1.w;
+  }
+  const int p = pos[t];
+  uint8_t* pg = pages + (size_t)bt[(long)seq_id[t] * max_pages + p / g.page_size] * g.page_bytes;
+  const int slot = p % g.page_size;
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float cs, sn;
+      rope_cs(p, (8 * c8 + e) >> 1, DR, theta, &cs, &sn);
+      const float x0 = v[e], x1 = v[e + 1];
+      v[e] = x0 * cs - x1 * sn;
+      v[e + 1] = x0 * sn + x1 * cs;
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16_t)v[e];
+    if (g.dtype == MLA_BF16) *(bf16x8*)(pg + bf16_page_off(slot, ch, g.page_size)) = o;
+    else *(bf16x8*)(pg + g.fp8_rope_off + fp8_rope_elem_off(slot, 8 * c8, g.page_size)) = o;
+    return;
+  }
+  if (g.dtype == MLA_BF16) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16_t)v[e];
+    *(bf16x8*)(pg + bf16_page_off(slot, ch, g.page_size)) = o;
+    return;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3(v[e] / sc) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hi |= (uint32_t)f32_to_e4m3(v[4 + e] / sc) << (8 * e);
+  *(uint2*)(pg + fp8_code_off(slot, ch, g.page_size)) = make_uint2(lo, hi);
+  if ((c8 & 15) == 0) ((float*)(pg + g.fp8_scale_off))[slot * (DC / 128) + (c8 >> 4)] = sc;
+}
+
 }  // namespace
+
+hipError_t append_reduce(const AppendArgs& a, const float* part, int kgroups) {
+  return launch(&k_append_reduce, dim3(a.n_tok), dim3(128), 0, a.stream, a.n_tok, kgroups, part, a.d.rope_theta,
+                a.seq_id, a.pos, a.pages, a.g, a.block_table, a.max_pages);
+}
 
 bool fast_append_shape(const mla_dims& d) { return d.d_c == DC && d.d_rope == DR && d.d_model % 32 == 0; }
 

@@ -784,6 +784,36 @@ hipError_t skinny_out(const OutProjArgs& a, int kgroups) {
                 (bf16_t*)a.y);
 }
 
+// The GEMM half of the decode-step append with a workspace: the latent rows
+// [c^KV | k^R before RoPE] = h [W^DKV; W^KR]^T of at most 64 tokens as fp32
+// partials per k-group of 896, part[kg][m][d_c + d_rope], W^DKV's columns
+// first.  Blocks of 32 columns and 7 waves x 4 k-steps: with 8 k-groups at
+// d_model 7168, 144 blocks stream the 8.26 MB of weights.
+struct EpiKPartOff {
+  float* part;
+  int M, ldp, off;
+  __device__ void operator()(int, int kg, int m, int n, float v0, float v1) const {
+    float2 v = {v0, v1};
+    *(float2*)(part + ((long)kg * M + m) * ldp + off + n) = v;
+  }
+};
+
+bool skinny_append_supported(const mla_dims& d, int n_tok) {
+  return n_tok >= 1 && n_tok <= 64 && d.d_model % 896 == 0 && d.d_c % 32 == 0 && d.d_rope % 32 == 0;
+}
+
+int skinny_append_kgroups(const mla_dims& d) { return d.d_model / 896; }
+
+hipError_t skinny_append_partials(const AppendArgs& a, float* part) {
+  const mla_dims& d = a.d;
+  const int kg = skinny_append_kgroups(d), ld = d.d_c + d.d_rope;
+  XPlain xs{(const bf16_t*)a.h, d.d_model, 0};
+  SkArgs s1{a.n_tok, 896, (const bf16_t*)a.W_DKV, d.d_model, 0};
+  MLA_TRY((launch_skinny<7, 4, 2, 2>(s1, xs, d.d_c / 32, kg, 1, EpiKPartOff{part, a.n_tok, ld, 0}, a.stream)));
+  SkArgs s2{a.n_tok, 896, (const bf16_t*)a.W_KR, d.d_model, 0};
+  return launch_skinny<7, 4, 2, 2>(s2, xs, d.d_rope / 32, kg, 1, EpiKPartOff{part, a.n_tok, ld, d.d_c}, a.stream);
+}
+
 // ------------------------------------------------------------ FP8 host side
 bool fp8_gemm_supported(int N, int K) { return N >= 16 && N % 16 == 0 && K >= 512 && K % 512 == 0; }
 

@@ -189,6 +189,13 @@ bool fast_append_supported(const mla_dims& d, int act, int cache_dtype);
 bool fast_append_shape(const mla_dims& d);
 bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q);
 hipError_t fast_append(const AppendArgs& a);
+// decode-step append with a workspace (at most 64 tokens, V3 head shape):
+// k-group partials of the latent rows (k_skinny), then their sum, RoPE,
+// conversion and page scatter (k_append_reduce)
+bool skinny_append_supported(const mla_dims& d, int n_tok);
+int skinny_append_kgroups(const mla_dims& d);
+hipError_t skinny_append_partials(const AppendArgs& a, float* part);
+hipError_t append_reduce(const AppendArgs& a, const float* part, int kgroups);
 hipError_t fast_combine(const CombineArgs& a);
 hipError_t fast_attention(const DecodeArgs& a);
 hipError_t fast_query(const DecodeArgs& a);

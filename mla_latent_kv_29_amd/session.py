@@ -63,9 +63,20 @@ class DecodeSession:
         L.mla_cache_append(self.cdims, self.act, h, n, seq_id, pos, W["W_DKV"], W["W_KR"], self.cache,
                            self.block_table, self.max_pages, stream)
 
-    def append_rows(self, h, seq_id, pos, W, stream=None):
-        L.mla_cache_append(self.cdims, self.act, h, h.shape[0], seq_id, pos, W["W_DKV"], W["W_KR"], self.cache,
-                           self.block_table, self.max_pages, stream)
+    def append_rows(self, h, seq_id, pos, W, stream=None, ws=False):
+        """Append rows h at (seq_id[r], pos[r]); ws=True takes the workspace
+        entry point (mla_cache_append_ws) with a workspace of its own."""
+        n = h.shape[0]
+        if not ws:
+            L.mla_cache_append(self.cdims, self.act, h, n, seq_id, pos, W["W_DKV"], W["W_KR"], self.cache,
+                               self.block_table, self.max_pages, stream)
+            return
+        need = L.mla_append_workspace_bytes(self.cdims, self.act, n)
+        if need and (getattr(self, "append_ws", None) is None or self.append_ws.numel() < need):
+            self.append_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        buf = self.append_ws if need else None
+        L.mla_cache_append_ws(self.cdims, self.act, h, n, seq_id, pos, W["W_DKV"], W["W_KR"], self.cache,
+                              self.block_table, self.max_pages, buf, need, stream)
 
     def write(self, c_kv, k_rope, b, t0, stream=None):
         n = c_kv.shape[0]

@@ -111,6 +111,23 @@ def test_decode_argument_errors():
     assert st == L.MLA_ERR_UNSUPPORTED                                               # fp8 needs d_c % 128 == 0
 
 
+def test_workspace_append_size_and_argument_errors():
+    d = _dims()
+    need = L.mla_append_workspace_bytes(d, m.MLA_BF16, 64)
+    assert need == (7168 // 896) * 64 * 576 * 4          # fp32 partials: 8 k-groups x 64 rows x 576
+    assert L.mla_append_workspace_bytes(d, m.MLA_BF16, 65) == 0   # more tokens: the workspace-free paths
+    assert L.mla_append_workspace_bytes(d, m.MLA_F32, 64) == 0
+    assert L.mla_append_workspace_bytes(m.make_dims(inputs.TINY_DIMS), m.MLA_F32, 4) == 0
+    cache = L.cache_struct(FAKE, m.MLA_BF16, 10)
+    call = lambda n, ws, wsb: L.mla_cache_append_ws(d, m.MLA_BF16, FAKE, n, FAKE, FAKE, FAKE, FAKE, cache, FAKE, 4,
+                                                    ws, wsb, stream=0, check=False)
+    assert call(0, None, 0) == L.MLA_OK                                # no-op
+    assert call(64, None, need) == L.MLA_ERR_NULL
+    assert call(64, FAKE + 8, need) == L.MLA_ERR_ALIGN
+    assert call(64, FAKE, need - 16) == L.MLA_ERR_WORKSPACE
+    assert call(-1, FAKE, need) == L.MLA_ERR_DIMS
+
+
 def test_append_and_combine_argument_errors():
     d = _dims()
     cache = L.cache_struct(FAKE, m.MLA_BF16, 10)

@@ -116,11 +116,11 @@ def test_fp8_bytes_past_the_end_are_ignored(splits):
         assert max_abs(out[b], o_q) <= 2e-2 * float(np.abs(o_q).max()), b
 
 
-@pytest.mark.parametrize("cache", ["fp8", "bf16"])
-def test_mfma_append_epilogue_bit_exact(cache):
+@pytest.mark.parametrize("cache,path", [("fp8", "plain"), ("bf16", "plain"), ("fp8", "ws"), ("bf16", "ws")])
+def test_mfma_append_epilogue_bit_exact(cache, path):
     """Both MFMA appends pinned bit for bit: the 64-token blocks that build
-    long sequences (the 2100-token call) and the few-token path (calls of at
-    most 2048 tokens: the 131-token call).  With W^DKV = [I_512 | 0] and a
+    long sequences (the 4200-token call) and the few-token path (calls of at
+    most 4096 tokens: the 131-token call).  With W^DKV = [I_512 | 0] and a
     W^KR that picks columns 512..575, every fp32 accumulation holds one exact
     product (in any summation order), so c^KV equals the first 512 channels
     of h exactly.  Its E4M3 codes and fp32 scales must then be the oracle's
@@ -128,7 +128,9 @@ def test_mfma_append_epilogue_bit_exact(cache):
     themselves (bf16); k^R, rotated in fp32 and rounded to bf16, within one
     bf16 step of the oracle's float64 rotation.  Tiles are scaled by powers
     of two from 2^-20 to 2^12 and one tile is all zero, so the scale, the
-    saturation edge and the zero-tile rule all occur."""
+    saturation edge and the zero-tile rule all occur.  path "ws": the
+    workspace entry point (mla_cache_append_ws: k-group partials, their sum
+    and the same epilogue) on sequences of 64 and 40 tokens, one call each."""
     from mla_latent_kv_29_amd.session import DecodeSession
     dims = V3
     d_model, dc, dr = dims["d_model"], dims["d_c"], dims["d_rope"]
@@ -137,7 +139,7 @@ def test_mfma_append_epilogue_bit_exact(cache):
     W_KR = torch.zeros((dr, d_model), dtype=torch.bfloat16, device=DEV)
     W_KR[torch.arange(dr), dc + torch.arange(dr)] = 1.0
     W = {"W_DKV": W_DKV, "W_KR": W_KR}
-    lengths = np.array([2100, 131])
+    lengths = np.array([4200, 131]) if path == "plain" else np.array([64, 40])
     bt, pool = inputs.block_table(lengths, dims["page_size"], "shuffled", 0, 9)
     sess = DecodeSession(dims, "bf16", cache, lengths, bt, pool, 1, 0, DEV)
     g = torch.Generator(device="cpu").manual_seed(1234)
@@ -148,7 +150,12 @@ def test_mfma_append_epilogue_bit_exact(cache):
         h[:, :dc] *= torch.repeat_interleave(2.0 ** tile_pow, 128, dim=1)
         h[3, 128:256] = 0.0                      # an all-zero tile: scale 1, codes 0
         hs.append(h.to(torch.bfloat16).to(DEV))
-        sess.append(hs[-1], b, 0, W)
+        if path == "plain":
+            sess.append(hs[-1], b, 0, W)
+        else:
+            n = int(Lb)
+            sess.append_rows(hs[-1], torch.full((n,), b, dtype=torch.int32, device=DEV),
+                             torch.arange(n, dtype=torch.int32, device=DEV), W, ws=True)
     torch.cuda.synchronize()
     for b, Lb in enumerate(lengths):
         Lb = int(Lb)
@@ -171,14 +178,15 @@ def test_mfma_append_epilogue_bit_exact(cache):
         assert np.all(np.abs(kr - kr_ref) <= step)
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8"])
-def test_decode_step_append_one_token_per_sequence(cache):
+@pytest.mark.parametrize("cache,ws", [("bf16", False), ("fp8", False), ("bf16", True), ("fp8", True)])
+def test_decode_step_append_one_token_per_sequence(cache, ws):
     """The append of a decode step: one call that writes the newest token of
     each of 37 sequences (ragged lengths, shuffled pages; 37 is not a multiple
     of the 16-token groups), after the earlier tokens went in whole-sequence
     calls.  Every row must match the oracle's latents as a whole-sequence
     append does: bf16 rows within 1e-2 of the largest value, E4M3 codes within
-    one E4M3 step of the exact latent, k^R within 2e-2."""
+    one E4M3 step of the exact latent, k^R within 2e-2.  ws: the batched call
+    goes through mla_cache_append_ws."""
     from mla_latent_kv_29_amd.session import DecodeSession
     dims = V3
     rng = np.random.default_rng(17)
@@ -193,7 +201,7 @@ def test_decode_step_append_one_token_per_sequence(cache):
     last = torch.stack([hs[b][int(Lb) - 1] for b, Lb in enumerate(lengths)]).contiguous()
     seq_id = torch.arange(len(lengths), dtype=torch.int32, device=DEV)
     pos = torch.tensor(lengths - 1, dtype=torch.int32, device=DEV)
-    sess.append_rows(last, seq_id, pos, W)
+    sess.append_rows(last, seq_id, pos, W, ws=ws)
     torch.cuda.synchronize()
     Wn = {k: to_np(v) for k, v in W.items()}
     for b, Lb in enumerate(lengths):
