@@ -8,7 +8,7 @@
 // v_mfma_f32_16x16x32_bf16 (each of the 4 waves owns 144 columns), the k loop
 // staged through a 3-deep LDS ring filled by global_load_lds_dwordx4.  The fp32
 // result tile then goes through LDS so that each token row is finished in one
-// place: RoPE on the last 64 channels (angles in double precision), then bf16
+// place: RoPE on the last 64 channels (angles reduced in double precision), then bf16
 // conversion or E4M3 quantisation with one fp32 scale per 1x128 tile (lesson
 // §3.3, item 2), and a scatter into the token's page slot.
 #include "internal.hpp"
@@ -31,6 +31,15 @@ constexpr int APPEND_LDS = OUT_BYTES > NSA * STA_BYTES ? OUT_BYTES : NSA * STA_B
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// RoPE rotation of pair m at position p: the frequency theta^(-2m/d_rope)
+// in double (through exp2), the angle reduced modulo 2 pi in double, then a
+// single-precision sincos of the remainder (full accuracy at any position,
+// far cheaper than double-precision sincos).  All three append kernels use
+// it, so a token's k^R does not depend on which of them wrote it.
+__device__ __forceinline__ void rope_rot(int p, int m, float theta, float* cs, float* sn) {
+  rope_cs_w(p, exp2(-2.0 * (double)m / DR * log2((double)theta)), cs, sn);
 }
 
 // rows x 32 k tile, row r chunk q at r*4 + (q ^ ((r>>2)&3))
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(256) void k_append_v3(int n_tok, int d_model, float
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             float cs, sn;
-            rope_cs(p, (8 * C - DC + e) >> 1, DR, theta, &cs, &sn);
+            rope_rot(p, (8 * C - DC + e) >> 1, theta, &cs, &sn);
             const float x0 = v[e], x1 = v[e + 1];
             v[e] = x0 * cs - x1 * sn;
             v[e + 1] = x0 * sn + x1 * cs;
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(256) void k_append_v3(int n_tok, int d_model, float
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           float cs, sn;
-          rope_cs(p, (8 * lane + e) >> 1, DR, theta, &cs, &sn);
+          rope_rot(p, (8 * lane + e) >> 1, theta, &cs, &sn);
           const float x0 = r8[e], x1 = r8[e + 1];
           r8[e] = x0 * cs - x1 * sn;
           r8[e + 1] = x0 * sn + x1 * cs;
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(AR_NW * 64) void k_append_rows(int n_tok, int d_mod
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       float cs, sn;
-      rope_cs(p, (8 * c8 + e) >> 1, DR, theta, &cs, &sn);
+      rope_rot(p, (8 * c8 + e) >> 1, theta, &cs, &sn);
       const float x0 = v[e], x1 = v[e + 1];
       v[e] = x0 * cs - x1 * sn;
       v[e + 1] = x0 * sn + x1 * cs;
@@ -357,7 +366,7 @@ __global__ __launch_bounds__(128) void k_append_reduce(int n_tok, int kgroups, c
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       float cs, sn;
-      rope_cs(p, (8 * c8 + e) >> 1, DR, theta, &cs, &sn);
+      rope_rot(p, (8 * c8 + e) >> 1, theta, &cs, &sn);
       const float x0 = v[e], x1 = v[e + 1];
       v[e] = x0 * cs - x1 * sn;
       v[e + 1] = x0 * sn + x1 * cs;

@@ -38,6 +38,10 @@ struct SkArgs {
   int kg_len;         // k per k-group = waves * KS * 32
   const bf16_t* W;    // W[batch][N][ldw]
   long ldw, bsw;
+  // columns from n_split on are rows n - n_split of W2 (two weights in one
+  // launch; n_split a multiple of the block's columns)
+  int n_split = 1 << 30;
+  const bf16_t* W2 = nullptr;
 };
 
 // Sources of the activation fragments: lane (i16, g) of a wave gets, for
@@ -136,7 +140,8 @@ __global__ __launch_bounds__(WPB * 64) void k_skinny(SkArgs a, XSrc xs, Epi epi)
   const int n0 = blockIdx.x * NB * 16;
   const int kg = blockIdx.y, batch = blockIdx.z;
   const long k0 = (long)kg * a.kg_len + wave * KS * 32 + 8 * g;
-  const bf16_t* W = a.W + (long)batch * a.bsw + (long)(n0 + i16) * a.ldw + k0;
+  const bf16_t* W = n0 < a.n_split ? a.W + (long)batch * a.bsw + (long)(n0 + i16) * a.ldw + k0
+                                   : a.W2 + (long)(n0 - a.n_split + i16) * a.ldw + k0;
 
   // W rows n0 + 16 nb + i16 of this wave's K-slice, DEPTH column blocks ahead
   bf16x8 wf[DEPTH][KS];
@@ -787,8 +792,8 @@ hipError_t skinny_out(const OutProjArgs& a, int kgroups) {
 // The GEMM half of the decode-step append with a workspace: the latent rows
 // [c^KV | k^R before RoPE] = h [W^DKV; W^KR]^T of at most 64 tokens as fp32
 // partials per k-group of 896, part[kg][m][d_c + d_rope], W^DKV's columns
-// first.  Blocks of 32 columns and 7 waves x 4 k-steps: with 8 k-groups at
-// d_model 7168, 144 blocks stream the 8.26 MB of weights.
+// first.  Blocks of 32 columns and 7 waves x 4 k-steps, both weights in one
+// launch: with 8 k-groups at d_model 7168, 144 blocks stream the 8.26 MB.
 struct EpiKPartOff {
   float* part;
   int M, ldp, off;
@@ -808,10 +813,8 @@ hipError_t skinny_append_partials(const AppendArgs& a, float* part) {
   const mla_dims& d = a.d;
   const int kg = skinny_append_kgroups(d), ld = d.d_c + d.d_rope;
   XPlain xs{(const bf16_t*)a.h, d.d_model, 0};
-  SkArgs s1{a.n_tok, 896, (const bf16_t*)a.W_DKV, d.d_model, 0};
-  MLA_TRY((launch_skinny<7, 4, 2, 2>(s1, xs, d.d_c / 32, kg, 1, EpiKPartOff{part, a.n_tok, ld, 0}, a.stream)));
-  SkArgs s2{a.n_tok, 896, (const bf16_t*)a.W_KR, d.d_model, 0};
-  return launch_skinny<7, 4, 2, 2>(s2, xs, d.d_rope / 32, kg, 1, EpiKPartOff{part, a.n_tok, ld, d.d_c}, a.stream);
+  SkArgs sa{a.n_tok, 896, (const bf16_t*)a.W_DKV, d.d_model, 0, d.d_c, (const bf16_t*)a.W_KR};
+  return launch_skinny<7, 4, 2, 2>(sa, xs, ld / 32, kg, 1, EpiKPartOff{part, a.n_tok, ld, 0}, a.stream);
 }
 
 // ------------------------------------------------------------ FP8 host side
