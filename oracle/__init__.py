@@ -24,7 +24,7 @@ Parity status per function is listed in each module header.
 from .mla import (rope, kv_latents, queries, attend_nonabsorbed, attend_absorbed,
                   decode_from_latents, decode_from_h, softmax_lse, output_projection)
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_values, e5m2_decode,
-                  quantize_tiles, dequantize_tiles, quantize_blocks, dequantize_blocks,
+                  quantize_tiles, dequantize_tiles, pow2_ceil, quantize_blocks, dequantize_blocks,
                   gemm_block_scaled)
 from .fp8w import decode_absorbed_exact, decode_fp8w_from_latents, bf16_round
 from .sizes import (cache_values_per_token, mha_values_per_token, cache_bytes,
@@ -35,7 +35,7 @@ __all__ = [
     "rope", "kv_latents", "queries", "attend_nonabsorbed", "attend_absorbed",
     "decode_from_latents", "decode_from_h", "softmax_lse", "output_projection",
     "e4m3_decode", "e4m3_encode", "e4m3_values", "e5m2_decode",
-    "quantize_tiles", "dequantize_tiles", "quantize_blocks", "dequantize_blocks", "gemm_block_scaled",
+    "quantize_tiles", "dequantize_tiles", "pow2_ceil", "quantize_blocks", "dequantize_blocks", "gemm_block_scaled",
     "decode_absorbed_exact", "decode_fp8w_from_latents", "bf16_round",
     "cache_values_per_token", "mha_values_per_token", "cache_bytes",
     "mla_params_per_layer", "tokens_per_step",

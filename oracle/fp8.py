@@ -18,6 +18,14 @@ Tile quantisation (a reading of item 2 for the latent cache): for each token
 and each group of 128 consecutive channels, scale s = amax/448 computed in
 float32 (s = 1 when amax = 0), code = encode(float32(x) / s) in float32, and the
 dequantised value is code * s.  Both sides decide codes in float32.
+
+Power-of-two tile scales (UE8M0): the lesson's continuation of §3.5 notes that
+DeepSeek V3.1 moved to FP8 with UE8M0 scales, i.e. scales that are bare powers
+of two (an 8-bit exponent, no mantissa).  Reading used here for that cache
+format: the scale is the smallest power of two not below amax/448 (the
+float32 quotient), and not below 2^-126, so that no code saturates; codes
+follow the same rule as above.  Every dequantised value code * scale is then
+exactly representable in bfloat16 (and float32) within the normal range.
 """
 import numpy as np
 
@@ -72,17 +80,29 @@ def e4m3_encode(x):
     return out.reshape(x.shape).astype(np.uint8)
 
 
-def quantize_tiles(x, tile=128):
+def pow2_ceil(s):
+    """Smallest power of two >= s for positive float32 s, at least 2^-126."""
+    s = np.asarray(s, dtype=np.float32).astype(np.float64)
+    m, e = np.frexp(s)                       # s = m 2^e with m in [0.5, 1)
+    p = np.where(m == 0.5, np.ldexp(1.0, e - 1), np.ldexp(1.0, e))
+    return np.maximum(p, 2.0 ** -126).astype(np.float32)
+
+
+def quantize_tiles(x, tile=128, scale_rule="amax"):
     """Per-row, per-`tile`-channel E4M3 quantisation of x [n, d] (d % tile == 0).
 
-    Returns (codes uint8 [n, d], scales float32 [n, d // tile]).
+    scale_rule "amax": s = amax/448; "ue8m0": s = the power of two above (see
+    the module docstring).  Returns (codes uint8 [n, d], scales float32
+    [n, d // tile]).
     """
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
     n, d = x32.shape
-    assert d % tile == 0
+    assert d % tile == 0 and scale_rule in ("amax", "ue8m0")
     g = x32.reshape(n, d // tile, tile)
     amax = np.abs(g).max(axis=2)
     scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    if scale_rule == "ue8m0":
+        scale = np.where(amax > 0, pow2_ceil(np.where(amax > 0, scale, 1.0)), np.float32(1.0)).astype(np.float32)
     y = (g / scale[:, :, None]).astype(np.float32)
     codes = e4m3_encode(y.astype(np.float64)).reshape(n, d)
     return codes, scale

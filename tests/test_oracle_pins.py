@@ -121,6 +121,62 @@ def test_tile_quantisation_error_bound_and_amax():
                 assert codes[r, t * 128 + k] & 0x7F == 0x7E
 
 
+def test_pow2_ceil_known_values():
+    """Smallest power of two not below s (the UE8M0 scale rule), by hand."""
+    s = np.array([1.0, 1.5, 0.75, 3.0e-3, 2.0 ** -130, 448.0], dtype=np.float32)
+    got = oracle.pow2_ceil(s)
+    np.testing.assert_array_equal(got, np.array([1.0, 2.0, 1.0, 2.0 ** -8, 2.0 ** -126, 512.0], dtype=np.float32))
+
+
+def test_ue8m0_tiles_hand_worked():
+    """amax 3 -> 3/448 = 0.0067 -> scale 2^-7; 3/2^-7 = 384 = 1.5 * 2^8 is code
+    0x7C; -0.1/2^-7 = -12.8 rounds to -13 = -1.625 * 2^3, code 0xD5."""
+    x = np.zeros((1, 128))
+    x[0, 0], x[0, 1] = 3.0, -0.1
+    codes, scales = oracle.quantize_tiles(x, scale_rule="ue8m0")
+    assert scales[0, 0] == np.float32(2.0 ** -7)
+    assert codes[0, 0] == 0x7C and codes[0, 1] == 0xD5 and np.all(codes[0, 2:] == 0)
+
+
+def test_ue8m0_tiles_powers_of_two_no_saturation_bf16_exact():
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 0.7, (9, 512)) * np.exp(rng.normal(0, 3, (9, 1)))
+    x[4, 128:256] = 0.0
+    codes, scales = oracle.quantize_tiles(x, scale_rule="ue8m0")
+    xt = oracle.dequantize_tiles(codes, scales)
+    assert scales[4, 1] == 1.0 and np.all(codes[4, 128:256] == 0)
+    g = np.abs(x.astype(np.float32).astype(np.float64)).reshape(9, 4, 128)
+    amax = g.max(axis=2)
+    m, _ = np.frexp(scales.astype(np.float64))
+    assert np.all(m == 0.5)                                  # bare powers of two
+    q = amax / 448.0
+    nz = amax > 0
+    assert np.all(scales[nz] >= q[nz] * (1 - 1e-6)) and np.all(scales[nz] / 2 < q[nz] * (1 + 1e-6))
+    # no code saturates: every value within half an E4M3 step of its tile
+    err = np.abs(xt - x).reshape(9, 4, 128)
+    bound = np.maximum(g * 2.0 ** -4, 2.0 ** -10 * scales[:, :, None]) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    # code * 2^k has at most 4 significant bits: exact in bfloat16
+    f = xt.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), xt)
+    assert np.all(f.view(np.uint32) & 0xFFFF == 0)
+
+
+def test_ue8m0_equals_amax_rule_when_amax_over_448_is_a_power_of_two():
+    rng = np.random.default_rng(6)
+    x = rng.uniform(-1, 1, (3, 256))
+    for r in range(3):
+        for t in range(2):
+            blk = x[r, 128 * t:128 * (t + 1)]
+            k = np.argmax(np.abs(blk))
+            blk[k] = np.sign(blk[k]) * 448.0 * 2.0 ** (-3 * r - t)
+            blk[np.arange(128) != k] *= 0.9 * 448.0 * 2.0 ** (-3 * r - t)
+    c1, s1 = oracle.quantize_tiles(x)
+    c2, s2 = oracle.quantize_tiles(x, scale_rule="ue8m0")
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(c1, c2)
+
+
 # ---------------------------------------------------------------- RoPE
 
 def test_rope_identity_norm_and_complex_form():
