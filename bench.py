@@ -35,7 +35,8 @@ def algorithmic(spec, dims, lengths):
     """Algorithmic bytes and flops of one step and of one attention launch."""
     H, dh, dr, dc, dq, d = (dims[k] for k in ("n_heads", "d_head", "d_rope", "d_c", "d_cq", "d_model"))
     s_q = spec["s_q"]
-    tok_bytes = {"bf16": (dc + dr) * 2, "fp8": dc + 4 * (dc // 128) + 2 * dr, "f32": (dc + dr) * 4}[spec["cache"]]
+    fp8_tok = dc + 4 * (dc // 128) + 2 * dr
+    tok_bytes = {"bf16": (dc + dr) * 2, "fp8": fp8_tok, "fp8e8": fp8_tok, "f32": (dc + dr) * 4}[spec["cache"]]
     es = 2 if spec["act"] == "bf16" else 4
     L = [int(x) for x in lengths]
     vis = sum(max(0, Lb - s_q + j + 1) for Lb in L for j in range(s_q))
@@ -59,6 +60,7 @@ def algorithmic(spec, dims, lengths):
 # unchanged since the measurement.
 ATTN_SOURCES = {"bf16": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
                 "fp8": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
+                "fp8e8": ["fast_attn2.hip", "layout.hpp", "common.hpp"],
                 "prefill": ["fast_prefill.hip", "internal.hpp", "common.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 MTP_ACCEPTANCE = 0.85  # second-token acceptance of MTP drafts, lower end of the pages' 85-90%
@@ -835,7 +837,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (spec["act"] if spec["cache"] != "fp8" else "bf16+fp8cache") + ("+fp8weights" if fp8w else ""),
+        "dtype": {"fp8": "bf16+fp8cache", "fp8e8": "bf16+fp8cache(ue8m0 scales)"}.get(spec["cache"], spec["act"])
+                 + ("+fp8weights" if fp8w else ""),
         "data": "synthetic (seeded N(0,1) hidden states, N(0,sigma^2) weights at DeepSeek-V3 MLA shapes)",
         "config": {"workload": args.workload, "batch": int(spec["batch"]), "seq_len": spec["lengths"][1]
                    if spec["lengths"][0] == "fixed" else f"U[{spec['lengths'][1]},{spec['lengths'][2]}]",

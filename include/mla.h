@@ -58,6 +58,11 @@
  *   one scale per 1x128 activation tile.  Scale s = amax/448 (1 for an
  *   all-zero tile), code = round-to-nearest-even(x/s) saturated to +-448,
  *   value = code*s.  Requires d_c % 128 == 0 and d_rope % 8 == 0.
+ *   FP8_E4M3_E8 pages: the FP8_E4M3 layout and codes, with power-of-two
+ *   (UE8M0) scales, the format the lesson's continuation of §3.5 says
+ *   DeepSeek V3.1 adopted: s = the smallest power of two >= amax/448 (the
+ *   float32 quotient), at least 2^-126, still stored as f32.  No code
+ *   saturates, and every value code*s is exact in bf16.
  * The chunk-major pages are what the gfx950 kernels copy to LDS verbatim;
  * mla_page_bytes() gives a page's size.
  */
@@ -91,7 +96,8 @@ typedef enum {
 typedef enum {
   MLA_F32 = 0,
   MLA_BF16 = 1,
-  MLA_FP8_E4M3 = 2 /* cache only */
+  MLA_FP8_E4M3 = 2,   /* cache only: E4M3 codes, f32 tile scales amax/448 */
+  MLA_FP8_E4M3_E8 = 3 /* cache only: E4M3 codes, power-of-two tile scales  */
 } mla_dtype;
 
 /* Model dimensions (lesson's V3 shape dictionary: d_model 7168, 128 heads of
@@ -108,7 +114,7 @@ typedef struct {
  * pages of mla_page_bytes(dims, dtype) bytes each.                          */
 typedef struct {
   void* pages;
-  int32_t dtype;     /* mla_dtype: MLA_F32, MLA_BF16 or MLA_FP8_E4M3 */
+  int32_t dtype;     /* mla_dtype: MLA_F32, MLA_BF16, MLA_FP8_E4M3 or MLA_FP8_E4M3_E8 */
   int32_t num_pages;
 } mla_cache;
 

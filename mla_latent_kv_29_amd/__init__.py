@@ -15,7 +15,7 @@ from ._lib import (mla_page_bytes, mla_cache_append, mla_cache_write, mla_defaul
                    mla_fp8_quantize_weight_t, mla_fp8_gemm_workspace_bytes, mla_fp8_gemm, mla_mtp_tokens_per_step,
                    mla_decode_fp8w_workspace_bytes, mla_decode_fp8w, mla_decode_fp8w_query, mla_combine_fp8w,
                    status_str, version, make_dims,
-                   MLAError, MLA_F32, MLA_BF16, MLA_FP8_E4M3)
+                   MLAError, MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_E8)
 
 __all__ = ["mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits", "mla_decode_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
@@ -24,4 +24,4 @@ __all__ = ["mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default
            "mla_fp8_quantize_weight_t", "mla_fp8_gemm_workspace_bytes", "mla_fp8_gemm", "mla_mtp_tokens_per_step",
            "mla_decode_fp8w_workspace_bytes", "mla_decode_fp8w", "mla_decode_fp8w_query", "mla_combine_fp8w",
            "status_str", "version", "make_dims",
-           "MLAError", "MLA_F32", "MLA_BF16", "MLA_FP8_E4M3"]
+           "MLAError", "MLA_F32", "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP8_E4M3_E8"]

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmla.so")
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE = 0, -1, -2, -3
 MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = -4, -5, -6, -7
-MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_E8 = 0, 1, 2, 3
 
 EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_append_workspace_bytes", "mla_cache_append_ws", "mla_cache_write", "mla_default_splits", "mla_decode_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",

@@ -22,11 +22,11 @@ static bool v3_shape(const mla_dims& d) {
 }
 
 bool fast_append_supported(const mla_dims& d, int act, int cache_dtype) {
-  return fast_append_shape(d) && act == MLA_BF16 && (cache_dtype == MLA_BF16 || cache_dtype == MLA_FP8_E4M3);
+  return fast_append_shape(d) && act == MLA_BF16 && (cache_dtype == MLA_BF16 || is_fp8_cache(cache_dtype));
 }
 
 bool fast_decode_supported(const mla_dims& d, int act, int cache_dtype, int s_q) {
-  return v3_shape(d) && act == MLA_BF16 && (cache_dtype == MLA_BF16 || cache_dtype == MLA_FP8_E4M3) && s_q >= 1 &&
+  return v3_shape(d) && act == MLA_BF16 && (cache_dtype == MLA_BF16 || is_fp8_cache(cache_dtype)) && s_q >= 1 &&
          s_q <= 8;
 }
 
@@ -79,12 +79,12 @@ int check_dims(const mla_dims* d) {
 }
 
 bool valid_act(int t) { return t == MLA_F32 || t == MLA_BF16; }
-bool valid_cache(int t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
+bool valid_cache(int t) { return t == MLA_F32 || t == MLA_BF16 || is_fp8_cache(t); }
 
 int check_cache(const mla_dims* d, const mla_cache* c, const int32_t* bt, int32_t max_pages) {
   if (!c || !c->pages || !bt) return MLA_ERR_NULL;
   if (!valid_cache(c->dtype)) return MLA_ERR_DTYPE;
-  if (c->dtype == MLA_FP8_E4M3 && (d->d_c % 128 || d->d_rope % 8)) return MLA_ERR_UNSUPPORTED;
+  if (is_fp8_cache(c->dtype) && (d->d_c % 128 || d->d_rope % 8)) return MLA_ERR_UNSUPPORTED;
   if (c->dtype == MLA_BF16 && (d->d_c + d->d_rope) % 8) return MLA_ERR_UNSUPPORTED;
   if (c->num_pages <= 0 || max_pages <= 0) return MLA_ERR_DIMS;
   if (!aligned16(c->pages) || !aligned16(bt)) return MLA_ERR_ALIGN;
@@ -154,7 +154,7 @@ extern "C" {
 
 size_t mla_page_bytes(const mla_dims* dims, int32_t cache_dtype) {
   if (check_dims(dims) || !valid_cache(cache_dtype)) return 0;
-  if (cache_dtype == MLA_FP8_E4M3 && (dims->d_c % 128 || dims->d_rope % 8)) return 0;
+  if (is_fp8_cache(cache_dtype) && (dims->d_c % 128 || dims->d_rope % 8)) return 0;
   if (cache_dtype == MLA_BF16 && (dims->d_c + dims->d_rope) % 8) return 0;
   return page_bytes_of(dims->d_c, dims->d_rope, dims->page_size, cache_dtype);
 }

@@ -57,6 +57,22 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
 }
 
 // ---------------------------------------------------------------- cache layout
+// The two FP8 cache formats share the page layout and the codes; they differ
+// only in how a tile's scale is chosen (see tile_scale).
+__host__ __device__ inline bool is_fp8_cache(int t) { return t == MLA_FP8_E4M3 || t == MLA_FP8_E4M3_E8; }
+
+// Scale of a 1x128 tile with largest magnitude amax: amax/448, or for the
+// power-of-two (UE8M0) format the smallest power of two >= amax/448 and at
+// least 2^-126 (adding a full mantissa and clearing it rounds a positive
+// float up to its binade's power of two; a subnormal quotient gives 2^-126).
+// 1 for an all-zero tile.
+__device__ inline float tile_scale(float amax, int dtype) {
+  if (!(amax > 0.0f)) return 1.0f;
+  const float s = amax / 448.0f;
+  if (dtype != MLA_FP8_E4M3_E8) return s;
+  return __uint_as_float((__float_as_uint(s) + 0x007FFFFFu) & 0x7F800000u);
+}
+
 struct CacheGeom {
   int d_c, d_rope, page_size, dtype;
   size_t page_bytes;

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void k_append_v3(int n_tok, int d_model, float
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-      const float s = am > 0.0f ? am / 448.0f : 1.0f;
+      const float s = tile_scale(am, g.dtype);
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3(v[e] / s) << (8 * e);
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(AR_NW * 64) void k_append_rows(int n_tok, int d_mod
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
   if (!live) return;
-  const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+  const float sc = tile_scale(am, g.dtype);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3(v[e] / sc) << (8 * e);
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(128) void k_append_reduce(int n_tok, int kgroups, c
   for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-  const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+  const float sc = tile_scale(am, g.dtype);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) lo |= (uint32_t)f32_to_e4m3(v[e] / sc) << (8 * e);

@@ -811,7 +811,7 @@ static hipError_t launch_attn(const DecodeArgs& a) {
 }
 
 hipError_t fast_attention(const DecodeArgs& a) {
-  if (a.cache_dtype == MLA_FP8_E4M3) {
+  if (is_fp8_cache(a.cache_dtype)) {
     // the page geometry the fp8 stage copies are compiled for
     if (a.g.fp8_scale_off != (size_t)F8_PG_SCALES || a.g.fp8_rope_off != (size_t)F8_PG_ROPE) return hipErrorInvalidValue;
     return launch_attn<true>(a);

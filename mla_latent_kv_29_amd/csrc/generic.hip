@@ -48,7 +48,7 @@ __device__ void store_row(const CacheGeom& g, uint8_t* pg, int slot, const float
     for (int tile = wave; tile < nt; tile += nw) {
       float v0 = row[tile * 128 + lane], v1 = row[tile * 128 + 64 + lane];
       float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-      float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+      float s = tile_scale(amax, g.dtype);
       pg[fp8_code_off(slot, tile * 128 + lane, g.page_size)] = f32_to_e4m3(v0 / s);
       pg[fp8_code_off(slot, tile * 128 + 64 + lane, g.page_size)] = f32_to_e4m3(v1 / s);
       if (lane == 0) ((float*)(pg + g.fp8_scale_off))[slot * nt + tile] = s;

@@ -33,6 +33,10 @@ WORKLOADS = {
                              lengths=("fixed", 131072), table="inorder", sigma=0.006),
     "v3_fp8_b128_l8192_sq2": dict(index=4, dims=V3_DIMS, act="bf16", cache="fp8", batch=128, s_q=2,
                                   lengths=("fixed", 8192), table="inorder", sigma=0.006),
+    # config 5's inputs (the same index, so the same values) in the FP8 cache
+    # format with power-of-two (UE8M0) tile scales
+    "v3_fp8e8_b128_l8192_sq2": dict(index=4, dims=V3_DIMS, act="bf16", cache="fp8e8", batch=128, s_q=2,
+                                    lengths=("fixed", 8192), table="inorder", sigma=0.006),
     # the headline batch with W^DQ, W^UQ, W^UK and W^UV in E4M3 (128 x 128-block scales)
     "v3_fp8w_b64_l4096": dict(index=11, dims=V3_DIMS, act="bf16", cache="bf16", batch=64, s_q=1,
                               lengths=("fixed", 4096), table="inorder", sigma=0.006, weights="fp8"),

@@ -11,12 +11,12 @@ import torch
 from . import _lib as L
 
 ACT = {"f32": L.MLA_F32, "bf16": L.MLA_BF16}
-CACHE = {"f32": L.MLA_F32, "bf16": L.MLA_BF16, "fp8": L.MLA_FP8_E4M3}
+CACHE = {"f32": L.MLA_F32, "bf16": L.MLA_BF16, "fp8": L.MLA_FP8_E4M3, "fp8e8": L.MLA_FP8_E4M3_E8}
 
 
 class DecodeSession:
     def __init__(self, dims, act, cache_dtype, lengths, table, num_pages, s_q, num_splits=0, device="cuda"):
-        """dims: dict of model dims; act: 'f32'|'bf16'; cache_dtype: 'f32'|'bf16'|'fp8';
+        """dims: dict of model dims; act: 'f32'|'bf16'; cache_dtype: 'f32'|'bf16'|'fp8'|'fp8e8';
         lengths: int array [batch] (seqlens, including the s_q query tokens);
         table: int32 numpy [batch, max_pages]; num_pages: size of the page pool."""
         self.dims = dict(dims)

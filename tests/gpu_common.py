@@ -28,6 +28,7 @@ class Case:
     def __init__(self, dims, act, cache, lengths, s_q, table="inorder", sigma=0.006, seed=0, wl=0,
                  num_splits=0, planted=None, chunk=16384):
         self.dims, self.act, self.cache_name, self.s_q = dims, act, cache, s_q
+        self.scale_rule = "ue8m0" if cache == "fp8e8" else "amax"   # FP8 tile scales of the cache format
         self.seed, self.wl = seed, wl
         self.lengths = np.asarray(lengths, dtype=np.int64)
         self.tdt = torch.float32 if act == "f32" else torch.bfloat16
@@ -81,7 +82,7 @@ class Case:
         if self.planted is not None:
             c, r = (to_np(x) for x in self.lat[b])
             if fp8:
-                codes, scales = oracle.quantize_tiles(c)
+                codes, scales = oracle.quantize_tiles(c, scale_rule=self.scale_rule)
                 c = oracle.dequantize_tiles(codes, scales)
                 r = to_np(torch.from_numpy(r).to(torch.bfloat16))
             hqb = to_np(hq[b * self.s_q:(b + 1) * self.s_q])
@@ -91,7 +92,7 @@ class Case:
         if not fp8:
             return oracle.decode_from_h(h, Wn, d, Lb, self.s_q, tau, heads)
         c, kr = oracle.kv_latents(h, Wn["W_DKV"], Wn["W_KR"], np.arange(Lb), d["rope_theta"])
-        codes, scales = oracle.quantize_tiles(c)
+        codes, scales = oracle.quantize_tiles(c, scale_rule=self.scale_rule)
         c = oracle.dequantize_tiles(codes, scales)
         kr = to_np(torch.from_numpy(kr).to(torch.bfloat16))   # the cache keeps k^R in bf16
         hq = h[Lb - self.s_q:Lb]

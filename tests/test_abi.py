@@ -40,8 +40,11 @@ def test_page_bytes_layouts():
     assert m.mla_page_bytes(d, m.MLA_BF16) == 64 * 576 * 2
     assert m.mla_page_bytes(d, m.MLA_F32) == 64 * 576 * 4
     assert m.mla_page_bytes(d, m.MLA_FP8_E4M3) == 64 * (512 + 4 * 4 + 2 * 64)  # 41 984
+    assert m.mla_page_bytes(d, m.MLA_FP8_E4M3_E8) == m.mla_page_bytes(d, m.MLA_FP8_E4M3)  # same layout
     t = m.make_dims(inputs.TINY_DIMS)
     assert m.mla_page_bytes(t, m.MLA_FP8_E4M3) == 0       # d_c % 128 != 0
+    assert m.mla_page_bytes(t, m.MLA_FP8_E4M3_E8) == 0
+    assert m.mla_page_bytes(d, 4) == 0
     assert m.mla_page_bytes(t, 7) == 0
 
 

@@ -18,15 +18,16 @@ pytestmark = pytest.mark.gpu
 V3 = inputs.V3_DIMS
 
 
-@pytest.mark.parametrize("act", ["f32", "bf16"])
-def test_fp8_write_codes_and_scales_bit_exact(act):
-    case = Case(V3, act, "fp8", [131, 64], s_q=1, table="shuffled", wl=4, planted=(0.5, 0.5))
+@pytest.mark.parametrize("act,cache", [("f32", "fp8"), ("bf16", "fp8"), ("f32", "fp8e8"), ("bf16", "fp8e8")])
+def test_fp8_write_codes_and_scales_bit_exact(act, cache):
+    """cache fp8e8: the power-of-two (UE8M0) scale rule of the same layout."""
+    case = Case(V3, act, cache, [131, 64], s_q=1, table="shuffled", wl=4, planted=(0.5, 0.5))
     for b in range(2):
         c, r = case.lat[b]
         Lb = int(case.lengths[b])
         npg = (Lb + 63) // 64
         codes, scales, rope = read_fp8_rows(case.sess.pages, case.bt[b, :npg], V3)
-        ref_codes, ref_scales = oracle.quantize_tiles(to_np(c))
+        ref_codes, ref_scales = oracle.quantize_tiles(to_np(c), scale_rule=case.scale_rule)
         np.testing.assert_array_equal(codes[:Lb], ref_codes)
         np.testing.assert_array_equal(scales[:Lb], ref_scales)
         np.testing.assert_array_equal(rope[:Lb], to_np(r.to(torch.bfloat16)))
@@ -59,9 +60,11 @@ def test_bf16_append_rows_match_oracle_latents():
         assert max_abs(rows, ref) <= 1e-2 * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("s_q,kappa,splits", [(2, 1.0, 2), (2, 56.0, 3), (1, 56.0, 1), (4, 56.0, 2)])
-def test_fp8_decode_parity(s_q, kappa, splits):
-    case = Case(V3, "bf16", "fp8", [300, 65, 128], s_q=s_q, table="shuffled", wl=4, num_splits=splits)
+@pytest.mark.parametrize("cache,s_q,kappa,splits", [("fp8", 2, 1.0, 2), ("fp8", 2, 56.0, 3), ("fp8", 1, 56.0, 1),
+                                                     ("fp8", 4, 56.0, 2), ("fp8e8", 2, 1.0, 2), ("fp8e8", 2, 56.0, 3),
+                                                     ("fp8e8", 1, 56.0, 1), ("fp8e8", 4, 56.0, 2)])
+def test_fp8_decode_parity(cache, s_q, kappa, splits):
+    case = Case(V3, "bf16", cache, [300, 65, 128], s_q=s_q, table="shuffled", wl=4, num_splits=splits)
     tau = tau_of(V3) * kappa
     out, lse, _ = case.run(tau)
     for b in range(3):
@@ -81,13 +84,13 @@ def test_fp8_planted_decode_vs_emulated_oracle():
         assert max_abs(out[b], o_q) <= 2e-2 * float(np.abs(o_q).max())
 
 
-@pytest.mark.parametrize("splits", [1, 2])
-def test_fp8_bytes_past_the_end_are_ignored(splits):
+@pytest.mark.parametrize("cache,splits", [("fp8", 1), ("fp8", 2), ("fp8e8", 1), ("fp8e8", 2)])
+def test_fp8_bytes_past_the_end_are_ignored(cache, splits):
     """Page slots past a sequence's length hold NaN patterns in all three
     blocks (E4M3 code 0xFF, fp32 scale 0xFFFFFFFF, bf16 k^R 0xFFFF): those
     tokens are not visible, so the output must stay finite and unchanged."""
     from gpu_common import slot_x
-    case = Case(V3, "bf16", "fp8", [300, 129, 64], s_q=1, table="shuffled", wl=4, num_splits=splits)
+    case = Case(V3, "bf16", cache, [300, 129, 64], s_q=1, table="shuffled", wl=4, num_splits=splits)
     ps, dc, dr = V3["page_size"], V3["d_c"], V3["d_rope"]
     s_off = ps * dc
     r_off = s_off + ps * (dc // 128) * 4
@@ -116,7 +119,8 @@ def test_fp8_bytes_past_the_end_are_ignored(splits):
         assert max_abs(out[b], o_q) <= 2e-2 * float(np.abs(o_q).max()), b
 
 
-@pytest.mark.parametrize("cache,path", [("fp8", "plain"), ("bf16", "plain"), ("fp8", "ws"), ("bf16", "ws")])
+@pytest.mark.parametrize("cache,path", [("fp8", "plain"), ("bf16", "plain"), ("fp8", "ws"), ("bf16", "ws"),
+                                        ("fp8e8", "plain"), ("fp8e8", "ws")])
 def test_mfma_append_epilogue_bit_exact(cache, path):
     """Both MFMA appends pinned bit for bit: the 64-token blocks that build
     long sequences (the 4200-token call) and the few-token path (calls of at
@@ -162,9 +166,10 @@ def test_mfma_append_epilogue_bit_exact(cache, path):
         hb = to_np(hs[b])
         npg = (Lb + 63) // 64
         kr_ref = oracle.rope(hb[:, dc:dc + dr], np.arange(Lb), dims["rope_theta"])
-        if cache == "fp8":
+        if cache != "bf16":
             codes, scales, rope = read_fp8_rows(sess.pages, bt[b, :npg], dims)
-            ref_codes, ref_scales = oracle.quantize_tiles(hb[:, :dc])
+            rule = "ue8m0" if cache == "fp8e8" else "amax"
+            ref_codes, ref_scales = oracle.quantize_tiles(hb[:, :dc], scale_rule=rule)
             np.testing.assert_array_equal(codes[:Lb], ref_codes)
             np.testing.assert_array_equal(scales[:Lb], ref_scales)
             assert np.all(ref_scales[3, 1] == 1.0) and np.all(ref_codes[3, 128:256] == 0)
@@ -178,7 +183,8 @@ def test_mfma_append_epilogue_bit_exact(cache, path):
         assert np.all(np.abs(kr - kr_ref) <= step)
 
 
-@pytest.mark.parametrize("cache,ws", [("bf16", False), ("fp8", False), ("bf16", True), ("fp8", True)])
+@pytest.mark.parametrize("cache,ws", [("bf16", False), ("fp8", False), ("bf16", True), ("fp8", True),
+                                      ("fp8e8", False), ("fp8e8", True)])
 def test_decode_step_append_one_token_per_sequence(cache, ws):
     """The append of a decode step: one call that writes the newest token of
     each of 37 sequences (ragged lengths, shuffled pages; 37 is not a multiple
@@ -219,3 +225,41 @@ def test_decode_step_append_one_token_per_sequence(cache, ws):
             step = np.maximum(g * 2.0 ** -3, 2.0 ** -9 * scales[:Lb, :, None])
             assert np.all(np.abs(deq - c).reshape(Lb, 4, 128) <= step), b
             assert max_abs(rope[:Lb], kr) <= 2e-2 * np.abs(kr).max(), b
+
+
+@pytest.mark.parametrize("s_q,splits", [(1, 1), (2, 3)])
+def test_fp8_formats_agree_bitwise_on_power_of_two_tiles(s_q, splits):
+    """Latents whose every 1x128 tile has its largest magnitude at 448 * 2^k:
+    amax/448 is then itself a power of two, so both FP8 formats store the
+    same codes and scales, and the two decodes (one kernel per format) must
+    return the same bits."""
+    from mla_latent_kv_29_amd.session import DecodeSession
+    dims, dc, dr = V3, V3["d_c"], V3["d_rope"]
+    lengths = np.array([300, 65, 128])
+    bt, pool = inputs.block_table(lengths, dims["page_size"], "shuffled", 0, 4)
+    W = inputs.weights(dims, 0.006, torch.bfloat16, DEV, 0, 4)
+    sess = {k: DecodeSession(dims, "bf16", k, lengths, bt, pool, s_q, splits, DEV) for k in ("fp8", "fp8e8")}
+    g = torch.Generator(device="cpu").manual_seed(77)
+    for b, Lb in enumerate(lengths):
+        Lb = int(Lb)
+        u = (torch.rand((Lb, dc // 128, 128), generator=g) * 2 - 1) * 0.99
+        pos = torch.randint(0, 128, (Lb, dc // 128), generator=g)
+        sign = torch.where(torch.rand((Lb, dc // 128), generator=g) < 0.5, -1.0, 1.0)
+        u.scatter_(2, pos[:, :, None], sign[:, :, None])
+        k = torch.randint(-14, 3, (Lb, dc // 128, 1), generator=g).to(torch.float32)
+        c = (u * 448.0 * 2.0 ** k).reshape(Lb, dc).to(torch.bfloat16).to(DEV)
+        r = (torch.randn((Lb, dr), generator=g) * 0.5).to(torch.bfloat16).to(DEV)
+        for sx in sess.values():
+            sx.write(c, r, b, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(sess["fp8"].pages, sess["fp8e8"].pages)
+    hq = torch.cat([inputs.hidden(dims, b, int(Lb) - s_q, int(Lb), torch.bfloat16, DEV, 0, 4)
+                    for b, Lb in enumerate(lengths)], 0).contiguous()
+    res = {}
+    for kappa in (1.0, 56.0):
+        tau = tau_of(dims) * kappa
+        for key, sx in sess.items():
+            out, lse = sx.decode(hq, W, tau)
+            res[key] = (out.clone(), lse.clone())
+        torch.cuda.synchronize()
+        assert torch.equal(res["fp8"][0], res["fp8e8"][0]) and torch.equal(res["fp8"][1], res["fp8e8"][1]), kappa

@@ -57,14 +57,15 @@ def check(name, samples, kappas, all_heads=()):
     of them, and every head for the sequences in all_heads) with the oracle."""
     spec, dims, lengths, W, sess, gen_h, hq = full_session(name)
     s_q = spec["s_q"]
-    fp8 = spec["cache"] == "fp8"
+    fp8 = spec["cache"] in ("fp8", "fp8e8")
+    rule = "ue8m0" if spec["cache"] == "fp8e8" else "amax"
     Wn = {k: to_np(v) for k, v in W.items()}
     lat = {}
     for b in samples:
         Lb = int(lengths[b])
         c, r = oracle_latents(dims, Wn, gen_h, b, Lb)
         if fp8:
-            codes, scales = oracle.quantize_tiles(c)
+            codes, scales = oracle.quantize_tiles(c, scale_rule=rule)
             lat[b] = (c, r, oracle.dequantize_tiles(codes, scales), bf16_round(r))
         else:
             lat[b] = (c, r, None, None)
@@ -116,6 +117,12 @@ def test_full_v3_bf16_b4_l128k():
 def test_full_v3_fp8_b128_l8192_sq2():
     """8 of the 128 sequences, both query rows, every head of sequence 64."""
     check("v3_fp8_b128_l8192_sq2", [0, 17, 36, 64, 80, 99, 113, 127], [1.0, 56.0], all_heads=(64,))
+
+
+def test_full_v3_fp8e8_b128_l8192_sq2():
+    """The same batch in the power-of-two-scale FP8 cache: 4 of the 128
+    sequences, both query rows, every head of sequence 99."""
+    check("v3_fp8e8_b128_l8192_sq2", [0, 50, 99, 127], [1.0, 56.0], all_heads=(99,))
 
 
 def test_full_v3_bf16_b64_l4096_sq4():
