@@ -139,6 +139,7 @@ struct Ctx {
   uint32_t dma_ofs;           // lane part of a stage copy
   uint32_t dma_ofs_w;         // bf16: the same plus this wave's first copy (4096 * wave)
   uint32_t koff_e, koff_o;    // K fragment of the scores MFMA (even / odd k-step), inside its stage
+  uint32_t k8base;            // power-of-two FP8 cache: lane part of its K codes (16 token + 8 half)
   int kst;                    // 1 if this lane's score rows are tokens of the step's second stage
   uint32_t qr_base;           // RoPE query fragments: row of the lane's head, its k-half
   int qr_key;                 // ... and the chunk-pair permutation of that row
@@ -263,6 +264,38 @@ __device__ __forceinline__ f32x16 mfma_s_last(bf16x8 a, bf16x8 b, f32x16 c) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(c) : "v"(a), "v"(b));
   return c;
 }
+// The same for the power-of-two FP8 cache, whose K operand is written by
+// VALU conversions shortly before: two wait states ahead of the MFMA cover a
+// VALU write that the MFMA reads (the compiler does not look into the asm).
+__device__ __forceinline__ f32x16 mfma_s0_v(bf16x8 a, bf16x8 b) {
+  f32x16 c;
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ f32x16 mfma_s_v(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ f32x16 mfma_s_last_v(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+
+// Power-of-two FP8 cache: eight E4M3 codes (two dwords, channel order) times
+// the tile's scale 2^e, as bf16.  v_cvt_scalef32_pk_bf16_fp8 applies only
+// the exponent of its scale operand, which for these scales is the whole
+// scale, so every result is exact.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x2 lu32x2;
+__device__ __forceinline__ bf16x8 cvt8_pow2(unsigned w0, unsigned w1, float sc) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, sc, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, sc, true);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, sc, false);
+  const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, sc, true);
+  return bf16x8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+}
 
 // S^T[32 tokens][32 heads] of the step's two stages (rows 0-15: the first
 // stage, 16-31: the second) = K . Q^T over the 576 channels: 36 k-steps of
@@ -355,7 +388,40 @@ struct Fused {
   const StageCopy &cx, &cy;
   float ml;
   float x[16];
+  // power-of-two FP8 cache: the 4 tile scales of the lane's token, and the
+  // converted K operands of the next k-steps (two, so that a conversion never
+  // rewrites the operand of the MFMA just issued)
+  f32x4 ksc;
+  bf16x8 cv[2];
 };
+
+// Power-of-two FP8 cache, k-step K (a constant): the lane's raw K fragment,
+// read KD k-steps ahead from the fp8 stage.  Content k-steps: the 8 code
+// bytes of 16-channel chunk K, half lane/32, in the low half (chunk K of
+// token t at 256 K + 16 (t ^ x(K))); RoPE k-steps: 8 bf16 k^R channels, laid
+// out like the bf16 stage's chunks.
+template <int K>
+__device__ __forceinline__ bf16x8 kraw_e8(const Fused& F) {
+  const Ctx& c = F.c;
+  if constexpr (K < 32) {
+    const u32x2 w = *(lu32x2*)(F.kb + ((c.k8base ^ (uint32_t)(16 * slot_x(K))) + 256 * K));
+    const u32x4 r = __builtin_shufflevector(w, w, 0, 1, -1, -1);
+    return __builtin_bit_cast(bf16x8, r);
+  } else {
+    return *(lbf16x8*)(F.kb + F8_ROPE + ((K & 1) ? c.koff_o : c.koff_e) + 512 * (K - 32));
+  }
+}
+// ... and its MFMA operand: content codes widened with the tile's scale (tile
+// K/8), k^R as read.
+template <int K>
+__device__ __forceinline__ bf16x8 kop_e8(const Fused& F) {
+  if constexpr (K < 32) {
+    const u32x4 r = __builtin_bit_cast(u32x4, F.f[K % KD]);
+    return cvt8_pow2(r[0], r[1], F.ksc[K / 8]);
+  } else {
+    return F.f[K % KD];
+  }
+}
 
 __device__ __forceinline__ void read_v(Fused& F, const lu8* st) {
 #pragma unroll
@@ -379,21 +445,31 @@ __device__ __forceinline__ void pv_mfma(Fused& F) {
 // Part 1, k-step KS: score MFMA, K read KD ahead, and the P.V MFMA of stage
 // 2m-2 that follows it (after k-steps 3, 5, .., 33); the P^T fragment of
 // head block hb is read two P.V MFMAs before its first use.
-template <bool F8, int KS>
+template <bool F8, bool E8, int KS>
 __device__ __forceinline__ void part1(Fused& F) {
   const Ctx& c = F.c;
   if constexpr (KS == 26) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) F.r[q] = rope_q<F8>(c, q);
   }
-  {
+  if constexpr (E8) {
+    // operand of k-step KS converted one part earlier; convert the next one,
+    // then read the raw fragment KD k-steps ahead into the slot just used
+    const bf16x8 a = F.cv[KS & 1];
+    const bf16x8 q = KS < 32 ? F.qf[KS] : F.r[KS - 32];
+    if constexpr (KS == 0) F.sc = mfma_s0_v(a, q);
+    else if constexpr (KS < KSTEPS - 1) F.sc = mfma_s_v(a, q, F.sc);
+    else F.sc = mfma_s_last_v(a, q, F.sc);
+    if constexpr (KS + 1 < KSTEPS) F.cv[(KS + 1) & 1] = kop_e8<KS + 1>(F);
+    if constexpr (KS + KD < KSTEPS) F.f[KS % KD] = kraw_e8<KS + KD>(F);
+  } else {
     const bf16x8 a = F.f[KS % KD];
     const bf16x8 q = KS < 32 ? F.qf[KS] : F.r[KS - 32];
     if constexpr (KS == 0) F.sc = mfma_s0(a, q);
     else if constexpr (KS < KSTEPS - 1) F.sc = mfma_s(a, q, F.sc);
     else F.sc = mfma_s_last(a, q, F.sc);
+    if constexpr (KS + KD < KSTEPS) F.f[KS % KD] = kfrag(F.kb, c, KS + KD);
   }
-  if constexpr (KS + KD < KSTEPS) F.f[KS % KD] = kfrag(F.kb, c, KS + KD);
   constexpr int t = (KS - 3) / 2;
   if constexpr (KS >= 3 && (KS - 3) % 2 == 0 && t < 16) {
     pv_mfma<t>(F);
@@ -408,9 +484,9 @@ __device__ __forceinline__ void part1(Fused& F) {
   }
   __builtin_amdgcn_sched_barrier(0);
 }
-template <bool F8, int... K>
+template <bool F8, bool E8, int... K>
 __device__ __forceinline__ void part1_all(Fused& F, std::integer_sequence<int, K...>) {
-  (part1<F8, K>(F), ...);
+  (part1<F8, E8, K>(F), ...);
 }
 
 // Part 2, P.V MFMA T of stage 2m-1 and the softmax item that follows it.
@@ -549,9 +625,37 @@ __device__ __forceinline__ void widen_stage(const Ctx& c, int fs, int bs) {
   // k^R chunk cq (threads < 128): the same slot order in both (x(64 + m) = x(m))
   if (tid < 128) *(__attribute__((address_space(3))) bf16x8*)(dst + 256 * 64) = *(lbf16x8*)(f8 + F8_ROPE + dofs);
 }
-template <bool F8>
+// Power-of-two FP8 cache: the bf16 V image (the 512 latent channels) of the
+// fp8 stage in slot fs, written to bf16 slot bs, exact (code * 2^e); tokens
+// from nvalid on are written as zeros, so that whatever bytes the page holds
+// past the end of the split cannot turn a zero weight into NaN in P.V.
+// Thread: token tid%16, 8-channel chunks tid/16 + 16 j (scale tile j).
+__device__ __forceinline__ void widen_v(const Ctx& c, int fs, int bs, int nvalid) {
+  const int tid = c.wave * 64 + c.lane, t = tid & 15, cq = tid >> 4;
+  const int dofs = 256 * cq + 16 * (t ^ slot_x(cq));
+  const lu8* f8 = c.lds + Lay<true>::F8_OFF + fs * F8_ST;
+  const lu8* src = f8 + 256 * (cq >> 1) + 16 * (t ^ slot_x(cq >> 1)) + 8 * (cq & 1);
+  const f32x4 sc = *(__attribute__((address_space(3))) const f32x4*)(f8 + F8_SCALES + 16 * t);
+  lu8* dst = c.lds + bs * ST_BYTES + dofs;
+  const bool live = t < nvalid;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x2 code = *(lu32x2*)(src + 2048 * j);
+    const bf16x8 v = cvt8_pow2(code[0], code[1], sc[j]);
+    *(__attribute__((address_space(3))) bf16x8*)(dst + 4096 * j) = live ? v : bf16x8{};
+  }
+}
+
+// E8 (power-of-two FP8 cache) step m, with one barrier: the barrier
+// publishes the fp8 stages 2m, 2m+1, the V images of 2m-2, 2m-1 (widened
+// during step m-1) and the weights of step m-1; the block then issues the
+// copies of 2m+3, 2m+4, widens the V images of 2m, 2m+1 (for step m+1),
+// scores 2m, 2m+1 with K read from the fp8 stages and widened in registers,
+// and multiplies the weights of 2m-2, 2m-1 with their V images.
+template <bool F8, bool E8>
 __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], float& m_ref, float& m_all,
                                          float& l_run, f32x16 (&o)[4][4]) {
+  static_assert(!E8 || F8, "the power-of-two format is an FP8 cache");
   using Ly = Lay<F8>;
   zero_p1<F8>(c);
   bool ovf = false;
@@ -560,7 +664,13 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
   for (int m = 0; m < c.nsteps; ++m) {
     wait_step<F8>(c, m);
     ring_barrier();
-    if constexpr (F8) {
+    if constexpr (E8) {
+      issue_stage<F8>(c, 2 * m + 3, wrap5(fa + 3));
+      issue_stage<F8>(c, 2 * m + 4, wrap5(fa + 4));
+      const int nv_last = c.ntok - (c.nst - 1) * T;
+      widen_v(c, fa, sa, 2 * m == c.nst - 1 ? nv_last : T);
+      if (2 * m + 1 < c.nst) widen_v(c, wrap5(fa + 1), wrap<F8>(sa + 1), 2 * m + 1 == c.nst - 1 ? nv_last : T);
+    } else if constexpr (F8) {
       // this step's two stages into the bf16 slots freed by the last P.V
       widen_stage(c, fa, sa);
       if (2 * m + 1 < c.nst) widen_stage(c, wrap5(fa + 1), wrap<F8>(sa + 1));
@@ -580,18 +690,31 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
       cy = plan_stage<F8>(c, 2 * m + 4, wrap<F8>(sa + 4));
     }
     const int sb = 2 * m + 1 < c.nst ? wrap<F8>(sa + 1) : sa;
-    if ((c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);
+    if (!E8 && (c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);  // E8: widen_v zeroes
     const lu8* stA = c.lds + sa * ST_BYTES;
     const lu8* stB = c.lds + sb * ST_BYTES;
-    Fused F{c, m, c.kst ? stB : stA, qf, {}, {}, {}, va, vb, prd, {}, {}, o, m_ref, m_all, l_run, ovf,
+    // K source: the lane's bf16 stage, or (E8) its fp8 stage
+    const int fb = 2 * m + 1 < c.nst ? wrap5(fa + 1) : fa;
+    const lu8* kb = E8 ? c.lds + Ly::F8_OFF + (c.kst ? fb : fa) * F8_ST : (c.kst ? stB : stA);
+    Fused F{c, m, kb, qf, {}, {}, {}, va, vb, prd, {}, {}, o, m_ref, m_all, l_run, ovf,
             c.lds + Ly::P_OFF + (m & 1) * P_BYTES + c.pw_ofs, cx, cy, 0.0f, {}};
+    if constexpr (E8) {
+      static_assert(KD == 4, "E8 prologue");
+      F.f[0] = kraw_e8<0>(F);
+      F.f[1] = kraw_e8<1>(F);
+      F.f[2] = kraw_e8<2>(F);
+      F.f[3] = kraw_e8<3>(F);
+      F.ksc = *(__attribute__((address_space(3))) const f32x4*)(kb + F8_SCALES + 16 * (c.lane & 15));
+      F.cv[0] = kop_e8<0>(F);
+    } else {
 #pragma unroll
-    for (int d = 0; d < KD; ++d) F.f[d] = kfrag(F.kb, c, d);
+      for (int d = 0; d < KD; ++d) F.f[d] = kfrag(F.kb, c, d);
+    }
     read_v(F, va);
     read_p(F, 0, 0);
     read_p(F, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
-    part1_all<F8>(F, std::make_integer_sequence<int, KSTEPS>{});
+    part1_all<F8, E8>(F, std::make_integer_sequence<int, KSTEPS>{});
     mask(c, F.sc, c.ntok - 2 * m * T);
     part2_all<F8>(F, std::make_integer_sequence<int, 16>{});
     sa = wrap<F8>(sa + 2);
@@ -657,7 +780,7 @@ __device__ __forceinline__ void write_out(const Ctx& c, const f32x16 (&o)[4][4],
   }
 }
 
-template <bool F8>
+template <bool F8, bool E8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__ qt,
                 const uint8_t* __restrict__ pages, size_t page_bytes, const int32_t* __restrict__ bt, int max_pages,
@@ -748,6 +871,7 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
   c.kst = (lane >> 4) & 1;
   c.koff_e = (uint32_t)(256 * hi + 16 * (i16 ^ slot_x(hi)));
   c.koff_o = (uint32_t)(256 * hi + 16 * (i16 ^ slot_x(2 + hi)));
+  c.k8base = (uint32_t)(16 * i16 + 8 * hi);
   // RoPE query fragment r (k-step 32 + r): chunk 2r + lane/32 of row hq,
   // stored at 16 (chunk ^ key), key = (hq/2) % 8
   {
@@ -786,7 +910,7 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
       for (int hb = 0; hb < 4; ++hb) o[i][hb] = f32x16{};
     m_all = -INFINITY;
     l_run = 0.0f;
-    const bool ovf = run_pass<F8>(c, qf, m_ref, m_all, l_run, o);
+    const bool ovf = run_pass<F8, E8>(c, qf, m_ref, m_all, l_run, o);
     const bool again = __syncthreads_or(ovf);  // also: every wave is done with the ring
     if (pass > 0 || !again) break;
     m_ref = m_all;
@@ -799,13 +923,13 @@ void k_attn_v3b(int s_q, int S, int pps, int P_items, const bf16_t* __restrict__
 
 }  // namespace
 
-template <bool F8>
+template <bool F8, bool E8 = false>
 static hipError_t launch_attn(const DecodeArgs& a) {
   constexpr int lds = Lay<F8>::LDS_BYTES;
-  MLA_TRY(lds_limit((const void*)&k_attn_v3b<F8>, lds));
+  MLA_TRY(lds_limit((const void*)&k_attn_v3b<F8, E8>, lds));
   const int P_items = a.batch * a.S;
   const int grid = ((P_items + 7) / 8) * 8 * a.s_q;
-  return launch(&k_attn_v3b<F8>, dim3(grid), dim3(256), lds, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
+  return launch(&k_attn_v3b<F8, E8>, dim3(grid), dim3(256), lds, a.stream, a.s_q, a.S, a.pages_per_split, P_items,
                 (const bf16_t*)(a.ws + a.L.qt), a.pages, a.g.page_bytes, a.block_table, a.max_pages, a.seqlens,
                 (bf16_t*)(a.ws + a.L.opart), (float*)(a.ws + a.L.lpart), (int32_t*)(a.ws + a.L.header), a.batch);
 }
@@ -814,7 +938,7 @@ hipError_t fast_attention(const DecodeArgs& a) {
   if (is_fp8_cache(a.cache_dtype)) {
     // the page geometry the fp8 stage copies are compiled for
     if (a.g.fp8_scale_off != (size_t)F8_PG_SCALES || a.g.fp8_rope_off != (size_t)F8_PG_ROPE) return hipErrorInvalidValue;
-    return launch_attn<true>(a);
+    return a.cache_dtype == MLA_FP8_E4M3_E8 ? launch_attn<true, true>(a) : launch_attn<true>(a);
   }
   return launch_attn<false>(a);
 }
