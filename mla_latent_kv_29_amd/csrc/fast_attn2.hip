@@ -393,7 +393,36 @@ struct Fused {
   // rewrites the operand of the MFMA just issued)
   f32x4 ksc;
   bf16x8 cv[2];
+  // ... and the V images of this step's stages, widened between the score
+  // MFMAs: eight jobs (stage k/4, tile k%4) of one 8-channel chunk a thread
+  const lu8* wsrc[2];            // fp8 stages (wave-uniform)
+  lu8* wdst[2];                  // their bf16 V slots
+  int wnv[2];                    // tokens of each stage to keep (the rest are zeroed)
+  uint32_t wr_ofs, ww_ofs, ws_ofs;  // the thread's code, image and scale offsets
+  int wt;                        // the thread's token
+  u32x2 wcode;
+  float wscl;
 };
+
+// E8 V-image job K (a constant): read the thread's 8 codes and their tile
+// scale; two parts later, widen and store them (tokens past the split's end
+// as zeros, so that whatever bytes the page holds there cannot turn a zero
+// weight into NaN in P.V).  Thread: token tid%16, 8-channel chunk tid/16 + 16 j.
+// Without a second stage, wsrc[1] is the first stage and wdst[1] a slot that
+// nothing reads (the next P.V takes the first stage's image for both), so
+// the jobs run unconditionally.
+template <int K>
+__device__ __forceinline__ void wload(Fused& F) {
+  constexpr int st = K / 4, j = K % 4;
+  F.wcode = *(lu32x2*)(F.wsrc[st] + F.wr_ofs + 2048 * j);
+  F.wscl = *(__attribute__((address_space(3))) const float*)(F.wsrc[st] + F.ws_ofs + 4 * j);
+}
+template <int K>
+__device__ __forceinline__ void wstore(Fused& F) {
+  constexpr int st = K / 4, j = K % 4;
+  const bf16x8 v = cvt8_pow2(F.wcode[0], F.wcode[1], F.wscl);
+  *(__attribute__((address_space(3))) bf16x8*)(F.wdst[st] + F.ww_ofs + 4096 * j) = F.wt < F.wnv[st] ? v : bf16x8{};
+}
 
 // Power-of-two FP8 cache, k-step K (a constant): the lane's raw K fragment,
 // read KD k-steps ahead from the fp8 stage.  Content k-steps: the 8 code
@@ -481,6 +510,11 @@ __device__ __forceinline__ void part1(Fused& F) {
   // stage copies: the first at k-steps 1, 8, 15, 22, 29
   if constexpr (!F8) {
     if constexpr (KS % 7 == 1) copy_at(c, F.cx, KS / 7);
+  }
+  // E8 V images: job k read at k-step 1 + 4k, widened and stored at 3 + 4k
+  if constexpr (E8) {
+    if constexpr (KS % 4 == 1 && KS / 4 < 8) wload<KS / 4>(F);
+    if constexpr (KS % 4 == 3 && KS / 4 < 8) wstore<KS / 4>(F);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -667,9 +701,6 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
     if constexpr (E8) {
       issue_stage<F8>(c, 2 * m + 3, wrap5(fa + 3));
       issue_stage<F8>(c, 2 * m + 4, wrap5(fa + 4));
-      const int nv_last = c.ntok - (c.nst - 1) * T;
-      widen_v(c, fa, sa, 2 * m == c.nst - 1 ? nv_last : T);
-      if (2 * m + 1 < c.nst) widen_v(c, wrap5(fa + 1), wrap<F8>(sa + 1), 2 * m + 1 == c.nst - 1 ? nv_last : T);
     } else if constexpr (F8) {
       // this step's two stages into the bf16 slots freed by the last P.V
       widen_stage(c, fa, sa);
@@ -706,6 +737,20 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
       F.f[3] = kraw_e8<3>(F);
       F.ksc = *(__attribute__((address_space(3))) const f32x4*)(kb + F8_SCALES + 16 * (c.lane & 15));
       F.cv[0] = kop_e8<0>(F);
+      // the V images of stages 2m, 2m+1 (for step m+1) go to the bf16 slots of
+      // 2m-4, 2m-3, multiplied last step
+      const int nv_last = c.ntok - (c.nst - 1) * T;
+      const int tid = c.wave * 64 + c.lane, cq = tid >> 4;
+      F.wt = tid & 15;
+      F.wr_ofs = (uint32_t)(256 * (cq >> 1) + 16 * (F.wt ^ slot_x(cq >> 1)) + 8 * (cq & 1));
+      F.ww_ofs = (uint32_t)(256 * cq + 16 * (F.wt ^ slot_x(cq)));
+      F.ws_ofs = (uint32_t)(F8_SCALES + 16 * F.wt);
+      F.wsrc[0] = c.lds + Ly::F8_OFF + fa * F8_ST;
+      F.wsrc[1] = c.lds + Ly::F8_OFF + fb * F8_ST;
+      F.wdst[0] = c.lds + sa * ST_BYTES;
+      F.wdst[1] = c.lds + wrap<F8>(sa + 1) * ST_BYTES;
+      F.wnv[0] = 2 * m == c.nst - 1 ? nv_last : T;
+      F.wnv[1] = 2 * m + 1 == c.nst - 1 ? nv_last : T;
     } else {
 #pragma unroll
       for (int d = 0; d < KD; ++d) F.f[d] = kfrag(F.kb, c, d);
