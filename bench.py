@@ -88,6 +88,58 @@ def measured_traffic(workload, cache):
     return rec.get("hbm_bytes_per_launch")
 
 
+def record_traffic(workload, fetch_csv, write_csv):
+    """Writes the HBM traffic of the workload's attention kernel into the
+    traffic record: the two counter files are `rocprofv3 --pmc FETCH_SIZE`
+    and `--pmc WRITE_SIZE` runs of `bench.py --workload W --steps 3 --warmup 1
+    --no-cpu-baseline --copy-calibration 1024`.  Each counter is averaged per
+    dispatch of the attention kernel and scaled by what it reads for the
+    plain copy of 1024 MiB (torch.neg over fp32) in the same run."""
+    import csv
+    from mla_latent_kv_29_amd import inputs
+    prefill = workload in inputs.PREFILL_WORKLOADS
+    cache = "prefill" if prefill else inputs.WORKLOADS[workload]["cache"]
+    key = "k_prefill_attn" if prefill else "k_attn_v3b"
+
+    def per_dispatch(path, counter):
+        vals = {"attn": {}, "copy": {}}
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                kind = "attn" if key in row["Kernel_Name"] else "copy" if "neg_kernel_cuda" in row["Kernel_Name"] \
+                    else None
+                if kind:
+                    d = vals[kind]
+                    d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+        if not vals["attn"] or not vals["copy"]:
+            raise SystemExit(f"{path}: no {key} or copy dispatch with {counter}")
+        return (sum(vals["attn"].values()) / len(vals["attn"]), sum(vals["copy"].values()) / len(vals["copy"]))
+
+    fa, fc = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wa, wc = per_dispatch(write_csv, "WRITE_SIZE")
+    copy_bytes = 1024 * 1024 * 1024
+    fscale, wscale = copy_bytes / (fc * 1024), copy_bytes / (wc * 1024)
+    cmd = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- python3 /root/repo/bench.py "
+           f"--workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration 1024")
+    rec = {"kernel_source_sha256": attn_source_sha(cache), "sources": ATTN_SOURCES[cache],
+           "fetch_kib_per_dispatch": fa, "write_kib_per_dispatch": wa, "copy_fetch_kib": fc, "copy_write_kib": wc,
+           "copy_bytes_each_way": copy_bytes, "fetch_scale": fscale, "write_scale": wscale,
+           "hbm_bytes_per_launch": fa * 1024 * fscale + wa * 1024 * wscale,
+           "command_fetch": cmd.format(c="FETCH_SIZE"), "command_write": cmd.format(c="WRITE_SIZE")}
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            allrec = json.load(fh)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allrec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({"workload": workload, "hbm_bytes_per_launch": rec["hbm_bytes_per_launch"],
+                      "fetch_scale": fscale, "write_scale": wscale}))
+
+
 def cpu_baseline(spec, dims, W, gen_h, lengths, budget_s, max_seqs=64):
     """The float64 oracle (decode from cached latents, explicit per-head k^C and
     v^C) on a bounded sample of sequences of the same workload; cached
@@ -685,7 +737,13 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB three times (untimed), as the "
                          "reference for hardware byte counters")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store the attention's HBM bytes of --workload from two rocprofv3 counter files "
+                         "(FETCH_SIZE, WRITE_SIZE) in profiles/attn_traffic.json; no GPU work")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures one GPU's "
@@ -849,7 +907,8 @@ def main():
                               "step_roofline",
                      "bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": measured_traffic(args.workload, spec["cache"]),
-                     "kernel": ("k_attn_v3b<false>" if spec["cache"] == "bf16" else "k_attn_v3b<true>") + " (mla_decode_attend)",
+                     "kernel": {"bf16": "k_attn_v3b<false>", "fp8": "k_attn_v3b<true>", "fp8e8": "k_attn_v3b<true, true>"}[spec["cache"]]
+                     + " (mla_decode_attend)",
                      "attn_ms_mean": float(np.mean(a_ms))},
         "step_roofline": {"t_bound_us": t_bound * 1e6, "frac": t_bound / (ms_per_step * 1e-3),
                           "step_bytes": alg["step_bytes"], "step_flops": alg["step_flops"]},

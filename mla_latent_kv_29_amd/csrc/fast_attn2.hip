@@ -48,6 +48,17 @@
 // accumulation.  The fp8 copies are issued in the widening phase rather than
 // between the score MFMAs, which keeps the step loop free of spills.
 //
+// FP8 cache with power-of-two (UE8M0) scales, a format the lesson's
+// continuation of §3.5 reports DeepSeek V3.1 moving to: here
+// v_cvt_scalef32_pk_bf16_fp8, which applies only the exponent of its scale
+// operand, widens codes exactly in one instruction per two values, so the
+// step needs one barrier.  Each lane reads its K fragments from the fp8
+// stage (8 code bytes, half the LDS bytes of a bf16 fragment) and widens
+// them in registers one k-step ahead of their MFMA; V is still multiplied
+// from bf16 images in LDS, which the block writes one step ahead, as eight
+// small jobs between the score MFMAs.  On data that both formats store alike
+// the two kernels give the same bits.
+//
 // Softmax reference: the first step's row maximum, with 96 log2 units of
 // headroom, so O is never rescaled.  The pass also collects the exact row
 // maximum.  If some score exceeded the reference by more than the headroom,
@@ -659,33 +670,13 @@ __device__ __forceinline__ void widen_stage(const Ctx& c, int fs, int bs) {
   // k^R chunk cq (threads < 128): the same slot order in both (x(64 + m) = x(m))
   if (tid < 128) *(__attribute__((address_space(3))) bf16x8*)(dst + 256 * 64) = *(lbf16x8*)(f8 + F8_ROPE + dofs);
 }
-// Power-of-two FP8 cache: the bf16 V image (the 512 latent channels) of the
-// fp8 stage in slot fs, written to bf16 slot bs, exact (code * 2^e); tokens
-// from nvalid on are written as zeros, so that whatever bytes the page holds
-// past the end of the split cannot turn a zero weight into NaN in P.V.
-// Thread: token tid%16, 8-channel chunks tid/16 + 16 j (scale tile j).
-__device__ __forceinline__ void widen_v(const Ctx& c, int fs, int bs, int nvalid) {
-  const int tid = c.wave * 64 + c.lane, t = tid & 15, cq = tid >> 4;
-  const int dofs = 256 * cq + 16 * (t ^ slot_x(cq));
-  const lu8* f8 = c.lds + Lay<true>::F8_OFF + fs * F8_ST;
-  const lu8* src = f8 + 256 * (cq >> 1) + 16 * (t ^ slot_x(cq >> 1)) + 8 * (cq & 1);
-  const f32x4 sc = *(__attribute__((address_space(3))) const f32x4*)(f8 + F8_SCALES + 16 * t);
-  lu8* dst = c.lds + bs * ST_BYTES + dofs;
-  const bool live = t < nvalid;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x2 code = *(lu32x2*)(src + 2048 * j);
-    const bf16x8 v = cvt8_pow2(code[0], code[1], sc[j]);
-    *(__attribute__((address_space(3))) bf16x8*)(dst + 4096 * j) = live ? v : bf16x8{};
-  }
-}
-
 // E8 (power-of-two FP8 cache) step m, with one barrier: the barrier
 // publishes the fp8 stages 2m, 2m+1, the V images of 2m-2, 2m-1 (widened
 // during step m-1) and the weights of step m-1; the block then issues the
 // copies of 2m+3, 2m+4, widens the V images of 2m, 2m+1 (for step m+1),
 // scores 2m, 2m+1 with K read from the fp8 stages and widened in registers,
-// and multiplies the weights of 2m-2, 2m-1 with their V images.
+// and multiplies the weights of 2m-2, 2m-1 with their V images; the V-image
+// jobs of 2m, 2m+1 run between the score MFMAs (wload / wstore).
 template <bool F8, bool E8>
 __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], float& m_ref, float& m_all,
                                          float& l_run, f32x16 (&o)[4][4]) {
@@ -721,7 +712,7 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
       cy = plan_stage<F8>(c, 2 * m + 4, wrap<F8>(sa + 4));
     }
     const int sb = 2 * m + 1 < c.nst ? wrap<F8>(sa + 1) : sa;
-    if (!E8 && (c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);  // E8: widen_v zeroes
+    if (!E8 && (c.nst - 1) >> 1 == m) zero_tail(c, (c.nst - 1) & 1 ? sb : sa);  // E8: wstore zeroes
     const lu8* stA = c.lds + sa * ST_BYTES;
     const lu8* stB = c.lds + sb * ST_BYTES;
     // K source: the lane's bf16 stage, or (E8) its fp8 stage
