@@ -41,9 +41,11 @@ def test_v3_bf16_ragged(splits, kappa):
     check_all(case, out, lse, tau, TOL_BF16)
 
 
-def test_v3_bf16_fast_matches_generic():
-    """The MFMA path and the generic VALU path agree (same inputs)."""
-    case = Case(V3, "bf16", "bf16", [200, 77], s_q=1, table="shuffled", wl=1, num_splits=2)
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp8e8"])
+def test_v3_bf16_fast_matches_generic(cache):
+    """The MFMA path and the generic VALU path agree (same inputs, the same
+    cache bytes: the generic path dequantises FP8 codes in fp32)."""
+    case = Case(V3, "bf16", cache, [200, 77], s_q=1, table="shuffled", wl=1, num_splits=2)
     tau = tau_of(V3) * 30.0
     fast, lfast, _ = case.run(tau)
     os.environ["MLA_FORCE_GENERIC"] = "1"

@@ -29,7 +29,7 @@ def noalloc_outputs(case, tau):
     return out, lse
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp8e8"])
 def test_noalloc_decode_step_equals_decode_and_combine(cache):
     tau = tau_of(V3) * 20.0
     cases = [Case(V3, "bf16", cache, [1024] * 48 + [700, 3, 0, 65], s_q=1, table="shuffled", wl=1, num_splits=0),
