@@ -275,23 +275,6 @@ __device__ __forceinline__ f32x16 mfma_s_last(bf16x8 a, bf16x8 b, f32x16 c) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(c) : "v"(a), "v"(b));
   return c;
 }
-// The same for the power-of-two FP8 cache, whose K operand is written by
-// VALU conversions shortly before: two wait states ahead of the MFMA cover a
-// VALU write that the MFMA reads (the compiler does not look into the asm).
-__device__ __forceinline__ f32x16 mfma_s0_v(bf16x8 a, bf16x8 b) {
-  f32x16 c;
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
-  return c;
-}
-__device__ __forceinline__ f32x16 mfma_s_v(bf16x8 a, bf16x8 b, f32x16 c) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-  return c;
-}
-__device__ __forceinline__ f32x16 mfma_s_last_v(bf16x8 a, bf16x8 b, f32x16 c) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(c) : "v"(a), "v"(b));
-  return c;
-}
-
 // Power-of-two FP8 cache: eight E4M3 codes (two dwords, channel order) times
 // the tile's scale 2^e, as bf16.  v_cvt_scalef32_pk_bf16_fp8 applies only
 // the exponent of its scale operand, which for these scales is the whole
@@ -400,10 +383,10 @@ struct Fused {
   float ml;
   float x[16];
   // power-of-two FP8 cache: the 4 tile scales of the lane's token, and the
-  // converted K operands of the next k-steps (two, so that a conversion never
-  // rewrites the operand of the MFMA just issued)
+  // converted K operands of the next k-steps (three: a conversion runs two
+  // k-steps ahead and never rewrites the operand of the MFMA just issued)
   f32x4 ksc;
-  bf16x8 cv[2];
+  bf16x8 cv[3];
   // ... and the V images of this step's stages, widened between the score
   // MFMAs: eight jobs (stage k/4, tile k%4) of one 8-channel chunk a thread
   const lu8* wsrc[2];            // fp8 stages (wave-uniform)
@@ -493,14 +476,16 @@ __device__ __forceinline__ void part1(Fused& F) {
     for (int q = 0; q < 4; ++q) F.r[q] = rope_q<F8>(c, q);
   }
   if constexpr (E8) {
-    // operand of k-step KS converted one part earlier; convert the next one,
-    // then read the raw fragment KD k-steps ahead into the slot just used
-    const bf16x8 a = F.cv[KS & 1];
+    // operand of k-step KS converted two parts earlier (a whole MFMA lies
+    // between a conversion's VALU writes and the MFMA that reads them);
+    // convert the one after next, then read the raw fragment KD k-steps
+    // ahead into the slot just used
+    const bf16x8 a = F.cv[KS % 3];
     const bf16x8 q = KS < 32 ? F.qf[KS] : F.r[KS - 32];
-    if constexpr (KS == 0) F.sc = mfma_s0_v(a, q);
-    else if constexpr (KS < KSTEPS - 1) F.sc = mfma_s_v(a, q, F.sc);
-    else F.sc = mfma_s_last_v(a, q, F.sc);
-    if constexpr (KS + 1 < KSTEPS) F.cv[(KS + 1) & 1] = kop_e8<KS + 1>(F);
+    if constexpr (KS == 0) F.sc = mfma_s0(a, q);
+    else if constexpr (KS < KSTEPS - 1) F.sc = mfma_s(a, q, F.sc);
+    else F.sc = mfma_s_last(a, q, F.sc);
+    if constexpr (KS + 2 < KSTEPS) F.cv[(KS + 2) % 3] = kop_e8<KS + 2>(F);
     if constexpr (KS + KD < KSTEPS) F.f[KS % KD] = kraw_e8<KS + KD>(F);
   } else {
     const bf16x8 a = F.f[KS % KD];
@@ -728,6 +713,7 @@ __device__ __forceinline__ bool run_pass(const Ctx& c, const bf16x8 (&qf)[32], f
       F.f[3] = kraw_e8<3>(F);
       F.ksc = *(__attribute__((address_space(3))) const f32x4*)(kb + F8_SCALES + 16 * (c.lane & 15));
       F.cv[0] = kop_e8<0>(F);
+      F.cv[1] = kop_e8<1>(F);
       // the V images of stages 2m, 2m+1 (for step m+1) go to the bf16 slots of
       // 2m-4, 2m-3, multiplied last step
       const int nv_last = c.ntok - (c.nst - 1) * T;
