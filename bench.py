@@ -74,16 +74,19 @@ def attn_source_sha(cache):
     return h.hexdigest()
 
 
-def measured_traffic(workload, cache):
+def measured_traffic(workload, cache, splits=None):
     """HBM bytes per attention launch from the committed counter measurement
     (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known size), or None if
-    there is none for this workload or the kernel changed since."""
+    there is none for this workload, the kernel changed since, or it was taken
+    at another split count (the partial rows written depend on it)."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh).get(workload)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel_source_sha256") != attn_source_sha(cache):
+        return None
+    if splits is not None and rec.get("splits", splits) != splits:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -116,13 +119,23 @@ def record_traffic(workload, fetch_csv, write_csv):
             raise SystemExit(f"{path}: no {key} or copy dispatch with {counter}")
         return (sum(vals["attn"].values()) / len(vals["attn"]), sum(vals["copy"].values()) / len(vals["copy"]))
 
+    splits = None
+    if not prefill:  # the split count the counter runs used: the session's plan for the workload's lengths
+        from mla_latent_kv_29_amd import _lib as L
+        spec = inputs.WORKLOADS[workload]
+        dims = spec["dims"]
+        lengths = inputs.seqlens(spec["lengths"], spec["batch"], 0, spec["index"])
+        table, _ = inputs.block_table(lengths, dims["page_size"], spec["table"], 0, spec["index"])
+        cd = L.make_dims(dims)
+        plan = L.mla_plan_splits(cd, spec["batch"], spec["s_q"], table.shape[1], lengths)
+        splits = L.mla_decode_splits(cd, spec["batch"], spec["s_q"], table.shape[1], plan)
     fa, fc = per_dispatch(fetch_csv, "FETCH_SIZE")
     wa, wc = per_dispatch(write_csv, "WRITE_SIZE")
     copy_bytes = 1024 * 1024 * 1024
     fscale, wscale = copy_bytes / (fc * 1024), copy_bytes / (wc * 1024)
     cmd = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- python3 /root/repo/bench.py "
            f"--workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration 1024")
-    rec = {"kernel_source_sha256": attn_source_sha(cache), "sources": ATTN_SOURCES[cache],
+    rec = {"kernel_source_sha256": attn_source_sha(cache), "sources": ATTN_SOURCES[cache], "splits": splits,
            "fetch_kib_per_dispatch": fa, "write_kib_per_dispatch": wa, "copy_fetch_kib": fc, "copy_write_kib": wc,
            "copy_bytes_each_way": copy_bytes, "fetch_scale": fscale, "write_scale": wscale,
            "hbm_bytes_per_launch": fa * 1024 * fscale + wa * 1024 * wscale,
@@ -906,7 +919,7 @@ def main():
         "roofline": {"scope": "dominant kernel (the split-KV attention launch) only; the whole step is in "
                               "step_roofline",
                      "bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                     "traffic": measured_traffic(args.workload, spec["cache"]),
+                     "traffic": measured_traffic(args.workload, spec["cache"], sess.num_splits),
                      "kernel": {"bf16": "k_attn_v3b<false>", "fp8": "k_attn_v3b<true>", "fp8e8": "k_attn_v3b<true, true>"}[spec["cache"]]
                      + " (mla_decode_attend)",
                      "attn_ms_mean": float(np.mean(a_ms))},

@@ -173,6 +173,18 @@ MLA_API int mla_cache_write(const mla_dims* dims, int32_t act_dtype, const void*
 MLA_API int32_t mla_default_splits(const mla_dims* dims, int32_t batch, int32_t s_q,
                            int32_t max_pages);
 
+/* Split count from the sequences' lengths, for callers that know them on the
+ * host (a serving loop keeps them): seqlens is a HOST array [batch], the
+ * values of the device seqlens that mla_decode will read.  When the longest
+ * length is within 1/16 of the mean, the smallest count that gives one
+ * (sequence, query block, split) work item per compute unit, without the
+ * page cap of mla_default_splits (whose shorter items only pay off when
+ * lengths are ragged); otherwise mla_default_splits.  Pass the result as
+ * num_splits.  0 for invalid arguments (NULL, a length below 0 or above
+ * max_pages * page_size).                                                   */
+MLA_API int32_t mla_plan_splits(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                int32_t max_pages, const int32_t* seqlens);
+
 /* Output projection of the attention layer: for each of `rows` rows,
  *     y_r = W^O [o_{r,1}; o_{r,2}; ...; o_{r,H}]
  * (the W_O of the attention_params docstring of "Читаем техотчёт

@@ -8,7 +8,7 @@ C names, `session` keeps the device buffers of one batch, `inputs` draws the
 seeded synthetic inputs.
 """
 from . import _lib
-from ._lib import (mla_page_bytes, mla_cache_append, mla_cache_write, mla_default_splits, mla_decode_splits,
+from ._lib import (mla_page_bytes, mla_cache_append, mla_cache_write, mla_default_splits, mla_plan_splits, mla_decode_splits,
                    mla_workspace_bytes, mla_decode, mla_decode_query, mla_decode_attend, mla_combine,
                    mla_prefill_workspace_bytes, mla_prefill, mla_prefill_project, mla_prefill_attend,
                    mla_output_project_workspace_bytes, mla_output_project, mla_fp8_quantize_weight,
@@ -17,7 +17,7 @@ from ._lib import (mla_page_bytes, mla_cache_append, mla_cache_write, mla_defaul
                    status_str, version, make_dims,
                    MLAError, MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_E8)
 
-__all__ = ["mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits", "mla_decode_splits",
+__all__ = ["mla_page_bytes", "mla_cache_append", "mla_cache_write", "mla_default_splits", "mla_plan_splits", "mla_decode_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",

@@ -15,7 +15,7 @@ MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE = 0, -1, -2, -3
 MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = -4, -5, -6, -7
 MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_E8 = 0, 1, 2, 3
 
-EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_append_workspace_bytes", "mla_cache_append_ws", "mla_cache_write", "mla_default_splits", "mla_decode_splits",
+EXPORTS = ("mla_page_bytes", "mla_cache_append", "mla_append_workspace_bytes", "mla_cache_append_ws", "mla_cache_write", "mla_default_splits", "mla_plan_splits", "mla_decode_splits",
            "mla_workspace_bytes", "mla_decode", "mla_decode_query", "mla_decode_attend", "mla_combine",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_project", "mla_prefill_attend",
            "mla_output_project_workspace_bytes", "mla_output_project", "mla_fp8_quantize_weight",
@@ -62,6 +62,7 @@ def _load():
         "mla_cache_append_ws": (ctypes.c_int, [D, I32, P, I32, P, P, P, P, C, P, I32, P, SZ, P]),
         "mla_cache_write": (ctypes.c_int, [D, I32, P, P, I32, P, P, C, P, I32, P]),
         "mla_default_splits": (I32, [D, I32, I32, I32]),
+        "mla_plan_splits": (I32, [D, I32, I32, I32, P]),
         "mla_decode_splits": (I32, [D, I32, I32, I32, I32]),
         "mla_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
         "mla_decode": (ctypes.c_int, [D, I32, P, I32, I32, P, P, P, C, P, I32, P, F, I32, P, SZ, P]),
@@ -205,6 +206,16 @@ def mla_mtp_tokens_per_step(acceptance, depth):
 
 def mla_default_splits(dims, batch, s_q, max_pages):
     return int(_lib.mla_default_splits(ctypes.byref(dims), int(batch), int(s_q), int(max_pages)))
+
+
+def mla_plan_splits(dims, batch, s_q, max_pages, seqlens):
+    """seqlens: host lengths (any int sequence), passed as an int32 array."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(seqlens), dtype=np.int32)
+    if arr.shape != (int(batch),):
+        raise ValueError("seqlens must hold batch lengths")
+    return int(_lib.mla_plan_splits(ctypes.byref(dims), int(batch), int(s_q), int(max_pages),
+                                    arr.ctypes.data_as(ctypes.c_void_p)))
 
 
 def mla_decode_splits(dims, batch, s_q, max_pages, num_splits):

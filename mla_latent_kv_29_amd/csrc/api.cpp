@@ -198,6 +198,32 @@ int32_t mla_default_splits(const mla_dims* dims, int32_t batch, int32_t s_q, int
   return s < 1 ? 1 : s;
 }
 
+// From the lengths: a batch whose longest sequence is within 1/16 of the mean
+// balances with one item per CU, and the page cap above would only add the
+// fixed cost of more items (query rows loaded, partial rows written and
+// merged); any other batch takes the default.
+int32_t mla_plan_splits(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_pages,
+                        const int32_t* seqlens) {
+  if (check_dims(dims) || batch <= 0 || s_q <= 0 || max_pages <= 0 || !seqlens) return 0;
+  long sum = 0;
+  int lmax = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int L = seqlens[b];
+    if (L < 0 || (long)L > (long)max_pages * dims->page_size) return 0;
+    sum += L;
+    lmax = L > lmax ? L : lmax;
+  }
+  const int fallback = mla_default_splits(dims, batch, s_q, max_pages);
+  if (lmax == 0 || (long)lmax * batch * 16 > sum * 17) return fallback;
+  const long items = (long)batch * ((dims->n_heads * s_q + 127) / 128);
+  int s = (int)((TARGET_ITEMS + items - 1) / items);
+  const int pages = (lmax + dims->page_size - 1) / dims->page_size;
+  if (s > pages) s = pages;
+  if (s > max_pages) s = max_pages;
+  if (s > MAX_SPLITS) s = MAX_SPLITS;
+  return s < 1 ? 1 : s;
+}
+
 size_t mla_workspace_bytes(const mla_dims* dims, int32_t act_dtype, int32_t batch, int32_t s_q, int32_t num_splits) {
   if (check_dims(dims) || !valid_act(act_dtype) || batch <= 0 || s_q <= 0 || s_q > MAX_S_Q || num_splits <= 0 ||
       num_splits > MAX_SPLITS)

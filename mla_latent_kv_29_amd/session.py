@@ -43,8 +43,11 @@ class DecodeSession:
         self.lse = torch.empty((self.batch, s_q, H), dtype=torch.float32, device=device)
 
     def set_splits(self, num_splits):
-        """Split plan: num_splits per sequence (0 = the library default), as
-        mla_decode resolves it; the combine takes the same count."""
+        """Split plan: num_splits per sequence (0 = the library's plan from the
+        batch's lengths, mla_plan_splits), as mla_decode resolves it; the
+        combine takes the same count."""
+        if num_splits == 0 and self.batch > 0:
+            num_splits = L.mla_plan_splits(self.cdims, self.batch, self.s_q, self.max_pages, self.lengths)
         s = L.mla_decode_splits(self.cdims, self.batch, self.s_q, self.max_pages, num_splits)
         if s <= 0:
             raise ValueError("invalid split request")

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -46,6 +47,34 @@ def test_page_bytes_layouts():
     assert m.mla_page_bytes(t, m.MLA_FP8_E4M3_E8) == 0
     assert m.mla_page_bytes(d, 4) == 0
     assert m.mla_page_bytes(t, 7) == 0
+
+
+def test_plan_splits_from_lengths():
+    """mla_plan_splits: near-uniform batches get one work item per compute
+    unit (256) without the default's 32-page cap; ragged ones the default."""
+    d = m.make_dims(inputs.V3_DIMS)
+    # config 5: 128 x 8192 tokens, 2 query rows -> 256 items at 1 split
+    assert m.mla_plan_splits(d, 128, 2, 128, [8192] * 128) == 1
+    assert m.mla_default_splits(d, 128, 2, 128) == 4
+    # the headline batch: 64 x 4096 -> 4 splits (256 items), as the default
+    assert m.mla_plan_splits(d, 64, 1, 64, [4096] * 64) == 4
+    # 4 x 128K -> 64 splits
+    assert m.mla_plan_splits(d, 4, 1, 2048, [131072] * 4) == 64
+    # 64 x 4096 with 4 query rows -> 1 split
+    assert m.mla_plan_splits(d, 64, 4, 64, [4096] * 64) == 1
+    # ragged lengths keep the default
+    rng = np.random.default_rng(0)
+    lens = rng.integers(1, 32769, size=128)
+    assert m.mla_plan_splits(d, 128, 1, 512, lens) == m.mla_default_splits(d, 128, 1, 512)
+    # within 1/16 of the mean counts as uniform; more than that does not
+    assert m.mla_plan_splits(d, 2, 1, 64, [4096, 3900]) == 64
+    assert m.mla_plan_splits(d, 2, 1, 64, [4096, 3000]) == m.mla_default_splits(d, 2, 1, 64)
+    # no more splits than pages; all-empty batches take the default
+    assert m.mla_plan_splits(d, 1, 1, 64, [100]) == 2
+    assert m.mla_plan_splits(d, 3, 1, 8, [0, 0, 0]) == m.mla_default_splits(d, 3, 1, 8)
+    # invalid: a length past the table, a negative length
+    assert m.mla_plan_splits(d, 2, 1, 2, [129, 5]) == 0
+    assert m.mla_plan_splits(d, 2, 1, 2, [-1, 5]) == 0
 
 
 def test_default_splits_and_workspace():
