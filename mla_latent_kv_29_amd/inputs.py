@@ -33,7 +33,7 @@ WORKLOADS = {
                              lengths=("fixed", 131072), table="inorder", sigma=0.006),
     "v3_fp8_b128_l8192_sq2": dict(index=4, dims=V3_DIMS, act="bf16", cache="fp8", batch=128, s_q=2,
                                   lengths=("fixed", 8192), table="inorder", sigma=0.006),
-    # config 5's inputs (the same index, so the same values) in the FP8 cache
+    # the inputs of v3_fp8_b128_l8192_sq2 (the same index, so the same values) in the FP8 cache
     # format with power-of-two (UE8M0) tile scales
     "v3_fp8e8_b128_l8192_sq2": dict(index=4, dims=V3_DIMS, act="bf16", cache="fp8e8", batch=128, s_q=2,
                                     lengths=("fixed", 8192), table="inorder", sigma=0.006),

@@ -53,7 +53,7 @@ def test_plan_splits_from_lengths():
     """mla_plan_splits: near-uniform batches get one work item per compute
     unit (256) without the default's 32-page cap; ragged ones the default."""
     d = m.make_dims(inputs.V3_DIMS)
-    # config 5: 128 x 8192 tokens, 2 query rows -> 256 items at 1 split
+    # 128 x 8192 tokens, 2 query rows -> 256 items at 1 split
     assert m.mla_plan_splits(d, 128, 2, 128, [8192] * 128) == 1
     assert m.mla_default_splits(d, 128, 2, 128) == 4
     # the headline batch: 64 x 4096 -> 4 splits (256 items), as the default
