@@ -263,3 +263,24 @@ def test_fp8_formats_agree_bitwise_on_power_of_two_tiles(s_q, splits):
             res[key] = (out.clone(), lse.clone())
         torch.cuda.synchronize()
         assert torch.equal(res["fp8"][0], res["fp8e8"][0]) and torch.equal(res["fp8"][1], res["fp8e8"][1]), kappa
+
+
+@pytest.mark.parametrize("cache", ["fp8", "fp8e8"])
+@pytest.mark.parametrize("lengths,s_q,splits", [([200, 0, 1, 65, 4097], 1, 3), ([70 + 37 * i for i in range(5)], 8, 2)])
+def test_fp8_edge_batches(cache, lengths, s_q, splits):
+    """Both FP8 formats on a batch with an empty sequence (output 0, lse
+    -inf), a one-token sequence, one of 4097 tokens (its last split ends in a
+    one-token stage), and on 8 causal query rows a sequence: against the
+    fp8-emulating oracle (2e-2 max|ref|) and the unquantised one (5e-2)."""
+    case = Case(V3, "bf16", cache, lengths, s_q=s_q, table="shuffled", wl=4, num_splits=splits)
+    tau = tau_of(V3) * 20.0
+    out, lse, _ = case.run(tau)
+    for b, Lb in enumerate(lengths):
+        if Lb == 0:
+            assert np.all(out[b] == 0.0) and np.all(np.isneginf(lse[b])), b
+            continue
+        o_q, _ = case.oracle(b, tau, fp8=True)
+        o, l = case.oracle(b, tau)
+        assert max_abs(out[b], o_q) <= 2e-2 * float(np.abs(o_q).max()), (b, "emulated")
+        assert max_abs(out[b], o) <= 5e-2 * float(np.abs(o).max()), (b, "unquantized")
+        assert max_abs(lse[b], l) <= 5e-2 * max(1.0, float(np.abs(l).max())), b
