@@ -110,13 +110,15 @@ def test_v3_planted_latents_sharp():
         assert max_abs(out[b], o) <= TOL_BF16 * float(np.abs(o).max())
 
 
-def test_v3_score_far_above_first_stage_max():
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp8e8"])
+def test_v3_score_far_above_first_stage_max(cache):
     """A token in a later pipeline stage whose score exceeds the first
     stage's maximum by ~2^150 (log2 units): the kernel must redo the item
-    against the exact maximum and still match the oracle."""
+    against the exact maximum and still match the oracle (for the FP8
+    caches, the oracle on the same quantised latents)."""
     import oracle
     from gpu_common import to_np
-    case = Case(V3, "bf16", "bf16", [300], s_q=1, table="shuffled", wl=1, num_splits=1, planted=(0.05, 0.05))
+    case = Case(V3, "bf16", cache, [300], s_q=1, table="shuffled", wl=1, num_splits=1, planted=(0.05, 0.05))
     tau = tau_of(V3)
     hq = case.hq()
     Wn = case.weights_np()
@@ -130,7 +132,7 @@ def test_v3_score_far_above_first_stage_max():
     case.sess.write(c[star:star + 1].contiguous(), r[star:star + 1].contiguous(), 0, star)
     torch.cuda.synchronize()
     out, lse, _ = case.run(tau)
-    o, l = case.oracle(0, tau, hq=hq)
+    o, l = case.oracle(0, tau, hq=hq, fp8=cache != "bf16")
     assert max_abs(out[0], o) <= TOL_BF16 * float(np.abs(o).max())
     assert abs(lse[0, 0, 0] - l[0, 0]) <= 1e-2 * abs(l[0, 0])
 
