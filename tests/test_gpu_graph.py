@@ -15,11 +15,11 @@ pytestmark = pytest.mark.gpu
 V3 = inputs.V3_DIMS
 
 
-def make_session(lengths, s_q, seed):
+def make_session(lengths, s_q, seed, cache="bf16"):
     lengths = np.asarray(lengths, dtype=np.int64)
     W = inputs.weights(V3, 0.006, torch.bfloat16, DEV, seed, 12)
     bt, pool = inputs.block_table(lengths, V3["page_size"], "shuffled", seed, 12)
-    sess = DecodeSession(V3, "bf16", "bf16", lengths, bt, pool, s_q, 0, DEV)
+    sess = DecodeSession(V3, "bf16", cache, lengths, bt, pool, s_q, 0, DEV)
     gen_h = lambda b, t0, t1: inputs.hidden(V3, b, t0, t1, torch.bfloat16, DEV, seed, 12)
     sess.build_from_h(gen_h, W)
     hq = torch.cat([gen_h(b, int(L) - s_q, int(L)) for b, L in enumerate(lengths)], 0).contiguous()
@@ -69,3 +69,13 @@ def test_fp8w_decode_step_from_a_graph():
     tau = tau_of(V3)
     sess.fp8w_workspace()
     replay_and_check(sess, lambda: sess.decode_fp8w(hq, Wq, tau), lambda: other_sess.decode(hq2, W2, tau))
+
+
+@pytest.mark.parametrize("cache", ["fp8", "fp8e8"])
+def test_fp8_cache_decode_step_from_a_graph(cache):
+    """Both FP8 cache formats (the two-barrier and the one-barrier attention)
+    at 2 query rows a sequence."""
+    sess, W, hq = make_session([300, 65, 2, 1000], 2, 7, cache)
+    other_sess, W2, hq2 = make_session([200, 33], 1, 8)
+    tau = tau_of(V3)
+    replay_and_check(sess, lambda: sess.decode(hq, W, tau), lambda: other_sess.decode(hq2, W2, tau))
